@@ -1,0 +1,213 @@
+"""CPU oracle for the quantized paged KV cache -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never loads it.
+
+The arithmetic lives in ``kvq_oracle.c`` (plain scalar C, compiled with gcc);
+this module only builds it and marshals numpy arrays through ctypes.  Each
+function's docstring names the passage of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_BUILD_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD_DIR, "libkvq_oracle.so")
+
+# Mode numbering shared by the tests' inputs (a plain enumeration, no arithmetic).
+BF16, FP8_PER_TENSOR, FP8_PER_HEAD, FP8_PER_TOKEN_HEAD, INT4_PER_TOKEN_HEAD = range(5)
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE arithmetic: no fast-math, no contraction)."""
+    os.makedirs(_BUILD_DIR, exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", "-frounding-math",
+               "-Wall", "-Wno-unknown-pragmas", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I32 = ctypes.c_int
+    lib.orc_cache_bytes.argtypes = [I32, I64, I64, I64, P, P, P]
+    lib.orc_layer_offsets.argtypes = [I32, I64, I64, I64, P, P, P, P]
+    lib.orc_layer_offsets.restype = I64
+    lib.orc_store.argtypes = [I32, I64, I64, I64, P, P, P, I32, P, P, P, I64, P]
+    lib.orc_gather.argtypes = [I32, I64, I64, I64, P, P, P, I32, P, I64, P, I64, P, P]
+    for name in ("orc_e4m3_encode_n", "orc_e4m3_decode_n", "orc_int4_encode_n",
+                 "orc_float_to_bf16_n"):
+        getattr(lib, name).argtypes = [P, P, I64]
+    lib.orc_quotient_n.argtypes = [P, P, P, I64]
+    lib.orc_dequant_fp8_n.argtypes = [P, P, P, I64]
+    lib.orc_dynamic_scale_n.argtypes = [P, ctypes.c_double, P, I64]
+    lib.orc_num_threads.restype = I32
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class Geometry:
+    """Cache geometry: layers, block size, KV heads, head_dim, per-layer mode and block count."""
+
+    def __init__(self, block_size, num_kv_heads, head_dim, layer_modes, layer_num_blocks):
+        self.bs = int(block_size)
+        self.hkv = int(num_kv_heads)
+        self.hd = int(head_dim)
+        self.modes = _c(layer_modes, np.int32)
+        self.nblocks = _c(layer_num_blocks, np.int64)
+        assert self.modes.shape == self.nblocks.shape
+        self.num_layers = int(self.modes.shape[0])
+
+    def _args(self):
+        return (self.num_layers, self.bs, self.hkv, self.hd, _ptr(self.modes), _ptr(self.nblocks))
+
+
+def cache_bytes(g: Geometry) -> dict:
+    """Byte accounting.  Payload and per-slot scale formulas: "Per-token-head KV
+    cache scale overhead", sections "Per-token-head KV cache scale overhead" and
+    "INT4 makes the metadata fraction larger"; static scale tables: "Per-tensor
+    vs per-head FP8 KV cache scales", "Static per-head metadata is almost free";
+    BF16 layers: "FP8 KV cache layer skipping vs per-head scales"."""
+    out = np.zeros(5, np.int64)
+    _load().orc_cache_bytes(*g._args(), _ptr(out))
+    return dict(zip(("payload", "token_scales", "static_scales", "padding", "total"),
+                    (int(v) for v in out)))
+
+
+def layer_offsets(g: Geometry):
+    """(layer_base[], static_base[], total) of the oracle's own layout."""
+    lb = np.zeros(g.num_layers, np.int64)
+    sb = np.zeros(g.num_layers, np.int64)
+    total = _load().orc_layer_offsets(*g._args(), _ptr(lb), _ptr(sb))
+    return lb, sb, int(total)
+
+
+def new_cache(g: Geometry) -> np.ndarray:
+    """A zeroed host image of the whole cache buffer."""
+    return np.zeros(cache_bytes(g)["total"], np.uint8)
+
+
+def store(g: Geometry, buf: np.ndarray, layer: int, keys_bits, values_bits,
+          slot_mapping, scales=None) -> None:
+    """Quantize-and-store of one layer call ("Per-tensor vs per-head FP8 KV cache
+    scales", "Dynamic per-token-head scales add 3.125 percent": reduce over each
+    new head vector, write the scales, write the codes into the slot)."""
+    assert buf.dtype == np.uint8 and buf.flags.c_contiguous
+    k = _c(keys_bits, np.uint16)
+    v = _c(values_bits, np.uint16)
+    sm = _c(slot_mapping, np.int64)
+    n = int(sm.shape[0])
+    assert k.size == n * g.hkv * g.hd and v.size == k.size
+    mode = int(g.modes[layer])
+    if mode in (FP8_PER_TENSOR, FP8_PER_HEAD):
+        sc = _c(scales, np.float32)
+        assert sc.size == (2 if mode == FP8_PER_TENSOR else 2 * g.hkv)
+        sp = _ptr(sc)
+    else:
+        sc = None
+        sp = None
+    _load().orc_store(*g._args(), _ptr(buf), int(layer), _ptr(k), _ptr(v), _ptr(sm), n, sp)
+
+
+def gather(g: Geometry, buf: np.ndarray, layer: int, block_table, seq_lens):
+    """Dequantizing paged read of one layer: returns (keys, values) as BF16 bits
+    [sum(seq_lens), hkv, hd] ("Per-tensor vs per-head FP8 KV cache scales",
+    "Dynamic per-token-head scales add 3.125 percent": scales are read back
+    when attention consumes the cache)."""
+    bt = _c(block_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    nseq = int(sl.shape[0])
+    maxb = int(bt.shape[1]) if bt.ndim == 2 else 0
+    total = int(np.clip(sl, 0, None).sum())
+    ok = np.zeros((total, g.hkv, g.hd), np.uint16)
+    ov = np.zeros((total, g.hkv, g.hd), np.uint16)
+    _load().orc_gather(*g._args(), _ptr(buf), int(layer), _ptr(bt), maxb, _ptr(sl), nseq,
+                       _ptr(ok), _ptr(ov))
+    return ok, ov
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Float -> OCP E4M3FN code, nearest with ties to even, saturating at 448."""
+    a = _c(v, np.float32)
+    out = np.zeros(a.shape, np.uint8)
+    _load().orc_e4m3_encode_n(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def e4m3_decode(c) -> np.ndarray:
+    a = _c(c, np.uint8)
+    out = np.zeros(a.shape, np.float32)
+    _load().orc_e4m3_decode_n(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def int4_encode(v) -> np.ndarray:
+    a = _c(v, np.float32)
+    out = np.zeros(a.shape, np.int8)
+    _load().orc_int4_encode_n(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def quotient(x, s) -> np.ndarray:
+    """RN32(x / s)."""
+    x = _c(x, np.float32)
+    s = _c(np.broadcast_to(s, x.shape), np.float32)
+    out = np.zeros(x.shape, np.float32)
+    _load().orc_quotient_n(_ptr(x), _ptr(s), _ptr(out), x.size)
+    return out
+
+
+def dynamic_scale(a, qmax: float) -> np.ndarray:
+    """RN32(a / qmax): 448 for FP8, 7 for INT4."""
+    a = _c(a, np.float32)
+    out = np.zeros(a.shape, np.float32)
+    _load().orc_dynamic_scale_n(_ptr(a), float(qmax), _ptr(out), a.size)
+    return out
+
+
+def float_to_bf16(v) -> np.ndarray:
+    a = _c(v, np.float32)
+    out = np.zeros(a.shape, np.uint16)
+    _load().orc_float_to_bf16_n(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def dequant_fp8(codes, s) -> np.ndarray:
+    """BF16_RNE(RN32(decode(code) * s)) as BF16 bits."""
+    c = _c(codes, np.uint8)
+    s = _c(np.broadcast_to(s, c.shape), np.float32)
+    out = np.zeros(c.shape, np.uint16)
+    _load().orc_dequant_fp8_n(_ptr(c), _ptr(s), _ptr(out), c.size)
+    return out
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
