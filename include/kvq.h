@@ -1,0 +1,225 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) quantized paged KV cache.
+ *
+ * The library quantizes new attention K/V vectors into a paged KV cache and
+ * dequantizes them back on read, under the scale layouts described on the
+ * pages "Per-tensor vs per-head FP8 KV cache scales" and "Per-token-head KV
+ * cache scale overhead", with BF16 layers for layer skipping as on "FP8 KV
+ * cache layer skipping vs per-head scales".
+ *
+ * Conventions for every entry point:
+ *  - Plain pointers and sizes only.  "Device" pointers are HIP device memory
+ *    of the current device; "host" pointers are ordinary CPU memory.
+ *  - The caller allocates and owns all device memory (cache buffer, inputs,
+ *    outputs).  The library allocates only the host-side handle and never
+ *    synchronizes a stream.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it and completes asynchronously.
+ *  - Every argument check happens before the first HIP call; on a
+ *    host-detected error nothing is enqueued and nothing is written.
+ *  - Return value 0 is success; negative values are kvq_status errors.
+ *
+ * Numerics (identical, bit for bit, to the CPU oracle that the tests use):
+ *  - FP8 is OCP E4M3FN (bias 7, largest finite 448), round to nearest even,
+ *    saturating at +-448.  Quotients are correctly rounded FP32 x / s.
+ *  - Dynamic FP8 scale s = RN32(absmax / 448); dynamic INT4 scale
+ *    s = RN32(absmax / 7), codes clamp(rint_even(x / s), -8, 7) as
+ *    two's-complement nibbles, even element in the low nibble.
+ *  - An all-zero vector stores s = 0 and zero codes (FP8 zeros keep the sign
+ *    of the input).
+ *  - Dequantized value = BF16_RNE(RN32(decode(code) * s)); BF16 layers are
+ *    copied bit for bit.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define KVQ_API __attribute__((visibility("default")))
+#else
+#define KVQ_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARG = -1,      /* null pointer, out-of-range value, bad scale */
+    KVQ_ERR_MODE_MISMATCH = -2,    /* kvq_store mode differs from the layer's mode */
+    KVQ_ERR_BUFFER_TOO_SMALL = -3, /* cache buffer smaller than kvq_cache_bytes().total */
+    KVQ_ERR_UNSUPPORTED = -4,      /* geometry outside what the kernels handle */
+    KVQ_ERR_HIP = -5               /* a HIP launch or runtime call failed */
+} kvq_status;
+
+/* Per-layer cache mode ("Per-tensor vs per-head FP8 KV cache scales",
+ * section "Per-tensor vs per-head FP8 KV cache scales"; BF16 skip from "FP8
+ * KV cache layer skipping vs per-head scales", "Layer skipping follows
+ * retained-token footprint"; INT4 from "Per-token-head KV cache scale
+ * overhead", "INT4 makes the metadata fraction larger"). */
+typedef enum kvq_mode {
+    KVQ_BF16 = 0,                /* layer kept in BF16 (skipped), 2 B per element */
+    KVQ_FP8_PER_TENSOR = 1,      /* one K and one V FP32 scale per layer */
+    KVQ_FP8_PER_HEAD = 2,        /* one K and one V FP32 scale per layer and KV head */
+    KVQ_FP8_PER_TOKEN_HEAD = 3,  /* FP32 K and V scales beside every token-head slot */
+    KVQ_INT4_PER_TOKEN_HEAD = 4  /* packed INT4 codes, same two FP32 scales per slot */
+} kvq_mode;
+
+/* Largest num_kv_heads a KVQ_FP8_PER_HEAD layer accepts. */
+#define KVQ_MAX_STATIC_KV_HEADS 256
+
+/* Cache geometry.  All pointers are host memory, read during the call only.
+ *  num_layers       >= 1
+ *  block_size       tokens per block; a power of two in [1, 1024]
+ *  num_kv_heads     >= 1
+ *  head_dim         64, 128 or 256
+ *  layer_mode       [num_layers] kvq_mode values
+ *  layer_num_blocks [num_layers] blocks of each layer, >= 0 (a sliding
+ *                   layer may hold only window / block_size blocks) */
+typedef struct kvq_cache_config {
+    int32_t num_layers;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    const int32_t* layer_mode;
+    const int64_t* layer_num_blocks;
+} kvq_cache_config;
+
+/* Byte accounting of a cache buffer.
+ *  payload       K and V code bytes of all layers (1 B/element FP8,
+ *                0.5 B INT4, 2 B BF16)
+ *  token_scales  8 B per token-head slot of the per-token-head layers
+ *  static_scales 8 B per per-tensor layer, 8 * num_kv_heads B per per-head layer
+ *  padding       bytes added to start each layer on a 256-byte boundary
+ *  total         payload + token_scales + static_scales + padding: the size
+ *                of the device buffer kvq_create_cache needs */
+typedef struct kvq_bytes {
+    uint64_t payload;
+    uint64_t token_scales;
+    uint64_t static_scales;
+    uint64_t padding;
+    uint64_t total;
+} kvq_bytes;
+
+/* Opaque host handle describing a cache laid out in caller-owned memory. */
+typedef struct kvq_cache kvq_cache;
+
+/*
+ * kvq_cache_bytes -- byte accounting of a geometry; pure host arithmetic, no
+ * device call.  Payload and per-slot scale formulas: "Per-token-head KV cache
+ * scale overhead", sections "Per-token-head KV cache scale overhead" (payload
+ * and metadata per retained token), "The FP8 scale tax is 4 divided by head
+ * size", "INT4 makes the metadata fraction larger" and "Convert bytes into
+ * block capacity" (whole blocks of block_size tokens); static scale bytes:
+ * "Per-tensor vs per-head FP8 KV cache scales", "Static per-head metadata is
+ * almost free"; BF16 layers: "FP8 KV cache layer skipping vs per-head scales",
+ * "Layer skipping follows retained-token footprint".
+ *   cfg  host, read only.  out: host, written on success.
+ *   Errors: KVQ_ERR_INVALID_ARG (null pointer, bad value),
+ *           KVQ_ERR_UNSUPPORTED (head_dim or block_size not supported).
+ *
+ * Layout of the buffer: layers in order, each starting on a 256-byte
+ * boundary; layer l is layer_num_blocks[l] blocks, each block
+ *   codes [block_size][num_kv_heads][K, V][row_bytes]   then, per-token-head
+ *   modes only, scales [block_size][num_kv_heads][K, V] FP32,
+ * where row_bytes is head_dim (FP8), head_dim/2 (INT4) or 2*head_dim (BF16).
+ * After the last layer (256-byte aligned) comes the static scale table:
+ * per-tensor layers [sK, sV], per-head layers [sK[0..H), sV[0..H)], in layer
+ * order.  The slot of (block, position, KV head) holds its K data, K scale,
+ * V data and V scale as the pages describe, with the scales grouped at the
+ * end of the block so that code rows stay 16-byte aligned.
+ */
+KVQ_API kvq_status kvq_cache_bytes(const kvq_cache_config* cfg, kvq_bytes* out);
+
+/*
+ * kvq_create_cache -- describe a cache that lives in dev_mem.  No device call
+ * is made; the memory is not touched (zero it yourself if unwritten slots
+ * must read as zero).
+ *   cfg        host geometry (copied).
+ *   dev_mem    device pointer, 256-byte aligned, dev_bytes >= total.
+ *   out        receives the handle; free it with kvq_destroy_cache.
+ *   Errors: KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_BUFFER_TOO_SMALL.
+ * The buffer must outlive the handle.
+ */
+KVQ_API kvq_status kvq_create_cache(const kvq_cache_config* cfg, void* dev_mem,
+                            uint64_t dev_bytes, kvq_cache** out);
+
+/* kvq_destroy_cache -- free the host handle (not the device buffer).  NULL is
+ * accepted. */
+KVQ_API kvq_status kvq_destroy_cache(kvq_cache* c);
+
+/*
+ * kvq_store -- quantize num_tokens new K and V vectors of one layer and
+ * scatter them into their cache slots.  "Per-tensor vs per-head FP8 KV cache
+ * scales", sections "Per-tensor vs per-head FP8 KV cache scales" (the three
+ * scale layouts; the dynamic one measures each new K or V vector over its
+ * head dimension) and "Dynamic per-token-head scales add 3.125 percent" (a
+ * reduction over each new head vector, then the scales are written beside
+ * the data); "Per-token-head KV cache scale overhead", "The FP8 scale tax is 4
+ * divided by head size" (slot = K data, K scale, V data, V scale, indexed by
+ * block, token position and KV head) and "INT4 makes the metadata fraction
+ * larger" (packed INT4 at half width with the same two FP32 scales).
+ *   keys, values   device, BF16 [num_tokens][num_kv_heads][head_dim], contiguous,
+ *                  16-byte aligned.
+ *   slot_mapping   device, int64 [num_tokens]; token t goes to block
+ *                  slot / block_size, position slot % block_size.  A negative
+ *                  slot, or one >= the layer's blocks * block_size, is not
+ *                  stored (ring buffers of sliding layers use -1 for tokens
+ *                  outside the window).  Two tokens with the same slot in one
+ *                  call race (undefined which one lands).
+ *   mode           must equal the layer's mode (else KVQ_ERR_MODE_MISMATCH).
+ *   scales         host FP32.  KVQ_FP8_PER_TENSOR: [sK, sV].
+ *                  KVQ_FP8_PER_HEAD: [sK[0..H), sV[0..H)].  Other modes: NULL.
+ *                  Positive and finite.  The first call on a static layer
+ *                  writes them into the cache's static table; later calls
+ *                  pass NULL or the identical values (else KVQ_ERR_INVALID_ARG).
+ *   num_tokens == 0 is a no-op returning KVQ_OK; num_tokens * num_kv_heads
+ *   must stay below 2^31.
+ *   Errors: KVQ_ERR_INVALID_ARG, KVQ_ERR_MODE_MISMATCH, KVQ_ERR_UNSUPPORTED
+ *           (as for kvq_gather_dequant), KVQ_ERR_HIP.
+ * Concurrent kvq_store calls on the same handle and layer are not allowed.
+ */
+KVQ_API kvq_status kvq_store(kvq_cache* c, int32_t layer, const void* keys, const void* values,
+                     const int64_t* slot_mapping, int64_t num_tokens,
+                     kvq_mode mode, const float* scales, void* stream);
+
+/*
+ * kvq_gather_dequant -- read one layer's cached tokens of num_seqs sequences
+ * through their block tables and write them back as BF16.  The scales are
+ * read back when the cache is consumed ("Per-tensor vs per-head FP8 KV cache
+ * scales", "Dynamic per-token-head scales add 3.125 percent"); blocks are the
+ * fixed-size pages of "Per-token-head KV cache scale overhead", "Convert
+ * bytes into block capacity".
+ *   block_table         device, int32 [num_seqs][max_blocks_per_seq]: physical
+ *                       block of each logical block.
+ *   seq_lens            device, int32 [num_seqs]: tokens of each sequence
+ *                       (negative counts as 0); must not exceed
+ *                       max_blocks_per_seq * block_size.
+ *   out_keys, out_values device, BF16 [sum(seq_lens)][num_kv_heads][head_dim],
+ *                       16-byte aligned; sequence b starts at row
+ *                       sum(seq_lens[0..b)).  Token t of sequence b comes from
+ *                       block block_table[b][t / block_size], position
+ *                       t % block_size.
+ *   A block-table entry outside [0, layer blocks) leaves its tokens' output
+ *   rows unwritten, as do tokens beyond max_blocks_per_seq * block_size.
+ *   A static-scale layer must have been stored to at least once.
+ *   num_seqs == 0 is a no-op returning KVQ_OK.
+ *   Errors: KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED (block bytes not a
+ *           multiple of 16, i.e. an odd block_size * num_kv_heads with a
+ *           per-token-head mode), KVQ_ERR_HIP.
+ */
+KVQ_API kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              int32_t num_seqs, void* out_keys, void* out_values,
+                              void* stream);
+
+/* kvq_status_string -- static description of a status code. */
+KVQ_API const char* kvq_status_string(kvq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

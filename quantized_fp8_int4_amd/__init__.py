@@ -1,0 +1,219 @@
+"""MI355X-native quantized paged KV cache (kvq): Python binding of libkvq.so.
+
+The binding marshals arguments to the C ABI declared in include/kvq.h and
+nothing else: every step of store and gather runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  If the
+library has not been built, importing the binding raises; there is no CPU
+fallback.
+
+    import quantized_fp8_int4_amd as kvq
+    cfg = kvq.CacheConfig(block_size=16, num_kv_heads=8, head_dim=128,
+                          layer_modes=[kvq.FP8_PER_TOKEN_HEAD] * 32,
+                          layer_num_blocks=[2048] * 32)
+    cache = kvq.Cache(cfg, device="cuda")
+    cache.store(layer, keys, values, slot_mapping)
+    k, v = cache.gather_dequant(layer, block_table, seq_lens)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch  # loads the HIP runtime that libkvq.so then shares
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_build", "libkvq.so")
+
+# kvq_mode
+BF16 = 0
+FP8_PER_TENSOR = 1
+FP8_PER_HEAD = 2
+FP8_PER_TOKEN_HEAD = 3
+INT4_PER_TOKEN_HEAD = 4
+MODE_NAMES = {BF16: "bf16", FP8_PER_TENSOR: "fp8_per_tensor", FP8_PER_HEAD: "fp8_per_head",
+              FP8_PER_TOKEN_HEAD: "fp8_per_token_head", INT4_PER_TOKEN_HEAD: "int4_per_token_head"}
+
+# kvq_status
+OK, ERR_INVALID_ARG, ERR_MODE_MISMATCH, ERR_BUFFER_TOO_SMALL, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4, -5
+
+EXPORTED_SYMBOLS = ("kvq_cache_bytes", "kvq_create_cache", "kvq_destroy_cache", "kvq_store",
+                    "kvq_gather_dequant", "kvq_status_string")
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("layer_mode", ctypes.POINTER(ctypes.c_int32)),
+                ("layer_num_blocks", ctypes.POINTER(ctypes.c_int64))]
+
+
+class _Bytes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("payload", "token_scales", "static_scales", "padding", "total")]
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libkvq.so is not built ({LIB_PATH}); run `python -m quantized_fp8_int4_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.kvq_cache_bytes.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Bytes)]
+    lib.kvq_create_cache.argtypes = [ctypes.POINTER(_Config), P, ctypes.c_uint64, ctypes.POINTER(P)]
+    lib.kvq_destroy_cache.argtypes = [P]
+    lib.kvq_store.argtypes = [P, I32, P, P, P, I64, ctypes.c_int, P, P]
+    lib.kvq_gather_dequant.argtypes = [P, I32, P, I32, P, I32, P, P, P]
+    lib.kvq_status_string.argtypes = [ctypes.c_int]
+    lib.kvq_status_string.restype = ctypes.c_char_p
+    for name in EXPORTED_SYMBOLS[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+_lib = _load_library()
+
+
+class KVQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.kvq_status_string(status).decode()} ({status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise KVQError(status, where)
+
+
+@dataclass
+class CacheConfig:
+    """kvq_cache_config: block_size (power of two <= 1024), num_kv_heads,
+    head_dim (64/128/256), and per layer a mode and a block count."""
+    block_size: int
+    num_kv_heads: int
+    head_dim: int
+    layer_modes: Sequence[int]
+    layer_num_blocks: Sequence[int]
+
+    def _c(self):
+        n = len(self.layer_modes)
+        modes = (ctypes.c_int32 * n)(*[int(m) for m in self.layer_modes])
+        blocks = (ctypes.c_int64 * n)(*[int(b) for b in self.layer_num_blocks])
+        cfg = _Config(n, int(self.block_size), int(self.num_kv_heads), int(self.head_dim),
+                      ctypes.cast(modes, ctypes.POINTER(ctypes.c_int32)),
+                      ctypes.cast(blocks, ctypes.POINTER(ctypes.c_int64)))
+        return cfg, (modes, blocks)          # keep the arrays alive with the struct
+
+
+def kvq_cache_bytes(cfg: CacheConfig) -> dict:
+    c, keep = cfg._c()
+    out = _Bytes()
+    _check(_lib.kvq_cache_bytes(ctypes.byref(c), ctypes.byref(out)), "kvq_cache_bytes")
+    return {n: int(getattr(out, n)) for n, _ in _Bytes._fields_}
+
+
+def kvq_create_cache(cfg: CacheConfig, dev_ptr: int, dev_bytes: int) -> ctypes.c_void_p:
+    c, keep = cfg._c()
+    h = ctypes.c_void_p()
+    _check(_lib.kvq_create_cache(ctypes.byref(c), ctypes.c_void_p(dev_ptr), int(dev_bytes), ctypes.byref(h)),
+           "kvq_create_cache")
+    return h
+
+
+def kvq_destroy_cache(handle) -> None:
+    _check(_lib.kvq_destroy_cache(handle), "kvq_destroy_cache")
+
+
+def _stream_ptr(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def kvq_store(handle, layer: int, keys: torch.Tensor, values: torch.Tensor, slot_mapping: torch.Tensor,
+              mode: int, scales=None, stream=None) -> None:
+    """keys/values: bf16 [N, Hkv, hd] on the device; slot_mapping: int64 [N] on
+    the device; scales: host float32 values for static layers, else None."""
+    n = int(slot_mapping.numel())
+    kp = _dev(keys, torch.bfloat16, "keys") if n else 0
+    vp = _dev(values, torch.bfloat16, "values") if n else 0
+    sp = _dev(slot_mapping, torch.int64, "slot_mapping") if n else 0
+    if n and (keys.shape != values.shape or keys.shape[0] != n):
+        raise ValueError("keys, values and slot_mapping disagree in token count")
+    sc = None
+    if scales is not None:
+        if isinstance(scales, torch.Tensor):
+            scales = scales.detach().cpu().to(torch.float32).reshape(-1).tolist()
+        vals = [float(x) for x in scales]
+        sc = (ctypes.c_float * len(vals))(*vals)
+    _check(_lib.kvq_store(handle, int(layer), ctypes.c_void_p(kp), ctypes.c_void_p(vp), ctypes.c_void_p(sp),
+                          n, int(mode), sc, _stream_ptr(stream, keys.device if n else None)), "kvq_store")
+
+
+def kvq_gather_dequant(handle, layer: int, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                       out_keys: torch.Tensor, out_values: torch.Tensor, stream=None) -> None:
+    """block_table: int32 [num_seqs, max_blocks] on the device; seq_lens: int32
+    [num_seqs] on the device; out_*: bf16 [sum(seq_lens), Hkv, hd] on the device."""
+    num_seqs = int(seq_lens.numel())
+    if num_seqs == 0:
+        return
+    bt = _dev(block_table, torch.int32, "block_table")
+    sl = _dev(seq_lens, torch.int32, "seq_lens")
+    ok = _dev(out_keys, torch.bfloat16, "out_keys")
+    ov = _dev(out_values, torch.bfloat16, "out_values")
+    if block_table.dim() != 2 or block_table.shape[0] != num_seqs:
+        raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
+    _check(_lib.kvq_gather_dequant(handle, int(layer), ctypes.c_void_p(bt), int(block_table.shape[1]),
+                                   ctypes.c_void_p(sl), num_seqs, ctypes.c_void_p(ok), ctypes.c_void_p(ov),
+                                   _stream_ptr(stream, out_keys.device)), "kvq_gather_dequant")
+
+
+class Cache:
+    """A cache buffer (zeroed torch uint8 tensor of kvq_cache_bytes().total
+    bytes) plus its library handle."""
+
+    def __init__(self, cfg: CacheConfig, device="cuda", buffer: Optional[torch.Tensor] = None):
+        self.cfg = cfg
+        self.bytes = kvq_cache_bytes(cfg)
+        if buffer is None:
+            buffer = torch.zeros(self.bytes["total"], dtype=torch.uint8, device=device)
+        if buffer.dtype != torch.uint8 or buffer.numel() < self.bytes["total"]:
+            raise ValueError("buffer must be uint8 with at least kvq_cache_bytes().total elements")
+        self.buffer = buffer
+        self.device = buffer.device
+        self.handle = kvq_create_cache(cfg, buffer.data_ptr(), buffer.numel())
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            kvq_destroy_cache(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def store(self, layer, keys, values, slot_mapping, scales=None, stream=None):
+        kvq_store(self.handle, layer, keys, values, slot_mapping, self.cfg.layer_modes[layer], scales, stream)
+
+    def gather_dequant(self, layer, block_table, seq_lens, total_tokens=None, out=None, stream=None):
+        """Returns (keys, values) bf16 [sum(seq_lens), Hkv, hd].  Pass
+        total_tokens (or out) to avoid reading seq_lens back to the host."""
+        if out is None:
+            if total_tokens is None:
+                total_tokens = int(seq_lens.clamp(min=0).sum().item())
+            shape = (int(total_tokens), self.cfg.num_kv_heads, self.cfg.head_dim)
+            out = (torch.empty(shape, dtype=torch.bfloat16, device=self.device),
+                   torch.empty(shape, dtype=torch.bfloat16, device=self.device))
+        kvq_gather_dequant(self.handle, layer, block_table, seq_lens, out[0], out[1], stream)
+        return out

@@ -1,0 +1,189 @@
+// kvq_api.cpp -- the C ABI declared in include/kvq.h: argument validation,
+// static-scale bookkeeping and kernel dispatch.  Every check runs before the
+// first HIP call, so a rejected call enqueues nothing and writes nothing.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kvq_internal.h"
+
+struct kvq_cache {
+    kvq::Layout layout;
+    uint8_t* dev = nullptr;
+    uint64_t dev_bytes = 0;
+    // Static scales of each layer as first stored (empty until then).
+    std::vector<std::vector<float>> static_values;
+};
+
+namespace {
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* v = std::getenv("KVQ_LOG");
+        return v && v[0] && v[0] != '0';
+    }();
+    return on;
+}
+
+const char* mode_name(int32_t m) {
+    switch (m) {
+        case KVQ_BF16: return "bf16";
+        case KVQ_FP8_PER_TENSOR: return "fp8_per_tensor";
+        case KVQ_FP8_PER_HEAD: return "fp8_per_head";
+        case KVQ_FP8_PER_TOKEN_HEAD: return "fp8_per_token_head";
+        case KVQ_INT4_PER_TOKEN_HEAD: return "int4_per_token_head";
+        default: return "?";
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status s) {
+    switch (s) {
+        case KVQ_OK: return "ok";
+        case KVQ_ERR_INVALID_ARG: return "invalid argument";
+        case KVQ_ERR_MODE_MISMATCH: return "mode does not match the layer's mode";
+        case KVQ_ERR_BUFFER_TOO_SMALL: return "cache buffer smaller than kvq_cache_bytes().total";
+        case KVQ_ERR_UNSUPPORTED: return "unsupported geometry";
+        case KVQ_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+kvq_status kvq_cache_bytes(const kvq_cache_config* cfg, kvq_bytes* out) {
+    if (!out) return KVQ_ERR_INVALID_ARG;
+    kvq::Layout L;
+    const kvq_status st = kvq::build_layout(cfg, &L);
+    if (st != KVQ_OK) return st;
+    *out = L.bytes;
+    return KVQ_OK;
+}
+
+kvq_status kvq_create_cache(const kvq_cache_config* cfg, void* dev_mem, uint64_t dev_bytes,
+                            kvq_cache** out) {
+    if (!out || !dev_mem) return KVQ_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(dev_mem) & 255u) != 0) return KVQ_ERR_INVALID_ARG;
+    kvq::Layout L;
+    const kvq_status st = kvq::build_layout(cfg, &L);
+    if (st != KVQ_OK) return st;
+    if (dev_bytes < L.bytes.total) return KVQ_ERR_BUFFER_TOO_SMALL;
+    kvq_cache* c = new (std::nothrow) kvq_cache;
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    c->layout = std::move(L);
+    c->dev = static_cast<uint8_t*>(dev_mem);
+    c->dev_bytes = dev_bytes;
+    c->static_values.resize(c->layout.num_layers);
+    *out = c;
+    return KVQ_OK;
+}
+
+kvq_status kvq_destroy_cache(kvq_cache* c) {
+    delete c;
+    return KVQ_OK;
+}
+
+kvq_status kvq_store(kvq_cache* c, int32_t layer, const void* keys, const void* values,
+                     const int64_t* slot_mapping, int64_t num_tokens, kvq_mode mode,
+                     const float* scales, void* stream) {
+    if (!c || layer < 0 || layer >= c->layout.num_layers || num_tokens < 0) return KVQ_ERR_INVALID_ARG;
+    const kvq::Layout& L = c->layout;
+    const int32_t lmode = L.mode[layer];
+    if (static_cast<int32_t>(mode) != lmode) return KVQ_ERR_MODE_MISMATCH;
+    const bool is_static = kvq::has_static_scales(lmode);
+    const int n_static = lmode == KVQ_FP8_PER_TENSOR ? 2 : 2 * L.num_kv_heads;
+    if (!is_static && scales) return KVQ_ERR_INVALID_ARG;
+    std::vector<float>& known = c->static_values[layer];
+    bool first_static = false;
+    if (is_static) {
+        if (known.empty()) {
+            if (!scales) return KVQ_ERR_INVALID_ARG;
+            for (int i = 0; i < n_static; ++i)
+                if (!(std::isfinite(scales[i]) && scales[i] > 0.0f)) return KVQ_ERR_INVALID_ARG;
+            first_static = true;
+        } else if (scales && std::memcmp(scales, known.data(), sizeof(float) * n_static) != 0) {
+            return KVQ_ERR_INVALID_ARG;
+        }
+    }
+    if (num_tokens == 0 && !first_static) return KVQ_OK;
+    if (num_tokens > 0) {
+        if (!keys || !values || !slot_mapping) return KVQ_ERR_INVALID_ARG;
+        if (!aligned16(keys) || !aligned16(values) || (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+            return KVQ_ERR_INVALID_ARG;
+        if (num_tokens * static_cast<int64_t>(L.num_kv_heads) >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
+    }
+    if (L.block_bytes[layer] % 16 != 0) return KVQ_ERR_UNSUPPORTED;
+
+    float* static_dev = reinterpret_cast<float*>(c->dev + L.static_base[layer]);
+    if (first_static) {
+        const int e = kvq::launch_write_static(static_dev, scales, n_static, stream);
+        if (e != 0) return KVQ_ERR_HIP;
+        known.assign(scales, scales + n_static);
+    }
+    if (num_tokens == 0 || L.num_blocks[layer] == 0) return KVQ_OK;
+
+    kvq::StoreLaunch a;
+    a.keys = keys;
+    a.values = values;
+    a.slots = slot_mapping;
+    a.layer = c->dev + L.layer_base[layer];
+    a.static_scales = static_dev;
+    a.num_rows = num_tokens * L.num_kv_heads;
+    a.num_slots = L.num_blocks[layer] * static_cast<int64_t>(L.block_size);
+    a.block_bytes = L.block_bytes[layer];
+    a.code_bytes = L.code_bytes[layer];
+    a.num_kv_heads = L.num_kv_heads;
+    a.bs_log2 = L.bs_log2;
+    a.head_dim = L.head_dim;
+    a.mode = lmode;
+    if (log_enabled())
+        std::fprintf(stderr, "[kvq] store layer=%d mode=%s hd=%d tokens=%lld rows=%lld\n", layer,
+                     mode_name(lmode), L.head_dim, static_cast<long long>(num_tokens),
+                     static_cast<long long>(a.num_rows));
+    return kvq::launch_store(a, stream) == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                              void* out_keys, void* out_values, void* stream) {
+    if (!c || layer < 0 || layer >= c->layout.num_layers || num_seqs < 0) return KVQ_ERR_INVALID_ARG;
+    if (num_seqs == 0) return KVQ_OK;
+    if (max_blocks_per_seq < 1 || !block_table || !seq_lens || !out_keys || !out_values)
+        return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(out_keys) || !aligned16(out_values)) return KVQ_ERR_INVALID_ARG;
+    const kvq::Layout& L = c->layout;
+    const int32_t lmode = L.mode[layer];
+    if (kvq::has_static_scales(lmode) && c->static_values[layer].empty()) return KVQ_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(num_seqs) * max_blocks_per_seq >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
+    if (L.block_bytes[layer] % 16 != 0) return KVQ_ERR_UNSUPPORTED;
+    if (L.num_blocks[layer] == 0) return KVQ_OK;
+
+    kvq::GatherLaunch a;
+    a.layer = c->dev + L.layer_base[layer];
+    a.static_scales = reinterpret_cast<const float*>(c->dev + L.static_base[layer]);
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.out_keys = out_keys;
+    a.out_values = out_values;
+    a.num_blocks = L.num_blocks[layer];
+    a.block_bytes = L.block_bytes[layer];
+    a.code_bytes = L.code_bytes[layer];
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = L.num_kv_heads;
+    a.block_size = L.block_size;
+    a.head_dim = L.head_dim;
+    a.mode = lmode;
+    if (log_enabled())
+        std::fprintf(stderr, "[kvq] gather layer=%d mode=%s hd=%d seqs=%d max_blocks=%d\n", layer,
+                     mode_name(lmode), L.head_dim, num_seqs, max_blocks_per_seq);
+    return kvq::launch_gather(a, stream) == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// kvq_internal.h -- host-side layout description and kernel launchers shared
+// by the C API (kvq_api.cpp), the layout module (kvq_layout.cpp) and the HIP
+// kernels (kvq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <vector>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// Geometry of a cache buffer: where each layer's blocks and static scales
+// live.  Layout as documented for kvq_cache_bytes in kvq.h.
+struct Layout {
+    int32_t num_layers = 0;
+    int32_t block_size = 0;
+    int32_t bs_log2 = 0;
+    int32_t num_kv_heads = 0;
+    int32_t head_dim = 0;
+    std::vector<int32_t> mode;           // kvq_mode per layer
+    std::vector<int64_t> num_blocks;     // blocks per layer
+    std::vector<uint64_t> layer_base;    // byte offset of the layer's first block
+    std::vector<uint64_t> static_base;   // byte offset of the layer's static scales
+    std::vector<uint64_t> block_bytes;   // bytes of one block (codes + scale trailer)
+    std::vector<uint64_t> code_bytes;    // bytes of a block's codes = trailer offset
+    kvq_bytes bytes{};
+};
+
+// Bytes of one K (or V) row of head_dim elements in a layer of this mode.
+uint64_t row_bytes(int32_t mode, int32_t head_dim);
+bool has_token_scales(int32_t mode);
+bool has_static_scales(int32_t mode);
+
+// Validate cfg and fill *out.  No device call.
+kvq_status build_layout(const kvq_cache_config* cfg, Layout* out);
+
+// Division of a row index n < 2^31 by d >= 1: n / d == (n * magic) >> shift
+// (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, with the 31-bit dividend bound).
+struct DivMagic {
+    uint32_t magic;
+    uint32_t shift;
+};
+DivMagic div_magic(uint32_t d);
+
+// ---- kernel launchers (kvq_kernels.hip) --------------------------------
+struct StoreLaunch {
+    const void* keys;
+    const void* values;
+    const int64_t* slots;
+    uint8_t* layer;                // device: layer base
+    const float* static_scales;    // device: this layer's static table entry (static modes)
+    int64_t num_rows;              // num_tokens * num_kv_heads (< 2^31)
+    int64_t num_slots;             // num_blocks * block_size
+    uint64_t block_bytes;
+    uint64_t code_bytes;
+    int32_t num_kv_heads;
+    int32_t bs_log2;
+    int32_t head_dim;
+    int32_t mode;
+};
+
+struct GatherLaunch {
+    const uint8_t* layer;
+    const float* static_scales;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    void* out_keys;
+    void* out_values;
+    int64_t num_blocks;
+    uint64_t block_bytes;
+    uint64_t code_bytes;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t num_kv_heads;
+    int32_t block_size;
+    int32_t head_dim;
+    int32_t mode;
+};
+
+// Each returns 0 on a successful enqueue, else the hipError_t value.
+int launch_store(const StoreLaunch& a, void* stream);
+int launch_gather(const GatherLaunch& a, void* stream);
+int launch_write_static(float* dst, const float* values, int n, void* stream);
+
+}  // namespace kvq

@@ -24,7 +24,7 @@ def _library_bytes():
     return f
 
 
-@pytest.fixture(params=["oracle"])
+@pytest.fixture(params=["oracle", "library"])
 def cache_bytes(request, orc):
     if request.param == "oracle":
         return _oracle_bytes(orc)

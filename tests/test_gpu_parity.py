@@ -1,0 +1,328 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, bit for
+bit (cache bytes, FP32 scales and dequantized BF16), on the same seeded
+inputs.  Small cases span several workgroups plus a ragged tail; full-size
+cases use the workloads' real shapes."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    import quantized_fp8_int4_amd as kvq
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return kvq
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+class Pair:
+    """One geometry held by both sides: a device cache and an oracle image."""
+
+    def __init__(self, kvq, orc, bs, hkv, hd, modes, nblocks):
+        self.kvq, self.orc = kvq, orc
+        self.cfg = kvq.CacheConfig(bs, hkv, hd, modes, nblocks)
+        self.cache = kvq.Cache(self.cfg, device=DEV)
+        self.g = orc.Geometry(bs, hkv, hd, modes, nblocks)
+        self.host = orc.new_cache(self.g)
+        assert self.host.size == self.cache.bytes["total"]
+
+    def store(self, layer, k, v, slots, scales=None):
+        self.cache.store(layer, k.to(DEV), v.to(DEV), slots.to(DEV), scales)
+        sc = None if scales is None else np.asarray(scales, np.float32)
+        self.orc.store(self.g, self.host, layer, _bits(k), _bits(v), slots.cpu().numpy(), sc)
+
+    def assert_buffers_equal(self):
+        torch.cuda.synchronize()
+        dev = self.cache.buffer.cpu().numpy()
+        if not np.array_equal(dev, self.host):
+            bad = np.nonzero(dev != self.host)[0]
+            pytest.fail(f"{bad.size} cache bytes differ; first at {bad[0]}: gpu {dev[bad[0]]:#x} "
+                        f"oracle {self.host[bad[0]]:#x}")
+
+    def gather_and_compare(self, layer, block_table, seq_lens):
+        total = int(np.clip(np.asarray(seq_lens), 0, None).sum())
+        shape = (total, self.cfg.num_kv_heads, self.cfg.head_dim)
+        out = (torch.zeros(shape, dtype=torch.bfloat16, device=DEV),
+               torch.zeros(shape, dtype=torch.bfloat16, device=DEV))
+        bt = torch.as_tensor(np.asarray(block_table), dtype=torch.int32).to(DEV)
+        sl = torch.as_tensor(np.asarray(seq_lens), dtype=torch.int32).to(DEV)
+        self.cache.gather_dequant(layer, bt, sl, out=out)
+        ko, vo = self.orc.gather(self.g, self.host, layer, np.asarray(block_table), np.asarray(seq_lens))
+        for name, d, o in (("keys", out[0], ko), ("values", out[1], vo)):
+            db = _bits(d)
+            if not np.array_equal(db, o):
+                bad = np.argwhere(db != o)
+                pytest.fail(f"gather {name}: {len(bad)} elements differ; first at {tuple(bad[0])}: "
+                            f"gpu {db[tuple(bad[0])]:#06x} oracle {o[tuple(bad[0])]:#06x}")
+
+
+def _adversarial_kv(n, hkv, hd, seed):
+    g = torch.Generator().manual_seed(seed)
+    out = []
+    for _ in range(2):
+        x = torch.randn((n, hkv, hd), generator=g)
+        kinds = torch.randint(0, 8, (n, hkv), generator=g)
+        scale = torch.ones((n, hkv))
+        scale[kinds == 1] = 0.0
+        scale[kinds == 2] = 2.0 ** -130          # BF16 subnormal rows
+        scale[kinds == 3] = 2.0 ** 100
+        scale[kinds == 4] = 2.0 ** -70            # normal but tiny absmax
+        x = x * scale[..., None]
+        e = torch.randint(-40, 40, (n, hkv, hd), generator=g).float()
+        x = torch.where((kinds == 5)[..., None], x * torch.exp2(e), x)
+        x = torch.where((kinds == 6)[..., None] & (torch.rand((n, hkv, hd), generator=g) < 0.5),
+                        -0.0 * x.abs(), x)
+        out.append(x.to(torch.bfloat16))
+    return out
+
+
+MODES = [W.BF16, W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=[W.MODE_NAMES[m] for m in MODES])
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("hkv", [1, 3, 8])
+def test_store_gather_parity_small(kvq, orc, mode, hd, hkv):
+    _flush(f"[parity] mode={W.MODE_NAMES[mode]} hd={hd} hkv={hkv}")
+    bs = 16 if hkv % 2 else 8
+    nblocks, n = 48, 301
+    modes = [W.FP8_PER_TOKEN_HEAD, mode, W.INT4_PER_TOKEN_HEAD]
+    pair = Pair(kvq, orc, bs, hkv, hd, modes, [3, nblocks, 2])
+    rng = np.random.default_rng(hd * 100 + hkv * 7 + mode)
+    k, v = _adversarial_kv(n, hkv, hd, seed=int(rng.integers(1 << 30)))
+    slots = rng.permutation(nblocks * bs)[:n].astype(np.int64)
+    slots[5] = -1
+    slots[17] = nblocks * bs + 3
+    slots[n - 1] = -7
+    scales = None
+    if mode == W.FP8_PER_TENSOR:
+        scales = [0.013, 0.021]
+    elif mode == W.FP8_PER_HEAD:
+        scales = list(rng.uniform(0.001, 0.05, 2 * hkv).astype(np.float32))
+    pair.store(1, k, v, torch.from_numpy(slots), scales)
+    pair.assert_buffers_equal()
+    perm = rng.permutation(nblocks).astype(np.int32)
+    maxb = 20
+    bt = np.full((3, maxb), -1, np.int32)
+    bt[0, :16] = perm[:16]
+    bt[1, :20] = perm[16:36]
+    bt[2, :12] = perm[36:]
+    bt[1, 7] = nblocks + 100                     # out-of-range entry: rows left unwritten
+    seq_lens = [16 * bs - 5, 20 * bs, 0]
+    pair.gather_and_compare(1, bt, seq_lens)
+    pair.gather_and_compare(1, bt, [3, -4, 12 * bs])
+    pair.cache.close()
+
+
+def _exhaustive_rows(start, stride, seed):
+    """Rows of 64 BF16 values: element 0 is a positive absmax a (every
+    stride-th finite BF16 magnitude from start), the others enumerate every
+    BF16 magnitude <= a with random signs."""
+    a = torch.arange(start, 0x7F80, stride, dtype=torch.int32)
+    counts = a + 1
+    rows_per = (counts + 62) // 63
+    row_a = torch.repeat_interleave(a, rows_per)
+    first = torch.repeat_interleave(torch.cumsum(rows_per, 0) - rows_per, rows_per)
+    k = torch.arange(row_a.numel()) - first
+    xb = k[:, None] * 63 + torch.arange(63, dtype=torch.int32)[None, :]
+    lim = torch.repeat_interleave(counts, rows_per)[:, None]
+    xb = torch.where(xb < lim, xb, torch.zeros_like(xb))
+    g = torch.Generator().manual_seed(seed)
+    sign = torch.randint(0, 2, xb.shape, generator=g, dtype=torch.int32) << 15
+    rows = torch.cat([row_a[:, None], xb | sign], dim=1)
+    asign = torch.randint(0, 2, (rows.shape[0],), generator=g, dtype=torch.int32) << 15
+    rows[:, 0] |= asign
+    return rows.to(torch.int16).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD],
+                         ids=["fp8_per_token_head", "int4_per_token_head"])
+def test_exhaustive_absmax_quotients(kvq, orc, mode):
+    """Every 5th positive BF16 absmax paired with every BF16 magnitude below
+    it (K: offsets 1 mod 5; V: 3 mod 5): codes, scales and dequantized values
+    bit-exact, covering subnormal inputs, subnormal scales and huge values."""
+    _flush(f"[exhaustive] mode={W.MODE_NAMES[mode]}")
+    k = _exhaustive_rows(1, 5, seed=1)
+    v = _exhaustive_rows(3, 5, seed=2)
+    n = min(k.shape[0], v.shape[0])
+    n -= n % 16
+    k, v = k[:n].reshape(n, 1, 64), v[:n].reshape(n, 1, 64)
+    # hkv = 2: pair rows so a block holds an even number of token-heads
+    n2 = n // 2
+    k, v = k.reshape(n2, 2, 64), v.reshape(n2, 2, 64)
+    pair = Pair(kvq, orc, 16, 2, 64, [mode], [(n2 + 15) // 16])
+    pair.store(0, k, v, torch.arange(n2, dtype=torch.int64))
+    pair.assert_buffers_equal()
+    nb = (n2 + 15) // 16
+    pair.gather_and_compare(0, np.arange(nb, dtype=np.int32)[None, :], [n2])
+    pair.cache.close()
+
+
+def _all_finite_bf16_rows(hkv):
+    b = torch.arange(0, 1 << 16, dtype=torch.int32)
+    f = b.to(torch.int16).view(torch.bfloat16)
+    f = f[torch.isfinite(f.float())]
+    per = hkv * 64
+    n = (f.numel() + per - 1) // per
+    pad = n * per - f.numel()
+    f = torch.cat([f, f[:pad]])
+    return f.reshape(n, hkv, 64)
+
+
+STATIC_SCALES = [1.0, 3.0, 1.0 / 3.0, 2.0 ** -70, 2.0 ** 70, 1e-40, 3e38, 0.0123]
+
+
+def test_static_scales_every_bf16_value(kvq, orc):
+    """Per-tensor layers with scales 1, 3, 1/3, 2^-70, 2^70, an FP32 subnormal,
+    3e38 and 0.0123 applied to every finite BF16 value: saturation, prescaled
+    division and the E4M3 conversion over the whole input range."""
+    _flush("[static] per-tensor all-bf16")
+    x = _all_finite_bf16_rows(2)
+    n = x.shape[0]
+    L = len(STATIC_SCALES)
+    pair = Pair(kvq, orc, 16, 2, 64, [W.FP8_PER_TENSOR] * L, [(n + 15) // 16] * L)
+    for layer, s in enumerate(STATIC_SCALES):
+        sv = float(np.float32(s))
+        pair.store(layer, x, x.flip(0).contiguous(), torch.arange(n, dtype=torch.int64), [sv, sv])
+    pair.assert_buffers_equal()
+    nb = (n + 15) // 16
+    for layer in range(L):
+        pair.gather_and_compare(layer, np.arange(nb, dtype=np.int32)[None, :], [n])
+    pair.cache.close()
+
+
+def test_static_per_head_extreme_scales(kvq, orc):
+    _flush("[static] per-head extremes")
+    hkv = 8
+    x = _all_finite_bf16_rows(hkv)
+    n = x.shape[0]
+    sc = [float(np.float32(s)) for s in STATIC_SCALES]
+    pair = Pair(kvq, orc, 16, hkv, 64, [W.FP8_PER_HEAD], [(n + 15) // 16])
+    pair.store(0, x, x, torch.arange(n, dtype=torch.int64), sc + sc[::-1])
+    pair.assert_buffers_equal()
+    pair.gather_and_compare(0, np.arange((n + 15) // 16, dtype=np.int32)[None, :], [n])
+    # static scales are fixed after first use
+    pair.cache.store(0, x.to(DEV), x.to(DEV), torch.arange(n, dtype=torch.int64, device=DEV))
+    with pytest.raises(kvq.KVQError):
+        pair.cache.store(0, x.to(DEV), x.to(DEV), torch.arange(n, dtype=torch.int64, device=DEV),
+                         [1.0] * (2 * hkv))
+    pair.cache.close()
+
+
+@pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.FP8_PER_TENSOR, W.FP8_PER_HEAD],
+                         ids=["fp8_per_token_head", "fp8_per_tensor", "fp8_per_head"])
+def test_gqa32_layer_full_size(kvq, orc, mode):
+    """32-layer GQA shape, one layer call at full size: 8 sequences x 4096
+    tokens, 8 KV heads, head_dim 128, permuted block table; every cache byte and
+    every gathered value compared."""
+    cfgw = W.WORKLOADS["gqa32"]
+    layer = 5
+    _flush(f"[gqa32] mode={W.MODE_NAMES[mode]} layer={layer}")
+    n = cfgw["num_seqs"] * cfgw["seq_len"]
+    nblocks = n // 16
+    k, v = W.gqa_kv(n, 8, 128, seed=1000 + layer, device=DEV)
+    bt = W.permuted_block_table(cfgw["num_seqs"], cfgw["seq_len"] // 16, nblocks, seed=1000)
+    slots = W.slots_from_block_table(bt, [cfgw["seq_len"]] * cfgw["num_seqs"], 16)
+    scales = None
+    if mode == W.FP8_PER_TENSOR:
+        scales = [1.0, 1.0]
+    elif mode == W.FP8_PER_HEAD:
+        kc, vc = W.gqa_kv(4096, 8, 128, seed=2000 + layer, device=DEV)
+        scales = W.static_scales_from_amax(W.calibration_amax(kc, vc)).tolist()
+    pair = Pair(kvq, orc, 16, 8, 128, [mode], [nblocks])
+    pair.store(0, k.cpu(), v.cpu(), slots, scales)
+    pair.assert_buffers_equal()
+    pair.gather_and_compare(0, bt.numpy(), [cfgw["seq_len"]] * cfgw["num_seqs"])
+    pair.cache.close()
+
+
+def test_gptoss_sliding_and_full_layers(kvq, orc):
+    """gpt-oss shape: a sliding layer kept BF16 in a 128-slot ring buffer and a
+    full layer in per-token-head FP8, head_dim 64, 32768 tokens."""
+    _flush("[gptoss]")
+    T, Wn = 32768, 128
+    modes = [W.BF16, W.FP8_PER_TOKEN_HEAD]
+    pair = Pair(kvq, orc, 16, 8, 64, modes, [Wn // 16, T // 16])
+    for layer in range(2):
+        k, v = W.normal_kv(T, 8, 64, seed=4000 + layer, device=DEV)
+        slots = W.ring_slots(T, Wn) if layer == 0 else torch.arange(T, dtype=torch.int64)
+        pair.store(layer, k.cpu(), v.cpu(), slots)
+    pair.assert_buffers_equal()
+    pair.gather_and_compare(0, W.ring_block_table(Wn, 16).numpy(), [Wn])
+    pair.gather_and_compare(1, np.arange(T // 16, dtype=np.int32)[None, :], [T])
+    pair.cache.close()
+
+
+@pytest.mark.parametrize("mode,hd", [(W.FP8_PER_TOKEN_HEAD, 128), (W.INT4_PER_TOKEN_HEAD, 128),
+                                     (W.FP8_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 64)],
+                         ids=["fp8-128", "int4-128", "fp8-64", "int4-64"])
+def test_decode_append_reduced(kvq, orc, mode, hd):
+    """Decode pattern at reduced context: 64 sequences x 512-token prefill in a
+    random free list of blocks, then 20 steps appending one token per sequence
+    (crossing into new blocks), with a full-context gather after some steps."""
+    _flush(f"[decode-reduced] mode={W.MODE_NAMES[mode]} hd={hd}")
+    S, ctx, steps = 64, 512, 20
+    maxb = (ctx + steps + 15) // 16
+    nblocks = S * maxb + 7
+    st = W.DecodeState(S, 16, nblocks, maxb, seed=5000)
+    pair = Pair(kvq, orc, 16, 8, hd, [mode], [nblocks])
+    slots = []
+    for b in range(S):
+        slots += st.append(b, ctx)
+    k, v = W.normal_kv(S * ctx, 8, hd, seed=5001, device=DEV)
+    pair.store(0, k.cpu(), v.cpu(), torch.tensor(slots, dtype=torch.int64))
+    for step in range(steps):
+        sl = [st.append(b, 1)[0] for b in range(S)]
+        k, v = W.normal_kv(S, 8, hd, seed=5100 + step, device=DEV)
+        pair.store(0, k.cpu(), v.cpu(), torch.tensor(sl, dtype=torch.int64))
+        if step in (0, 15, steps - 1):
+            pair.gather_and_compare(0, st.block_table.numpy(), st.seq_lens)
+    pair.assert_buffers_equal()
+    pair.cache.close()
+
+
+def test_long80_layer_full_size(kvq, orc):
+    """80-layer long-context shape, one layer: a single 131072-token sequence,
+    heads alternating N(0,1) and Student-t(3), per-token-head FP8, full
+    store and full gather compared."""
+    _flush("[long80] one layer")
+    T = 131072
+    k, v = W.heavy_tail_kv(T, 8, 128, seed=3000, device=DEV)
+    pair = Pair(kvq, orc, 16, 8, 128, [W.FP8_PER_TOKEN_HEAD], [T // 16])
+    pair.store(0, k.cpu(), v.cpu(), torch.arange(T, dtype=torch.int64))
+    pair.assert_buffers_equal()
+    pair.gather_and_compare(0, np.arange(T // 16, dtype=np.int32)[None, :], [T])
+    pair.cache.close()
+
+
+def test_edge_cases(kvq, orc):
+    """Zero tokens, zero sequences, a layer with no blocks, tokens beyond the
+    block table, and repeated stores of the same tokens."""
+    _flush("[edge]")
+    pair = Pair(kvq, orc, 16, 2, 64, [W.FP8_PER_TOKEN_HEAD, W.BF16], [4, 0])
+    e = torch.empty((0, 2, 64), dtype=torch.bfloat16, device=DEV)
+    pair.cache.store(0, e, e, torch.empty(0, dtype=torch.int64, device=DEV))
+    k, v = W.normal_kv(64, 2, 64, seed=9, device=DEV)
+    pair.cache.store(1, k, v, torch.arange(64, dtype=torch.int64, device=DEV))   # no blocks: nothing stored
+    pair.store(0, k.cpu(), v.cpu(), torch.arange(64, dtype=torch.int64))
+    pair.store(0, k.cpu(), v.cpu(), torch.arange(64, dtype=torch.int64))           # idempotent
+    pair.assert_buffers_equal()
+    out = pair.cache.gather_dequant(0, torch.zeros((0, 4), dtype=torch.int32, device=DEV),
+                                    torch.zeros(0, dtype=torch.int32, device=DEV), total_tokens=0)
+    assert out[0].numel() == 0
+    # seq_len beyond max_blocks * block_size: tokens past the table are not written
+    pair.gather_and_compare(0, np.array([[2, 3]], np.int32), [40])
+    pair.gather_and_compare(0, np.array([[0, 1, 2, 3], [3, 2, 1, 0]], np.int32), [64, 33])
+    pair.cache.close()

@@ -1,0 +1,150 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, it
+exports every function include/kvq.h declares, and every argument check
+returns its status before any HIP call (so these run on a CPU-only machine)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_DEV = 0x7F0000000000          # 256-byte aligned; never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    import quantized_fp8_int4_amd as kvq
+    return kvq
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    return sorted(set(re.findall(r"KVQ_API\s+[\w\s\*]+?\b(kvq_\w+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(kvq):
+    declared = _declared_functions()
+    assert declared == sorted(kvq.EXPORTED_SYMBOLS)
+    lib = ctypes.CDLL(kvq.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_library_exports_nothing_else(kvq):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True).stdout
+    names = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    public = {n for n in names if n.startswith("kvq")}
+    assert public == set(kvq.EXPORTED_SYMBOLS)
+
+
+def test_status_strings(kvq):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert kvq._lib.kvq_status_string(s)
+    assert b"unknown" in kvq._lib.kvq_status_string(-99)
+
+
+def _cfg(kvq, modes, hd=64, bs=16, hkv=2, nblocks=4):
+    return kvq.CacheConfig(bs, hkv, hd, modes, [nblocks] * len(modes))
+
+
+def _handle(kvq, cfg):
+    return kvq.kvq_create_cache(cfg, FAKE_DEV, kvq.kvq_cache_bytes(cfg)["total"])
+
+
+def test_cache_bytes_rejects_bad_geometry(kvq):
+    for hd in (32, 96, 512):
+        with pytest.raises(kvq.KVQError) as e:
+            kvq.kvq_cache_bytes(_cfg(kvq, [kvq.FP8_PER_TOKEN_HEAD], hd=hd))
+        assert e.value.status == kvq.ERR_UNSUPPORTED
+    for bs in (3, 2048):
+        with pytest.raises(kvq.KVQError) as e:
+            kvq.kvq_cache_bytes(_cfg(kvq, [kvq.BF16], bs=bs))
+        assert e.value.status == kvq.ERR_UNSUPPORTED
+    with pytest.raises(kvq.KVQError) as e:
+        kvq.kvq_cache_bytes(_cfg(kvq, [7]))
+    assert e.value.status == kvq.ERR_INVALID_ARG
+    with pytest.raises(kvq.KVQError) as e:
+        kvq.kvq_cache_bytes(kvq.CacheConfig(16, 2, 64, [kvq.BF16], [-1]))
+    assert e.value.status == kvq.ERR_INVALID_ARG
+    with pytest.raises(kvq.KVQError) as e:
+        kvq.kvq_cache_bytes(kvq.CacheConfig(16, 0, 64, [kvq.BF16], [1]))
+    assert e.value.status == kvq.ERR_INVALID_ARG
+    with pytest.raises(kvq.KVQError) as e:
+        kvq.kvq_cache_bytes(kvq.CacheConfig(16, 300, 64, [kvq.FP8_PER_HEAD], [1]))
+    assert e.value.status == kvq.ERR_UNSUPPORTED
+    assert kvq._lib.kvq_cache_bytes(None, None) == kvq.ERR_INVALID_ARG
+
+
+def test_create_cache_checks(kvq):
+    cfg = _cfg(kvq, [kvq.FP8_PER_TOKEN_HEAD])
+    total = kvq.kvq_cache_bytes(cfg)["total"]
+    with pytest.raises(kvq.KVQError) as e:
+        kvq.kvq_create_cache(cfg, FAKE_DEV, total - 1)
+    assert e.value.status == kvq.ERR_BUFFER_TOO_SMALL
+    with pytest.raises(kvq.KVQError) as e:
+        kvq.kvq_create_cache(cfg, FAKE_DEV + 16, total)
+    assert e.value.status == kvq.ERR_INVALID_ARG
+    with pytest.raises(kvq.KVQError) as e:
+        kvq.kvq_create_cache(cfg, 0, total)
+    assert e.value.status == kvq.ERR_INVALID_ARG
+    h = kvq.kvq_create_cache(cfg, FAKE_DEV, total)
+    kvq.kvq_destroy_cache(h)
+    assert kvq._lib.kvq_destroy_cache(None) == kvq.OK
+
+
+def _store(kvq, h, layer, n, mode, scales=None, keys=FAKE_DEV, values=FAKE_DEV, slots=FAKE_DEV):
+    sc = None
+    if scales is not None:
+        sc = (ctypes.c_float * len(scales))(*scales)
+    return kvq._lib.kvq_store(h, layer, ctypes.c_void_p(keys), ctypes.c_void_p(values), ctypes.c_void_p(slots),
+                              n, mode, sc, None)
+
+
+def _gather(kvq, h, layer, nseq, maxb=4, out=FAKE_DEV):
+    return kvq._lib.kvq_gather_dequant(h, layer, ctypes.c_void_p(FAKE_DEV), maxb, ctypes.c_void_p(FAKE_DEV),
+                                       nseq, ctypes.c_void_p(out), ctypes.c_void_p(out), None)
+
+
+def test_store_argument_checks(kvq):
+    cfg = _cfg(kvq, [kvq.FP8_PER_TOKEN_HEAD, kvq.FP8_PER_TENSOR, kvq.FP8_PER_HEAD, kvq.BF16])
+    h = _handle(kvq, cfg)
+    try:
+        assert _store(kvq, h, 4, 1, kvq.BF16) == kvq.ERR_INVALID_ARG              # layer out of range
+        assert _store(kvq, h, -1, 1, kvq.BF16) == kvq.ERR_INVALID_ARG
+        assert _store(kvq, h, 0, 1, kvq.INT4_PER_TOKEN_HEAD) == kvq.ERR_MODE_MISMATCH
+        assert _store(kvq, h, 3, 1, kvq.FP8_PER_TOKEN_HEAD) == kvq.ERR_MODE_MISMATCH
+        assert _store(kvq, h, 0, -1, kvq.FP8_PER_TOKEN_HEAD) == kvq.ERR_INVALID_ARG
+        assert _store(kvq, h, 0, 0, kvq.FP8_PER_TOKEN_HEAD) == kvq.OK              # no-op, no HIP call
+        assert _store(kvq, h, 0, 1, kvq.FP8_PER_TOKEN_HEAD, [1.0, 1.0]) == kvq.ERR_INVALID_ARG
+        assert _store(kvq, h, 0, 1, kvq.FP8_PER_TOKEN_HEAD, keys=0) == kvq.ERR_INVALID_ARG
+        assert _store(kvq, h, 0, 1, kvq.FP8_PER_TOKEN_HEAD, values=FAKE_DEV + 8) == kvq.ERR_INVALID_ARG
+        assert _store(kvq, h, 0, 1, kvq.FP8_PER_TOKEN_HEAD, slots=FAKE_DEV + 4) == kvq.ERR_INVALID_ARG
+        assert _store(kvq, h, 0, 1 << 30, kvq.FP8_PER_TOKEN_HEAD) == kvq.ERR_UNSUPPORTED
+        # static layers: first call needs positive finite scales of the right count
+        assert _store(kvq, h, 1, 1, kvq.FP8_PER_TENSOR) == kvq.ERR_INVALID_ARG
+        for bad in ([0.0, 1.0], [1.0, -2.0], [float("nan"), 1.0], [1.0, float("inf")]):
+            assert _store(kvq, h, 1, 1, kvq.FP8_PER_TENSOR, bad) == kvq.ERR_INVALID_ARG
+        assert _store(kvq, h, 2, 1, kvq.FP8_PER_HEAD, [1.0, 1.0, 1.0, 0.0]) == kvq.ERR_INVALID_ARG
+        # gather: a static layer never stored to has no scales yet
+        assert _gather(kvq, h, 1, 1) == kvq.ERR_INVALID_ARG
+        assert _gather(kvq, h, 0, 0) == kvq.OK                                    # no-op
+        assert _gather(kvq, h, 0, -1) == kvq.ERR_INVALID_ARG
+        assert _gather(kvq, h, 0, 1, maxb=0) == kvq.ERR_INVALID_ARG
+        assert _gather(kvq, h, 0, 1, out=FAKE_DEV + 2) == kvq.ERR_INVALID_ARG
+        assert _gather(kvq, h, 9, 1) == kvq.ERR_INVALID_ARG
+        assert _gather(kvq, h, 0, 1 << 20, maxb=1 << 12) == kvq.ERR_UNSUPPORTED
+    finally:
+        kvq.kvq_destroy_cache(h)
+
+
+def test_odd_block_with_scales_is_unsupported(kvq):
+    """An odd block_size * num_kv_heads makes per-token-head blocks 8 mod 16
+    bytes long; the kernels' 16-byte accesses need 16-byte blocks."""
+    cfg = kvq.CacheConfig(1, 1, 64, [kvq.FP8_PER_TOKEN_HEAD], [4])
+    h = _handle(kvq, cfg)
+    try:
+        assert _store(kvq, h, 0, 1, kvq.FP8_PER_TOKEN_HEAD) == kvq.ERR_UNSUPPORTED
+        assert _gather(kvq, h, 0, 1) == kvq.ERR_UNSUPPORTED
+    finally:
+        kvq.kvq_destroy_cache(h)
