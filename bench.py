@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized paged KV cache on one MI355X.
+
+A step is one pass of the whole hot path over one batch: quantize-and-store
+of every layer's new K/V (kvq_store), then the dequantizing paged read of
+every layer (kvq_gather_dequant).  Default workload: the 32-layer GQA shape
+(8 KV heads, head_dim 128, blocks of 16 tokens), a prefill of 8 sequences x
+4096 tokens per layer call, dynamic per-token-head FP8, synthetic inputs
+(per-head std log-uniform in [0.25, 16], 0.1% outliers x20) resident in HBM
+before timing.  Every layer has its own inputs, cache region and output
+buffers, so a step streams ~10 GiB and nothing is served from the 256 MB
+Infinity Cache.
+
+Prints one JSON line (rank 0).  Algorithmic bytes per token-head (no
+padding, no re-reads):
+  store  = 4*hd (BF16 K+V in) + 2*row_bytes (codes out) + 8 (FP32 scales, per-token-head)
+           + 8/Hkv (int64 slot)
+  gather = 2*row_bytes + 8 + 4/(block_size*Hkv) (int32 block-table entry) + 4*hd (BF16 out)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gqa32_fp8_per_token_head.md")
+KERNEL_SOURCE = os.path.join(ROOT, "quantized_fp8_int4_amd", "csrc", "kvq_kernels.hip")
+METRIC = "kvq_store/gather GB/s and % of HBM peak; cached tokens/s (per-token-head FP8)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def row_bytes(mode, hd):
+    import quantized_fp8_int4_amd as kvq
+    return {kvq.BF16: 2 * hd, kvq.INT4_PER_TOKEN_HEAD: hd // 2}.get(mode, hd)
+
+
+def algorithmic_bytes(mode, hd, hkv, bs, token_heads):
+    import quantized_fp8_int4_amd as kvq
+    rb = row_bytes(mode, hd)
+    sigma = 8 if mode in (kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD) else 0
+    store = token_heads * (4 * hd + 2 * rb + sigma) + token_heads * 8 / hkv
+    gather = token_heads * (2 * rb + sigma + 4 * hd) + token_heads * 4 / (bs * hkv)
+    return store, gather
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """Per-launch HBM bytes of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    text = open(PROFILE_TRAFFIC).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"traffic_bytes_per_launch\[(\w+)\]:\s*([0-9.eE+]+)", text)
+    if not m_hash or m_hash.group(1) != kernel_source_hash():
+        return None
+    vals = dict(re.findall(r"traffic_bytes_per_launch\[(\w+)\]:\s*([0-9.eE+]+)", text))
+    return {k: float(v) for k, v in vals.items()}
+
+
+def setup(args, torch, kvq, W):
+    spec = W.WORKLOADS["gqa32"]
+    L, hkv, hd, bs = spec["num_layers"], spec["hkv"], spec["hd"], spec["block_size"]
+    nseq, slen = spec["num_seqs"], spec["seq_len"]
+    n = nseq * slen
+    mode = {v: k for k, v in W.MODE_NAMES.items()}[args.mode]
+    nblocks = n // bs
+    dev = torch.device("cuda", 0)
+    cfg = kvq.CacheConfig(bs, hkv, hd, [mode] * L, [nblocks] * L)
+    cache = kvq.Cache(cfg, device=dev)
+    bt = W.permuted_block_table(nseq, slen // bs, nblocks, seed=1000)
+    slots = W.slots_from_block_table(bt, [slen] * nseq, bs).to(dev)
+    bt_d = bt.to(dev)
+    seq_lens = torch.full((nseq,), slen, dtype=torch.int32, device=dev)
+    keys, values, outs, scales = [], [], [], []
+    for layer in range(L):
+        k, v = W.gqa_kv(n, hkv, hd, seed=1000 + layer, device=dev)
+        keys.append(k)
+        values.append(v)
+        outs.append((torch.empty_like(k), torch.empty_like(v)))
+        if mode == kvq.FP8_PER_TENSOR:
+            scales.append([1.0, 1.0])
+        elif mode == kvq.FP8_PER_HEAD:
+            kc, vc = W.gqa_kv(4096, hkv, hd, seed=2000 + layer, device=dev)
+            scales.append(W.static_scales_from_amax(W.calibration_amax(kc, vc)).tolist())
+        else:
+            scales.append(None)
+    torch.cuda.synchronize()
+    return dict(L=L, hkv=hkv, hd=hd, bs=bs, n=n, nseq=nseq, slen=slen, mode=mode, nblocks=nblocks,
+                cfg=cfg, cache=cache, bt=bt, bt_d=bt_d, slots=slots, seq_lens=seq_lens, keys=keys,
+                values=values, outs=outs, scales=scales)
+
+
+def cpu_baseline(S, torch, W, n_layers):
+    """The oracle, as it stands, on the first n_layers layers of the same step
+    (store then gather), on this host's cores; also checks those layers' cache
+    bytes and gathered values against the GPU's."""
+    import numpy as np
+    import oracle
+
+    oracle.build(force=False)
+    g = oracle.Geometry(S["bs"], S["hkv"], S["hd"], [S["mode"]] * S["L"], [S["nblocks"]] * S["L"])
+    host = oracle.new_cache(g)
+    slots = S["slots"].cpu().numpy()
+    bt = S["bt"].numpy()
+    lens = np.full(S["nseq"], S["slen"], np.int32)
+    ins = []
+    for layer in range(n_layers):
+        kb = S["keys"][layer].cpu().view(torch.int16).numpy().view(np.uint16)
+        vb = S["values"][layer].cpu().view(torch.int16).numpy().view(np.uint16)
+        ins.append((kb, vb))
+    t0 = time.perf_counter()
+    gathered = []
+    for layer in range(n_layers):
+        sc = S["scales"][layer]
+        oracle.store(g, host, layer, ins[layer][0], ins[layer][1], slots,
+                     None if sc is None else np.asarray(sc, np.float32))
+    for layer in range(n_layers):
+        gathered.append(oracle.gather(g, host, layer, bt, lens))
+    secs = time.perf_counter() - t0
+    lb, _, _ = oracle.layer_offsets(g)
+    import quantized_fp8_int4_amd as kvq
+    sigma = 8 if S["mode"] in (kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD) else 0
+    layer_bytes = S["nblocks"] * S["bs"] * S["hkv"] * (2 * row_bytes(S["mode"], S["hd"]) + sigma)
+    end = int(lb[n_layers - 1]) + layer_bytes
+    dev_buf = S["cache"].buffer[:end].cpu().numpy()
+    ok = bool(np.array_equal(dev_buf, host[:end]))
+    for layer in range(n_layers):
+        dk = S["outs"][layer][0].cpu().view(torch.int16).numpy().view(np.uint16)
+        dv = S["outs"][layer][1].cpu().view(torch.int16).numpy().view(np.uint16)
+        ok = ok and np.array_equal(dk, gathered[layer][0]) and np.array_equal(dv, gathered[layer][1])
+    return secs, oracle.num_threads(), ok
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mode", default="fp8_per_token_head",
+                    choices=["fp8_per_token_head", "fp8_per_tensor", "fp8_per_head", "int4_per_token_head", "bf16"])
+    ap.add_argument("--cpu-layers", type=int, default=16, help="layers of one step timed on the CPU oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the store/gather path needs no collective and this build "
+              "runs on a single MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_fp8_int4_amd as kvq
+    import workloads as W
+
+    log("[bench] setting up gqa32 inputs on the device")
+    S = setup(args, torch, kvq, W)
+    L, cache = S["L"], S["cache"]
+    token_heads = S["n"] * S["hkv"]
+    store_bytes, gather_bytes = algorithmic_bytes(S["mode"], S["hd"], S["hkv"], S["bs"], token_heads)
+
+    # Launch arguments prepared once, so the host stays far ahead of the GPU
+    # and every kernel starts as soon as the previous one ends.
+    import ctypes
+    lib, handle = kvq._lib, cache.handle
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
+    store_args, gather_args = [], []
+    for layer in range(L):
+        sc = S["scales"][layer]
+        csc = None if sc is None else (ctypes.c_float * len(sc))(*[float(x) for x in sc])
+        store_args.append((handle, layer, P(S["keys"][layer].data_ptr()), P(S["values"][layer].data_ptr()),
+                           P(S["slots"].data_ptr()), S["n"], S["mode"], csc, stream))
+        gather_args.append((handle, layer, P(S["bt_d"].data_ptr()), S["bt_d"].shape[1],
+                            P(S["seq_lens"].data_ptr()), S["nseq"], P(S["outs"][layer][0].data_ptr()),
+                            P(S["outs"][layer][1].data_ptr()), stream))
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        for a in store_args:
+            st = lib.kvq_store(*a)
+            if st != 0:
+                raise kvq.KVQError(st, "kvq_store")
+        if ev is not None:
+            ev[1].record()
+        for a in gather_args:
+            st = lib.kvq_gather_dequant(*a)
+            if st != 0:
+                raise kvq.KVQError(st, "kvq_gather_dequant")
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    # HIP events on the launch stream bracket each step's 32 stores and 32 gathers.
+    all_events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(all_events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_store_s = sum(ev[0].elapsed_time(ev[1]) for ev in all_events) / (args.steps * L) / 1e3
+    avg_gather_s = sum(ev[1].elapsed_time(ev[2]) for ev in all_events) / (args.steps * L) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    step_bytes = L * (store_bytes + gather_bytes)
+    value = step_bytes / (wall / args.steps) / 1e9
+    store_gbps = store_bytes / avg_store_s / 1e9
+    gather_gbps = gather_bytes / avg_gather_s / 1e9
+    dominant = "store" if avg_store_s >= avg_gather_s else "gather"
+    dom_gbps = store_gbps if dominant == "store" else gather_gbps
+    log(f"[bench] {ms_per_step:.3f} ms/step; store {avg_store_s * 1e6:.1f} us ({store_gbps:.0f} GB/s), "
+        f"gather {avg_gather_s * 1e6:.1f} us ({gather_gbps:.0f} GB/s)")
+
+    traffic = measured_traffic()
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        nl = max(1, min(args.cpu_layers, L))
+        log(f"[bench] cpu baseline: oracle on {nl} layers (store + gather)")
+        secs, cores, parity = cpu_baseline(S, torch, W, nl)
+        cpu = {"value": round(nl * (store_bytes + gather_bytes) / secs / 1e9, 3), "unit": "GB/s",
+               "cores": cores, "kind": "oracle",
+               "sample": f"{nl} of {L} layers of one step (store then gather of {S['n']} tokens each), "
+                         f"{secs:.2f} s wall"}
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "gqa32: 32 layers, 8 KV heads, head_dim 128, block 16, prefill of 8 x 4096 "
+                               f"tokens per layer call, store + gather_dequant of every layer, {args.mode}",
+                   "mode": args.mode, "layers": L, "tokens_per_layer_call": S["n"], "num_kv_heads": S["hkv"],
+                   "head_dim": S["hd"], "block_size": S["bs"]},
+        "store_GBps": round(store_gbps, 1),
+        "gather_GBps": round(gather_gbps, 1),
+        "store_frac_of_peak": round(store_gbps / HBM_PEAK_GBPS, 4),
+        "gather_frac_of_peak": round(gather_gbps / HBM_PEAK_GBPS, 4),
+        "store_us": round(avg_store_s * 1e6, 2),
+        "gather_us": round(avg_gather_s * 1e6, 2),
+        "cached_tokens_per_s": round(S["n"] / (L * avg_store_s), 1),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "roofline": {"bound": "hbm", "kernel": f"{dominant}_kernel", "achieved": round(dom_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else traffic.get(dominant)},
+        "cpu_baseline": cpu,
+        "parity_vs_oracle_sampled": parity,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

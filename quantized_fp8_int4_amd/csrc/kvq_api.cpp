@@ -160,9 +160,7 @@ kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const int32_t* 
     const kvq::Layout& L = c->layout;
     const int32_t lmode = L.mode[layer];
     if (kvq::has_static_scales(lmode) && c->static_values[layer].empty()) return KVQ_ERR_INVALID_ARG;
-    if (static_cast<int64_t>(num_seqs) * max_blocks_per_seq >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
     if (L.block_bytes[layer] % 16 != 0) return KVQ_ERR_UNSUPPORTED;
-    if (L.num_blocks[layer] == 0) return KVQ_OK;
 
     kvq::GatherLaunch a;
     a.layer = c->dev + L.layer_base[layer];
@@ -180,6 +178,8 @@ kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const int32_t* 
     a.block_size = L.block_size;
     a.head_dim = L.head_dim;
     a.mode = lmode;
+    if (kvq::gather_grid(a) >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
+    if (L.num_blocks[layer] == 0) return KVQ_OK;
     if (log_enabled())
         std::fprintf(stderr, "[kvq] gather layer=%d mode=%s hd=%d seqs=%d max_blocks=%d\n", layer,
                      mode_name(lmode), L.head_dim, num_seqs, max_blocks_per_seq);

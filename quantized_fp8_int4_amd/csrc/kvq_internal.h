@@ -83,6 +83,8 @@ struct GatherLaunch {
 // Each returns 0 on a successful enqueue, else the hipError_t value.
 int launch_store(const StoreLaunch& a, void* stream);
 int launch_gather(const GatherLaunch& a, void* stream);
+// Workgroups launch_gather would use (to reject grids of 2^31 or more).
+int64_t gather_grid(const GatherLaunch& a);
 int launch_write_static(float* dst, const float* values, int n, void* stream);
 
 }  // namespace kvq

@@ -165,6 +165,41 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// ------------------------------------------------------- memory helpers
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// NT selects the non-temporal form: data read or written once by this call
+// is streamed instead of kept in the caches.
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+    u32x4 v;
+    if constexpr (NT) v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    else v = *static_cast<const u32x4*>(p);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st16(void* p, const uint4& x) {
+    const u32x4 v = {x.x, x.y, x.z, x.w};
+    if constexpr (NT) __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
+    else *static_cast<u32x4*>(p) = v;
+}
+
+template <bool NT>
+__device__ __forceinline__ void st8(void* p, const uint2& x) {
+    const u32x2 v = {x.x, x.y};
+    if constexpr (NT) __builtin_nontemporal_store(v, static_cast<u32x2*>(p));
+    else *static_cast<u32x2*>(p) = v;
+}
+
+template <bool NT>
+__device__ __forceinline__ void st4(void* p, uint32_t x) {
+    if constexpr (NT) __builtin_nontemporal_store(x, static_cast<uint32_t*>(p));
+    else *static_cast<uint32_t*>(p) = x;
+}
+
 // ------------------------------------------------------------------ store
 
 struct StoreArgs {
@@ -183,38 +218,20 @@ struct StoreArgs {
     uint32_t bs_log2;
 };
 
-// One row = one (token, KV head) of K and the same of V.  LPR = HD / EPL
-// lanes per row; chunk k of a lane is elements [(k * LPR + sub) * 8, +8), so
-// each load instruction reads LPR * 16 contiguous bytes of every row.
-template <int HD, int MODE, int EPL>
-__global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs p) {
-    constexpr int LPR = HD / EPL;
-    constexpr int CPL = EPL / 8;
-    constexpr int RPW = 64 / LPR;
-    constexpr int RPB = RPW * kWaves;
+// Tuning knobs of the store kernel: EPL elements of a row per lane (LPR =
+// HD / EPL lanes per row), RPL rows per lane (more loads in flight per
+// wave), NTL non-temporal loads of the new K/V, NTS non-temporal stores of
+// the codes.
+
+// Quantize the K and V chunks of one row (already loaded) and scatter them.
+template <int HD, int MODE, int LPR, int CPL, bool NTS>
+__device__ __forceinline__ void store_row(const StoreArgs& p, uint32_t rowc, bool valid, uint32_t sub,
+                                          const uint4 (&kx)[CPL], const uint4 (&vx)[CPL]) {
     constexpr uint32_t HB = row_bytes_of<MODE>(HD);
-    static_assert(LPR >= 1 && LPR <= 32 && CPL >= 1, "bad row split");
-
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t sub = lane % LPR;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + wave * RPW + lane / LPR;
-    const bool valid = row < p.num_rows;
-    const uint32_t rowc = valid ? static_cast<uint32_t>(row) : 0u;
-
-    uint4 kx[CPL], vx[CPL];
-    const uint4* kp = p.keys + static_cast<uint64_t>(rowc) * (HD / 8) + sub;
-    const uint4* vp = p.values + static_cast<uint64_t>(rowc) * (HD / 8) + sub;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        kx[k] = valid ? kp[k * LPR] : make_uint4(0, 0, 0, 0);
-        vx[k] = valid ? vp[k * LPR] : make_uint4(0, 0, 0, 0);
-    }
-
     const uint32_t t = static_cast<uint32_t>((static_cast<uint64_t>(rowc) * p.hkv_magic) >> p.hkv_shift);
     const uint32_t h = rowc - t * p.hkv;
-    const int64_t slot = valid ? p.slots[t] : -1;
-    const bool write = slot >= 0 && slot < p.num_slots;
+    const int64_t slot = p.slots[t];
+    const bool write = valid && slot >= 0 && slot < p.num_slots;
     const uint64_t blk = static_cast<uint64_t>(slot) >> p.bs_log2;
     const uint32_t pos = static_cast<uint32_t>(slot) & ((1u << p.bs_log2) - 1u);
     uint8_t* const bp = p.layer + blk * p.block_bytes;
@@ -227,11 +244,10 @@ __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs p) {
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
                 const uint32_t c = k * LPR + sub;
-                *reinterpret_cast<uint4*>(krow + c * 16) = kx[k];
-                *reinterpret_cast<uint4*>(vrow + c * 16) = vx[k];
+                st16<NTS>(krow + c * 16, kx[k]);
+                st16<NTS>(vrow + c * 16, vx[k]);
             }
         }
-        return;
     } else {
         float sK, sV;
         if constexpr (dynamic_mode<MODE>()) {
@@ -272,8 +288,8 @@ __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs p) {
 #pragma unroll
                 for (int k = 0; k < CPL; ++k) {
                     const uint32_t c = k * LPR + sub;
-                    *reinterpret_cast<uint32_t*>(krow + c * 4) = ck[k];
-                    *reinterpret_cast<uint32_t*>(vrow + c * 4) = cv[k];
+                    st4<NTS>(krow + c * 4, ck[k]);
+                    st4<NTS>(vrow + c * 4, cv[k]);
                 }
             }
         } else {
@@ -289,8 +305,8 @@ __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs p) {
 #pragma unroll
                 for (int k = 0; k < CPL; ++k) {
                     const uint32_t c = k * LPR + sub;
-                    *reinterpret_cast<uint2*>(krow + c * 8) = ck[k];
-                    *reinterpret_cast<uint2*>(vrow + c * 8) = cv[k];
+                    st8<NTS>(krow + c * 8, ck[k]);
+                    st8<NTS>(vrow + c * 8, cv[k]);
                 }
             }
         }
@@ -298,6 +314,48 @@ __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs p) {
             if (write && sub == 0)
                 *reinterpret_cast<float2*>(bp + p.code_bytes + static_cast<uint64_t>(ph) * 8) = make_float2(sK, sV);
         }
+    }
+}
+
+// One row = one (token, KV head) of K and the same of V, owned by LPR
+// adjacent lanes.  Chunk k of a lane is elements [(k * LPR + sub) * 8, +8),
+// so each load instruction reads LPR * 16 contiguous bytes of every row.  A
+// wave owns RPL groups of 64 / LPR consecutive rows and loads all of them
+// before quantizing any.
+template <int HD, int MODE, int EPL, int RPL, bool NTL, bool NTS>
+__global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs p) {
+    constexpr int LPR = HD / EPL;
+    constexpr int CPL = EPL / 8;
+    constexpr int RPW = 64 / LPR;
+    constexpr int RPB = RPW * RPL * kWaves;
+    static_assert(LPR >= 1 && LPR <= 32 && CPL >= 1 && RPL >= 1, "bad row split");
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t sub = lane % LPR;
+    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * RPB + wave * (RPW * RPL) + lane / LPR;
+
+    uint4 kx[RPL][CPL], vx[RPL][CPL];
+#pragma unroll
+    for (int j = 0; j < RPL; ++j) {
+        const int64_t row = row0 + j * RPW;
+        const bool valid = row < p.num_rows;
+        const uint64_t rowc = valid ? static_cast<uint64_t>(row) : 0u;
+        const uint4* kp = p.keys + rowc * (HD / 8) + sub;
+        const uint4* vp = p.values + rowc * (HD / 8) + sub;
+        // Unconditional loads (rows past the end read row 0 and never write):
+        // no branch, so every load of the wave stays in flight together.
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            kx[j][k] = ld16<NTL>(kp + k * LPR);
+            vx[j][k] = ld16<NTL>(vp + k * LPR);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < RPL; ++j) {
+        const int64_t row = row0 + j * RPW;
+        const bool valid = row < p.num_rows;
+        store_row<HD, MODE, LPR, CPL, NTS>(p, valid ? static_cast<uint32_t>(row) : 0u, valid, sub, kx[j], vx[j]);
     }
 }
 
@@ -319,6 +377,7 @@ struct GatherArgs {
     int32_t max_blocks;
     int32_t num_seqs;
     int32_t block_size;
+    uint32_t parts;           // workgroups per logical block
 };
 
 __device__ __forceinline__ int64_t wave_sum(int64_t v) {
@@ -327,101 +386,139 @@ __device__ __forceinline__ int64_t wave_sum(int64_t v) {
     return v;
 }
 
-// One workgroup per (sequence, logical block).  The block's code bytes are
-// contiguous in the cache, rows ordered [position][head][K, V]; a 16-byte
-// chunk c belongs to row c / (HB / 16), and the row's FP32 scale sits at the
-// same row index in the block's scale trailer.
-template <int HD, int MODE>
+template <int N>
+__device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&w)[N]) {
+    if constexpr (N == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (N == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        w[0] = v.x; w[1] = v.y;
+    } else {
+        w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+}
+
+// Sequences whose offset is summed without a loop: 64 lanes x kOffsetLoads.
+constexpr int kOffsetLoads = 4;
+
+// Tuning knobs of the gather kernel: CB code bytes per thread chunk, U
+// chunks per thread, NTS non-temporal stores of the BF16 output.
+//
+// One workgroup per (sequence, logical block, part); a part is up to
+// kThreads * U chunks of the block.  The block's code bytes are contiguous in
+// the cache with rows ordered [position][head][K, V]; a chunk of CB code bytes
+// belongs to row c / (HB / CB), and the row's FP32 scale sits at the same row
+// index of the block's scale trailer.  The body is straight-line so every
+// load of a workgroup is in flight at once: lanes past the last chunk load,
+// decode and store the last chunk again (identical bytes to the same place).
+template <int HD, int MODE, int CB, int U, bool NTS>
 __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs p) {
     constexpr uint32_t HB = row_bytes_of<MODE>(HD);
-    constexpr uint32_t CPR = HB / 16;                        // chunks per row
-    constexpr uint32_t EPC = (MODE == KVQ_BF16) ? 8 : (MODE == KVQ_INT4_PER_TOKEN_HEAD ? 32 : 16);
-    constexpr int U = 4;
+    constexpr int DW = CB / 4;                               // code dwords per chunk
+    constexpr uint32_t CPR = HB / CB;                        // chunks per row
+    constexpr int OUT_PER_DW = (MODE == KVQ_BF16) ? 1 : (MODE == KVQ_INT4_PER_TOKEN_HEAD ? 4 : 2);
+    constexpr int ODW = DW * OUT_PER_DW;                     // output dwords per chunk
+    constexpr uint32_t EPC = ODW * 2;                        // output elements per chunk
+    static_assert(ODW % 4 == 0, "output chunk must be whole 16-byte stores");
+    static_assert(HB % CB == 0, "row must be whole chunks");
 
     const uint32_t wg = blockIdx.x;
-    const uint32_t b = wg / static_cast<uint32_t>(p.max_blocks);
-    const uint32_t j = wg - b * static_cast<uint32_t>(p.max_blocks);
-    int64_t len = max(p.seq_lens[b], 0);
-    len = min<int64_t>(len, static_cast<int64_t>(p.max_blocks) * p.block_size);
+    const uint32_t bj = wg / p.parts;
+    const uint32_t part = wg - bj * p.parts;
+    const uint32_t b = bj / static_cast<uint32_t>(p.max_blocks);
+    const uint32_t j = bj - b * static_cast<uint32_t>(p.max_blocks);
+    // Both scalar loads are in bounds for every (b, j); issue them together.
+    const int32_t raw_len = p.seq_lens[b];
+    const int32_t pb = p.block_table[static_cast<int64_t>(b) * p.max_blocks + j];
+    const int64_t len = min<int64_t>(max(raw_len, 0), static_cast<int64_t>(p.max_blocks) * p.block_size);
     const int64_t t0 = static_cast<int64_t>(j) * p.block_size;
     if (t0 >= len) return;
-    const int32_t pb = p.block_table[static_cast<int64_t>(b) * p.max_blocks + j];
     if (pb < 0 || pb >= p.num_blocks) return;
-
-    const uint32_t lane = threadIdx.x & 63u;
-    int64_t off = 0;
-    for (uint32_t i = lane; i < b; i += 64) off += max(p.seq_lens[i], 0);
-    off = wave_sum(off);
-
     const uint32_t ntok = static_cast<uint32_t>(min<int64_t>(p.block_size, len - t0));
     const uint32_t nchunks = ntok * p.hkv * 2 * CPR;
-    const uint8_t* const bp = p.layer + static_cast<uint64_t>(pb) * p.block_bytes;
-    const uint4* const codes = reinterpret_cast<const uint4*>(bp);
-    const float* const trailer = reinterpret_cast<const float*>(bp + p.code_bytes);
-    const int64_t out_row0 = (off + t0) * p.hkv;
+    const uint32_t c0 = part * (kThreads * U);
+    if (c0 >= nchunks) return;
 
-    float s_static[2] = {0.0f, 0.0f};
-    if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
-        s_static[0] = p.static_scales[0];
-        s_static[1] = p.static_scales[1];
+    // Offset of sequence b in the packed output: sum of the earlier lengths.
+    // These loads go out first, so waiting for them never waits for codes.
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t last_seq = static_cast<uint32_t>(p.num_seqs - 1);
+    int32_t lens[kOffsetLoads];
+#pragma unroll
+    for (int k = 0; k < kOffsetLoads; ++k) lens[k] = p.seq_lens[min(lane + 64u * k, last_seq)];
+    int64_t off_tail = 0;
+    if (b > 64u * kOffsetLoads) {
+        for (uint32_t i = lane + 64u * kOffsetLoads; i < b; i += 64) off_tail += max(p.seq_lens[i], 0);
     }
 
-    for (uint32_t base = threadIdx.x; base < nchunks; base += kThreads * U) {
-        uint4 cw[U];
+    const uint8_t* const bp = p.layer + static_cast<uint64_t>(pb) * p.block_bytes;
+    const float* const trailer = reinterpret_cast<const float*>(bp + p.code_bytes);
+    uint32_t cw[U][DW];
+    float sc[U];
+    uint32_t chunk[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t c = base + u * kThreads;
-            cw[u] = (c < nchunks) ? codes[c] : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+        chunk[u] = min(c0 + threadIdx.x + u * kThreads, nchunks - 1);
+        load_codes<DW>(bp + static_cast<uint64_t>(chunk[u]) * CB, cw[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t row = chunk[u] / CPR;
+        if constexpr (dynamic_mode<MODE>()) {
+            sc[u] = trailer[row];
+        } else if constexpr (MODE == KVQ_FP8_PER_HEAD) {
+            const uint32_t th = row >> 1;
+            const uint32_t tt = static_cast<uint32_t>((static_cast<uint64_t>(th) * p.hkv_magic) >> p.hkv_shift);
+            sc[u] = p.static_scales[(row & 1u) * p.hkv + (th - tt * p.hkv)];
+        } else if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
+            sc[u] = p.static_scales[row & 1u];
+        } else {
+            sc[u] = 0.0f;
         }
+    }
+
+    int64_t off = off_tail;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t c = base + u * kThreads;
-            if (c >= nchunks) continue;
-            const uint32_t row = c / CPR;
-            const uint32_t col = c % CPR;
-            uint16_t* const outp = ((row & 1u) ? p.out_v : p.out_k) +
-                                   static_cast<uint64_t>(out_row0 + (row >> 1)) * HD + col * EPC;
-            uint4* const o = reinterpret_cast<uint4*>(outp);
-            if constexpr (MODE == KVQ_BF16) {
-                o[0] = cw[u];
-            } else {
-                float s;
-                if constexpr (dynamic_mode<MODE>()) {
-                    s = trailer[row];
-                } else if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
-                    s = s_static[row & 1u];
-                } else {
-                    const uint32_t th = row >> 1;
-                    const uint32_t tt = static_cast<uint32_t>((static_cast<uint64_t>(th) * p.hkv_magic) >> p.hkv_shift);
-                    s = p.static_scales[(row & 1u) * p.hkv + (th - tt * p.hkv)];
-                }
-                const uint32_t ws[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
-                if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+    for (int k = 0; k < kOffsetLoads; ++k)
+        off += (lane + 64u * k < b) ? max(lens[k], 0) : 0;
+    off = wave_sum(off);
+    const int64_t out_row0 = (off + t0) * p.hkv;
+
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        uint32_t r[4];
+    for (int u = 0; u < U; ++u) {
+        const uint32_t row = chunk[u] / CPR;
+        const uint32_t col = chunk[u] % CPR;
+        uint16_t* const outp = ((row & 1u) ? p.out_v : p.out_k) +
+                               static_cast<uint64_t>(out_row0 + (row >> 1)) * HD + col * EPC;
+        const float s = sc[u];
+        uint32_t o[ODW];
+        if constexpr (MODE == KVQ_BF16) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float a = static_cast<float>(static_cast<int32_t>(ws[d] << (28 - 8 * e)) >> 28);
-                            const float bb = static_cast<float>(static_cast<int32_t>(ws[d] << (24 - 8 * e)) >> 28);
-                            r[e] = pack_bf16(a * s, bb * s);
-                        }
-                        o[d] = make_uint4(r[0], r[1], r[2], r[3]);
-                    }
-                } else {
-                    uint32_t r[8];
+            for (int d = 0; d < DW; ++d) o[d] = cw[u][d];
+        } else if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(ws[d]), false);
-                        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(ws[d]), true);
-                        r[2 * d] = pack_bf16(lo[0] * s, lo[1] * s);
-                        r[2 * d + 1] = pack_bf16(hi[0] * s, hi[1] * s);
-                    }
-                    o[0] = make_uint4(r[0], r[1], r[2], r[3]);
-                    o[1] = make_uint4(r[4], r[5], r[6], r[7]);
+            for (int d = 0; d < DW; ++d) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // byte e holds elements 2e (low nibble) and 2e+1
+                    const float a = static_cast<float>(static_cast<int32_t>(cw[u][d] << (28 - 8 * e)) >> 28);
+                    const float bb = static_cast<float>(static_cast<int32_t>(cw[u][d] << (24 - 8 * e)) >> 28);
+                    o[4 * d + e] = pack_bf16(a * s, bb * s);
                 }
             }
+        } else {
+#pragma unroll
+            for (int d = 0; d < DW; ++d) {
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(cw[u][d]), false);
+                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(cw[u][d]), true);
+                o[2 * d] = pack_bf16(lo[0] * s, lo[1] * s);
+                o[2 * d + 1] = pack_bf16(hi[0] * s, hi[1] * s);
+            }
         }
+#pragma unroll
+        for (int q = 0; q < ODW / 4; ++q)
+            st16<NTS>(outp + 8 * q, make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]));
     }
 }
 
@@ -437,10 +534,26 @@ __global__ void write_static_kernel(float* dst, StaticValues vals, int n) {
 
 // --------------------------------------------------------------- dispatch
 
+// Default tuning, chosen by measurement on MI355X (32768 tokens x 8 KV heads
+// per call): 8 lanes per row, so every load instruction reads whole 128-byte
+// lines of each row; two rows per lane where a lane's row share is small
+// (head_dim 64, INT4) or the path has no arithmetic to hide latency behind
+// (BF16); non-temporal streams for data that one call touches once.  The
+// gather moves 8 code bytes (FP8) or 4 (INT4) per thread chunk, so each
+// wave-wide store writes 1 KiB of contiguous BF16 output.
 template <int HD, int MODE>
-int launch_store_t(const StoreLaunch& a, void* stream) {
-    constexpr int EPL = 32;
-    constexpr int RPB = (64 / (HD / EPL)) * kWaves;
+struct Tune {
+    static constexpr int store_epl = HD / 8;
+    static constexpr int store_rpl = (MODE == KVQ_BF16) ? (HD == 64 ? 4 : 2)
+                                   : ((HD == 64 || MODE == KVQ_INT4_PER_TOKEN_HEAD) ? 2 : 1);
+    static constexpr bool store_nt_load = true;
+    static constexpr bool store_nt_store = true;
+    static constexpr int gather_cb = (MODE == KVQ_BF16) ? 16 : (MODE == KVQ_INT4_PER_TOKEN_HEAD ? 4 : 8);
+    static constexpr int gather_u = (HD == 64 || MODE == KVQ_INT4_PER_TOKEN_HEAD || MODE == KVQ_BF16) ? 8 : 4;
+    static constexpr bool gather_nt_store = true;
+};
+
+StoreArgs make_store_args(const StoreLaunch& a) {
     StoreArgs p;
     p.keys = static_cast<const uint4*>(a.keys);
     p.values = static_cast<const uint4*>(a.values);
@@ -456,23 +569,16 @@ int launch_store_t(const StoreLaunch& a, void* stream) {
     p.hkv_magic = dm.magic;
     p.hkv_shift = dm.shift;
     p.bs_log2 = static_cast<uint32_t>(a.bs_log2);
-    const uint32_t grid = static_cast<uint32_t>((a.num_rows + RPB - 1) / RPB);
-    hipLaunchKernelGGL((store_kernel<HD, MODE, EPL>), dim3(grid), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), p);
-    return static_cast<int>(hipGetLastError());
+    return p;
 }
 
-template <int MODE>
-int launch_store_m(const StoreLaunch& a, void* stream) {
-    switch (a.head_dim) {
-        case 64: return launch_store_t<64, MODE>(a, stream);
-        case 128: return launch_store_t<128, MODE>(a, stream);
-        default: return launch_store_t<256, MODE>(a, stream);
-    }
+int64_t gather_parts(int64_t block_size, int64_t hkv, uint64_t hb, int cb, int u) {
+    const int64_t chunks = block_size * hkv * 2 * static_cast<int64_t>(hb / cb);
+    const int64_t per = static_cast<int64_t>(kThreads) * u;
+    return (chunks + per - 1) / per;
 }
 
-template <int HD, int MODE>
-int launch_gather_t(const GatherLaunch& a, void* stream) {
+GatherArgs make_gather_args(const GatherLaunch& a) {
     GatherArgs p;
     p.layer = a.layer;
     p.static_scales = a.static_scales;
@@ -490,10 +596,49 @@ int launch_gather_t(const GatherLaunch& a, void* stream) {
     p.max_blocks = a.max_blocks;
     p.num_seqs = a.num_seqs;
     p.block_size = a.block_size;
-    const uint32_t grid = static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.max_blocks);
-    hipLaunchKernelGGL((gather_kernel<HD, MODE>), dim3(grid), dim3(kThreads), 0,
+    p.parts = 1;
+    return p;
+}
+
+template <int HD, int MODE, int EPL, int RPL, bool NTL, bool NTS>
+int launch_store_v(const StoreLaunch& a, void* stream) {
+    constexpr int RPB = (64 / (HD / EPL)) * RPL * kWaves;
+    const StoreArgs p = make_store_args(a);
+    const uint32_t grid = static_cast<uint32_t>((a.num_rows + RPB - 1) / RPB);
+    hipLaunchKernelGGL((store_kernel<HD, MODE, EPL, RPL, NTL, NTS>), dim3(grid), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), p);
     return static_cast<int>(hipGetLastError());
+}
+
+template <int HD, int MODE, int CB, int U, bool NTS>
+int launch_gather_v(const GatherLaunch& a, void* stream) {
+    GatherArgs p = make_gather_args(a);
+    p.parts = static_cast<uint32_t>(gather_parts(a.block_size, a.num_kv_heads, row_bytes(a.mode, HD), CB, U));
+    const uint32_t grid = static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.max_blocks * p.parts);
+    hipLaunchKernelGGL((gather_kernel<HD, MODE, CB, U, NTS>), dim3(grid), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), p);
+    return static_cast<int>(hipGetLastError());
+}
+
+template <int HD, int MODE>
+int launch_store_t(const StoreLaunch& a, void* stream) {
+    using T = Tune<HD, MODE>;
+    return launch_store_v<HD, MODE, T::store_epl, T::store_rpl, T::store_nt_load, T::store_nt_store>(a, stream);
+}
+
+template <int MODE>
+int launch_store_m(const StoreLaunch& a, void* stream) {
+    switch (a.head_dim) {
+        case 64: return launch_store_t<64, MODE>(a, stream);
+        case 128: return launch_store_t<128, MODE>(a, stream);
+        default: return launch_store_t<256, MODE>(a, stream);
+    }
+}
+
+template <int HD, int MODE>
+int launch_gather_t(const GatherLaunch& a, void* stream) {
+    using T = Tune<HD, MODE>;
+    return launch_gather_v<HD, MODE, T::gather_cb, T::gather_u, T::gather_nt_store>(a, stream);
 }
 
 template <int MODE>
@@ -505,7 +650,33 @@ int launch_gather_m(const GatherLaunch& a, void* stream) {
     }
 }
 
+template <int HD, int MODE>
+int64_t gather_grid_t(const GatherLaunch& a) {
+    using T = Tune<HD, MODE>;
+    return static_cast<int64_t>(a.num_seqs) * a.max_blocks *
+           gather_parts(a.block_size, a.num_kv_heads, row_bytes(a.mode, HD), T::gather_cb, T::gather_u);
+}
+
+template <int MODE>
+int64_t gather_grid_m(const GatherLaunch& a) {
+    switch (a.head_dim) {
+        case 64: return gather_grid_t<64, MODE>(a);
+        case 128: return gather_grid_t<128, MODE>(a);
+        default: return gather_grid_t<256, MODE>(a);
+    }
+}
+
 }  // namespace
+
+int64_t gather_grid(const GatherLaunch& a) {
+    switch (a.mode) {
+        case KVQ_BF16: return gather_grid_m<KVQ_BF16>(a);
+        case KVQ_FP8_PER_TENSOR: return gather_grid_m<KVQ_FP8_PER_TENSOR>(a);
+        case KVQ_FP8_PER_HEAD: return gather_grid_m<KVQ_FP8_PER_HEAD>(a);
+        case KVQ_FP8_PER_TOKEN_HEAD: return gather_grid_m<KVQ_FP8_PER_TOKEN_HEAD>(a);
+        default: return gather_grid_m<KVQ_INT4_PER_TOKEN_HEAD>(a);
+    }
+}
 
 int launch_store(const StoreLaunch& a, void* stream) {
     switch (a.mode) {
