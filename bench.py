@@ -34,6 +34,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gqa32_fp8_per_token_head.md")
 KERNEL_SOURCE = os.path.join(ROOT, "quantized_fp8_int4_amd", "csrc", "kvq_kernels.hip")
 METRIC = "kvq_store/gather GB/s and % of HBM peak; cached tokens/s (per-token-head FP8)"
+COPY_BYTES = 256 << 20
+PROFILE_KERNEL_TRACE = os.path.join(ROOT, "profiles", "kernel_trace_gqa32_fp8_per_token_head.md")
 
 
 def log(msg):
@@ -71,6 +73,85 @@ def measured_traffic():
         return None
     vals = dict(re.findall(r"traffic_bytes_per_launch\[(\w+)\]:\s*([0-9.eE+]+)", text))
     return {k: float(v) for k, v in vals.items()}
+
+
+def _read_csv(directory, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_per_kernel(rows, counter):
+    """Mean counter value (KiB) per dispatch of the store kernel, the gather
+    kernel and the calibration copy (the largest device-to-device copies)."""
+    acc = {}
+    copies = []
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        name, val = r["Kernel_Name"], float(r["Counter_Value"])
+        if "store_kernel" in name:
+            acc.setdefault("store", []).append(val)
+        elif "gather_kernel" in name:
+            acc.setdefault("gather", []).append(val)
+        elif "copyBuffer" in name:
+            copies.append(val)
+    top = max(copies)
+    acc["copy"] = [v for v in copies if v >= 0.5 * top]
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def summarize_profiles(kt_dir, fetch_dir, write_dir):
+    """profiles/ summaries from three rocprofv3 runs of bench.py (kernel trace
+    with --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, the latter two with
+    --calibrate-copy).  Counter KiB are scaled by the copy kernel's reading of
+    a copy of known size."""
+    stats = _read_csv(kt_dir, "kernel_stats.csv")
+    lines = ["# Kernel trace: GQA-32 store + gather, per-token-head FP8", "",
+             "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(kt_dir))} -o run -- python3 $R/bench.py",
+             "", "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r.get("Name") or r.get("KernelName") or ""
+        if "kvq" not in name:
+            continue
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    with open(PROFILE_KERNEL_TRACE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    fetch = _counter_per_kernel(_read_csv(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    write = _counter_per_kernel(_read_csv(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    f_scale = COPY_BYTES / (fetch["copy"][0] * 1024.0)
+    w_scale = COPY_BYTES / (write["copy"][0] * 1024.0)
+    import quantized_fp8_int4_amd as kvq
+    store_b, gather_b = algorithmic_bytes(kvq.FP8_PER_TOKEN_HEAD, 128, 8, 16, 32768 * 8)
+    algo = {"store": store_b, "gather": gather_b}
+    out = ["# HBM traffic per launch: GQA-32 per-token-head FP8 (32768 tokens x 8 KV heads x head_dim 128)", "",
+           "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+           f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(fetch_dir))} -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
+           f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(write_dir))} -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
+           "",
+           f"Calibration: a {COPY_BYTES >> 20} MiB device-to-device copy reads FETCH_SIZE {fetch['copy'][0]:.0f} KiB and "
+           f"WRITE_SIZE {write['copy'][0]:.0f} KiB per dispatch; scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
+           "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched bytes (scaled) | written bytes (scaled) | traffic | algorithmic | traffic / algorithmic |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for k in ("store", "gather"):
+        fb = fetch[k][0] * 1024.0 * f_scale
+        wb = write[k][0] * 1024.0 * w_scale
+        out.append(f"| {k}_kernel | {fetch[k][1]} | {fetch[k][0]:.0f} | {write[k][0]:.0f} | {fb:.4g} | {wb:.4g} | "
+                   f"{fb + wb:.4g} | {algo[k]:.4g} | {(fb + wb) / algo[k]:.3f} |")
+    out += ["", f"kernel_source_sha256_16: {kernel_source_hash()}"]
+    for k in ("store", "gather"):
+        out.append(f"traffic_bytes_per_launch[{k}]: {fetch[k][0] * 1024.0 * f_scale + write[k][0] * 1024.0 * w_scale:.6g}")
+    with open(PROFILE_TRAFFIC, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(lines + [""] + out))
 
 
 def setup(args, torch, kvq, W):
@@ -156,7 +237,14 @@ def main():
                     choices=["fp8_per_token_head", "fp8_per_tensor", "fp8_per_head", "int4_per_token_head", "bf16"])
     ap.add_argument("--cpu-layers", type=int, default=16, help="layers of one step timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, copy 256 MiB device-to-device 3 times (reference for counter scaling)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summaries from rocprofv3 csv output and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -230,6 +318,13 @@ def main():
     dom_gbps = store_gbps if dominant == "store" else gather_gbps
     log(f"[bench] {ms_per_step:.3f} ms/step; store {avg_store_s * 1e6:.1f} us ({store_gbps:.0f} GB/s), "
         f"gather {avg_gather_s * 1e6:.1f} us ({gather_gbps:.0f} GB/s)")
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     traffic = measured_traffic()
     cpu = None
