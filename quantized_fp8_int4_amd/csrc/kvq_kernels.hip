@@ -403,7 +403,9 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&w)[N]) {
 constexpr int kOffsetLoads = 4;
 
 // Tuning knobs of the gather kernel: CB code bytes per thread chunk, U
-// chunks per thread, NTS non-temporal stores of the BF16 output.
+// chunks per thread, NTS non-temporal stores of the BF16 output, LDSS stage
+// the part's per-row scales in LDS (one load per row instead of one per
+// chunk).
 //
 // One workgroup per (sequence, logical block, part); a part is up to
 // kThreads * U chunks of the block.  The block's code bytes are contiguous in
@@ -412,7 +414,7 @@ constexpr int kOffsetLoads = 4;
 // index of the block's scale trailer.  The body is straight-line so every
 // load of a workgroup is in flight at once: lanes past the last chunk load,
 // decode and store the last chunk again (identical bytes to the same place).
-template <int HD, int MODE, int CB, int U, bool NTS>
+template <int HD, int MODE, int CB, int U, bool NTS, bool LDSS>
 __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs p) {
     constexpr uint32_t HB = row_bytes_of<MODE>(HD);
     constexpr int DW = CB / 4;                               // code dwords per chunk
@@ -454,6 +456,31 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs p) {
 
     const uint8_t* const bp = p.layer + static_cast<uint64_t>(pb) * p.block_bytes;
     const float* const trailer = reinterpret_cast<const float*>(bp + p.code_bytes);
+    auto row_scale = [&](uint32_t row) -> float {
+        if constexpr (dynamic_mode<MODE>()) {
+            return trailer[row];
+        } else if constexpr (MODE == KVQ_FP8_PER_HEAD) {
+            const uint32_t th = row >> 1;
+            const uint32_t tt = static_cast<uint32_t>((static_cast<uint64_t>(th) * p.hkv_magic) >> p.hkv_shift);
+            return p.static_scales[(row & 1u) * p.hkv + (th - tt * p.hkv)];
+        } else if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
+            return p.static_scales[row & 1u];
+        } else {
+            return 0.0f;
+        }
+    };
+    // Rows this part touches: [row_lo, row_lo + kPartRows).
+    constexpr uint32_t kPartRows = (kThreads * U + CPR - 1) / CPR + 1;
+    constexpr bool STAGE = LDSS && MODE != KVQ_BF16;
+    __shared__ float s_rows[STAGE ? kPartRows : 1];
+    const uint32_t row_lo = c0 / CPR;
+    const uint32_t nrows = nchunks / CPR;
+    float staged = 0.0f;
+    if constexpr (STAGE) {
+        // issued before the code loads, so waiting for it never waits for codes
+        if (threadIdx.x < kPartRows) staged = row_scale(min(row_lo + threadIdx.x, nrows - 1));
+    }
+
     uint32_t cw[U][DW];
     float sc[U];
     uint32_t chunk[U];
@@ -462,20 +489,18 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs p) {
         chunk[u] = min(c0 + threadIdx.x + u * kThreads, nchunks - 1);
         load_codes<DW>(bp + static_cast<uint64_t>(chunk[u]) * CB, cw[u]);
     }
+    if constexpr (STAGE) {
+        if (threadIdx.x < kPartRows) s_rows[threadIdx.x] = staged;
+        // LDS-only fence: the barrier waits for the LDS writes, not for the
+        // code loads in flight.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint32_t row = chunk[u] / CPR;
-        if constexpr (dynamic_mode<MODE>()) {
-            sc[u] = trailer[row];
-        } else if constexpr (MODE == KVQ_FP8_PER_HEAD) {
-            const uint32_t th = row >> 1;
-            const uint32_t tt = static_cast<uint32_t>((static_cast<uint64_t>(th) * p.hkv_magic) >> p.hkv_shift);
-            sc[u] = p.static_scales[(row & 1u) * p.hkv + (th - tt * p.hkv)];
-        } else if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
-            sc[u] = p.static_scales[row & 1u];
-        } else {
-            sc[u] = 0.0f;
-        }
+        for (int u = 0; u < U; ++u) sc[u] = s_rows[chunk[u] / CPR - row_lo];
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) sc[u] = row_scale(chunk[u] / CPR);
     }
 
     int64_t off = off_tail;
@@ -551,6 +576,7 @@ struct Tune {
     static constexpr int gather_cb = (MODE == KVQ_BF16) ? 16 : (MODE == KVQ_INT4_PER_TOKEN_HEAD ? 4 : 8);
     static constexpr int gather_u = (HD == 64 || MODE == KVQ_INT4_PER_TOKEN_HEAD || MODE == KVQ_BF16) ? 8 : 4;
     static constexpr bool gather_nt_store = true;
+    static constexpr bool gather_lds_scales = true;
 };
 
 StoreArgs make_store_args(const StoreLaunch& a) {
@@ -610,12 +636,12 @@ int launch_store_v(const StoreLaunch& a, void* stream) {
     return static_cast<int>(hipGetLastError());
 }
 
-template <int HD, int MODE, int CB, int U, bool NTS>
+template <int HD, int MODE, int CB, int U, bool NTS, bool LDSS>
 int launch_gather_v(const GatherLaunch& a, void* stream) {
     GatherArgs p = make_gather_args(a);
     p.parts = static_cast<uint32_t>(gather_parts(a.block_size, a.num_kv_heads, row_bytes(a.mode, HD), CB, U));
     const uint32_t grid = static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.max_blocks * p.parts);
-    hipLaunchKernelGGL((gather_kernel<HD, MODE, CB, U, NTS>), dim3(grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((gather_kernel<HD, MODE, CB, U, NTS, LDSS>), dim3(grid), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), p);
     return static_cast<int>(hipGetLastError());
 }
@@ -638,7 +664,7 @@ int launch_store_m(const StoreLaunch& a, void* stream) {
 template <int HD, int MODE>
 int launch_gather_t(const GatherLaunch& a, void* stream) {
     using T = Tune<HD, MODE>;
-    return launch_gather_v<HD, MODE, T::gather_cb, T::gather_u, T::gather_nt_store>(a, stream);
+    return launch_gather_v<HD, MODE, T::gather_cb, T::gather_u, T::gather_nt_store, T::gather_lds_scales>(a, stream);
 }
 
 template <int MODE>
