@@ -61,5 +61,24 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+HW_CHECK_SRC = os.path.join(ROOT, "tests", "hw_checks", "rcp_newton.hip")
+HW_CHECK_LIB = os.path.join(ROOT, "tests", "hw_checks", "_build", "libkvq_hwcheck.so")
+
+
+def build_hw_checks(verbose: bool = False) -> str:
+    """The device test library that checks the exact scale arithmetic."""
+    os.makedirs(os.path.dirname(HW_CHECK_LIB), exist_ok=True)
+    tmp = HW_CHECK_LIB + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", CSRC, HW_CHECK_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {HW_CHECK_SRC}:\n{r.stderr}")
+    os.replace(tmp, HW_CHECK_LIB)
+    return HW_CHECK_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_hw_checks(verbose="-v" in sys.argv))

@@ -15,7 +15,7 @@
 // elements, so the absmax reduction is a few DPP steps inside a 16-lane row.
 //
 // Exactness.  The stored quotient must be the correctly rounded FP32 x / s.
-// Each row computes r = RN(1/s) once with an IEEE division; each element then
+// Each row computes r = RN(1/s) once (rcp_exact); each element then
 // takes y = RN(|x| r), e = fma(-y, s, |x|) (exact), q = fma(e, r, y), which is
 // the correctly rounded quotient when r is the correctly rounded reciprocal
 // and nothing is subnormal (P. Markstein, "Computation of elementary
@@ -29,13 +29,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kvq_exact.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kThreads = 256;          // 4 wavefronts of 64
-constexpr int kWaves = kThreads / 64;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -100,8 +99,8 @@ struct RowQ {
 __device__ __forceinline__ RowQ row_prep(float s) {
     RowQ q;
     q.f = (s < 0x1p-64f) ? 0x1p64f : ((s > 0x1p64f) ? 0x1p-64f : 1.0f);
-    q.s = s * q.f;
-    q.r = (q.s == 0.0f) ? 0.0f : 1.0f / q.s;       // IEEE division
+    q.s = s * q.f;                                  // normal unless s == 0
+    q.r = (q.s == 0.0f) ? 0.0f : rcp_exact(q.s);
     return q;
 }
 
@@ -224,7 +223,12 @@ struct StoreArgs {
 // the codes.
 
 // Quantize the K and V chunks of one row (already loaded) and scatter them.
-template <int HD, int MODE, int LPR, int CPL, bool NTS>
+template <int LPR, int CPL, bool CONTIG>
+__device__ __forceinline__ uint32_t chunk_index(int k, uint32_t sub) {
+    return CONTIG ? sub * CPL + k : k * LPR + sub;
+}
+
+template <int HD, int MODE, int LPR, int CPL, bool CONTIG, bool NTS>
 __device__ __forceinline__ void store_row(const StoreArgs& p, uint32_t rowc, bool valid, uint32_t sub,
                                           const uint4 (&kx)[CPL], const uint4 (&vx)[CPL]) {
     constexpr uint32_t HB = row_bytes_of<MODE>(HD);
@@ -243,7 +247,7 @@ __device__ __forceinline__ void store_row(const StoreArgs& p, uint32_t rowc, boo
         if (write) {
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
-                const uint32_t c = k * LPR + sub;
+                const uint32_t c = chunk_index<LPR, CPL, CONTIG>(k, sub);
                 st16<NTS>(krow + c * 16, kx[k]);
                 st16<NTS>(vrow + c * 16, vx[k]);
             }
@@ -259,9 +263,18 @@ __device__ __forceinline__ void store_row(const StoreArgs& p, uint32_t rowc, boo
             }
             const uint32_t amk = row_max<LPR>(umax(ak.x, ak.y));
             const uint32_t amv = row_max<LPR>(umax(av.x, av.y));
-            constexpr float qmax = (MODE == KVQ_FP8_PER_TOKEN_HEAD) ? 448.0f : 7.0f;
-            sK = __uint_as_float(amk << 16) / qmax;     // IEEE division
-            sV = __uint_as_float(amv << 16) / qmax;
+            constexpr int QMAX = (MODE == KVQ_FP8_PER_TOKEN_HEAD) ? 448 : 7;
+            const float aK = __uint_as_float(amk << 16);
+            const float aV = __uint_as_float(amv << 16);
+            // Waves holding a row with absmax below 2^-100 (a subnormal or
+            // near-subnormal scale) take the IEEE division.
+            if (__builtin_amdgcn_ballot_w64(fminf(aK, aV) < 0x1p-100f) != 0) {
+                sK = aK / static_cast<float>(QMAX);
+                sV = aV / static_cast<float>(QMAX);
+            } else {
+                sK = div_by_const<QMAX>(aK);
+                sV = div_by_const<QMAX>(aV);
+            }
         } else if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
             sK = p.static_scales[0];
             sV = p.static_scales[1];
@@ -285,11 +298,20 @@ __device__ __forceinline__ void store_row(const StoreArgs& p, uint32_t rowc, boo
                 for (int k = 0; k < CPL; ++k) { ck[k] = encode_int4<false>(kx[k], qk); cv[k] = encode_int4<false>(vx[k], qv); }
             }
             if (write) {
+                if constexpr (CONTIG && CPL % 2 == 0) {
 #pragma unroll
-                for (int k = 0; k < CPL; ++k) {
-                    const uint32_t c = k * LPR + sub;
-                    st4<NTS>(krow + c * 4, ck[k]);
-                    st4<NTS>(vrow + c * 4, cv[k]);
+                    for (int k = 0; k < CPL; k += 2) {
+                        const uint32_t c = chunk_index<LPR, CPL, CONTIG>(k, sub);
+                        st8<NTS>(krow + c * 4, make_uint2(ck[k], ck[k + 1]));
+                        st8<NTS>(vrow + c * 4, make_uint2(cv[k], cv[k + 1]));
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < CPL; ++k) {
+                        const uint32_t c = chunk_index<LPR, CPL, CONTIG>(k, sub);
+                        st4<NTS>(krow + c * 4, ck[k]);
+                        st4<NTS>(vrow + c * 4, cv[k]);
+                    }
                 }
             }
         } else {
@@ -302,11 +324,20 @@ __device__ __forceinline__ void store_row(const StoreArgs& p, uint32_t rowc, boo
                 for (int k = 0; k < CPL; ++k) { ck[k] = encode_fp8<false, CLAMP>(kx[k], qk); cv[k] = encode_fp8<false, CLAMP>(vx[k], qv); }
             }
             if (write) {
+                if constexpr (CONTIG && CPL % 2 == 0) {
 #pragma unroll
-                for (int k = 0; k < CPL; ++k) {
-                    const uint32_t c = k * LPR + sub;
-                    st8<NTS>(krow + c * 8, ck[k]);
-                    st8<NTS>(vrow + c * 8, cv[k]);
+                    for (int k = 0; k < CPL; k += 2) {
+                        const uint32_t c = chunk_index<LPR, CPL, CONTIG>(k, sub);
+                        st16<NTS>(krow + c * 8, make_uint4(ck[k].x, ck[k].y, ck[k + 1].x, ck[k + 1].y));
+                        st16<NTS>(vrow + c * 8, make_uint4(cv[k].x, cv[k].y, cv[k + 1].x, cv[k + 1].y));
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < CPL; ++k) {
+                        const uint32_t c = chunk_index<LPR, CPL, CONTIG>(k, sub);
+                        st8<NTS>(krow + c * 8, ck[k]);
+                        st8<NTS>(vrow + c * 8, cv[k]);
+                    }
                 }
             }
         }
@@ -322,12 +353,12 @@ __device__ __forceinline__ void store_row(const StoreArgs& p, uint32_t rowc, boo
 // so each load instruction reads LPR * 16 contiguous bytes of every row.  A
 // wave owns RPL groups of 64 / LPR consecutive rows and loads all of them
 // before quantizing any.
-template <int HD, int MODE, int EPL, int RPL, bool NTL, bool NTS>
-__global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs p) {
+template <int HD, int MODE, int EPL, int RPL, bool NTL, bool NTS, bool CONTIG, int TPB>
+__global__ __launch_bounds__(TPB) void store_kernel(StoreArgs p) {
     constexpr int LPR = HD / EPL;
     constexpr int CPL = EPL / 8;
     constexpr int RPW = 64 / LPR;
-    constexpr int RPB = RPW * RPL * kWaves;
+    constexpr int RPB = RPW * RPL * (TPB / 64);
     static_assert(LPR >= 1 && LPR <= 32 && CPL >= 1 && RPL >= 1, "bad row split");
 
     const uint32_t lane = threadIdx.x & 63u;
@@ -347,15 +378,16 @@ __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs p) {
         // no branch, so every load of the wave stays in flight together.
 #pragma unroll
         for (int k = 0; k < CPL; ++k) {
-            kx[j][k] = ld16<NTL>(kp + k * LPR);
-            vx[j][k] = ld16<NTL>(vp + k * LPR);
+            const uint32_t c = chunk_index<LPR, CPL, CONTIG>(k, 0) + (CONTIG ? sub * (CPL - 1) : 0);
+            kx[j][k] = ld16<NTL>(kp + c);
+            vx[j][k] = ld16<NTL>(vp + c);
         }
     }
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
         const int64_t row = row0 + j * RPW;
         const bool valid = row < p.num_rows;
-        store_row<HD, MODE, LPR, CPL, NTS>(p, valid ? static_cast<uint32_t>(row) : 0u, valid, sub, kx[j], vx[j]);
+        store_row<HD, MODE, LPR, CPL, CONTIG, NTS>(p, valid ? static_cast<uint32_t>(row) : 0u, valid, sub, kx[j], vx[j]);
     }
 }
 
@@ -408,14 +440,15 @@ constexpr int kOffsetLoads = 4;
 // chunk).
 //
 // One workgroup per (sequence, logical block, part); a part is up to
-// kThreads * U chunks of the block.  The block's code bytes are contiguous in
+// TPB * U chunks of the block.  The block's code bytes are contiguous in
 // the cache with rows ordered [position][head][K, V]; a chunk of CB code bytes
 // belongs to row c / (HB / CB), and the row's FP32 scale sits at the same row
 // index of the block's scale trailer.  The body is straight-line so every
 // load of a workgroup is in flight at once: lanes past the last chunk load,
 // decode and store the last chunk again (identical bytes to the same place).
-template <int HD, int MODE, int CB, int U, bool NTS, bool LDSS>
-__global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs p) {
+template <int HD, int MODE, int CB, int U, bool NTS, bool LDSS, int TPB>
+__global__ __launch_bounds__(TPB) void gather_kernel(GatherArgs p) {
+    constexpr int kThreads = TPB;
     constexpr uint32_t HB = row_bytes_of<MODE>(HD);
     constexpr int DW = CB / 4;                               // code dwords per chunk
     constexpr uint32_t CPR = HB / CB;                        // chunks per row
@@ -573,10 +606,13 @@ struct Tune {
                                    : ((HD == 64 || MODE == KVQ_INT4_PER_TOKEN_HEAD) ? 2 : 1);
     static constexpr bool store_nt_load = true;
     static constexpr bool store_nt_store = true;
+    static constexpr bool store_contig = false;
+    static constexpr int store_tpb = 256;
     static constexpr int gather_cb = (MODE == KVQ_BF16) ? 16 : (MODE == KVQ_INT4_PER_TOKEN_HEAD ? 4 : 8);
     static constexpr int gather_u = (HD == 64 || MODE == KVQ_INT4_PER_TOKEN_HEAD || MODE == KVQ_BF16) ? 8 : 4;
     static constexpr bool gather_nt_store = true;
     static constexpr bool gather_lds_scales = true;
+    static constexpr int gather_tpb = 256;
 };
 
 StoreArgs make_store_args(const StoreLaunch& a) {
@@ -598,9 +634,9 @@ StoreArgs make_store_args(const StoreLaunch& a) {
     return p;
 }
 
-int64_t gather_parts(int64_t block_size, int64_t hkv, uint64_t hb, int cb, int u) {
+int64_t gather_parts(int64_t block_size, int64_t hkv, uint64_t hb, int cb, int u, int tpb) {
     const int64_t chunks = block_size * hkv * 2 * static_cast<int64_t>(hb / cb);
-    const int64_t per = static_cast<int64_t>(kThreads) * u;
+    const int64_t per = static_cast<int64_t>(tpb) * u;
     return (chunks + per - 1) / per;
 }
 
@@ -626,22 +662,22 @@ GatherArgs make_gather_args(const GatherLaunch& a) {
     return p;
 }
 
-template <int HD, int MODE, int EPL, int RPL, bool NTL, bool NTS>
+template <int HD, int MODE, int EPL, int RPL, bool NTL, bool NTS, bool CONTIG = false, int TPB = 256>
 int launch_store_v(const StoreLaunch& a, void* stream) {
-    constexpr int RPB = (64 / (HD / EPL)) * RPL * kWaves;
+    constexpr int RPB = (64 / (HD / EPL)) * RPL * (TPB / 64);
     const StoreArgs p = make_store_args(a);
     const uint32_t grid = static_cast<uint32_t>((a.num_rows + RPB - 1) / RPB);
-    hipLaunchKernelGGL((store_kernel<HD, MODE, EPL, RPL, NTL, NTS>), dim3(grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((store_kernel<HD, MODE, EPL, RPL, NTL, NTS, CONTIG, TPB>), dim3(grid), dim3(TPB), 0,
                        static_cast<hipStream_t>(stream), p);
     return static_cast<int>(hipGetLastError());
 }
 
-template <int HD, int MODE, int CB, int U, bool NTS, bool LDSS>
+template <int HD, int MODE, int CB, int U, bool NTS, bool LDSS, int TPB = 256>
 int launch_gather_v(const GatherLaunch& a, void* stream) {
     GatherArgs p = make_gather_args(a);
-    p.parts = static_cast<uint32_t>(gather_parts(a.block_size, a.num_kv_heads, row_bytes(a.mode, HD), CB, U));
+    p.parts = static_cast<uint32_t>(gather_parts(a.block_size, a.num_kv_heads, row_bytes(a.mode, HD), CB, U, TPB));
     const uint32_t grid = static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.max_blocks * p.parts);
-    hipLaunchKernelGGL((gather_kernel<HD, MODE, CB, U, NTS, LDSS>), dim3(grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((gather_kernel<HD, MODE, CB, U, NTS, LDSS, TPB>), dim3(grid), dim3(TPB), 0,
                        static_cast<hipStream_t>(stream), p);
     return static_cast<int>(hipGetLastError());
 }
@@ -649,7 +685,8 @@ int launch_gather_v(const GatherLaunch& a, void* stream) {
 template <int HD, int MODE>
 int launch_store_t(const StoreLaunch& a, void* stream) {
     using T = Tune<HD, MODE>;
-    return launch_store_v<HD, MODE, T::store_epl, T::store_rpl, T::store_nt_load, T::store_nt_store>(a, stream);
+    return launch_store_v<HD, MODE, T::store_epl, T::store_rpl, T::store_nt_load, T::store_nt_store,
+                          T::store_contig, T::store_tpb>(a, stream);
 }
 
 template <int MODE>
@@ -664,7 +701,8 @@ int launch_store_m(const StoreLaunch& a, void* stream) {
 template <int HD, int MODE>
 int launch_gather_t(const GatherLaunch& a, void* stream) {
     using T = Tune<HD, MODE>;
-    return launch_gather_v<HD, MODE, T::gather_cb, T::gather_u, T::gather_nt_store, T::gather_lds_scales>(a, stream);
+    return launch_gather_v<HD, MODE, T::gather_cb, T::gather_u, T::gather_nt_store, T::gather_lds_scales,
+                           T::gather_tpb>(a, stream);
 }
 
 template <int MODE>
@@ -680,7 +718,7 @@ template <int HD, int MODE>
 int64_t gather_grid_t(const GatherLaunch& a) {
     using T = Tune<HD, MODE>;
     return static_cast<int64_t>(a.num_seqs) * a.max_blocks *
-           gather_parts(a.block_size, a.num_kv_heads, row_bytes(a.mode, HD), T::gather_cb, T::gather_u);
+           gather_parts(a.block_size, a.num_kv_heads, row_bytes(a.mode, HD), T::gather_cb, T::gather_u, T::gather_tpb);
 }
 
 template <int MODE>

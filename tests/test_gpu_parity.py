@@ -150,22 +150,24 @@ def _exhaustive_rows(start, stride, seed):
 @pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD],
                          ids=["fp8_per_token_head", "int4_per_token_head"])
 def test_exhaustive_absmax_quotients(kvq, orc, mode):
-    """Every 5th positive BF16 absmax paired with every BF16 magnitude below
-    it (K: offsets 1 mod 5; V: 3 mod 5): codes, scales and dequantized values
-    bit-exact, covering subnormal inputs, subnormal scales and huge values."""
+    """Every positive finite BF16 absmax a (odd bit patterns in K, even in V)
+    paired with every BF16 magnitude <= a, random signs: codes, scales and
+    dequantized values bit-exact.  Covers every scale the dynamic modes can
+    produce (subnormal, tiny, huge) and every quotient below each."""
     _flush(f"[exhaustive] mode={W.MODE_NAMES[mode]}")
-    k = _exhaustive_rows(1, 5, seed=1)
-    v = _exhaustive_rows(3, 5, seed=2)
-    n = min(k.shape[0], v.shape[0])
-    n -= n % 16
-    k, v = k[:n].reshape(n, 1, 64), v[:n].reshape(n, 1, 64)
-    # hkv = 2: pair rows so a block holds an even number of token-heads
+    k = _exhaustive_rows(1, 2, seed=1)
+    v = _exhaustive_rows(2, 2, seed=2)
+    n = max(k.shape[0], v.shape[0])
+    n += (-n) % 2
+    pad = lambda x: torch.cat([x, torch.zeros((n - x.shape[0], 64), dtype=x.dtype)])   # all-zero rows
+    k, v = pad(k), pad(v)
+    # two KV heads per token so a block holds an even number of token-heads
     n2 = n // 2
     k, v = k.reshape(n2, 2, 64), v.reshape(n2, 2, 64)
-    pair = Pair(kvq, orc, 16, 2, 64, [mode], [(n2 + 15) // 16])
+    nb = (n2 + 15) // 16
+    pair = Pair(kvq, orc, 16, 2, 64, [mode], [nb])
     pair.store(0, k, v, torch.arange(n2, dtype=torch.int64))
     pair.assert_buffers_equal()
-    nb = (n2 + 15) // 16
     pair.gather_and_compare(0, np.arange(nb, dtype=np.int32)[None, :], [n2])
     pair.cache.close()
 
