@@ -594,16 +594,16 @@ __global__ void write_static_kernel(float* dst, StaticValues vals, int n) {
 
 // Default tuning, chosen by measurement on MI355X (32768 tokens x 8 KV heads
 // per call): 8 lanes per row, so every load instruction reads whole 128-byte
-// lines of each row; two rows per lane where a lane's row share is small
-// (head_dim 64, INT4) or the path has no arithmetic to hide latency behind
-// (BF16); non-temporal streams for data that one call touches once.  The
+// lines of each row; more rows per lane for INT4 at head_dim 128 and for BF16
+// (little arithmetic to hide latency behind); non-temporal streams for data
+// that one call touches once.  The
 // gather moves 8 code bytes (FP8) or 4 (INT4) per thread chunk, so each
 // wave-wide store writes 1 KiB of contiguous BF16 output.
 template <int HD, int MODE>
 struct Tune {
     static constexpr int store_epl = HD / 8;
     static constexpr int store_rpl = (MODE == KVQ_BF16) ? (HD == 64 ? 4 : 2)
-                                   : ((HD == 64 || MODE == KVQ_INT4_PER_TOKEN_HEAD) ? 2 : 1);
+                                   : ((MODE == KVQ_INT4_PER_TOKEN_HEAD && HD == 128) ? 2 : 1);
     static constexpr bool store_nt_load = true;
     static constexpr bool store_nt_store = true;
     static constexpr bool store_contig = false;

@@ -172,15 +172,15 @@ class DecodeState:
 
     def append(self, b: int, n: int):
         """Reserve n more tokens for sequence b; returns their slots (int64)."""
-        slots = []
-        for _ in range(n):
-            t = self.seq_lens[b]
-            j = t // self.block_size
-            if t % self.block_size == 0:
-                self.block_table[b, j] = self.free.pop()
-            slots.append(int(self.block_table[b, j]) * self.block_size + t % self.block_size)
-            self.seq_lens[b] = t + 1
-        return slots
+        t0 = self.seq_lens[b]
+        t = torch.arange(t0, t0 + n, dtype=torch.int64)
+        j = t // self.block_size
+        first_new = (t0 + self.block_size - 1) // self.block_size    # first block index not yet held
+        last = (t0 + n - 1) // self.block_size if n > 0 else first_new - 1
+        for jj in range(first_new, last + 1):
+            self.block_table[b, jj] = self.free.pop()
+        self.seq_lens[b] = t0 + n
+        return (self.block_table[b].to(torch.int64)[j] * self.block_size + t % self.block_size).tolist()
 
 
 # --------------------------------------------------------------------------
