@@ -443,6 +443,44 @@ def run_other_workload(args, torch, kvq, W):
                       step_bytes / sec / 1e9, sec * 1e3, sb, gb, store_s, gather_s, cpu, bool(parity),
                       {"sliding_store_us": round(slide_store_s * 1e6, 2), "sliding_gather_us": round(slide_gather_s * 1e6, 2),
                        "cache_MiB": round(cache.bytes["total"] / 2**20, 3)})
+    elif name == "calib":
+        # on-the-fly calibration over the GQA-32 prefill: one amax pass per layer
+        spec = W.WORKLOADS["gqa32"]
+        L, hkv, hd, n = spec["num_layers"], spec["hkv"], spec["hd"], spec["num_seqs"] * spec["seq_len"]
+        ins = [W.gqa_kv(n, hkv, hd, seed=1000 + l, device=dev) for l in range(L)]
+        amax = torch.zeros((L, 2 * hkv), dtype=torch.float32, device=dev)
+        ct = __import__("ctypes")
+        stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+        args_c = [(ct.c_void_p(ins[l][0].data_ptr()), ct.c_void_p(ins[l][1].data_ptr()), n, hkv, hd,
+                   ct.c_void_p(amax[l].data_ptr()), 0, stream) for l in range(L)]
+
+        def step(ev):
+            if ev: ev[0].record()
+            for a in args_c:
+                st_ = kvq._lib.kvq_calibrate_amax(*a)
+                if st_ != 0:
+                    raise kvq.KVQError(st_, "kvq_calibrate_amax")
+            if ev: ev[1].record(); ev[2].record()
+        sec, evs = _timed(torch, step, args.steps, args.warmup)
+        cal_s = sum(e[0].elapsed_time(e[1]) for e in evs) / (args.steps * L) / 1e3
+        cal_b = n * hkv * 4 * hd
+        t0 = time.perf_counter()
+        ref = oracle.calibrate_amax(_bits(torch, ins[0][0]), _bits(torch, ins[0][1]), hkv, hd)
+        csec = time.perf_counter() - t0
+        parity = bool(np.array_equal(amax[0].cpu().numpy().view(np.uint32), ref.view(np.uint32)))
+        gbps = cal_b / cal_s / 1e9
+        res = {"metric": "kvq_calibrate_amax GB/s (on-the-fly static-scale calibration)", "value": round(gbps, 1),
+               "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+               "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+               "vs_baseline": None, "dtype": "bf16->f32 max", "data": "synthetic",
+               "config": {"workload": "calibration amax of each GQA-32 layer's prefill K/V (32768 tokens x 8 KV heads x 128)",
+                          "layers": L},
+               "calib_us": round(cal_s * 1e6, 2),
+               "roofline": {"bound": "hbm", "kernel": "calib_kernel", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+               "cpu_baseline": {"value": round(cal_b / csec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                "sample": f"one layer's amax (single-threaded loop), {csec:.2f} s wall"},
+               "parity_vs_oracle_sampled": parity}
     else:  # decode
         spec = W.WORKLOADS["decode"]
         L, hkv, bs, S, ctx = spec["num_layers"], spec["hkv"], spec["block_size"], spec["num_seqs"], spec["context"]
@@ -537,7 +575,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gqa32", choices=["gqa32", "long80", "gptoss", "decode"],
+    ap.add_argument("--workload", default="gqa32", choices=["gqa32", "long80", "gptoss", "decode", "calib"],
                     help="gqa32 is the headline line; the others measure the remaining shapes")
     ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128], help="decode workload only")
     ap.add_argument("--mode", default="fp8_per_token_head",

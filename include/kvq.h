@@ -215,6 +215,42 @@ KVQ_API kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const i
                               int32_t num_seqs, void* out_keys, void* out_values,
                               void* stream);
 
+/*
+ * kvq_calibrate_amax -- on-the-fly calibration for the static layouts: the
+ * running absolute maximum of K and of V per KV head over a batch of new
+ * vectors.  "Per-tensor vs per-head FP8 KV cache scales", "Calibration
+ * changes which scale layout exists" (static scales estimated during warmup);
+ * "Per-token-head KV cache scale overhead", "Static per-head calibration pays
+ * once" (the scales must cover every value expected at serving time).
+ *   keys, values  device, BF16 [num_tokens][num_kv_heads][head_dim], contiguous,
+ *                 16-byte aligned.
+ *   amax          device, float [2 * num_kv_heads] (K heads, then V heads),
+ *                 4-byte aligned.  amax[i] becomes max(prior, max |x|) where
+ *                 prior is amax[i] when accumulate != 0, else 0.
+ *   num_tokens == 0 with accumulate == 0 zeroes amax.
+ *   Errors: KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED (head_dim not 64/128/256,
+ *           num_kv_heads above KVQ_MAX_STATIC_KV_HEADS, num_tokens *
+ *           num_kv_heads >= 2^31), KVQ_ERR_HIP.
+ */
+KVQ_API kvq_status kvq_calibrate_amax(const void* keys, const void* values, int64_t num_tokens,
+                                      int32_t num_kv_heads, int32_t head_dim, float* amax,
+                                      int32_t accumulate, void* stream);
+
+/*
+ * kvq_static_scales -- static scales from calibrated maxima (host arithmetic):
+ * per-head: scales[i] = RN32(amax[i] / 448) for the 2 * num_kv_heads entries;
+ * per-tensor: scales[0] = RN32(max_h amax[h] / 448) (K), scales[1] the same
+ * over the V heads.  The absolute maximum maps to the largest E4M3 value, as
+ * for the dynamic layout.  A zero maximum gives the smallest positive FP32
+ * value instead of 0, so the scale stays valid for kvq_store.
+ *   amax    host, float [2 * num_kv_heads], finite and >= 0.
+ *   mode    KVQ_FP8_PER_TENSOR or KVQ_FP8_PER_HEAD.
+ *   scales  host, float [2] or [2 * num_kv_heads], written on success.
+ *   Errors: KVQ_ERR_INVALID_ARG.
+ */
+KVQ_API kvq_status kvq_static_scales(const float* amax, int32_t num_kv_heads, kvq_mode mode,
+                                     float* scales);
+
 /* kvq_status_string -- static description of a status code. */
 KVQ_API const char* kvq_status_string(kvq_status s);
 

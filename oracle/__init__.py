@@ -62,6 +62,7 @@ def _load():
     lib.orc_dequant_fp8_n.argtypes = [P, P, P, I64]
     lib.orc_dynamic_scale_n.argtypes = [P, ctypes.c_double, P, I64]
     lib.orc_num_threads.restype = I32
+    lib.orc_calibrate_amax.argtypes = [P, P, I64, I64, I64, P, I32]
     _lib = lib
     return lib
 
@@ -152,6 +153,19 @@ def gather(g: Geometry, buf: np.ndarray, layer: int, block_table, seq_lens):
     _load().orc_gather(*g._args(), _ptr(buf), int(layer), _ptr(bt), maxb, _ptr(sl), nseq,
                        _ptr(ok), _ptr(ov))
     return ok, ov
+
+
+def calibrate_amax(keys_bits, values_bits, hkv: int, hd: int, amax=None) -> np.ndarray:
+    """Per-(K/V, head) absolute maximum over a batch, float32 [2 * hkv]
+    (K heads, then V heads); with amax given, the running maximum continues
+    from it ("Per-tensor vs per-head FP8 KV cache scales", "Calibration
+    changes which scale layout exists")."""
+    k = _c(keys_bits, np.uint16)
+    v = _c(values_bits, np.uint16)
+    n = k.size // (hkv * hd)
+    out = np.zeros(2 * hkv, np.float32) if amax is None else np.array(amax, np.float32).copy()
+    _load().orc_calibrate_amax(_ptr(k), _ptr(v), n, hkv, hd, _ptr(out), 0 if amax is None else 1)
+    return out
 
 
 def e4m3_encode(v) -> np.ndarray:

@@ -441,6 +441,37 @@ void orc_gather(int num_layers, int64_t bs, int64_t hkv, int64_t hd,
 }
 
 /* ------------------------------------------------------------------ */
+/* Calibration                                                         */
+/* ------------------------------------------------------------------ */
+
+/*
+ * On-the-fly calibration ("Per-tensor vs per-head FP8 KV cache scales",
+ * "Calibration changes which scale layout exists": static scales estimated
+ * during warmup; "Per-token-head KV cache scale overhead", "Static per-head
+ * calibration pays once": they must cover every value seen).  out[kv * hkv + h]
+ * = max(out[...], max |x| over the batch's tokens and head_dim) for K (kv = 0)
+ * and V (kv = 1); out starts at 0 unless accumulate.
+ */
+void orc_calibrate_amax(const uint16_t* keys, const uint16_t* values, int64_t num_tokens,
+                        int64_t hkv, int64_t hd, float* out, int accumulate)
+{
+    if (!accumulate)
+        for (int64_t i = 0; i < 2 * hkv; ++i) out[i] = 0.0f;
+    for (int kv = 0; kv < 2; ++kv) {
+        const uint16_t* x = kv == 0 ? keys : values;
+        for (int64_t h = 0; h < hkv; ++h) {
+            float m = out[kv * hkv + h];
+            for (int64_t t = 0; t < num_tokens; ++t)
+                for (int64_t i = 0; i < hd; ++i) {
+                    float a = fabsf(orc_bf16_to_float(x[(t * hkv + h) * hd + i]));
+                    if (a > m) m = a;
+                }
+            out[kv * hkv + h] = m;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Element-wise entry points for the pins                              */
 /* ------------------------------------------------------------------ */
 

@@ -39,7 +39,7 @@ MODE_NAMES = {BF16: "bf16", FP8_PER_TENSOR: "fp8_per_tensor", FP8_PER_HEAD: "fp8
 OK, ERR_INVALID_ARG, ERR_MODE_MISMATCH, ERR_BUFFER_TOO_SMALL, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4, -5
 
 EXPORTED_SYMBOLS = ("kvq_cache_bytes", "kvq_create_cache", "kvq_destroy_cache", "kvq_store",
-                    "kvq_gather_dequant", "kvq_status_string")
+                    "kvq_gather_dequant", "kvq_calibrate_amax", "kvq_static_scales", "kvq_status_string")
 
 
 class _Config(ctypes.Structure):
@@ -63,6 +63,8 @@ def _load_library():
     lib.kvq_destroy_cache.argtypes = [P]
     lib.kvq_store.argtypes = [P, I32, P, P, P, I64, ctypes.c_int, P, P]
     lib.kvq_gather_dequant.argtypes = [P, I32, P, I32, P, I32, P, P, P]
+    lib.kvq_calibrate_amax.argtypes = [P, P, I64, I32, I32, P, I32, P]
+    lib.kvq_static_scales.argtypes = [P, I32, ctypes.c_int, P]
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     for name in EXPORTED_SYMBOLS[:-1]:
@@ -175,6 +177,33 @@ def kvq_gather_dequant(handle, layer: int, block_table: torch.Tensor, seq_lens: 
     _check(_lib.kvq_gather_dequant(handle, int(layer), ctypes.c_void_p(bt), int(block_table.shape[1]),
                                    ctypes.c_void_p(sl), num_seqs, ctypes.c_void_p(ok), ctypes.c_void_p(ov),
                                    _stream_ptr(stream, out_keys.device)), "kvq_gather_dequant")
+
+
+def kvq_calibrate_amax(keys: torch.Tensor, values: torch.Tensor, amax: torch.Tensor,
+                       accumulate: bool = False, stream=None) -> None:
+    """Running per-(K/V, head) absolute maximum into amax (float32 [2 * Hkv] on
+    the device); keys/values bf16 [N, Hkv, hd] on the device."""
+    n = int(keys.shape[0]) if keys.dim() == 3 else 0
+    hkv, hd = int(keys.shape[1]), int(keys.shape[2])
+    kp = _dev(keys, torch.bfloat16, "keys") if n else 0
+    vp = _dev(values, torch.bfloat16, "values") if n else 0
+    ap = _dev(amax, torch.float32, "amax")
+    if keys.shape != values.shape or amax.numel() != 2 * hkv:
+        raise ValueError("keys/values must match and amax must hold 2 * num_kv_heads values")
+    _check(_lib.kvq_calibrate_amax(ctypes.c_void_p(kp), ctypes.c_void_p(vp), n, hkv, hd, ctypes.c_void_p(ap),
+                                   1 if accumulate else 0, _stream_ptr(stream, amax.device)), "kvq_calibrate_amax")
+
+
+def kvq_static_scales(amax, num_kv_heads: int, mode: int) -> list:
+    """Static scales (host floats) for kvq_store from calibrated maxima."""
+    vals = [float(x) for x in (amax.detach().cpu().reshape(-1).tolist() if isinstance(amax, torch.Tensor) else amax)]
+    if len(vals) != 2 * num_kv_heads:
+        raise ValueError("amax must hold 2 * num_kv_heads values")
+    a = (ctypes.c_float * len(vals))(*vals)
+    n_out = 2 if mode == FP8_PER_TENSOR else 2 * num_kv_heads
+    out = (ctypes.c_float * n_out)()
+    _check(_lib.kvq_static_scales(a, int(num_kv_heads), int(mode), out), "kvq_static_scales")
+    return [float(x) for x in out]
 
 
 class Cache:

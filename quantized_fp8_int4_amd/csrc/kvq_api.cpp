@@ -1,7 +1,9 @@
 // kvq_api.cpp -- the C ABI declared in include/kvq.h: argument validation,
 // static-scale bookkeeping and kernel dispatch.  Every check runs before the
 // first HIP call, so a rejected call enqueues nothing and writes nothing.
+#include <algorithm>
 #include <cmath>
+#include <limits>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -184,6 +186,51 @@ kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const int32_t* 
         std::fprintf(stderr, "[kvq] gather layer=%d mode=%s hd=%d seqs=%d max_blocks=%d\n", layer,
                      mode_name(lmode), L.head_dim, num_seqs, max_blocks_per_seq);
     return kvq::launch_gather(a, stream) == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_calibrate_amax(const void* keys, const void* values, int64_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, float* amax, int32_t accumulate, void* stream) {
+    if (num_tokens < 0 || num_kv_heads < 1 || !amax) return KVQ_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(amax) & 3u) != 0) return KVQ_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+    if (num_kv_heads > KVQ_MAX_STATIC_KV_HEADS) return KVQ_ERR_UNSUPPORTED;
+    if (num_tokens * static_cast<int64_t>(num_kv_heads) >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
+    if (num_tokens > 0) {
+        if (!keys || !values) return KVQ_ERR_INVALID_ARG;
+        if (!aligned16(keys) || !aligned16(values)) return KVQ_ERR_INVALID_ARG;
+    }
+    if (num_tokens == 0 && accumulate) return KVQ_OK;
+    kvq::CalibLaunch a;
+    a.keys = keys;
+    a.values = values;
+    a.num_rows = num_tokens * num_kv_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.amax = amax;
+    a.accumulate = accumulate;
+    return kvq::launch_calibrate(a, stream) == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_static_scales(const float* amax, int32_t num_kv_heads, kvq_mode mode, float* scales) {
+    if (!amax || !scales || num_kv_heads < 1) return KVQ_ERR_INVALID_ARG;
+    if (mode != KVQ_FP8_PER_TENSOR && mode != KVQ_FP8_PER_HEAD) return KVQ_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < 2 * num_kv_heads; ++i)
+        if (!(std::isfinite(amax[i]) && amax[i] >= 0.0f)) return KVQ_ERR_INVALID_ARG;
+    // RN32(a / 448); the smallest positive FP32 value stands in for a zero scale
+    auto scale = [](float a) {
+        const float s = a / 448.0f;
+        return s > 0.0f ? s : std::numeric_limits<float>::denorm_min();
+    };
+    if (mode == KVQ_FP8_PER_HEAD) {
+        for (int32_t i = 0; i < 2 * num_kv_heads; ++i) scales[i] = scale(amax[i]);
+    } else {
+        for (int kv = 0; kv < 2; ++kv) {
+            float m = 0.0f;
+            for (int32_t h = 0; h < num_kv_heads; ++h) m = std::max(m, amax[kv * num_kv_heads + h]);
+            scales[kv] = scale(m);
+        }
+    }
+    return KVQ_OK;
 }
 
 }  // extern "C"

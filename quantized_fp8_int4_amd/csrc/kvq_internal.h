@@ -87,4 +87,15 @@ int launch_gather(const GatherLaunch& a, void* stream);
 int64_t gather_grid(const GatherLaunch& a);
 int launch_write_static(float* dst, const float* values, int n, void* stream);
 
+struct CalibLaunch {
+    const void* keys;
+    const void* values;
+    int64_t num_rows;              // num_tokens * num_kv_heads (< 2^31)
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    float* amax;                   // device [2 * num_kv_heads]
+    int32_t accumulate;
+};
+int launch_calibrate(const CalibLaunch& a, void* stream);
+
 }  // namespace kvq

@@ -148,3 +148,36 @@ def test_odd_block_with_scales_is_unsupported(kvq):
         assert _gather(kvq, h, 0, 1) == kvq.ERR_UNSUPPORTED
     finally:
         kvq.kvq_destroy_cache(h)
+
+
+def test_static_scales_match_ieee_float32_division(kvq):
+    import numpy as np
+    rng = np.random.default_rng(3)
+    amax = rng.uniform(0, 40, 16).astype(np.float32)
+    amax[3] = 0.0
+    amax[5] = np.float32(2.0 ** -130)
+    got = np.array(kvq.kvq_static_scales(amax, 8, kvq.FP8_PER_HEAD), np.float32)
+    want = amax / np.float32(448.0)
+    want[3] = np.float32(1e-45)                      # zero maximum -> smallest positive float
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    pt = np.array(kvq.kvq_static_scales(amax, 8, kvq.FP8_PER_TENSOR), np.float32)
+    assert np.array_equal(pt, np.array([amax[:8].max(), amax[8:].max()], np.float32) / np.float32(448.0))
+    with pytest.raises(kvq.KVQError):
+        kvq.kvq_static_scales([1.0, float("nan")], 1, kvq.FP8_PER_HEAD)
+    with pytest.raises(kvq.KVQError):
+        kvq.kvq_static_scales([1.0, -1.0], 1, kvq.FP8_PER_TENSOR)
+    with pytest.raises(kvq.KVQError):
+        kvq.kvq_static_scales([1.0, 1.0], 1, kvq.FP8_PER_TOKEN_HEAD)
+
+
+def test_calibrate_argument_checks(kvq):
+    lib = kvq._lib
+    P = ctypes.c_void_p
+    assert lib.kvq_calibrate_amax(P(FAKE_DEV), P(FAKE_DEV), 4, 8, 128, None, 0, None) == kvq.ERR_INVALID_ARG
+    assert lib.kvq_calibrate_amax(P(FAKE_DEV), P(FAKE_DEV), 4, 8, 96, P(FAKE_DEV), 0, None) == kvq.ERR_UNSUPPORTED
+    assert lib.kvq_calibrate_amax(P(FAKE_DEV), P(FAKE_DEV), 4, 300, 128, P(FAKE_DEV), 0, None) == kvq.ERR_UNSUPPORTED
+    assert lib.kvq_calibrate_amax(P(FAKE_DEV), P(FAKE_DEV), -1, 8, 128, P(FAKE_DEV), 0, None) == kvq.ERR_INVALID_ARG
+    assert lib.kvq_calibrate_amax(P(FAKE_DEV + 8), P(FAKE_DEV), 4, 8, 128, P(FAKE_DEV), 0, None) == kvq.ERR_INVALID_ARG
+    assert lib.kvq_calibrate_amax(P(FAKE_DEV), P(FAKE_DEV), 4, 8, 128, P(FAKE_DEV + 2), 0, None) == kvq.ERR_INVALID_ARG
+    assert lib.kvq_calibrate_amax(None, None, 0, 8, 128, P(FAKE_DEV), 1, None) == kvq.OK     # no-op
+    assert lib.kvq_calibrate_amax(None, None, 4, 8, 128, P(FAKE_DEV), 0, None) == kvq.ERR_INVALID_ARG

@@ -276,3 +276,18 @@ def test_gather_packs_sequences_in_order(orc):
     orc.store(g, buf, 0, _bits(x), _bits(x), np.array(slots))
     ko, _ = orc.gather(g, buf, 0, st.block_table.numpy(), np.array(lens, np.int32))
     assert np.array_equal(ko, _bits(x))
+
+
+def test_calibration_amax_vs_numpy(orc):
+    """Running per-(K/V, head) absmax over two batches equals numpy's max of
+    |x| over both batches; a per-tensor scale is the max over heads."""
+    k1, v1 = W.gqa_kv(300, 3, 64, seed=41)
+    k2, v2 = W.gqa_kv(77, 3, 64, seed=42)
+    a = orc.calibrate_amax(_bits(k1), _bits(v1), 3, 64)
+    a = orc.calibrate_amax(_bits(k2), _bits(v2), 3, 64, amax=a)
+    kk = np.abs(np.concatenate([k1.float().numpy(), k2.float().numpy()]))
+    vv = np.abs(np.concatenate([v1.float().numpy(), v2.float().numpy()]))
+    want = np.concatenate([kk.max(axis=(0, 2)), vv.max(axis=(0, 2))]).astype(np.float32)
+    assert np.array_equal(a, want)
+    zero = orc.calibrate_amax(np.zeros((5, 3, 64), np.uint16), np.zeros((5, 3, 64), np.uint16), 3, 64)
+    assert (zero == 0).all()
