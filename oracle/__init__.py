@@ -63,6 +63,8 @@ def _load():
     lib.orc_dynamic_scale_n.argtypes = [P, ctypes.c_double, P, I64]
     lib.orc_num_threads.restype = I32
     lib.orc_calibrate_amax.argtypes = [P, P, I64, I64, I64, P, I32]
+    lib.orc_decode_attention.argtypes = [I32, I64, I64, I64, P, P, P, I32, P, I64, P, I64, P, I64,
+                                         ctypes.c_double, P, P]
     _lib = lib
     return lib
 
@@ -153,6 +155,25 @@ def gather(g: Geometry, buf: np.ndarray, layer: int, block_table, seq_lens):
     _load().orc_gather(*g._args(), _ptr(buf), int(layer), _ptr(bt), maxb, _ptr(sl), nseq,
                        _ptr(ok), _ptr(ov))
     return ok, ov
+
+
+def decode_attention(g: Geometry, buf: np.ndarray, layer: int, q_bits, block_table, seq_lens,
+                     sm_scale: float, with_absv: bool = False):
+    """Attention of one query token per sequence over its cached tokens, from
+    the dequantized cache values, all in double ("Per-tensor vs per-head FP8 KV
+    cache scales", "Dynamic per-token-head scales add 3.125 percent": scales
+    are read during attention).  q_bits: BF16 bits [num_seqs, H, hd].  Returns
+    out [num_seqs, H, hd] (float64) and, if asked, sum_t p_t |V^_t| alike."""
+    q = _c(q_bits, np.uint16)
+    nseq, nqh = int(q.shape[0]), int(q.shape[1])
+    bt = _c(block_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    out = np.zeros((nseq, nqh, g.hd), np.float64)
+    absv = np.zeros_like(out) if with_absv else None
+    _load().orc_decode_attention(*g._args(), _ptr(buf), int(layer), _ptr(q), nqh, _ptr(bt), int(bt.shape[1]),
+                                 _ptr(sl), nseq, float(sm_scale), _ptr(out),
+                                 _ptr(absv) if absv is not None else None)
+    return (out, absv) if with_absv else out
 
 
 def calibrate_amax(keys_bits, values_bits, hkv: int, hd: int, amax=None) -> np.ndarray:

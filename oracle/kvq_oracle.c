@@ -62,6 +62,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* Modes, in the numbering the tests pass in. */
@@ -467,6 +468,103 @@ void orc_calibrate_amax(const uint16_t* keys, const uint16_t* values, int64_t nu
                     if (a > m) m = a;
                 }
             out[kv * hkv + h] = m;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Decode attention over the quantized cache                           */
+/* ------------------------------------------------------------------ */
+
+/* Dequantized value of element i of the K (kv = 0) or V (kv = 1) row of
+ * (block, position, head), exact in double: decode(code) * s. */
+static double orc_cached_value(int mode, const uint8_t* buf, int64_t layer_base, int64_t static_base,
+                               int64_t bs, int64_t hkv, int64_t hd, int64_t blk, int64_t pos,
+                               int64_t h, int kv, int64_t i)
+{
+    const int64_t rb = orc_row_bytes(mode, hd);
+    const uint8_t* block = buf + layer_base + blk * orc_block_bytes(mode, bs, hkv, hd);
+    const uint8_t* src = block + ((pos * hkv + h) * 2 + kv) * rb;
+    if (mode == ORC_BF16)
+        return (double)orc_bf16_to_float((uint16_t)(src[2 * i] | (src[2 * i + 1] << 8)));
+    double s;
+    if (orc_has_token_scales(mode))
+        s = (double)orc_get_f32(block + orc_block_code_bytes(mode, bs, hkv, hd) + ((pos * hkv + h) * 2 + kv) * 4);
+    else if (mode == ORC_FP8_PER_TENSOR)
+        s = (double)orc_get_f32(buf + static_base + 4 * kv);
+    else
+        s = (double)orc_get_f32(buf + static_base + 4 * (kv * hkv + h));
+    if (mode == ORC_INT4_PER_TOKEN_HEAD) {
+        unsigned byte = src[i / 2];
+        return (double)orc_int4_decode((i % 2 == 0) ? (byte & 0xF) : (byte >> 4)) * s;
+    }
+    return (double)orc_e4m3_decode(src[i]) * s;
+}
+
+/*
+ * Attention of one new query token per sequence over the sequence's cached
+ * tokens, read through the block table ("Per-tensor vs per-head FP8 KV cache
+ * scales", "Dynamic per-token-head scales add 3.125 percent": the scales are
+ * read during attention).  Query head qh attends with KV head qh / (H / hkv):
+ *   score_t = sm_scale * sum_d q[b][qh][d] * K^[t][d],  p = softmax(score),
+ *   out[b][qh][d] = sum_t p_t * V^[t][d],
+ * with K^, V^ the dequantized cache values, all in double.  q: BF16 bits
+ * [num_seqs][H][hd]; out: double [num_seqs][H][hd]; a sequence of length 0
+ * gives zeros.  Also returns sum_t p_t |V^[t][d]| in out_absv (for error
+ * bounds), when out_absv is not NULL.
+ */
+void orc_decode_attention(int num_layers, int64_t bs, int64_t hkv, int64_t hd,
+                          const int32_t* modes, const int64_t* nblocks,
+                          const uint8_t* buf, int layer, const uint16_t* q, int64_t num_q_heads,
+                          const int32_t* block_table, int64_t max_blocks,
+                          const int32_t* seq_lens, int64_t num_seqs, double sm_scale,
+                          double* out, double* out_absv)
+{
+    int64_t layer_base[num_layers > 0 ? num_layers : 1];
+    int64_t static_base[num_layers > 0 ? num_layers : 1];
+    orc_layout(num_layers, bs, hkv, hd, modes, nblocks, layer_base, static_base);
+    const int mode = modes[layer];
+    const int64_t group = num_q_heads / hkv;
+
+    #pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int64_t b = 0; b < num_seqs; ++b) {
+        for (int64_t qh = 0; qh < num_q_heads; ++qh) {
+            const int64_t h = qh / group;
+            int64_t len = seq_lens[b] > 0 ? seq_lens[b] : 0;
+            if (len > max_blocks * bs) len = max_blocks * bs;
+            double* o = out + (b * num_q_heads + qh) * hd;
+            double* oa = out_absv ? out_absv + (b * num_q_heads + qh) * hd : NULL;
+            for (int64_t i = 0; i < hd; ++i) { o[i] = 0.0; if (oa) oa[i] = 0.0; }
+            if (len == 0)
+                continue;
+            double* score = (double*)malloc(sizeof(double) * (size_t)len);
+            double m = -INFINITY;
+            for (int64_t t = 0; t < len; ++t) {
+                int64_t blk = block_table[b * max_blocks + t / bs], pos = t % bs;
+                double acc = 0.0;
+                for (int64_t i = 0; i < hd; ++i)
+                    acc += (double)orc_bf16_to_float(q[(b * num_q_heads + qh) * hd + i]) *
+                           orc_cached_value(mode, buf, layer_base[layer], static_base[layer], bs, hkv, hd,
+                                            blk, pos, h, 0, i);
+                score[t] = acc * sm_scale;
+                if (score[t] > m) m = score[t];
+            }
+            double l = 0.0;
+            for (int64_t t = 0; t < len; ++t) {
+                score[t] = exp(score[t] - m);
+                l += score[t];
+            }
+            for (int64_t t = 0; t < len; ++t) {
+                int64_t blk = block_table[b * max_blocks + t / bs], pos = t % bs;
+                double p = score[t] / l;
+                for (int64_t i = 0; i < hd; ++i) {
+                    double v = orc_cached_value(mode, buf, layer_base[layer], static_base[layer], bs, hkv, hd,
+                                                blk, pos, h, 1, i);
+                    o[i] += p * v;
+                    if (oa) oa[i] += p * fabs(v);
+                }
+            }
+            free(score);
         }
     }
 }

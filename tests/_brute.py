@@ -134,3 +134,44 @@ def gather(buf, bs, hkv, hd, modes, nblocks, layer, block_table, seq_lens):
                     outs[c][row + t, h] = prod.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
         row += max(int(n), 0)
     return outs[0], outs[1]
+
+
+def dequant_f64(buf, bs, hkv, hd, modes, nblocks, layer, block_table, seq_lens):
+    """Exact dequantized K and V (float64 [sum(seq_lens), hkv, hd]): decode(code)
+    times the slot's scale, read with this module's own layout arithmetic."""
+    bases, statics, _ = layout(bs, hkv, hd, modes, nblocks)
+    mode = modes[layer]
+    rb = row_bytes(mode, hd)
+    cb = bs * hkv * 2 * rb
+    blk_bytes = cb + (bs * hkv * 8 if dynamic(mode) else 0)
+    total = int(sum(max(int(n), 0) for n in seq_lens))
+    outs = [np.zeros((total, hkv, hd)), np.zeros((total, hkv, hd))]
+    row = 0
+    for b, n in enumerate(seq_lens):
+        for t in range(max(int(n), 0)):
+            blk, pos = int(block_table[b, t // bs]), t % bs
+            for h in range(hkv):
+                for c in range(2):
+                    off = bases[layer] + blk * blk_bytes + ((pos * hkv + h) * 2 + c) * rb
+                    raw = buf[off: off + rb]
+                    if mode == BF16:
+                        outs[c][row + t, h] = torch.from_numpy(raw.copy()).view(torch.bfloat16).double().numpy()
+                        continue
+                    if dynamic(mode):
+                        so = bases[layer] + blk * blk_bytes + cb + ((pos * hkv + h) * 2 + c) * 4
+                        s = float(buf[so: so + 4].view(np.float32)[0])
+                    elif mode == FP8_PER_TENSOR:
+                        s = float(buf[statics[layer] + 4 * c: statics[layer] + 4 * c + 4].view(np.float32)[0])
+                    else:
+                        o = statics[layer] + 4 * (c * hkv + h)
+                        s = float(buf[o: o + 4].view(np.float32)[0])
+                    if mode == INT4_PER_TOKEN_HEAD:
+                        nib = np.empty(hd, np.int64)
+                        nib[0::2] = raw & 0xF
+                        nib[1::2] = raw >> 4
+                        dec = np.where(nib >= 8, nib - 16, nib).astype(np.float64)
+                    else:
+                        dec = torch.from_numpy(raw.copy()).view(torch.float8_e4m3fn).double().numpy()
+                    outs[c][row + t, h] = dec * s
+        row += max(int(n), 0)
+    return outs[0], outs[1]

@@ -1,0 +1,77 @@
+"""Pins of the oracle's decode attention over the quantized cache: it equals
+a plain numpy float64 softmax attention over independently dequantized
+values (tests/_brute.py), and reduces to known answers in special cases."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import _brute
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _numpy_attention(q, kh, vh, lens, group, sm_scale):
+    """Reference softmax attention (float64) over packed [sum(lens), hkv, hd] values."""
+    nseq, nqh, hd = q.shape
+    out = np.zeros((nseq, nqh, hd))
+    row = 0
+    for b, n in enumerate(lens):
+        for qh in range(nqh):
+            if n == 0:
+                continue
+            k = kh[row: row + n, qh // group]
+            v = vh[row: row + n, qh // group]
+            s = (k @ q[b, qh]) * sm_scale
+            p = np.exp(s - s.max())
+            out[b, qh] = (p / p.sum()) @ v
+        row += n
+    return out
+
+
+def _setup(orc, mode, hkv=2, hd=64, bs=16, nblocks=12, lens=(37, 0, 80), seed=0):
+    g = orc.Geometry(bs, hkv, hd, [mode], [nblocks])
+    buf = orc.new_cache(g)
+    st = W.DecodeState(len(lens), bs, nblocks, 6, seed=seed)
+    slots = []
+    for b, n in enumerate(lens):
+        slots += st.append(b, n)
+    k, v = W.gqa_kv(len(slots), hkv, hd, seed=seed + 1)
+    sc = None
+    if mode == W.FP8_PER_TENSOR:
+        sc = np.array([0.05, 0.04], np.float32)
+    elif mode == W.FP8_PER_HEAD:
+        sc = np.linspace(0.02, 0.06, 2 * hkv).astype(np.float32)
+    orc.store(g, buf, 0, _bits(k), _bits(v), np.array(slots), sc)
+    return g, buf, st
+
+
+@pytest.mark.parametrize("mode", [W.BF16, W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD,
+                                  W.INT4_PER_TOKEN_HEAD])
+@pytest.mark.parametrize("group", [1, 4])
+def test_attention_matches_numpy_over_brute_force_dequant(orc, mode, group):
+    hkv, hd = 2, 64
+    g, buf, st = _setup(orc, mode, hkv, hd)
+    lens = st.seq_lens
+    q = torch.randn((len(lens), hkv * group, hd), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    out = orc.decode_attention(g, buf, 0, _bits(q), st.block_table.numpy(), lens, 0.125)
+    kh, vh = _brute.dequant_f64(buf, g.bs, hkv, hd, [mode], [12], 0, st.block_table.numpy(), lens)
+    ref = _numpy_attention(q.double().numpy(), kh, vh, lens, group, 0.125)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_special_cases(orc):
+    hkv, hd = 1, 64
+    g, buf, st = _setup(orc, W.BF16, hkv, hd, lens=(1, 5))
+    kh, vh = _brute.dequant_f64(buf, g.bs, hkv, hd, [W.BF16], [12], 0, st.block_table.numpy(), [1, 5])
+    q = torch.randn((2, 1, hd), generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    out = orc.decode_attention(g, buf, 0, _bits(q), st.block_table.numpy(), [1, 5], 0.3)
+    assert np.array_equal(out[0, 0], vh[0, 0])                   # one token: its value
+    uni = orc.decode_attention(g, buf, 0, _bits(q), st.block_table.numpy(), [1, 5], 0.0)
+    assert np.allclose(uni[1, 0], vh[1:6, 0].mean(axis=0), rtol=1e-14, atol=1e-14)  # zero scale: mean
+    empty = orc.decode_attention(g, buf, 0, _bits(q), st.block_table.numpy(), [0, 0], 0.3)
+    assert not empty.any()
+    out2, absv = orc.decode_attention(g, buf, 0, _bits(q), st.block_table.numpy(), [1, 5], 0.3, with_absv=True)
+    assert np.array_equal(out2, out) and (absv >= np.abs(out) - 1e-12).all()
