@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gqa32_fp8_per_token_head.md")
-KERNEL_SOURCE = os.path.join(ROOT, "quantized_fp8_int4_amd", "csrc", "kvq_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_fp8_int4_amd", "csrc", f)
+                  for f in ("kvq_kernels.hip", "kvq_device.h", "kvq_exact.h")]
 METRIC = "kvq_store/gather GB/s and % of HBM peak; cached tokens/s (per-token-head FP8)"
 COPY_BYTES = 256 << 20
 PROFILE_KERNEL_TRACE = os.path.join(ROOT, "profiles", "kernel_trace_gqa32_fp8_per_token_head.md")
@@ -57,8 +58,12 @@ def algorithmic_bytes(mode, hd, hkv, bs, token_heads):
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources the store and gather kernels are built from."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

@@ -29,175 +29,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "kvq_exact.h"
+#include "kvq_device.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-template <int MODE>
-constexpr uint32_t row_bytes_of(int hd) {
-    return MODE == KVQ_BF16 ? 2 * hd : (MODE == KVQ_INT4_PER_TOKEN_HEAD ? hd / 2 : hd);
-}
-
-template <int MODE>
-constexpr bool dynamic_mode() {
-    return MODE == KVQ_FP8_PER_TOKEN_HEAD || MODE == KVQ_INT4_PER_TOKEN_HEAD;
-}
-
-// ---------------------------------------------------------------- helpers
-
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
-}
-
-// Max over the LPR adjacent lanes that own one row (LPR a power of two <= 32).
-// quad_perm [1,0,3,2] and [2,3,0,1] make each quad uniform, row_half_mirror
-// joins quad pairs, row_mirror joins half-rows, a swizzle with xor 16 joins
-// rows.
-template <int LPR>
-__device__ __forceinline__ uint32_t row_max(uint32_t v) {
-    if constexpr (LPR >= 2) v = umax(v, dpp<0xB1>(v));
-    if constexpr (LPR >= 4) v = umax(v, dpp<0x4E>(v));
-    if constexpr (LPR >= 8) v = umax(v, dpp<0x141>(v));
-    if constexpr (LPR >= 16) v = umax(v, dpp<0x140>(v));
-    if constexpr (LPR >= 32)
-        v = umax(v, static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x401F)));
-    return v;
-}
-
-// Packed max of |bf16| bit patterns (sign cleared): unsigned order of
-// 0x7FFF-masked BF16 bits is the order of finite magnitudes.
-__device__ __forceinline__ u16x2 abs_bits2(uint32_t w) {
-    return __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
-}
-
-__device__ __forceinline__ u16x2 absmax_chunk(const uint4& w, u16x2 acc) {
-    u16x2 m01 = __builtin_elementwise_max(abs_bits2(w.x), abs_bits2(w.y));
-    u16x2 m23 = __builtin_elementwise_max(abs_bits2(w.z), abs_bits2(w.w));
-    return __builtin_elementwise_max(acc, __builtin_elementwise_max(m01, m23));
-}
-
-// Per-row quotient constants: s' = s * f, r = RN(1 / s') (0 when s == 0).
-struct RowQ {
-    float s;
-    float r;
-    float f;
-};
-
-__device__ __forceinline__ RowQ row_prep(float s) {
-    RowQ q;
-    q.f = (s < 0x1p-64f) ? 0x1p64f : ((s > 0x1p64f) ? 0x1p-64f : 1.0f);
-    q.s = s * q.f;                                  // normal unless s == 0
-    q.r = (q.s == 0.0f) ? 0.0f : rcp_exact(q.s);
-    return q;
-}
-
-// RN(|x| / s) for |x| >= 0.  CLAMP bounds y for static scales, whose
-// quotients may overflow; any y >= 2^20 saturates both formats anyway.
-template <bool PRESCALE, bool CLAMP>
-__device__ __forceinline__ float quotient(float x, const RowQ& q) {
-    float ax = fabsf(x);
-    if constexpr (PRESCALE) ax *= q.f;
-    float y = ax * q.r;
-    if constexpr (CLAMP) y = fminf(y, 0x1p20f);
-    const float e = fmaf(-y, q.s, ax);
-    return fmaf(e, q.r, y);
-}
-
-// 8 BF16 values -> 8 E4M3FN codes.  The magnitude is clamped to 448 and
-// converted (round to nearest even); the sign bits of the inputs are then
-// copied into the code bytes, so zero and tiny quotients keep their sign.
-template <bool PRESCALE, bool CLAMP>
-__device__ __forceinline__ uint2 encode_fp8(const uint4& w, const RowQ& q) {
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    uint32_t out[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const uint32_t w0 = ws[2 * i], w1 = ws[2 * i + 1];
-        const float q0 = fminf(quotient<PRESCALE, CLAMP>(bf16_lo(w0), q), 448.0f);
-        const float q1 = fminf(quotient<PRESCALE, CLAMP>(bf16_hi(w0), q), 448.0f);
-        const float q2 = fminf(quotient<PRESCALE, CLAMP>(bf16_lo(w1), q), 448.0f);
-        const float q3 = fminf(quotient<PRESCALE, CLAMP>(bf16_hi(w1), q), 448.0f);
-        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, pk, true);
-        // high byte of each BF16 (bit 7 = sign) -> byte lanes 0..3
-        const uint32_t sign = __builtin_amdgcn_perm(w1, w0, 0x07050301u) & 0x80808080u;
-        out[i] = static_cast<uint32_t>(pk) | sign;
-    }
-    return make_uint2(out[0], out[1]);
-}
-
-// 8 BF16 values -> 8 two's-complement nibbles, element 2j in the low nibble
-// of byte j.  Adding 1.5 * 2^23 rounds the signed quotient to the nearest
-// integer, ties to even, and leaves that integer in the low mantissa bits.
-// Dynamic INT4 quotients are at most a / RN(a / 7) < 7.5 in magnitude, so the
-// rounded value already lies in [-7, 7] and the clamp to [-8, 7] is a no-op.
-template <bool PRESCALE>
-__device__ __forceinline__ uint32_t encode_int4(const uint4& w, const RowQ& q) {
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    uint32_t acc = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t xb = (e & 1) ? (ws[e >> 1] & 0xFFFF0000u) : (ws[e >> 1] << 16);
-        const float mag = quotient<PRESCALE, false>(__uint_as_float(xb), q);
-        const float sq = __uint_as_float((__float_as_uint(mag) & 0x7FFFFFFFu) | (xb & 0x80000000u));
-        const float t = sq + 12582912.0f;
-        acc |= (__float_as_uint(t) & 0xFu) << (4 * e);
-    }
-    return acc;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    const f32x2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// ------------------------------------------------------- memory helpers
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// NT selects the non-temporal form: data read or written once by this call
-// is streamed instead of kept in the caches.
-template <bool NT>
-__device__ __forceinline__ uint4 ld16(const void* p) {
-    u32x4 v;
-    if constexpr (NT) v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
-    else v = *static_cast<const u32x4*>(p);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-template <bool NT>
-__device__ __forceinline__ void st16(void* p, const uint4& x) {
-    const u32x4 v = {x.x, x.y, x.z, x.w};
-    if constexpr (NT) __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
-    else *static_cast<u32x4*>(p) = v;
-}
-
-template <bool NT>
-__device__ __forceinline__ void st8(void* p, const uint2& x) {
-    const u32x2 v = {x.x, x.y};
-    if constexpr (NT) __builtin_nontemporal_store(v, static_cast<u32x2*>(p));
-    else *static_cast<u32x2*>(p) = v;
-}
-
-template <bool NT>
-__device__ __forceinline__ void st4(void* p, uint32_t x) {
-    if constexpr (NT) __builtin_nontemporal_store(x, static_cast<uint32_t*>(p));
-    else *static_cast<uint32_t*>(p) = x;
-}
+using namespace dev;
 
 // ------------------------------------------------------------------ store
 
@@ -590,82 +428,6 @@ __global__ void write_static_kernel(float* dst, StaticValues vals, int n) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = vals.v[i];
 }
 
-// ------------------------------------------------------------ calibration
-
-struct CalibArgs {
-    const uint4* __restrict__ keys;
-    const uint4* __restrict__ values;
-    uint32_t* __restrict__ amax;   // FP32 bits of non-negative maxima
-    int64_t num_rows;
-    uint32_t hkv;
-    uint32_t hkv_magic;
-    uint32_t hkv_shift;
-};
-
-// Running absolute maximum per (K/V, KV head).  Rows are read with the store
-// kernel's layout (8 lanes per row, whole 128-byte lines per instruction);
-// each row's maximum goes into a per-workgroup LDS table with an LDS atomic
-// max, and each workgroup then merges its table into amax with one global
-// atomic max per entry.  Non-negative FP32 values order like their bits.
-template <int HD, int RPL>
-__global__ __launch_bounds__(256) void calib_kernel(CalibArgs p) {
-    constexpr int LPR = 8;
-    constexpr int CPL = HD / (8 * LPR);
-    constexpr int RPW = 64 / LPR;
-    constexpr int RPB = RPW * 4;
-    __shared__ uint32_t smax[2 * KVQ_MAX_STATIC_KV_HEADS];
-    for (uint32_t i = threadIdx.x; i < 2 * p.hkv; i += 256) smax[i] = 0;
-    __syncthreads();
-
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t sub = lane % LPR;
-    // each iteration covers RPL groups of RPB rows; all of a lane's loads for
-    // the iteration go out before any row is reduced
-    const int64_t supers = (p.num_rows + RPB * RPL - 1) / (RPB * RPL);
-    for (int64_t g = blockIdx.x; g < supers; g += gridDim.x) {
-        uint4 kx[RPL][CPL], vx[RPL][CPL];
-#pragma unroll
-        for (int j = 0; j < RPL; ++j) {
-            const int64_t row = (g * RPL + j) * RPB + wave * RPW + lane / LPR;
-            const uint64_t rowc = row < p.num_rows ? static_cast<uint64_t>(row) : 0u;
-            const uint4* kp = p.keys + rowc * (HD / 8) + sub;
-            const uint4* vp = p.values + rowc * (HD / 8) + sub;
-#pragma unroll
-            for (int k = 0; k < CPL; ++k) {
-                kx[j][k] = ld16<true>(kp + k * LPR);
-                vx[j][k] = ld16<true>(vp + k * LPR);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < RPL; ++j) {
-            const int64_t row = (g * RPL + j) * RPB + wave * RPW + lane / LPR;
-            u16x2 ak = {0, 0}, av = {0, 0};
-#pragma unroll
-            for (int k = 0; k < CPL; ++k) {
-                ak = absmax_chunk(kx[j][k], ak);
-                av = absmax_chunk(vx[j][k], av);
-            }
-            const uint32_t mk = row_max<LPR>(umax(ak.x, ak.y)) << 16;
-            const uint32_t mv = row_max<LPR>(umax(av.x, av.y)) << 16;
-            if (row < p.num_rows && sub == 0) {
-                const uint32_t r32 = static_cast<uint32_t>(row);
-                const uint32_t t = static_cast<uint32_t>((static_cast<uint64_t>(r32) * p.hkv_magic) >> p.hkv_shift);
-                const uint32_t h = r32 - t * p.hkv;
-                atomicMax(&smax[h], mk);
-                atomicMax(&smax[p.hkv + h], mv);
-            }
-        }
-    }
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < 2 * p.hkv; i += 256)
-        if (smax[i] != 0) atomicMax(&p.amax[i], smax[i]);
-}
-
-__global__ void zero_kernel(uint32_t* dst, int n) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = 0;
-}
-
 // --------------------------------------------------------------- dispatch
 
 // Default tuning, chosen by measurement on MI355X (32768 tokens x 8 KV heads
@@ -836,38 +598,6 @@ int launch_gather(const GatherLaunch& a, void* stream) {
         case KVQ_FP8_PER_TOKEN_HEAD: return launch_gather_m<KVQ_FP8_PER_TOKEN_HEAD>(a, stream);
         default: return launch_gather_m<KVQ_INT4_PER_TOKEN_HEAD>(a, stream);
     }
-}
-
-int launch_calibrate(const CalibLaunch& a, void* stream) {
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    const int n = 2 * a.num_kv_heads;
-    if (!a.accumulate) {
-        hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<uint32_t*>(a.amax), n);
-        const int e = static_cast<int>(hipGetLastError());
-        if (e != 0 || a.num_rows == 0) return e;
-    }
-    if (a.num_rows == 0) return 0;
-    CalibArgs p;
-    p.keys = static_cast<const uint4*>(a.keys);
-    p.values = static_cast<const uint4*>(a.values);
-    p.amax = reinterpret_cast<uint32_t*>(a.amax);
-    p.num_rows = a.num_rows;
-    p.hkv = static_cast<uint32_t>(a.num_kv_heads);
-    const DivMagic dm = div_magic(p.hkv);
-    p.hkv_magic = dm.magic;
-    p.hkv_shift = dm.shift;
-    constexpr int kCalibRpl = 4;                         // rows per lane per iteration
-    // A capped grid keeps the final global atomics (2 * Hkv per workgroup, all
-    // on the same few addresses) from serialising behind each other.
-    constexpr int64_t kCalibMaxGrid = 512;
-    const int64_t supers = (a.num_rows + 32 * kCalibRpl - 1) / (32 * kCalibRpl);
-    const uint32_t grid = static_cast<uint32_t>(supers < kCalibMaxGrid ? supers : kCalibMaxGrid);
-    switch (a.head_dim) {
-        case 64: hipLaunchKernelGGL((calib_kernel<64, kCalibRpl>), dim3(grid), dim3(256), 0, st, p); break;
-        case 128: hipLaunchKernelGGL((calib_kernel<128, kCalibRpl>), dim3(grid), dim3(256), 0, st, p); break;
-        default: hipLaunchKernelGGL((calib_kernel<256, kCalibRpl>), dim3(grid), dim3(256), 0, st, p); break;
-    }
-    return static_cast<int>(hipGetLastError());
 }
 
 int launch_write_static(float* dst, const float* values, int n, void* stream) {
