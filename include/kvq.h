@@ -251,6 +251,55 @@ KVQ_API kvq_status kvq_calibrate_amax(const void* keys, const void* values, int6
 KVQ_API kvq_status kvq_static_scales(const float* amax, int32_t num_kv_heads, kvq_mode mode,
                                      float* scales);
 
+/*
+ * kvq_decode_attention_workspace -- device workspace bytes that
+ * kvq_decode_attention needs for this cache and call shape (0 when the
+ * sequences need not be split).  Host arithmetic only; no device call.
+ * Arguments as for kvq_decode_attention.
+ *   Errors: KVQ_ERR_INVALID_ARG.
+ */
+KVQ_API kvq_status kvq_decode_attention_workspace(const kvq_cache* c, int32_t num_q_heads,
+                                                  int32_t max_blocks_per_seq, int32_t num_seqs,
+                                                  uint64_t* bytes);
+
+/*
+ * kvq_decode_attention -- attention of one new query token per sequence over
+ * that sequence's cached tokens of one layer, reading the codes and their
+ * scales straight from the paged blocks ("Per-tensor vs per-head FP8 KV cache
+ * scales" and "Dynamic per-token-head scales add 3.125 percent": the scales
+ * are read during attention; "FP8 KV cache layer skipping vs per-head
+ * scales": BF16 layers are attended alike).  Query head g uses KV head
+ * g / (num_q_heads / num_kv_heads):
+ *   out[b][g] = sum_t softmax_t(sm_scale * q[b][g] . K^[t]) * V^[t]
+ * over t < seq_lens[b], with K^, V^ the dequantized cache values.
+ *   q             device, BF16 [num_seqs][num_q_heads][head_dim], 16-byte aligned.
+ *   num_q_heads   a positive multiple of the cache's num_kv_heads.
+ *   block_table, max_blocks_per_seq, seq_lens, num_seqs
+ *                 as for kvq_gather_dequant; lengths are clamped to
+ *                 [0, max_blocks_per_seq * block_size].  A token whose
+ *                 block-table entry lies outside [0, layer blocks) takes no
+ *                 part; a sequence left with no token gives zeros.
+ *   sm_scale      finite softmax scale (1/sqrt(head_dim) for the usual model).
+ *   out           device, BF16 [num_seqs][num_q_heads][head_dim], 16-byte aligned.
+ *   workspace     device, 16-byte aligned, at least the bytes that
+ *                 kvq_decode_attention_workspace reports (NULL when 0).  Owned
+ *                 by the caller; it may be reused once the call's work on
+ *                 the stream has finished.
+ *   Results are FP32-accumulated: scores exactly of the widened codes, the
+ *   softmax weights times per-token V scales rounded to BF16 before the value
+ *   product, the output rounded to BF16.
+ *   A static-scale layer must have been stored to at least once.
+ *   num_seqs == 0 is a no-op returning KVQ_OK.
+ *   Errors: KVQ_ERR_INVALID_ARG, KVQ_ERR_BUFFER_TOO_SMALL (workspace),
+ *           KVQ_ERR_UNSUPPORTED (a block of 2 GiB or more,
+ *           max_blocks_per_seq * block_size >= 2^31, block bytes not a
+ *           multiple of 16), KVQ_ERR_HIP.
+ */
+KVQ_API kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q, int32_t num_q_heads,
+                                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                                        const int32_t* seq_lens, int32_t num_seqs, float sm_scale, void* out,
+                                        void* workspace, uint64_t workspace_bytes, void* stream);
+
 /* kvq_status_string -- static description of a status code. */
 KVQ_API const char* kvq_status_string(kvq_status s);
 

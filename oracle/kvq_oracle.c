@@ -509,8 +509,10 @@ static double orc_cached_value(int mode, const uint8_t* buf, int64_t layer_base,
  *   score_t = sm_scale * sum_d q[b][qh][d] * K^[t][d],  p = softmax(score),
  *   out[b][qh][d] = sum_t p_t * V^[t][d],
  * with K^, V^ the dequantized cache values, all in double.  q: BF16 bits
- * [num_seqs][H][hd]; out: double [num_seqs][H][hd]; a sequence of length 0
- * gives zeros.  Also returns sum_t p_t |V^[t][d]| in out_absv (for error
+ * [num_seqs][H][hd]; out: double [num_seqs][H][hd].  Lengths are clamped to
+ * [0, max_blocks * bs]; a token whose block-table entry does not name a block
+ * of the layer takes no part (no score, no weight), and a sequence with no
+ * token left gives zeros.  Also returns sum_t p_t |V^[t][d]| in out_absv (for error
  * bounds), when out_absv is not NULL.
  */
 void orc_decode_attention(int num_layers, int64_t bs, int64_t hkv, int64_t hd,
@@ -541,6 +543,10 @@ void orc_decode_attention(int num_layers, int64_t bs, int64_t hkv, int64_t hd,
             double m = -INFINITY;
             for (int64_t t = 0; t < len; ++t) {
                 int64_t blk = block_table[b * max_blocks + t / bs], pos = t % bs;
+                if (blk < 0 || blk >= nblocks[layer]) {
+                    score[t] = -INFINITY;
+                    continue;
+                }
                 double acc = 0.0;
                 for (int64_t i = 0; i < hd; ++i)
                     acc += (double)orc_bf16_to_float(q[(b * num_q_heads + qh) * hd + i]) *
@@ -549,6 +555,10 @@ void orc_decode_attention(int num_layers, int64_t bs, int64_t hkv, int64_t hd,
                 score[t] = acc * sm_scale;
                 if (score[t] > m) m = score[t];
             }
+            if (m == -INFINITY) {           /* no token of this sequence is in the layer */
+                free(score);
+                continue;
+            }
             double l = 0.0;
             for (int64_t t = 0; t < len; ++t) {
                 score[t] = exp(score[t] - m);
@@ -556,6 +566,8 @@ void orc_decode_attention(int num_layers, int64_t bs, int64_t hkv, int64_t hd,
             }
             for (int64_t t = 0; t < len; ++t) {
                 int64_t blk = block_table[b * max_blocks + t / bs], pos = t % bs;
+                if (blk < 0 || blk >= nblocks[layer])
+                    continue;
                 double p = score[t] / l;
                 for (int64_t i = 0; i < hd; ++i) {
                     double v = orc_cached_value(mode, buf, layer_base[layer], static_base[layer], bs, hkv, hd,

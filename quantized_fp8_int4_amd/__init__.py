@@ -39,7 +39,8 @@ MODE_NAMES = {BF16: "bf16", FP8_PER_TENSOR: "fp8_per_tensor", FP8_PER_HEAD: "fp8
 OK, ERR_INVALID_ARG, ERR_MODE_MISMATCH, ERR_BUFFER_TOO_SMALL, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4, -5
 
 EXPORTED_SYMBOLS = ("kvq_cache_bytes", "kvq_create_cache", "kvq_destroy_cache", "kvq_store",
-                    "kvq_gather_dequant", "kvq_calibrate_amax", "kvq_static_scales", "kvq_status_string")
+                    "kvq_gather_dequant", "kvq_calibrate_amax", "kvq_static_scales",
+                    "kvq_decode_attention_workspace", "kvq_decode_attention", "kvq_status_string")
 
 
 class _Config(ctypes.Structure):
@@ -65,6 +66,8 @@ def _load_library():
     lib.kvq_gather_dequant.argtypes = [P, I32, P, I32, P, I32, P, P, P]
     lib.kvq_calibrate_amax.argtypes = [P, P, I64, I32, I32, P, I32, P]
     lib.kvq_static_scales.argtypes = [P, I32, ctypes.c_int, P]
+    lib.kvq_decode_attention_workspace.argtypes = [P, I32, I32, I32, ctypes.POINTER(ctypes.c_uint64)]
+    lib.kvq_decode_attention.argtypes = [P, I32, P, I32, P, I32, P, I32, ctypes.c_float, P, P, ctypes.c_uint64, P]
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     for name in EXPORTED_SYMBOLS[:-1]:
@@ -206,6 +209,43 @@ def kvq_static_scales(amax, num_kv_heads: int, mode: int) -> list:
     return [float(x) for x in out]
 
 
+def kvq_decode_attention_workspace(handle, num_q_heads: int, max_blocks_per_seq: int, num_seqs: int) -> int:
+    """Device workspace bytes kvq_decode_attention needs for this call shape."""
+    n = ctypes.c_uint64(0)
+    _check(_lib.kvq_decode_attention_workspace(handle, int(num_q_heads), int(max_blocks_per_seq), int(num_seqs),
+                                               ctypes.byref(n)), "kvq_decode_attention_workspace")
+    return int(n.value)
+
+
+def kvq_decode_attention(handle, layer: int, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                         sm_scale: float, out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> None:
+    """q: bf16 [num_seqs, H, hd] on the device; block_table int32 [num_seqs,
+    max_blocks]; seq_lens int32 [num_seqs]; out: bf16 [num_seqs, H, hd];
+    workspace: a device tensor of at least kvq_decode_attention_workspace()
+    bytes (None when that is 0)."""
+    num_seqs = int(seq_lens.numel())
+    if num_seqs == 0:
+        return
+    qp = _dev(q, torch.bfloat16, "q")
+    op = _dev(out, torch.bfloat16, "out")
+    bt = _dev(block_table, torch.int32, "block_table")
+    sl = _dev(seq_lens, torch.int32, "seq_lens")
+    if q.dim() != 3 or q.shape[0] != num_seqs or out.shape != q.shape:
+        raise ValueError("q and out must be [num_seqs, num_q_heads, head_dim]")
+    if block_table.dim() != 2 or block_table.shape[0] != num_seqs:
+        raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
+    wp, wb = 0, 0
+    if workspace is not None:
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        wp, wb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(_lib.kvq_decode_attention(handle, int(layer), ctypes.c_void_p(qp), int(q.shape[1]), ctypes.c_void_p(bt),
+                                     int(block_table.shape[1]), ctypes.c_void_p(sl), num_seqs, float(sm_scale),
+                                     ctypes.c_void_p(op), ctypes.c_void_p(wp), wb, _stream_ptr(stream, q.device)),
+           "kvq_decode_attention")
+
+
 class Cache:
     """A cache buffer (zeroed torch uint8 tensor of kvq_cache_bytes().total
     bytes) plus its library handle."""
@@ -245,4 +285,15 @@ class Cache:
             out = (torch.empty(shape, dtype=torch.bfloat16, device=self.device),
                    torch.empty(shape, dtype=torch.bfloat16, device=self.device))
         kvq_gather_dequant(self.handle, layer, block_table, seq_lens, out[0], out[1], stream)
+        return out
+
+    def decode_attention(self, layer, q, block_table, seq_lens, sm_scale, out=None, workspace=None, stream=None):
+        """Fused decode attention over one layer; returns bf16 [num_seqs, H, hd].
+        Allocates the workspace with torch when none is given."""
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            nbytes = kvq_decode_attention_workspace(self.handle, q.shape[1], block_table.shape[1], seq_lens.numel())
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device) if nbytes else None
+        kvq_decode_attention(self.handle, layer, q, block_table, seq_lens, sm_scale, out, workspace, stream)
         return out

@@ -188,6 +188,79 @@ kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const int32_t* 
     return kvq::launch_gather(a, stream) == 0 ? KVQ_OK : KVQ_ERR_HIP;
 }
 
+namespace {
+
+kvq_status attention_args(const kvq_cache* c, int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t num_seqs) {
+    if (!c || num_seqs < 0 || max_blocks_per_seq < 1) return KVQ_ERR_INVALID_ARG;
+    const kvq::Layout& L = c->layout;
+    if (num_q_heads < 1 || num_q_heads % L.num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
+    if ((static_cast<int64_t>(max_blocks_per_seq) << L.bs_log2) >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(num_seqs) * num_q_heads >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
+    return KVQ_OK;
+}
+
+}  // namespace
+
+kvq_status kvq_decode_attention_workspace(const kvq_cache* c, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                          int32_t num_seqs, uint64_t* bytes) {
+    if (!bytes) return KVQ_ERR_INVALID_ARG;
+    const kvq_status st = attention_args(c, num_q_heads, max_blocks_per_seq, num_seqs);
+    if (st != KVQ_OK) return st;
+    const kvq::Layout& L = c->layout;
+    *bytes = num_seqs == 0 ? 0
+                           : kvq::attention_plan(L.block_size, L.num_kv_heads, L.head_dim, num_q_heads,
+                                                 max_blocks_per_seq, num_seqs).workspace_bytes;
+    return KVQ_OK;
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q, int32_t num_q_heads,
+                                const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                int32_t num_seqs, float sm_scale, void* out, void* workspace,
+                                uint64_t workspace_bytes, void* stream) {
+    if (!c || layer < 0 || layer >= c->layout.num_layers || num_seqs < 0) return KVQ_ERR_INVALID_ARG;
+    if (num_seqs == 0) return KVQ_OK;
+    const kvq_status st = attention_args(c, num_q_heads, max_blocks_per_seq, num_seqs);
+    if (st != KVQ_OK) return st;
+    if (!q || !block_table || !seq_lens || !out || !std::isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+        return KVQ_ERR_INVALID_ARG;
+    const kvq::Layout& L = c->layout;
+    const int32_t lmode = L.mode[layer];
+    if (kvq::has_static_scales(lmode) && c->static_values[layer].empty()) return KVQ_ERR_INVALID_ARG;
+    if (L.block_bytes[layer] % 16 != 0) return KVQ_ERR_UNSUPPORTED;
+    if (L.block_bytes[layer] >= (uint64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
+    const kvq::AttnPlan plan =
+        kvq::attention_plan(L.block_size, L.num_kv_heads, L.head_dim, num_q_heads, max_blocks_per_seq, num_seqs);
+    if (plan.grid >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
+    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+        return KVQ_ERR_BUFFER_TOO_SMALL;
+
+    kvq::AttnLaunch a;
+    a.layer = c->dev + L.layer_base[layer];
+    a.static_scales = reinterpret_cast<const float*>(c->dev + L.static_base[layer]);
+    a.q = q;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.workspace = workspace;
+    a.num_blocks = L.num_blocks[layer];
+    a.block_bytes = L.block_bytes[layer];
+    a.code_bytes = L.code_bytes[layer];
+    a.num_kv_heads = L.num_kv_heads;
+    a.num_q_heads = num_q_heads;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.bs_log2 = L.bs_log2;
+    a.head_dim = L.head_dim;
+    a.mode = lmode;
+    a.sm_scale = sm_scale;
+    if (log_enabled())
+        std::fprintf(stderr, "[kvq] attention layer=%d mode=%s hd=%d seqs=%d H=%d splits=%d tiles/split=%d\n", layer,
+                     mode_name(lmode), L.head_dim, num_seqs, num_q_heads, plan.splits, plan.tiles_per_split);
+    return kvq::launch_attention(a, plan, stream) == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
 kvq_status kvq_calibrate_amax(const void* keys, const void* values, int64_t num_tokens, int32_t num_kv_heads,
                               int32_t head_dim, float* amax, int32_t accumulate, void* stream) {
     if (num_tokens < 0 || num_kv_heads < 1 || !amax) return KVQ_ERR_INVALID_ARG;

@@ -1,0 +1,640 @@
+// kvq_attention.hip -- fused paged decode attention over the quantized cache
+// (gfx950).  One new query token per sequence attends over the sequence's
+// cached tokens; the kernel reads FP8 / INT4 codes and their scales (or BF16
+// rows) straight from the paged blocks, so no dequantized copy of the cache
+// is ever written.  Scales are read during attention, as "Per-tensor vs
+// per-head FP8 KV cache scales" and "Dynamic per-token-head scales add 3.125
+// percent" describe; the layer-skip BF16 layers ("FP8 KV cache layer
+// skipping vs per-head scales") are attended by the same kernel.
+//
+// Arithmetic.  Codes widen exactly to BF16 (every E4M3 value and every INT4
+// value / 16 is a BF16 number), so both products run on MFMA with exact
+// operands and FP32 accumulation; the scales stay out of the products:
+//   S[t][g]  = (sum_d code_K[t][d] * q[g][d]) * s_K[t] * sm_scale * log2(e)
+//   P'[t][g] = BF16(exp2(S[t][g] - m[g]) * s_V[t])            (per-token-head)
+//   O[g][d] += sum_t P'[t][g] * code_V[t][d]
+// with an online (running-maximum) softmax over 16-token tiles; static
+// scales are applied once, s_K folded into the score factor and s_V into the
+// final output.
+//
+// Work split.  A workgroup holds one wave per KV head of a run of heads and
+// walks a range of tiles of one sequence; the waves of a workgroup read
+// adjacent rows of the same blocks, and share the blocks' scale lines.  Each
+// wave serves up to 16 query heads of its KV head (the MFMA N dimension).
+// Long sequences are cut into splits whose partial (O, m, l) a second kernel
+// combines; with one split the first kernel writes the output itself.
+//
+// MFMA operand layouts used here (gfx950, lane l, r = l % 16, q = l / 16):
+//   mfma_f32_16x16x32_bf16:     A[m=r][k=8q+i], B[k=8q+i][n=r], D[m=4q+i][n=r]
+//   mfma_f32_16x16x16_bf16_1k:  A[m=r][k=4q+i], B[k=4q+i][n=r], D[m=4q+i][n=r]
+// Q K^T takes m = token, n = query head and its k slots permuted so that lane
+// l holds the contiguous dims [q*hd/4, (q+1)*hd/4) of token r's K row; the
+// result D[t=4q+i][g=r] is already the B operand of P V (k = token, n =
+// head), which takes m = 16 dims spaced J = hd/16 apart, so that lane l
+// loads J contiguous dims of 4 tokens' V rows and ends up holding hd/4
+// contiguous output dims of query head r.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+using namespace dev;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 16;                 // tokens per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int HD, int MODE>
+struct Geo {
+    static constexpr int J = HD / 16;                 // 16-dim output tiles of P V
+    static constexpr int KSTEPS = HD / 32;            // 32-dim k steps of Q K^T
+    static constexpr int BITS = MODE == KVQ_BF16 ? 16 : (MODE == KVQ_INT4_PER_TOKEN_HEAD ? 4 : 8);
+    static constexpr int RB = HD * BITS / 8;          // bytes of one K or V row
+    static constexpr int KB = RB / 4;                 // K bytes per lane (hd/4 dims)
+    static constexpr int VB = J * BITS / 8;           // V bytes per lane and token (J dims)
+    static constexpr int KW = (KB + 3) / 4;
+    static constexpr int VW = (VB + 3) / 4;
+    static constexpr bool DYN = dynamic_mode<MODE>();
+    // INT4 codes widen to n / 16 (exact); the 16 goes back in with the scales.
+    static constexpr float CODE_UNIT = MODE == KVQ_INT4_PER_TOKEN_HEAD ? 16.0f : 1.0f;
+};
+
+struct AttnArgs {
+    const uint8_t* layer;          // layer base
+    const float* statics;          // layer's static scale table (static modes)
+    const uint16_t* q;             // BF16 [num_seqs][H][hd]
+    const int32_t* block_table;    // [num_seqs][max_blocks]
+    const int32_t* seq_lens;       // [num_seqs]
+    uint16_t* out;                 // BF16 [num_seqs][H][hd]      (one split)
+    float* part_o;                 // [num_seqs][H][splits][hd]   (several splits)
+    float* part_ml;                // [num_seqs][H][splits][2]
+    int64_t block_bytes;
+    int64_t num_blocks;
+    int32_t code_bytes;            // offset of the scale trailer in a block
+    int32_t hkv;
+    int32_t num_q_heads;
+    int32_t group;                 // query heads per KV head
+    int32_t qgroups;               // ceil(group / 16)
+    int32_t heads_per_wg;          // waves per workgroup
+    int32_t head_chunks;           // hkv / heads_per_wg
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t splits;
+    int32_t tiles_per_split;
+    int32_t bs_log2;
+    int32_t max_len;               // max_blocks * block_size, 0 for a layer without blocks
+    uint32_t total_wg;
+    float c;                       // sm_scale * log2(e)
+};
+
+// ------------------------------------------------------------ lane helpers
+
+template <int N, bool NT>
+__device__ __forceinline__ void load_n(uint32_t* dst, const uint8_t* p) {
+    if constexpr (N >= 16) {
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k) {
+            const uint4 v = ld16<NT>(p + 16 * k);
+            dst[4 * k] = v.x;
+            dst[4 * k + 1] = v.y;
+            dst[4 * k + 2] = v.z;
+            dst[4 * k + 3] = v.w;
+        }
+    } else if constexpr (N == 8) {
+        u32x2 v;
+        if constexpr (NT) v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        else v = *reinterpret_cast<const u32x2*>(p);
+        dst[0] = v[0];
+        dst[1] = v[1];
+    } else if constexpr (N == 4) {
+        if constexpr (NT) dst[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+        else dst[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+        static_assert(N == 2, "row slice of 2, 4, 8 or a multiple of 16 bytes");
+        dst[0] = *reinterpret_cast<const uint16_t*>(p);
+    }
+}
+
+// Pair (a, b) of a wave's lanes l and l ^ 16, and of l and l ^ 32, through
+// the gfx950 row swaps: each lane receives its partner's value beside its own.
+__device__ __forceinline__ float max_q4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_q4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Two E4M3 codes (byte pair HI of w) -> two BF16 values, exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// INT4 nibble k of w -> n / 16 as FP32, exact.
+template <int K>
+__device__ __forceinline__ float int4_over16(uint32_t w) {
+    return __builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(w >> (4 * K)));
+}
+
+// K step j of the lane's K slice -> 8 BF16 A-operand values (dims 8j .. 8j+7
+// of the slice).
+template <int HD, int MODE>
+__device__ __forceinline__ bf16x8 k_operand(const uint32_t* k, int j) {
+    uint32_t o[4];
+    if constexpr (MODE == KVQ_BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = k[4 * j + e];
+    } else if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+        const uint32_t w = k[j];
+        o[0] = pack_bf16(int4_over16<0>(w), int4_over16<1>(w));
+        o[1] = pack_bf16(int4_over16<2>(w), int4_over16<3>(w));
+        o[2] = pack_bf16(int4_over16<4>(w), int4_over16<5>(w));
+        o[3] = pack_bf16(int4_over16<6>(w), int4_over16<7>(w));
+    } else {
+        o[0] = fp8x2_to_bf16x2<false>(k[2 * j]);
+        o[1] = fp8x2_to_bf16x2<true>(k[2 * j]);
+        o[2] = fp8x2_to_bf16x2<false>(k[2 * j + 1]);
+        o[3] = fp8x2_to_bf16x2<true>(k[2 * j + 1]);
+    }
+    const u32x4 v = {o[0], o[1], o[2], o[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// V operands of the J P V tiles from the lane's 4 token slices
+// (v[i] = J dims of token 4q+i): A_j = (V[0][j], V[1][j], V[2][j], V[3][j]).
+template <int HD, int MODE>
+__device__ __forceinline__ void v_operands(const uint32_t (*v)[Geo<HD, MODE>::VW], s16x4* a) {
+    constexpr int J = Geo<HD, MODE>::J;
+    if constexpr (MODE == KVQ_BF16) {
+#pragma unroll
+        for (int j = 0; j < J; j += 2) {
+            // dword j/2 of each token holds dims j (low half) and j+1 (high half)
+            const uint32_t lo01 = __builtin_amdgcn_perm(v[1][j / 2], v[0][j / 2], 0x05040100u);
+            const uint32_t lo23 = __builtin_amdgcn_perm(v[3][j / 2], v[2][j / 2], 0x05040100u);
+            const uint32_t hi01 = __builtin_amdgcn_perm(v[1][j / 2], v[0][j / 2], 0x07060302u);
+            const uint32_t hi23 = __builtin_amdgcn_perm(v[3][j / 2], v[2][j / 2], 0x07060302u);
+            const u32x2 x = {lo01, lo23};
+            const u32x2 y = {hi01, hi23};
+            a[j] = __builtin_bit_cast(s16x4, x);
+            a[j + 1] = __builtin_bit_cast(s16x4, y);
+        }
+    } else if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int w = j / 8, sh = 4 * (j % 8);
+            const uint32_t p01 = pack_bf16(__builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(v[0][w] >> sh)),
+                                           __builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(v[1][w] >> sh)));
+            const uint32_t p23 = pack_bf16(__builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(v[2][w] >> sh)),
+                                           __builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(v[3][w] >> sh)));
+            const u32x2 x = {p01, p23};
+            a[j] = __builtin_bit_cast(s16x4, x);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < J; j += 2) {
+            // bytes b, b+1 of dword j/4 hold dims j, j+1; interleave two tokens
+            const int w = j / 4, b = j % 4;
+            const uint32_t sel = static_cast<uint32_t>(b) | (static_cast<uint32_t>(4 + b) << 8) |
+                                 (static_cast<uint32_t>(b + 1) << 16) | (static_cast<uint32_t>(5 + b) << 24);
+            const uint32_t t01 = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
+            const uint32_t t23 = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
+            const u32x2 x = {fp8x2_to_bf16x2<false>(t01), fp8x2_to_bf16x2<false>(t23)};
+            const u32x2 y = {fp8x2_to_bf16x2<true>(t01), fp8x2_to_bf16x2<true>(t23)};
+            a[j] = __builtin_bit_cast(s16x4, x);
+            a[j + 1] = __builtin_bit_cast(s16x4, y);
+        }
+    }
+}
+
+// ------------------------------------------------------------ the kernel
+
+template <int HD, int MODE>
+struct Tile {
+    uint32_t k[Geo<HD, MODE>::KW];
+    uint32_t v[4][Geo<HD, MODE>::VW];
+    f32x2 s[4];                    // (s_K, s_V) of tokens 4q+i (per-token-head modes)
+    uint32_t ok;                   // bit i: token 4q+i's block names a block of the layer
+};
+
+// Loads of tile tau of sequence b for KV head h.  Entries of the block table
+// that do not name a block of the layer read block 0 instead and are masked.
+// With blocks of 16 or more tokens a tile lies in one block, whose id (blk,
+// read by the caller one tile ahead) is the same for the whole wave.
+template <int HD, int MODE, bool SMALL_BS>
+__device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt_row, int blk, int h, int tau, int r,
+                                          int q4, Tile<HD, MODE>& T) {
+    using G = Geo<HD, MODE>;
+    const int t0 = tau * kTile;
+    const int bs_mask = (1 << a.bs_log2) - 1;
+    if constexpr (!SMALL_BS) {
+        // (layers hold at most 2^31 blocks, so the unsigned compare also
+        // rejects negative ids)
+        const bool ok = static_cast<uint32_t>(blk) < static_cast<uint32_t>(a.num_blocks);
+        const uint32_t ublk = ok ? static_cast<uint32_t>(blk) : 0u;
+        const uint8_t* base = a.layer + static_cast<uint64_t>(ublk) * static_cast<uint64_t>(a.block_bytes);
+        const int pos0 = t0 & bs_mask;
+        load_n<G::KB, true>(T.k, base + (((pos0 + r) * a.hkv + h) * 2) * G::RB + q4 * G::KB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int pos = pos0 + 4 * q4 + i;
+            load_n<G::VB, true>(T.v[i], base + (((pos * a.hkv + h) * 2) + 1) * G::RB + r * G::VB);
+            if constexpr (G::DYN)
+                T.s[i] = *reinterpret_cast<const f32x2*>(base + a.code_bytes + (pos * a.hkv + h) * 8);
+        }
+        T.ok = ok ? 0xFu : 0u;
+    } else {
+        const int last = a.max_blocks - 1;
+        {
+            const int t = t0 + r;
+            int blk = bt_row[min(t >> a.bs_log2, last)];
+            blk = static_cast<uint64_t>(static_cast<int64_t>(blk)) < static_cast<uint64_t>(a.num_blocks) ? blk : 0;
+            const uint8_t* base = a.layer + static_cast<int64_t>(blk) * a.block_bytes;
+            load_n<G::KB, true>(T.k, base + ((((t & bs_mask) * a.hkv) + h) * 2) * G::RB + q4 * G::KB);
+        }
+        uint32_t ok = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 4 * q4 + i;
+            int blk = bt_row[min(t >> a.bs_log2, last)];
+            const bool good = static_cast<uint64_t>(static_cast<int64_t>(blk)) < static_cast<uint64_t>(a.num_blocks);
+            blk = good ? blk : 0;
+            ok |= good ? (1u << i) : 0u;
+            const uint8_t* base = a.layer + static_cast<int64_t>(blk) * a.block_bytes;
+            const int pos = t & bs_mask;
+            load_n<G::VB, true>(T.v[i], base + (((pos * a.hkv + h) * 2) + 1) * G::RB + r * G::VB);
+            if constexpr (G::DYN)
+                T.s[i] = *reinterpret_cast<const f32x2*>(base + a.code_bytes + (pos * a.hkv + h) * 8);
+        }
+        T.ok = ok;
+    }
+}
+
+// An empty use of every register of T, so that no load of T is moved past
+// the point where the loop may exit.
+template <int HD, int MODE>
+__device__ __forceinline__ void consume(const Tile<HD, MODE>& T) {
+    using G = Geo<HD, MODE>;
+#pragma unroll
+    for (int w = 0; w < G::KW; ++w) asm volatile("" ::"v"(T.k[w]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int w = 0; w < G::VW; ++w) asm volatile("" ::"v"(T.v[i][w]));
+        if constexpr (G::DYN) asm volatile("" ::"v"(T.s[i][0]), "v"(T.s[i][1]));
+    }
+}
+
+template <int HD, int MODE>
+struct State {
+    f32x4 o[Geo<HD, MODE>::J];     // O^T[dim slot 4q+i][head r], one per 16-dim tile
+    float m;                       // running maximum of head r (log2 domain)
+    float l;                       // this lane's share of the running sum
+};
+
+template <int HD, int MODE>
+__device__ __forceinline__ void tile_step(const Tile<HD, MODE>& T, State<HD, MODE>& st, const bf16x8* qb, int t0,
+                                          int len, int q4, float k_factor) {
+    using G = Geo<HD, MODE>;
+    f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < G::KSTEPS; ++j)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(T.k, j), qb[j], sacc, 0, 0, 0);
+
+    float s[4];
+    bool valid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        valid[i] = (t0 + 4 * q4 + i < len) && ((T.ok >> i) & 1u);
+        const float f = G::DYN ? T.s[i][0] * k_factor : k_factor;
+        s[i] = valid[i] ? sacc[i] * f : -INFINITY;
+    }
+    const float tmax = max_q4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+    const float mnew = fmaxf(st.m, tmax);
+    const float mref = mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mref);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - mref);
+    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    st.m = mnew;
+
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = valid[i] ? (G::DYN ? p[i] * (T.s[i][1] * G::CODE_UNIT) : p[i]) : 0.0f;
+    const u32x2 pb = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
+    const s16x4 b = __builtin_bit_cast(s16x4, pb);
+
+    // masked tokens may hold any bytes (NaN codes included): zero them
+    uint32_t vz[4][G::VW];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int w = 0; w < G::VW; ++w) vz[i][w] = valid[i] ? T.v[i][w] : 0u;
+    s16x4 av[G::J];
+    v_operands<HD, MODE>(vz, av);
+#pragma unroll
+    for (int j = 0; j < G::J; ++j) {
+        st.o[j] *= alpha;
+        st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], b, st.o[j], 0, 0, 0);
+    }
+}
+
+template <int HD, int MODE, bool SMALL_BS>
+__global__ void __launch_bounds__(512) attention_kernel(AttnArgs a) {
+    using G = Geo<HD, MODE>;
+    // Workgroup -> work item, spreading consecutive items over one XCD
+    // (workgroups are dealt to the 8 XCDs round robin).
+    const uint32_t p = blockIdx.x;
+    const uint32_t xcd = p % 8u, slot = p / 8u;
+    const uint32_t per = a.total_wg / 8u, rem = a.total_wg % 8u;
+    uint32_t item = xcd * per + min(xcd, rem) + slot;
+    const int qg = static_cast<int>(item % static_cast<uint32_t>(a.qgroups));
+    item /= static_cast<uint32_t>(a.qgroups);
+    const int chunk = static_cast<int>(item % static_cast<uint32_t>(a.head_chunks));
+    item /= static_cast<uint32_t>(a.head_chunks);
+    const int split = static_cast<int>(item % static_cast<uint32_t>(a.splits));
+    const int b = static_cast<int>(item / static_cast<uint32_t>(a.splits));
+
+    const int lane = threadIdx.x & 63;
+    const int h = chunk * a.heads_per_wg + static_cast<int>(threadIdx.x >> 6);
+    const int r = lane & 15, q4 = lane >> 4;
+
+    const int len = max(0, min(a.seq_lens[b], a.max_len));
+    const int ntiles = (len + kTile - 1) / kTile;
+    const int tbeg = split * a.tiles_per_split;
+    const int tend = min(ntiles, tbeg + a.tiles_per_split);
+    if (a.splits > 1 && tbeg >= tend) return;      // the combine reads only non-empty splits
+
+    // query head of this lane's column
+    const int gi = qg * 16 + r;
+    const bool qvalid = gi < a.group;
+    const int qh = h * a.group + (qvalid ? gi : 0);
+    bf16x8 qb[G::KSTEPS];
+    {
+        const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.num_q_heads + qh) * HD + q4 * (HD / 4);
+#pragma unroll
+        for (int j = 0; j < G::KSTEPS; ++j) {
+            const uint4 v = qvalid ? ld16<false>(qp + 8 * j) : make_uint4(0, 0, 0, 0);
+            const u32x4 w = {v.x, v.y, v.z, v.w};
+            qb[j] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    float k_factor = a.c * G::CODE_UNIT;
+    float v_factor = 1.0f;
+    if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
+        k_factor *= a.statics[0];
+        v_factor = a.statics[1];
+    } else if constexpr (MODE == KVQ_FP8_PER_HEAD) {
+        k_factor *= a.statics[h];
+        v_factor = a.statics[a.hkv + h];
+    }
+
+    State<HD, MODE> st;
+#pragma unroll
+    for (int j = 0; j < G::J; ++j) st.o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    st.m = -INFINITY;
+    st.l = 0.0f;
+
+    const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+    if (tbeg < tend) {
+        // Two tiles in flight: the next tile's loads are issued before the
+        // current tile's arithmetic.  An odd count ends on a fully masked
+        // tile (tokens at or past the split's end take no part), so the loop
+        // has no exit between a load and its use; loads past the end re-read
+        // the last tile, and the final prefetch is consumed at the exit.
+        const int lim = min(len, tend * kTile);
+        auto block_of = [&](int tau) { return SMALL_BS ? 0 : bt_row[(tau * kTile) >> a.bs_log2]; };
+        Tile<HD, MODE> ta, tb;
+        load_tile<HD, MODE, SMALL_BS>(a, bt_row, block_of(tbeg), h, tbeg, r, q4, ta);
+        int nb = block_of(min(tbeg + 1, tend - 1));
+        // (the scheduling barriers keep each prefetch ahead of the arithmetic)
+        for (int tau = tbeg; tau < tend; tau += 2) {
+            load_tile<HD, MODE, SMALL_BS>(a, bt_row, nb, h, min(tau + 1, tend - 1), r, q4, tb);
+            nb = block_of(min(tau + 2, tend - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            tile_step<HD, MODE>(ta, st, qb, tau * kTile, lim, q4, k_factor);
+            __builtin_amdgcn_sched_barrier(0);
+            load_tile<HD, MODE, SMALL_BS>(a, bt_row, nb, h, min(tau + 2, tend - 1), r, q4, ta);
+            nb = block_of(min(tau + 3, tend - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            tile_step<HD, MODE>(tb, st, qb, (tau + 1) * kTile, lim, q4, k_factor);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        consume(ta);
+    }
+
+    const float l = sum_q4(st.l);
+    // lane holds dims J*(4*q4 + i) + j, i < 4, j < J: hd/4 contiguous dims
+    const int64_t row = static_cast<int64_t>(b) * a.num_q_heads + qh;
+    if (a.splits == 1) {
+        if (!qvalid) return;
+        const float inv = l > 0.0f ? v_factor / l : 0.0f;
+        uint16_t* op = a.out + row * HD + q4 * (HD / 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t w[G::J / 2];
+#pragma unroll
+            for (int j = 0; j < G::J; j += 2) w[j / 2] = pack_bf16(st.o[j][i] * inv, st.o[j + 1][i] * inv);
+            uint16_t* dst = op + i * G::J;
+            if constexpr (G::J >= 8) {
+#pragma unroll
+                for (int k = 0; k < G::J / 8; ++k) st16<false>(dst + 8 * k, make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]));
+            } else {
+                st8<false>(dst, make_uint2(w[0], w[1]));
+            }
+        }
+    } else {
+        if (!qvalid) return;
+        const int64_t prow = row * a.splits + split;
+        float* op = a.part_o + prow * HD + q4 * (HD / 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < G::J; j += 4) {
+                const uint4 w = make_uint4(__float_as_uint(st.o[j][i] * v_factor), __float_as_uint(st.o[j + 1][i] * v_factor),
+                                           __float_as_uint(st.o[j + 2][i] * v_factor),
+                                           __float_as_uint(st.o[j + 3][i] * v_factor));
+                st16<false>(op + i * G::J + j, w);
+            }
+        }
+        if (q4 == 0) {
+            const u32x2 ml = {__float_as_uint(st.m), __float_as_uint(l)};
+            *reinterpret_cast<u32x2*>(a.part_ml + prow * 2) = ml;
+        }
+    }
+}
+
+// Combine of the splits' partial results: one wave per (sequence, query head).
+struct CombineArgs {
+    const float* part_o;
+    const float* part_ml;
+    const int32_t* seq_lens;
+    uint16_t* out;
+    int64_t rows;                  // num_seqs * H
+    int32_t num_q_heads;
+    int32_t splits;
+    int32_t tiles_per_split;
+    int32_t max_len;               // as in AttnArgs
+};
+
+template <int HD>
+__global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
+    constexpr int DPL = HD / 64;   // dims per lane
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= a.rows) return;
+    const int lane = threadIdx.x & 63;
+    const int b = static_cast<int>(row / a.num_q_heads);
+    const int len = max(0, min(a.seq_lens[b], a.max_len));
+    const int ntiles = (len + kTile - 1) / kTile;
+    const int nsp = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+    const float* ml = a.part_ml + row * a.splits * 2;
+    float M = -INFINITY;
+    for (int s = 0; s < nsp; ++s) M = fmaxf(M, ml[2 * s]);
+    float L = 0.0f;
+    float acc[DPL];
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) acc[d] = 0.0f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < nsp; ++s) {
+            const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
+            L += w * ml[2 * s + 1];
+            const float* o = a.part_o + (row * a.splits + s) * HD + lane * DPL;
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) acc[d] += w * o[d];
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    uint16_t* dst = a.out + row * HD + lane * DPL;
+    if constexpr (DPL == 1) {
+        dst[0] = static_cast<uint16_t>(pack_bf16(acc[0] * inv, 0.0f) & 0xFFFFu);
+    } else {
+        uint32_t w[DPL / 2];
+#pragma unroll
+        for (int d = 0; d < DPL; d += 2) w[d / 2] = pack_bf16(acc[d] * inv, acc[d + 1] * inv);
+        if constexpr (DPL == 2) st4<false>(dst, w[0]);
+        else st8<false>(dst, make_uint2(w[0], w[1]));
+    }
+}
+
+template <int HD, int MODE>
+void launch_attention_v(const AttnArgs& p, int threads, bool small_bs, hipStream_t st) {
+    if (small_bs) hipLaunchKernelGGL((attention_kernel<HD, MODE, true>), dim3(p.total_wg), dim3(threads), 0, st, p);
+    else hipLaunchKernelGGL((attention_kernel<HD, MODE, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
+}
+
+template <int HD>
+void launch_attention_hd(const AttnArgs& p, int mode, int threads, bool small_bs, hipStream_t st) {
+    switch (mode) {
+        case KVQ_BF16: launch_attention_v<HD, KVQ_BF16>(p, threads, small_bs, st); break;
+        case KVQ_FP8_PER_TENSOR: launch_attention_v<HD, KVQ_FP8_PER_TENSOR>(p, threads, small_bs, st); break;
+        case KVQ_FP8_PER_HEAD: launch_attention_v<HD, KVQ_FP8_PER_HEAD>(p, threads, small_bs, st); break;
+        case KVQ_FP8_PER_TOKEN_HEAD: launch_attention_v<HD, KVQ_FP8_PER_TOKEN_HEAD>(p, threads, small_bs, st); break;
+        default: launch_attention_v<HD, KVQ_INT4_PER_TOKEN_HEAD>(p, threads, small_bs, st); break;
+    }
+}
+
+}  // namespace
+
+AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t num_q_heads,
+                        int32_t max_blocks, int32_t num_seqs) {
+    AttnPlan pl{};
+    int hpw = 1;
+    while (hpw < 8 && num_kv_heads % (2 * hpw) == 0) hpw *= 2;
+    pl.heads_per_wg = hpw;
+    const int group = num_q_heads / num_kv_heads;
+    pl.qgroups = (group + 15) / 16;
+    const int64_t units = static_cast<int64_t>(num_seqs) * (num_kv_heads / hpw) * pl.qgroups;
+    const int64_t max_tiles = (static_cast<int64_t>(max_blocks) * block_size + kTile - 1) / kTile;
+    // About 4096 waves fill the chip with a few waves per SIMD; a split keeps
+    // at least 8 tiles so that the partial results stay small next to the
+    // cache bytes it reads.
+    constexpr int64_t kTargetWaves = 4096, kMinTilesPerSplit = 8;
+    const int64_t want = (kTargetWaves / hpw + units - 1) / units;
+    const int64_t cap = (max_tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
+    int64_t splits = want < cap ? want : cap;
+    if (splits < 1) splits = 1;
+    int64_t tps = (max_tiles + splits - 1) / splits;
+    if (tps < 1) tps = 1;
+    splits = (max_tiles + tps - 1) / tps;
+    if (splits < 1) splits = 1;
+    pl.splits = static_cast<int32_t>(splits);
+    pl.tiles_per_split = static_cast<int32_t>(tps);
+    pl.grid = units * splits;
+    pl.workspace_bytes = splits > 1 ? static_cast<uint64_t>(num_seqs) * num_q_heads * splits * (head_dim + 2) * 4 : 0;
+    return pl;
+}
+
+int launch_attention(const AttnLaunch& a, const AttnPlan& pl, void* stream) {
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    AttnArgs p;
+    p.layer = a.layer;
+    p.statics = a.static_scales;
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.block_table = a.block_table;
+    p.seq_lens = a.seq_lens;
+    p.out = static_cast<uint16_t*>(a.out);
+    const uint64_t o_bytes = static_cast<uint64_t>(a.num_seqs) * a.num_q_heads * pl.splits * a.head_dim * 4;
+    p.part_o = pl.splits > 1 ? static_cast<float*>(a.workspace) : nullptr;
+    p.part_ml = pl.splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + o_bytes) : nullptr;
+    p.block_bytes = static_cast<int64_t>(a.block_bytes);
+    p.num_blocks = a.num_blocks;
+    p.code_bytes = static_cast<int32_t>(a.code_bytes);
+    p.hkv = a.num_kv_heads;
+    p.num_q_heads = a.num_q_heads;
+    p.group = a.num_q_heads / a.num_kv_heads;
+    p.qgroups = pl.qgroups;
+    p.heads_per_wg = pl.heads_per_wg;
+    p.head_chunks = a.num_kv_heads / pl.heads_per_wg;
+    p.max_blocks = a.max_blocks;
+    p.num_seqs = a.num_seqs;
+    p.splits = pl.splits;
+    p.tiles_per_split = pl.tiles_per_split;
+    p.bs_log2 = a.bs_log2;
+    p.max_len = a.num_blocks > 0 ? a.max_blocks << a.bs_log2 : 0;
+    p.total_wg = static_cast<uint32_t>(pl.grid);
+    p.c = a.sm_scale * kLog2e;
+    const int threads = 64 * pl.heads_per_wg;
+    const bool small_bs = a.bs_log2 < 4;
+    switch (a.head_dim) {
+        case 64: launch_attention_hd<64>(p, a.mode, threads, small_bs, st); break;
+        case 128: launch_attention_hd<128>(p, a.mode, threads, small_bs, st); break;
+        default: launch_attention_hd<256>(p, a.mode, threads, small_bs, st); break;
+    }
+    int e = static_cast<int>(hipGetLastError());
+    if (e != 0 || pl.splits == 1) return e;
+    CombineArgs c;
+    c.part_o = p.part_o;
+    c.part_ml = p.part_ml;
+    c.seq_lens = a.seq_lens;
+    c.out = p.out;
+    c.rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+    c.num_q_heads = a.num_q_heads;
+    c.splits = pl.splits;
+    c.tiles_per_split = pl.tiles_per_split;
+    c.max_len = p.max_len;
+    const uint32_t grid = static_cast<uint32_t>((c.rows + 3) / 4);
+    switch (a.head_dim) {
+        case 64: hipLaunchKernelGGL(combine_kernel<64>, dim3(grid), dim3(256), 0, st, c); break;
+        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, st, c); break;
+        default: hipLaunchKernelGGL(combine_kernel<256>, dim3(grid), dim3(256), 0, st, c); break;
+    }
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace kvq

@@ -98,4 +98,38 @@ struct CalibLaunch {
 };
 int launch_calibrate(const CalibLaunch& a, void* stream);
 
+// ---- decode attention (kvq_attention.hip) ------------------------------
+struct AttnPlan {
+    int32_t splits;                // tile ranges per sequence
+    int32_t tiles_per_split;       // 16-token tiles per range
+    int32_t heads_per_wg;          // KV heads (waves) per workgroup
+    int32_t qgroups;               // 16-query-head groups per KV head
+    int64_t grid;                  // workgroups of the attention kernel
+    uint64_t workspace_bytes;      // partial results (0 with one split)
+};
+AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t num_q_heads,
+                        int32_t max_blocks, int32_t num_seqs);
+
+struct AttnLaunch {
+    const uint8_t* layer;
+    const float* static_scales;
+    const void* q;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    void* out;
+    void* workspace;
+    int64_t num_blocks;
+    uint64_t block_bytes;
+    uint64_t code_bytes;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t bs_log2;
+    int32_t head_dim;
+    int32_t mode;
+    float sm_scale;
+};
+int launch_attention(const AttnLaunch& a, const AttnPlan& plan, void* stream);
+
 }  // namespace kvq

@@ -1,0 +1,313 @@
+"""GPU parity of the fused decode attention: the HIP kernel, called through
+the C ABI, against the oracle's float64 attention over the same cache image.
+The image is written by the oracle's own store on the CPU and uploaded byte
+for byte, so no input of the oracle comes from the HIP path.
+
+Tolerance, per output element (derived from the kernel's arithmetic):
+  |o_gpu - o_ref| <= (2^-8 + 2.5 eps_S) * sum_t p_t |V^_t[d]| + 2^-8 |o_ref|
+  - the softmax weights times the V scales are rounded to BF16 before the
+    value product (relative 2^-9 per term), FP32 accumulation and the
+    running-maximum rescaling add at most (tiles + 8) 2^-24 relative;
+  - eps_S bounds the score error of an FP32 dot product of hd exact terms:
+    (hd + 4) 2^-24 max_t sum_d |K^_t[d] q[d]| * sm_scale, and a score error e
+    moves each weight by a factor within exp(+-2e);
+  - the output is rounded to BF16 (relative 2^-9) after a division by the
+    FP32 sum of weights (relative error below 2^-12 at these lengths);
+  - FP32 and the matrix cores have an underflow floor: a product of weight
+    and code below 2^-126 may be lost, so sequences of n tokens add an
+    absolute (n + 16) 2^-120 (times a static V scale above 1).
+Short sequences make a dropped or stray token exceed the bound; long ones
+exercise the split and combine kernels."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    import quantized_fp8_int4_amd as kvq
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return kvq
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+class Scenario:
+    """One layer of one mode: an oracle-written cache image, the same bytes
+    on the device, a block table, lengths and queries."""
+
+    def __init__(self, kvq, orc, mode, hd, hkv, bs, lens, group, seed=0, extra_blocks=3, kv=None):
+        self.kvq, self.orc = kvq, orc
+        self.mode, self.hd, self.hkv, self.bs, self.group = mode, hd, hkv, bs, group
+        self.lens = [int(x) for x in lens]
+        need = [-(-n // bs) for n in self.lens]
+        self.maxb = max(need + [1]) + 1
+        self.nblocks = sum(need) + extra_blocks
+        self.g = orc.Geometry(bs, hkv, hd, [mode], [self.nblocks])
+        self.img = orc.new_cache(self.g)
+        st = W.DecodeState(len(self.lens), bs, self.nblocks, self.maxb, seed)
+        slots = []
+        for b, n in enumerate(self.lens):
+            slots += st.append(b, n)
+        self.bt = st.block_table.numpy().copy()
+        n = len(slots)
+        k, v = kv if kv is not None else W.gqa_kv(n, hkv, hd, seed=seed + 1)
+        self.scales = None
+        if mode in (W.FP8_PER_TENSOR, W.FP8_PER_HEAD):
+            per_head = W.static_scales_from_amax(W.calibration_amax(k, v))
+            if mode == W.FP8_PER_TENSOR:
+                amax = W.calibration_amax(k, v).amax(dim=1, keepdim=True)
+                per_head = W.static_scales_from_amax(amax)
+            self.scales = per_head.numpy().astype(np.float32)
+        if n:
+            orc.store(self.g, self.img, 0, _bits(k), _bits(v), np.array(slots, np.int64), self.scales)
+        elif self.scales is not None:
+            orc.store(self.g, self.img, 0, np.zeros((0, hkv, hd), np.uint16), np.zeros((0, hkv, hd), np.uint16),
+                      np.zeros(0, np.int64), self.scales)
+        self.cfg = kvq.CacheConfig(bs, hkv, hd, [mode], [self.nblocks])
+        self.cache = kvq.Cache(self.cfg, device=DEV, buffer=torch.from_numpy(self.img).to(DEV))
+        if self.scales is not None:          # registers the static table (same bytes)
+            e = torch.zeros((0, hkv, hd), dtype=torch.bfloat16, device=DEV)
+            self.cache.store(0, e, e, torch.zeros(0, dtype=torch.int64, device=DEV), self.scales.tolist())
+        gq = torch.Generator().manual_seed(seed + 7)
+        self.q = torch.randn((len(self.lens), hkv * group, hd), generator=gq).to(torch.bfloat16)
+        self.sm_scale = 1.0 / math.sqrt(hd)
+
+    def run_gpu(self, bt=None, lens=None):
+        bt = self.bt if bt is None else bt
+        lens = self.lens if lens is None else lens
+        out = self.cache.decode_attention(0, self.q.to(DEV), torch.as_tensor(bt, dtype=torch.int32).to(DEV),
+                                          torch.as_tensor(np.asarray(lens), dtype=torch.int32).to(DEV),
+                                          self.sm_scale)
+        torch.cuda.synchronize()
+        return _f64(_bits(out))
+
+    def reference(self, rows=None, bt=None, lens=None):
+        """Oracle output, weighted |V| sums and the tolerance, for sequences rows."""
+        bt = self.bt if bt is None else bt
+        lens = np.asarray(self.lens if lens is None else lens)
+        rows = np.arange(len(lens)) if rows is None else np.asarray(rows)
+        qb = _bits(self.q)[rows]
+        ref, absv = self.orc.decode_attention(self.g, self.img, 0, qb, bt[rows], lens[rows], self.sm_scale,
+                                              with_absv=True)
+        # score error bound from the oracle's dequantized keys (BF16 of K^,
+        # widened by 2^-8 to bound K^ itself)
+        eps = np.zeros(ref.shape[:2])
+        ko, _ = self.orc.gather(self.g, self.img, 0, bt[rows], lens[rows])
+        kabs = np.abs(_f64(ko)) * (1 + 2.0 ** -8)
+        qabs = np.abs(_f64(qb))
+        row0 = 0
+        for i, n in enumerate(np.clip(lens[rows], 0, self.maxb * self.bs)):
+            if n:
+                kk = kabs[row0: row0 + n]                                  # [n, hkv, hd]
+                for qh in range(qabs.shape[1]):
+                    dots = kk[:, qh // self.group, :] @ qabs[i, qh]
+                    eps[i, qh] = (self.hd + 4) * 2.0 ** -24 * dots.max() * self.sm_scale
+            row0 += int(max(lens[rows][i], 0))
+        n_tok = np.clip(lens[rows], 0, self.maxb * self.bs).astype(np.float64)
+        v_big = 1.0 if self.scales is None else max(1.0, float(self.scales[len(self.scales) // 2:].max()))
+        floor = (n_tok[:, None, None] + 16) * 2.0 ** -120 * v_big
+        tol = (2.0 ** -8 + 2.5 * eps[:, :, None]) * absv + 2.0 ** -8 * np.abs(ref) + floor
+        return ref, tol
+
+    def check(self, out, ref, tol, what):
+        err = np.abs(out - ref)
+        if not (err <= tol).all():
+            i = np.unravel_index(np.argmax(err - tol), err.shape)
+            pytest.fail(f"{what}: {(err > tol).sum()} of {err.size} outside the bound; worst at {i}: "
+                        f"gpu {out[i]:.6g} oracle {ref[i]:.6g} bound {tol[i]:.3g}")
+
+    def close(self):
+        self.cache.close()
+
+
+def _run(kvq, orc, what, **kw):
+    _flush(f"[attention] {what}")
+    sc = Scenario(kvq, orc, **kw)
+    try:
+        out = sc.run_gpu()
+        ref, tol = sc.reference()
+        sc.check(out, ref, tol, what)
+        return sc, out, ref
+    finally:
+        sc.close()
+
+
+MODES = [W.BF16, W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD]
+RAGGED = [0, 1, 15, 16, 17, 100, 260]          # empty, single, partial and whole tiles
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("mode", MODES)
+def test_attention_modes_and_head_dims(kvq, orc, mode, hd):
+    """Several splits per sequence (maximum context 288 tokens)."""
+    _run(kvq, orc, f"mode {W.MODE_NAMES[mode]} hd {hd} ragged", mode=mode, hd=hd, hkv=2, bs=16, lens=RAGGED,
+         group=4, seed=hd + mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_attention_single_split(kvq, orc, mode):
+    """Contexts of at most 8 tiles: one split, output written by the first kernel."""
+    _run(kvq, orc, f"mode {W.MODE_NAMES[mode]} single split", mode=mode, hd=128, hkv=2, bs=16,
+         lens=[0, 1, 7, 16, 33, 100], group=4, seed=20 + mode)
+
+
+@pytest.mark.parametrize("group", [1, 2, 8, 16, 20, 33])
+def test_attention_query_groups(kvq, orc, group):
+    """Query heads per KV head below, at and above one 16-wide MFMA column block."""
+    _run(kvq, orc, f"group {group}", mode=W.FP8_PER_TOKEN_HEAD, hd=128, hkv=2, bs=16, lens=[5, 70, 200],
+         group=group, seed=30 + group)
+
+
+@pytest.mark.parametrize("hkv", [1, 3, 6, 12, 16])
+def test_attention_kv_heads(kvq, orc, hkv):
+    """KV-head counts that give 1, 2, 4 and 8 waves per workgroup and several head chunks."""
+    _run(kvq, orc, f"hkv {hkv}", mode=W.FP8_PER_TOKEN_HEAD, hd=64, hkv=hkv, bs=16, lens=[3, 50, 129],
+         group=2, seed=40 + hkv)
+
+
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 32, 128])
+@pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD, W.BF16])
+def test_attention_block_sizes(kvq, orc, mode, bs):
+    """Blocks smaller than a 16-token tile (per-token block lookups) and larger ones."""
+    _run(kvq, orc, f"mode {W.MODE_NAMES[mode]} bs {bs}", mode=mode, hd=64, hkv=2, bs=bs, lens=[1, 9, 40, 77],
+         group=4, seed=50 + bs + mode)
+
+
+def test_attention_heavy_tails(kvq, orc):
+    """Student-t heads with large scores (a peaked softmax)."""
+    n = 16 + 90 + 300
+    k, v = W.heavy_tail_kv(n, 2, 128, seed=61)
+    _run(kvq, orc, "heavy tails", mode=W.FP8_PER_TOKEN_HEAD, hd=128, hkv=2, bs=16, lens=[16, 90, 300],
+         group=4, seed=60, kv=(k, v))
+
+
+@pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.BF16, W.FP8_PER_HEAD])
+def test_attention_skips_blocks_outside_the_layer(kvq, orc, mode):
+    """Table entries that are negative or past the layer's blocks drop their
+    tokens; a sequence left with none gives zeros."""
+    _flush(f"[attention] foreign blocks mode {W.MODE_NAMES[mode]}")
+    sc = Scenario(kvq, orc, mode=mode, hd=64, hkv=2, bs=16, lens=[70, 300, 40], group=4, seed=70)
+    try:
+        bt = sc.bt.copy()
+        bt[0, 1] = -1
+        bt[1, 3] = sc.nblocks
+        bt[1, 10] = 2 ** 31 - 1
+        bt[2, :] = -5
+        out = sc.run_gpu(bt=bt)
+        ref, tol = sc.reference(bt=bt)
+        sc.check(out, ref, tol, "foreign blocks")
+        assert not out[2].any() and not ref[2].any()
+    finally:
+        sc.close()
+
+
+def test_attention_lengths_clamped_to_the_table(kvq, orc):
+    """Negative lengths count as 0; lengths past max_blocks * block_size are cut there."""
+    _flush("[attention] clamped lengths")
+    sc = Scenario(kvq, orc, mode=W.FP8_PER_TOKEN_HEAD, hd=64, hkv=2, bs=16, lens=[20, 40], group=2, seed=80)
+    try:
+        lens = [-3, 10 ** 6]
+        out = sc.run_gpu(lens=lens)
+        ref, tol = sc.reference(lens=lens)
+        sc.check(out, ref, tol, "clamped lengths")
+        assert not out[0].any()
+    finally:
+        sc.close()
+
+
+@pytest.mark.parametrize("mode", [W.BF16, W.FP8_PER_TENSOR, W.FP8_PER_HEAD])
+def test_attention_single_token_is_the_dequantized_value(kvq, orc, mode):
+    """With one cached token and a static (or no) V scale the weight is exactly
+    1, so the output is exactly the token's dequantized BF16 value."""
+    _flush(f"[attention] single token mode {W.MODE_NAMES[mode]}")
+    sc = Scenario(kvq, orc, mode=mode, hd=128, hkv=2, bs=16, lens=[1, 1, 1], group=3, seed=90)
+    try:
+        out = sc.run_gpu()
+        _, vo = orc.gather(sc.g, sc.img, 0, sc.bt, sc.lens)
+        want = np.repeat(_f64(vo), 3, axis=1)                     # [3 tokens, 6 query heads, hd]
+        assert np.array_equal(out, want)
+    finally:
+        sc.close()
+
+
+def test_attention_workspace_reuse_and_sizes(kvq, orc):
+    """The workspace query matches what the call accepts: a smaller buffer is
+    refused, an exact one gives the same bytes as a fresh allocation."""
+    _flush("[attention] workspace")
+    sc = Scenario(kvq, orc, mode=W.INT4_PER_TOKEN_HEAD, hd=128, hkv=2, bs=16, lens=[300, 500], group=4, seed=95)
+    try:
+        need = kvq.kvq_decode_attention_workspace(sc.cache.handle, 8, sc.maxb, 2)
+        assert need > 0
+        q = sc.q.to(DEV)
+        bt = torch.as_tensor(sc.bt, dtype=torch.int32).to(DEV)
+        sl = torch.as_tensor(sc.lens, dtype=torch.int32).to(DEV)
+        out1 = torch.zeros_like(q)
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)      # stale contents do not matter
+        kvq.kvq_decode_attention(sc.cache.handle, 0, q, bt, sl, sc.sm_scale, out1, ws)
+        with pytest.raises(kvq.KVQError) as e:
+            kvq.kvq_decode_attention(sc.cache.handle, 0, q, bt, sl, sc.sm_scale, out1, ws[: need - 16])
+        assert e.value.status == kvq.ERR_BUFFER_TOO_SMALL
+        out2 = sc.cache.decode_attention(0, q, bt, sl, sc.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out1, out2)
+    finally:
+        sc.close()
+
+
+def test_attention_decode_workload_sampled(kvq, orc):
+    """Full decode shape: 256 sequences of 8192-8207 cached tokens, 8 KV heads,
+    32 query heads, head_dim 128, per-token-head FP8, in the launch
+    configuration the benchmark times; eight sampled sequences against the
+    oracle."""
+    _flush("[attention] decode 256 x 8192 fp8_per_token_head (sampled)")
+    g = torch.Generator().manual_seed(11)
+    lens = (8192 + torch.randint(0, 16, (256,), generator=g)).tolist()
+    n = sum(lens)
+    k, v = (t.cpu() for t in W.normal_kv(n, 8, 128, seed=12, device=DEV))
+    sc = Scenario(kvq, orc, mode=W.FP8_PER_TOKEN_HEAD, hd=128, hkv=8, bs=16, lens=lens, group=4, seed=13,
+                  extra_blocks=0, kv=(k, v))
+    del k, v
+    try:
+        assert sc.maxb == 514
+        out = sc.run_gpu()
+        rows = [0, 1, 77, 128, 200, 254, 255, 31]
+        ref, tol = sc.reference(rows=rows)
+        sc.check(out[rows], ref, tol, "decode sampled")
+    finally:
+        sc.close()
+
+
+def test_attention_layer_without_blocks_gives_zeros(kvq, orc):
+    """A layer configured with no blocks has no token to attend to."""
+    _flush("[attention] layer without blocks")
+    cfg = kvq.CacheConfig(16, 2, 64, [W.FP8_PER_TOKEN_HEAD, W.FP8_PER_TOKEN_HEAD], [4, 0])
+    cache = kvq.Cache(cfg, device=DEV)
+    try:
+        for maxb in (2, 64):                                  # one split, several splits
+            q = torch.randn((3, 4, 64), generator=torch.Generator().manual_seed(maxb)).to(torch.bfloat16).to(DEV)
+            bt = torch.zeros((3, maxb), dtype=torch.int32, device=DEV)
+            sl = torch.tensor([5, 0, 20], dtype=torch.int32, device=DEV)
+            out = torch.full_like(q, 1.0)
+            cache.decode_attention(1, q, bt, sl, 0.125, out=out)
+            torch.cuda.synchronize()
+            assert not out.any()
+    finally:
+        cache.close()

@@ -181,3 +181,44 @@ def test_calibrate_argument_checks(kvq):
     assert lib.kvq_calibrate_amax(P(FAKE_DEV), P(FAKE_DEV), 4, 8, 128, P(FAKE_DEV + 2), 0, None) == kvq.ERR_INVALID_ARG
     assert lib.kvq_calibrate_amax(None, None, 0, 8, 128, P(FAKE_DEV), 1, None) == kvq.OK     # no-op
     assert lib.kvq_calibrate_amax(None, None, 4, 8, 128, P(FAKE_DEV), 0, None) == kvq.ERR_INVALID_ARG
+
+
+def _attn(kvq, h, layer, nseq, H=4, maxb=4, q=FAKE_DEV, out=FAKE_DEV, ws=0, wsb=0, sm=0.125):
+    return kvq._lib.kvq_decode_attention(h, layer, ctypes.c_void_p(q), H, ctypes.c_void_p(FAKE_DEV), maxb,
+                                         ctypes.c_void_p(FAKE_DEV), nseq, sm, ctypes.c_void_p(out),
+                                         ctypes.c_void_p(ws), wsb, None)
+
+
+def test_attention_argument_checks(kvq):
+    cfg = _cfg(kvq, [kvq.FP8_PER_TOKEN_HEAD, kvq.FP8_PER_TENSOR, kvq.BF16], hd=128)
+    h = _handle(kvq, cfg)
+    try:
+        assert _attn(kvq, h, 3, 1) == kvq.ERR_INVALID_ARG                 # layer out of range
+        assert _attn(kvq, h, 0, 0) == kvq.OK                              # no-op, no HIP call
+        assert _attn(kvq, h, 0, -1) == kvq.ERR_INVALID_ARG
+        assert _attn(kvq, h, 0, 1, H=3) == kvq.ERR_INVALID_ARG            # not a multiple of Hkv
+        assert _attn(kvq, h, 0, 1, H=0) == kvq.ERR_INVALID_ARG
+        assert _attn(kvq, h, 0, 1, maxb=0) == kvq.ERR_INVALID_ARG
+        assert _attn(kvq, h, 0, 1, q=0) == kvq.ERR_INVALID_ARG
+        assert _attn(kvq, h, 0, 1, q=FAKE_DEV + 8) == kvq.ERR_INVALID_ARG
+        assert _attn(kvq, h, 0, 1, out=FAKE_DEV + 2) == kvq.ERR_INVALID_ARG
+        for sm in (float("nan"), float("inf")):
+            assert _attn(kvq, h, 0, 1, sm=sm) == kvq.ERR_INVALID_ARG
+        assert _attn(kvq, h, 1, 1) == kvq.ERR_INVALID_ARG                 # static layer never stored
+        assert _attn(kvq, h, 0, 1, maxb=1 << 27) == kvq.ERR_UNSUPPORTED   # max_blocks * bs >= 2^31
+        # a context of more than 8 tiles is split and needs the workspace
+        need = kvq.kvq_decode_attention_workspace(h, 4, 64, 2)
+        assert need > 0 and need % (2 * 4 * (128 + 2) * 4) == 0
+        assert _attn(kvq, h, 0, 2, maxb=64) == kvq.ERR_BUFFER_TOO_SMALL
+        assert _attn(kvq, h, 0, 2, maxb=64, ws=FAKE_DEV, wsb=need - 1) == kvq.ERR_BUFFER_TOO_SMALL
+        assert _attn(kvq, h, 0, 2, maxb=64, ws=FAKE_DEV + 8, wsb=need) == kvq.ERR_INVALID_ARG
+        # at most 8 tiles of context: one split, no workspace
+        assert kvq.kvq_decode_attention_workspace(h, 4, 8, 2) == 0
+        assert kvq.kvq_decode_attention_workspace(h, 4, 64, 0) == 0
+        for args in ((3, 64, 2), (0, 64, 2), (4, 0, 2), (4, 64, -1)):
+            with pytest.raises(kvq.KVQError) as e:
+                kvq.kvq_decode_attention_workspace(h, *args)
+            assert e.value.status == kvq.ERR_INVALID_ARG
+        assert kvq._lib.kvq_decode_attention_workspace(h, 4, 64, 2, None) == kvq.ERR_INVALID_ARG
+    finally:
+        kvq.kvq_destroy_cache(h)

@@ -75,3 +75,22 @@ def test_attention_special_cases(orc):
     assert not empty.any()
     out2, absv = orc.decode_attention(g, buf, 0, _bits(q), st.block_table.numpy(), [1, 5], 0.3, with_absv=True)
     assert np.array_equal(out2, out) and (absv >= np.abs(out) - 1e-12).all()
+
+
+def test_attention_skips_blocks_outside_the_layer(orc):
+    """Tokens whose block-table entry is negative or past the layer's block
+    count take no part; the rest is softmax attention over what remains."""
+    hkv, hd, bs = 1, 64, 16
+    g, buf, st = _setup(orc, W.FP8_PER_TOKEN_HEAD, hkv, hd, bs=bs, lens=(70,))
+    bt = st.block_table.numpy().copy()
+    lens = [70]
+    kh, vh = _brute.dequant_f64(buf, bs, hkv, hd, [W.FP8_PER_TOKEN_HEAD], [12], 0, bt, lens)
+    bt[0, 1] = -1
+    bt[0, 3] = 12                                   # one past the last block
+    keep = np.array([not (16 <= t < 32 or 48 <= t < 64) for t in range(70)])
+    q = torch.randn((1, 2, hd), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    out = orc.decode_attention(g, buf, 0, _bits(q), bt, lens, 0.2)
+    ref = _numpy_attention(q.double().numpy(), kh[keep], vh[keep], [int(keep.sum())], 2, 0.2)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+    bt[0, :] = -1
+    assert not orc.decode_attention(g, buf, 0, _bits(q), bt, lens, 0.2).any()
