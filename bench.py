@@ -22,6 +22,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -303,6 +304,74 @@ def _bits(torch, t):
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
+def attention_bytes(mode, hd, hkv, bs, H, num_seqs, total_tokens):
+    """Algorithmic bytes of one decode-attention launch: every cached token's
+    K and V codes (and per-token scales) once, the block-table entries, the
+    BF16 queries and outputs."""
+    rb = row_bytes(mode, hd)
+    sigma = 8 if mode in (3, 4) else 0
+    return (total_tokens * hkv * (2 * rb + sigma) + -(-total_tokens // bs) * 4
+            + num_seqs * H * hd * 2 * 2)
+
+
+def _decode_setup(args, torch, kvq, W, dev):
+    """The decode workload: a 32-layer cache of 256 sequences prefilled with
+    8192 seeded N(0,1) tokens each, plus the slots, lengths and new K/V of
+    every decode step the run will take."""
+    spec = W.WORKLOADS["decode"]
+    L, hkv, bs, S, ctx = spec["num_layers"], spec["hkv"], spec["block_size"], spec["num_seqs"], spec["context"]
+    hd = args.head_dim
+    mode = {v: k for k, v in W.MODE_NAMES.items()}[args.mode]
+    if mode not in (kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD):
+        raise SystemExit("decode workloads: --mode fp8_per_token_head or int4_per_token_head")
+    # the workload's 513 blocks per sequence hold 8192 + 16 tokens; room is
+    # added for every appended step this run takes
+    maxb = ctx // bs + 1 + (args.warmup + args.steps) // bs
+    nb = S * maxb
+    cfg = kvq.CacheConfig(bs, hkv, hd, [mode] * L, [nb] * L)
+    cache = kvq.Cache(cfg, device=dev)
+    log(f"[bench] decode: cache {cache.bytes['total'] / 2**30:.2f} GiB; prefilling {L} layers x {S} x {ctx} tokens")
+    st = W.DecodeState(S, bs, nb, maxb, seed=5000)
+    slots = []
+    for b in range(S):
+        slots += st.append(b, ctx)
+    slots = torch.tensor(slots, dtype=torch.int64, device=dev)
+    Lc = Launcher(torch, kvq, cache)
+    chunk = 32768
+    for l in range(L):
+        for c0 in range(0, S * ctx, chunk):
+            k, v = W.normal_kv(chunk, hkv, hd, seed=5000 + 1000 * l + c0 // chunk, device=dev)
+            Lc.store(Lc.store_args(l, k, v, slots[c0: c0 + chunk], mode))
+        torch.cuda.synchronize()
+    steps_slots = []
+    for _ in range(args.warmup + args.steps):
+        steps_slots.append(torch.tensor([st.append(b, 1)[0] for b in range(S)], dtype=torch.int64, device=dev))
+    kdec, vdec = W.normal_kv(S, hkv, hd, seed=6000, device=dev)
+    lens_at = [torch.tensor([ctx + s_ + 1] * S, dtype=torch.int32, device=dev)
+               for s_ in range(args.warmup + args.steps)]
+    return {"L": L, "S": S, "hkv": hkv, "hd": hd, "bs": bs, "ctx": ctx, "mode": mode, "nb": nb, "cache": cache,
+            "st": st, "slots": slots, "chunk": chunk, "Lc": Lc, "steps_slots": steps_slots, "kdec": kdec,
+            "vdec": vdec, "lens_at": lens_at, "bt": st.block_table.to(dev),
+            "desc": spec["desc"] + f", head_dim {hd}, {args.mode}"}
+
+
+def _decode_oracle_layer(D, torch, W, oracle):
+    """The oracle's own image of the last layer after every step: its store
+    of the same seeded prefill chunks and appended tokens."""
+    l = D["L"] - 1
+    g = oracle.Geometry(D["bs"], D["hkv"], D["hd"], [D["mode"]], [D["nb"]])
+    host = oracle.new_cache(g)
+    slots = D["slots"].cpu().numpy()
+    dev = D["slots"].device
+    for c0 in range(0, D["S"] * D["ctx"], D["chunk"]):
+        k, v = W.normal_kv(D["chunk"], D["hkv"], D["hd"], seed=5000 + 1000 * l + c0 // D["chunk"], device=dev)
+        oracle.store(g, host, 0, _bits(torch, k), _bits(torch, v), slots[c0: c0 + D["chunk"]])
+    kb, vb = _bits(torch, D["kdec"]), _bits(torch, D["vdec"])
+    for ss in D["steps_slots"]:
+        oracle.store(g, host, 0, kb, vb, ss.cpu().numpy())
+    return g, host
+
+
 def run_other_workload(args, torch, kvq, W):
     """long80, gptoss and decode: the remaining shapes, each with its own
     timing, oracle sample and parity cross-check.  Printed as one JSON line."""
@@ -486,51 +555,19 @@ def run_other_workload(args, torch, kvq, W):
                "cpu_baseline": {"value": round(cal_b / csec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                                 "sample": f"one layer's amax (single-threaded loop), {csec:.2f} s wall"},
                "parity_vs_oracle_sampled": parity}
-    else:  # decode
-        spec = W.WORKLOADS["decode"]
-        L, hkv, bs, S, ctx = spec["num_layers"], spec["hkv"], spec["block_size"], spec["num_seqs"], spec["context"]
-        hd = args.head_dim
-        mode = {v: k for k, v in W.MODE_NAMES.items()}[args.mode]
-        if mode not in (kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD):
-            raise SystemExit("decode workload: --mode fp8_per_token_head or int4_per_token_head")
-        # the workload's 513 blocks per sequence hold 8192 + 16 tokens; room is
-        # added for every appended step this run takes
-        maxb = ctx // bs + 1 + (args.warmup + args.steps) // bs
-        nb = S * maxb
-        cfg = kvq.CacheConfig(bs, hkv, hd, [mode] * L, [nb] * L)
-        cache = kvq.Cache(cfg, device=dev)
-        log(f"[bench] decode: cache {cache.bytes['total'] / 2**30:.2f} GiB; prefilling {L} layers x {S} x {ctx} tokens")
-        st = W.DecodeState(S, bs, nb, maxb, seed=5000)
-        slots = []
-        for b in range(S):
-            slots += st.append(b, ctx)
-        slots = torch.tensor(slots, dtype=torch.int64, device=dev)
-        Lc = Launcher(torch, kvq, cache)
-        chunk = 32768
-        for l in range(L):
-            for c0 in range(0, S * ctx, chunk):
-                k, v = W.normal_kv(chunk, hkv, hd, seed=5000 + 1000 * l + c0 // chunk, device=dev)
-                Lc.store(Lc.store_args(l, k, v, slots[c0: c0 + chunk], mode))
-            torch.cuda.synchronize()
-        steps_slots = []
-        for s_ in range(args.warmup + args.steps):
-            steps_slots.append(torch.tensor([st.append(b, 1)[0] for b in range(S)], dtype=torch.int64, device=dev))
-        bt = st.block_table.to(dev)
-        kdec, vdec = W.normal_kv(S, hkv, hd, seed=6000, device=dev)
-        tot_max = sum(st.seq_lens)
+    elif name == "decode":
+        D = _decode_setup(args, torch, kvq, W, dev)
+        L, S, hkv, hd, bs, mode, Lc = D["L"], D["S"], D["hkv"], D["hd"], D["bs"], D["mode"], D["Lc"]
+        tot_max = sum(D["st"].seq_lens)
         ok = torch.empty((tot_max, hkv, hd), dtype=torch.bfloat16, device=dev)
         ov = torch.empty_like(ok)
-        lens_at = []
-        base = [ctx] * S
-        for s_ in range(args.warmup + args.steps):
-            lens_at.append(torch.tensor([n + s_ + 1 for n in base], dtype=torch.int32, device=dev))
         counter = {"i": 0}
 
         def step(ev):
             i = counter["i"]
             counter["i"] += 1
-            sa = [Lc.store_args(l, kdec, vdec, steps_slots[i], mode) for l in range(L)]
-            ga = [Lc.gather_args(l, bt, lens_at[i], ok, ov) for l in range(L)]
+            sa = [Lc.store_args(l, D["kdec"], D["vdec"], D["steps_slots"][i], mode) for l in range(L)]
+            ga = [Lc.gather_args(l, D["bt"], D["lens_at"][i], ok, ov) for l in range(L)]
             if ev: ev[0].record()
             for a in sa: Lc.store(a)
             if ev: ev[1].record()
@@ -539,39 +576,119 @@ def run_other_workload(args, torch, kvq, W):
         sec, evs = _timed(torch, step, args.steps, args.warmup)
         store_s = sum(e[0].elapsed_time(e[1]) for e in evs) / (args.steps * L) / 1e3
         gather_s = sum(e[1].elapsed_time(e[2]) for e in evs) / (args.steps * L) / 1e3
-        ntok = int(lens_at[-1].sum())
+        lens_last = D["lens_at"][-1].cpu().numpy()
+        ntok = int(lens_last.sum())
         sb, _ = algorithmic_bytes(mode, hd, hkv, bs, S * hkv)
         _, gb = algorithmic_bytes(mode, hd, hkv, bs, ntok * hkv)
-        # oracle sample: the gather of layer L-1 for 8 sequences, from an oracle cache
-        # rebuilt from the device cache bytes of that layer (the store path is covered
-        # by the parity tests; here the read path is timed and cross-checked)
-        g_all = oracle.Geometry(bs, hkv, hd, [mode] * L, [nb] * L)
-        base_last = int(oracle.layer_offsets(g_all)[0][L - 1])
-        g = oracle.Geometry(bs, hkv, hd, [mode], [nb])          # the last layer alone
-        layer_bytes = int(oracle.layer_offsets(g)[2])
-        host = cache.buffer[base_last: base_last + layer_bytes].cpu().numpy()
+        # oracle sample: the oracle's own image of layer L-1 (its store of the
+        # same seeded inputs), then its gather of 8 sequences, timed
+        g, host = _decode_oracle_layer(D, torch, W, oracle)
         pick = list(range(0, S, S // 8))[:8]
+        bt_h = D["st"].block_table.numpy()
         t0 = time.perf_counter()
-        ko, vo = oracle.gather(g, host, 0, st.block_table.numpy()[pick], lens_at[-1].cpu().numpy()[pick])
+        ko, vo = oracle.gather(g, host, 0, bt_h[pick], lens_last[pick])
         csec = time.perf_counter() - t0
-        offs = np.concatenate([[0], np.cumsum(lens_at[-1].cpu().numpy())])
+        offs = np.concatenate([[0], np.cumsum(lens_last)])
         dk = np.concatenate([_bits(torch, ok[offs[b]: offs[b + 1]]) for b in pick])
         dv = np.concatenate([_bits(torch, ov[offs[b]: offs[b + 1]]) for b in pick])
         parity = bool(np.array_equal(dk, ko) and np.array_equal(dv, vo))
-        sample_tok = int(lens_at[-1].cpu().numpy()[pick].sum())
+        sample_tok = int(lens_last[pick].sum())
         _, cgb = algorithmic_bytes(mode, hd, hkv, bs, sample_tok * hkv)
         cpu = {"value": round(cgb / csec / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
                "kind": "oracle", "sample": f"gather of 8 of {S} sequences ({sample_tok} tokens) of one layer, {csec:.2f} s wall"}
-        res = _result(args, {"workload": spec["desc"] + f", head_dim {hd}, {args.mode}", "layers": L, "num_seqs": S,
-                             "context": ctx, "num_kv_heads": hkv, "head_dim": hd, "block_size": bs, "mode": args.mode},
+        res = _result(args, {"workload": D["desc"], "layers": L, "num_seqs": S, "context": D["ctx"],
+                             "num_kv_heads": hkv, "head_dim": hd, "block_size": bs, "mode": args.mode},
                       L * (sb + gb) / sec / 1e9, sec * 1e3, sb, gb, store_s, gather_s, cpu, parity,
                       {"decode_store_us": round(store_s * 1e6, 2),
                        "appended_tokens_per_s": round(S / (L * store_s), 1),
-                       "cache_GiB": round(cache.bytes["total"] / 2**30, 3)})
+                       "cache_GiB": round(D["cache"].bytes["total"] / 2**30, 3)})
         res["roofline"]["kernel"] = "gather_kernel"
         gg = gb / gather_s / 1e9
         res["roofline"]["achieved"] = round(gg, 1)
         res["roofline"]["frac"] = round(gg / HBM_PEAK_GBPS, 4)
+    else:  # attention: one decode step = per layer, append one token per sequence, then attend
+        D = _decode_setup(args, torch, kvq, W, dev)
+        L, S, hkv, hd, bs, mode, Lc = D["L"], D["S"], D["hkv"], D["hd"], D["bs"], D["mode"], D["Lc"]
+        H = hkv * args.q_per_kv
+        sm_scale = 1.0 / math.sqrt(hd)
+        nsteps = args.warmup + args.steps
+        qs = [W.normal_kv(S, H, hd, seed=7000 + i, device=dev)[0] for i in range(nsteps)]
+        out = torch.empty((S, H, hd), dtype=torch.bfloat16, device=dev)
+        maxb = int(D["bt"].shape[1])
+        wsb = kvq.kvq_decode_attention_workspace(D["cache"].handle, H, maxb, S)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        ct = __import__("ctypes")
+
+        def attn_args(l, i):
+            return (D["cache"].handle, l, ct.c_void_p(qs[i].data_ptr()), H, ct.c_void_p(D["bt"].data_ptr()), maxb,
+                    ct.c_void_p(D["lens_at"][i].data_ptr()), S, ct.c_float(sm_scale), ct.c_void_p(out.data_ptr()),
+                    ct.c_void_p(ws.data_ptr()), wsb, Lc.stream)
+        counter = {"i": 0}
+
+        def step(ev):
+            i = counter["i"]
+            counter["i"] += 1
+            sa = [Lc.store_args(l, D["kdec"], D["vdec"], D["steps_slots"][i], mode) for l in range(L)]
+            aa = [attn_args(l, i) for l in range(L)]
+            if ev: ev[0].record()
+            for l in range(L):
+                Lc.store(sa[l])
+                st_ = kvq._lib.kvq_decode_attention(*aa[l])
+                if st_ != 0:
+                    raise kvq.KVQError(st_, "kvq_decode_attention")
+            if ev: ev[1].record(); ev[2].record()
+        sec, evs = _timed(torch, step, args.steps, args.warmup)
+        step_s = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps / 1e3
+        # the attention launches of the last step alone, for their own time
+        last = [attn_args(l, nsteps - 1) for l in range(L)]
+
+        def attn_only(ev):
+            if ev: ev[0].record()
+            for a in last:
+                kvq._lib.kvq_decode_attention(*a)
+            if ev: ev[1].record(); ev[2].record()
+        _, aevs = _timed(torch, attn_only, args.steps, 1)
+        attn_s = sum(e[0].elapsed_time(e[1]) for e in aevs) / (args.steps * L) / 1e3
+        lens_last = D["lens_at"][-1].cpu().numpy()
+        ntok = int(lens_last.sum())
+        sb, _ = algorithmic_bytes(mode, hd, hkv, bs, S * hkv)
+        ab = attention_bytes(mode, hd, hkv, bs, H, S, ntok)
+        agbps = ab / attn_s / 1e9
+        # oracle check: layer L-1 of the last step for 8 sequences, from the
+        # oracle's own image of that layer, within the kernel's error bound
+        g, host = _decode_oracle_layer(D, torch, W, oracle)
+        pick = list(range(0, S, S // 8))[:8]
+        bt_h = D["st"].block_table.numpy()
+        qb = _bits(torch, qs[-1])[pick]
+        t0 = time.perf_counter()
+        ref, absv = oracle.decode_attention(g, host, 0, qb, bt_h[pick], lens_last[pick], sm_scale, with_absv=True)
+        csec = time.perf_counter() - t0
+        tol = oracle.attention_error_bound(g, host, 0, qb, bt_h[pick], lens_last[pick], sm_scale, ref, absv)
+        got = (_bits(torch, out[pick]).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        parity = bool((np.abs(got - ref) <= tol).all())
+        sample_tok = int(lens_last[pick].sum())
+        cab = attention_bytes(mode, hd, hkv, bs, H, len(pick), sample_tok)
+        res = {"metric": "decode attention over the quantized cache: cache GB/s read and decode tokens/s "
+                         "(per-token-head FP8)",
+               "value": round(L * (sb + ab) / sec / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+               "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "fp8/int4 codes, bf16 MFMA, f32 accumulate",
+               "data": "synthetic",
+               "config": {"workload": D["desc"] + f", {H} query heads, fused append + attention per layer",
+                          "layers": L, "num_seqs": S, "context": D["ctx"], "num_kv_heads": hkv,
+                          "num_q_heads": H, "head_dim": hd, "block_size": bs, "mode": args.mode},
+               "attention_us": round(attn_s * 1e6, 2), "attention_GBps": round(agbps, 1),
+               "step_ms_events": round(step_s * 1e3, 4),
+               "decode_tokens_per_s": round(S / sec, 1),
+               "roofline": {"bound": "hbm", "kernel": "attention_kernel", "achieved": round(agbps, 1),
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(agbps / HBM_PEAK_GBPS, 4),
+                            "traffic": None},
+               "cpu_baseline": {"value": round(cab / csec / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+                                "kind": "oracle",
+                                "sample": f"fp64 attention of 8 of {S} sequences ({sample_tok} cached tokens) "
+                                          f"of one layer, {csec:.2f} s wall"},
+               "parity_vs_oracle_sampled": parity,
+               "workspace_bytes": wsb, "cache_GiB": round(D["cache"].bytes["total"] / 2**30, 3)}
     print(json.dumps(res), flush=True)
 
 
@@ -580,9 +697,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gqa32", choices=["gqa32", "long80", "gptoss", "decode", "calib"],
+    ap.add_argument("--workload", default="gqa32",
+                    choices=["gqa32", "long80", "gptoss", "decode", "attention", "calib"],
                     help="gqa32 is the headline line; the others measure the remaining shapes")
-    ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128], help="decode workload only")
+    ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128], help="decode and attention workloads")
+    ap.add_argument("--q-per-kv", type=int, default=4, help="attention workload: query heads per KV head")
     ap.add_argument("--mode", default="fp8_per_token_head",
                     choices=["fp8_per_token_head", "fp8_per_tensor", "fp8_per_head", "int4_per_token_head", "bf16"])
     ap.add_argument("--cpu-layers", type=int, default=16, help="layers of one step timed on the CPU oracle")

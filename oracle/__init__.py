@@ -176,6 +176,39 @@ def decode_attention(g: Geometry, buf: np.ndarray, layer: int, q_bits, block_tab
     return (out, absv) if with_absv else out
 
 
+def attention_error_bound(g: Geometry, buf: np.ndarray, layer: int, q_bits, block_table, seq_lens,
+                          sm_scale: float, ref, absv, static_v_max: float = 1.0):
+    """Per-element bound on |o_kernel - o_exact| for an attention kernel that
+    takes the dequantized-cache attention with FP32 accumulation, BF16
+    softmax weights (times per-token V scales) in the value product and a
+    BF16 output:
+      (2^-8 + 2.5 eps_S) * sum_t p_t |V^_t| + 2^-8 |o| + (n + 16) 2^-120 max(1, s_V)
+    eps_S = (hd + 4) 2^-24 max_t sum_d |K^_t[d] q[d]| * sm_scale bounds the
+    score error of an FP32 dot product of hd exact products (a score error e
+    moves each weight by a factor within exp(+-2e)); 2^-8 covers the BF16
+    rounding of the weights (2^-9) and of the output (2^-9) plus FP32
+    accumulation and rescaling over fewer than 2^11 tiles; the last term is
+    the FP32 underflow floor (products below 2^-126 may be lost).  ref and
+    absv are this module's decode_attention results for the same inputs."""
+    q = _c(q_bits, np.uint16)
+    bt = _c(block_table, np.int32)
+    lens = np.clip(_c(seq_lens, np.int64), 0, int(bt.shape[1]) * g.bs)
+    nqh = int(q.shape[1])
+    group = nqh // g.hkv
+    kb, _ = gather(g, buf, layer, bt, lens)
+    kabs = np.abs((kb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)) * (1 + 2.0 ** -8)
+    qabs = np.abs((q.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    eps = np.zeros((q.shape[0], nqh))
+    row0 = 0
+    for i, n in enumerate(lens):
+        if n:
+            kk = kabs[row0: row0 + n]
+            for qh in range(nqh):
+                eps[i, qh] = (g.hd + 4) * 2.0 ** -24 * (kk[:, qh // group, :] @ qabs[i, qh]).max() * sm_scale
+        row0 += int(n)
+    floor = (lens.astype(np.float64)[:, None, None] + 16) * 2.0 ** -120 * max(1.0, float(static_v_max))
+    return (2.0 ** -8 + 2.5 * eps[:, :, None]) * absv + 2.0 ** -8 * np.abs(ref) + floor
+
 def calibrate_amax(keys_bits, values_bits, hkv: int, hd: int, amax=None) -> np.ndarray:
     """Per-(K/V, head) absolute maximum over a batch, float32 [2 * hkv]
     (K heads, then V heads); with amax given, the running maximum continues

@@ -3,19 +3,9 @@ the C ABI, against the oracle's float64 attention over the same cache image.
 The image is written by the oracle's own store on the CPU and uploaded byte
 for byte, so no input of the oracle comes from the HIP path.
 
-Tolerance, per output element (derived from the kernel's arithmetic):
-  |o_gpu - o_ref| <= (2^-8 + 2.5 eps_S) * sum_t p_t |V^_t[d]| + 2^-8 |o_ref|
-  - the softmax weights times the V scales are rounded to BF16 before the
-    value product (relative 2^-9 per term), FP32 accumulation and the
-    running-maximum rescaling add at most (tiles + 8) 2^-24 relative;
-  - eps_S bounds the score error of an FP32 dot product of hd exact terms:
-    (hd + 4) 2^-24 max_t sum_d |K^_t[d] q[d]| * sm_scale, and a score error e
-    moves each weight by a factor within exp(+-2e);
-  - the output is rounded to BF16 (relative 2^-9) after a division by the
-    FP32 sum of weights (relative error below 2^-12 at these lengths);
-  - FP32 and the matrix cores have an underflow floor: a product of weight
-    and code below 2^-126 may be lost, so sequences of n tokens add an
-    absolute (n + 16) 2^-120 (times a static V scale above 1).
+Tolerance, per output element: oracle.attention_error_bound, derived from
+the kernel's arithmetic (BF16 softmax weights times the V scales in the value
+product, FP32 accumulation, a BF16 output, FP32 score error and underflow).
 Short sequences make a dropped or stray token exceed the bound; long ones
 exercise the split and combine kernels."""
 import math
@@ -107,24 +97,9 @@ class Scenario:
         qb = _bits(self.q)[rows]
         ref, absv = self.orc.decode_attention(self.g, self.img, 0, qb, bt[rows], lens[rows], self.sm_scale,
                                               with_absv=True)
-        # score error bound from the oracle's dequantized keys (BF16 of K^,
-        # widened by 2^-8 to bound K^ itself)
-        eps = np.zeros(ref.shape[:2])
-        ko, _ = self.orc.gather(self.g, self.img, 0, bt[rows], lens[rows])
-        kabs = np.abs(_f64(ko)) * (1 + 2.0 ** -8)
-        qabs = np.abs(_f64(qb))
-        row0 = 0
-        for i, n in enumerate(np.clip(lens[rows], 0, self.maxb * self.bs)):
-            if n:
-                kk = kabs[row0: row0 + n]                                  # [n, hkv, hd]
-                for qh in range(qabs.shape[1]):
-                    dots = kk[:, qh // self.group, :] @ qabs[i, qh]
-                    eps[i, qh] = (self.hd + 4) * 2.0 ** -24 * dots.max() * self.sm_scale
-            row0 += int(max(lens[rows][i], 0))
-        n_tok = np.clip(lens[rows], 0, self.maxb * self.bs).astype(np.float64)
-        v_big = 1.0 if self.scales is None else max(1.0, float(self.scales[len(self.scales) // 2:].max()))
-        floor = (n_tok[:, None, None] + 16) * 2.0 ** -120 * v_big
-        tol = (2.0 ** -8 + 2.5 * eps[:, :, None]) * absv + 2.0 ** -8 * np.abs(ref) + floor
+        v_big = 1.0 if self.scales is None else float(self.scales[len(self.scales) // 2:].max())
+        tol = self.orc.attention_error_bound(self.g, self.img, 0, qb, bt[rows], lens[rows], self.sm_scale, ref, absv,
+                                             v_big)
         return ref, tol
 
     def check(self, out, ref, tol, what):
