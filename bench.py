@@ -656,18 +656,24 @@ def run_other_workload(args, torch, kvq, W):
         agbps = ab / attn_s / 1e9
         # oracle check: layer L-1 of the last step for 8 sequences, from the
         # oracle's own image of that layer, within the kernel's error bound
-        g, host = _decode_oracle_layer(D, torch, W, oracle)
-        pick = list(range(0, S, S // 8))[:8]
-        bt_h = D["st"].block_table.numpy()
-        qb = _bits(torch, qs[-1])[pick]
-        t0 = time.perf_counter()
-        ref, absv = oracle.decode_attention(g, host, 0, qb, bt_h[pick], lens_last[pick], sm_scale, with_absv=True)
-        csec = time.perf_counter() - t0
-        tol = oracle.attention_error_bound(g, host, 0, qb, bt_h[pick], lens_last[pick], sm_scale, ref, absv)
-        got = (_bits(torch, out[pick]).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-        parity = bool((np.abs(got - ref) <= tol).all())
-        sample_tok = int(lens_last[pick].sum())
-        cab = attention_bytes(mode, hd, hkv, bs, H, len(pick), sample_tok)
+        parity, cpu = None, None
+        if not args.no_cpu_baseline:
+            g, host = _decode_oracle_layer(D, torch, W, oracle)
+            pick = list(range(0, S, S // 8))[:8]
+            bt_h = D["st"].block_table.numpy()
+            qb = _bits(torch, qs[-1])[pick]
+            t0 = time.perf_counter()
+            ref, absv = oracle.decode_attention(g, host, 0, qb, bt_h[pick], lens_last[pick], sm_scale, with_absv=True)
+            csec = time.perf_counter() - t0
+            tol = oracle.attention_error_bound(g, host, 0, qb, bt_h[pick], lens_last[pick], sm_scale, ref, absv)
+            got = (_bits(torch, out[pick]).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            parity = bool((np.abs(got - ref) <= tol).all())
+            sample_tok = int(lens_last[pick].sum())
+            cab = attention_bytes(mode, hd, hkv, bs, H, len(pick), sample_tok)
+            cpu = {"value": round(cab / csec / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+                   "kind": "oracle",
+                   "sample": f"fp64 attention of 8 of {S} sequences ({sample_tok} cached tokens) "
+                             f"of one layer, {csec:.2f} s wall"}
         res = {"metric": "decode attention over the quantized cache: cache GB/s read and decode tokens/s "
                          "(per-token-head FP8)",
                "value": round(L * (sb + ab) / sec / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -683,10 +689,7 @@ def run_other_workload(args, torch, kvq, W):
                "roofline": {"bound": "hbm", "kernel": "attention_kernel", "achieved": round(agbps, 1),
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(agbps / HBM_PEAK_GBPS, 4),
                             "traffic": None},
-               "cpu_baseline": {"value": round(cab / csec / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-                                "kind": "oracle",
-                                "sample": f"fp64 attention of 8 of {S} sequences ({sample_tok} cached tokens) "
-                                          f"of one layer, {csec:.2f} s wall"},
+               "cpu_baseline": cpu,
                "parity_vs_oracle_sampled": parity,
                "workspace_bytes": wsb, "cache_GiB": round(D["cache"].bytes["total"] / 2**30, 3)}
     print(json.dumps(res), flush=True)

@@ -50,6 +50,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 16;                 // tokens per tile
+constexpr int kMaxHeadsPerWg = 8;        // waves (KV heads) per attention workgroup
+constexpr int kMaxAttnThreads = 64 * kMaxHeadsPerWg;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int HD, int MODE>
@@ -60,8 +62,10 @@ struct Geo {
     static constexpr int RB = HD * BITS / 8;          // bytes of one K or V row
     static constexpr int KB = RB / 4;                 // K bytes per lane (hd/4 dims)
     static constexpr int VB = J * BITS / 8;           // V bytes per lane and token (J dims)
+    static constexpr int VL = VB < 4 ? 4 : VB;        // V bytes loaded (a 2-byte slice comes
+                                                      // with its neighbour's, in one aligned dword)
     static constexpr int KW = (KB + 3) / 4;
-    static constexpr int VW = (VB + 3) / 4;
+    static constexpr int VW = VL / 4;
     static constexpr bool DYN = dynamic_mode<MODE>();
     // INT4 codes widen to n / 16 (exact); the 16 goes back in with the scales.
     static constexpr float CODE_UNIT = MODE == KVQ_INT4_PER_TOKEN_HEAD ? 16.0f : 1.0f;
@@ -114,12 +118,36 @@ __device__ __forceinline__ void load_n(uint32_t* dst, const uint8_t* p) {
         else v = *reinterpret_cast<const u32x2*>(p);
         dst[0] = v[0];
         dst[1] = v[1];
-    } else if constexpr (N == 4) {
+    } else {
+        static_assert(N == 4, "row slice of 4, 8 or a multiple of 16 bytes");
         if constexpr (NT) dst[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
         else dst[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+}
+
+// Raw buffer loads (gfx9 descriptor word 3; cache-policy bit 1 = non-temporal).
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+
+template <int N, int AUX>
+__device__ __forceinline__ void buf_load(uint32_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff) {
+    if constexpr (N >= 16) {
+#pragma unroll
+        for (int k = 0; k < N / 16; ++k) {
+            const u32x4 v = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(voff) + 16 * k, soff, AUX));
+            dst[4 * k] = v[0];
+            dst[4 * k + 1] = v[1];
+            dst[4 * k + 2] = v[2];
+            dst[4 * k + 3] = v[3];
+        }
+    } else if constexpr (N == 8) {
+        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, static_cast<int>(voff), soff, AUX));
+        dst[0] = v[0];
+        dst[1] = v[1];
     } else {
-        static_assert(N == 2, "row slice of 2, 4, 8 or a multiple of 16 bytes");
-        dst[0] = *reinterpret_cast<const uint16_t*>(p);
+        static_assert(N == 4, "row slice of 4, 8 or a multiple of 16 bytes");
+        dst[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(voff), soff, AUX);
     }
 }
 
@@ -145,10 +173,13 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// INT4 nibble k of w -> n / 16 as FP32, exact.
-template <int K>
-__device__ __forceinline__ float int4_over16(uint32_t w) {
-    return __builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(w >> (4 * K)));
+// The low INT4 nibble of byte B of x -> n / 16 as FP32, exact.  Written as
+// byte extracts so that the conversion reads the byte through an SDWA operand
+// select instead of a separate shift.
+template <int B>
+__device__ __forceinline__ float int4_over16(uint32_t x) {
+    const uint32_t b = B == 0 ? x : (B == 3 ? x >> 24 : (x >> (8 * B)) & 0xFFu);
+    return __builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(b));
 }
 
 // K step j of the lane's K slice -> 8 BF16 A-operand values (dims 8j .. 8j+7
@@ -160,11 +191,14 @@ __device__ __forceinline__ bf16x8 k_operand(const uint32_t* k, int j) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = k[4 * j + e];
     } else if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
-        const uint32_t w = k[j];
-        o[0] = pack_bf16(int4_over16<0>(w), int4_over16<1>(w));
-        o[1] = pack_bf16(int4_over16<2>(w), int4_over16<3>(w));
-        o[2] = pack_bf16(int4_over16<4>(w), int4_over16<5>(w));
-        o[3] = pack_bf16(int4_over16<6>(w), int4_over16<7>(w));
+        // elements 2b and 2b+1 are the low and high nibbles of byte b; hi is
+        // w rotated right by 4 (a rotate, so that the byte extracts below are
+        // not folded back into bit-field extracts of w)
+        const uint32_t w = k[j], hi = __builtin_amdgcn_alignbit(w, w, 4);
+        o[0] = pack_bf16(int4_over16<0>(w), int4_over16<0>(hi));
+        o[1] = pack_bf16(int4_over16<1>(w), int4_over16<1>(hi));
+        o[2] = pack_bf16(int4_over16<2>(w), int4_over16<2>(hi));
+        o[3] = pack_bf16(int4_over16<3>(w), int4_over16<3>(hi));
     } else {
         o[0] = fp8x2_to_bf16x2<false>(k[2 * j]);
         o[1] = fp8x2_to_bf16x2<true>(k[2 * j]);
@@ -194,14 +228,26 @@ __device__ __forceinline__ void v_operands(const uint32_t (*v)[Geo<HD, MODE>::VW
             a[j + 1] = __builtin_bit_cast(s16x4, y);
         }
     } else if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+        // dim j of a token: nibble j % 8 of dword j / 8, i.e. the low (j even)
+        // or high (j odd) nibble of byte (j % 8) / 2
+        constexpr int VW = Geo<HD, MODE>::VW;
+        uint32_t hv[4][VW];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int w = 0; w < VW; ++w) hv[i][w] = __builtin_amdgcn_alignbit(v[i][w], v[i][w], 4);
+        auto nib = [&](int i, int j) -> float {
+            const uint32_t x = (j & 1) ? hv[i][j / 8] : v[i][j / 8];
+            switch ((j % 8) / 2) {
+                case 0: return int4_over16<0>(x);
+                case 1: return int4_over16<1>(x);
+                case 2: return int4_over16<2>(x);
+                default: return int4_over16<3>(x);
+            }
+        };
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int w = j / 8, sh = 4 * (j % 8);
-            const uint32_t p01 = pack_bf16(__builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(v[0][w] >> sh)),
-                                           __builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(v[1][w] >> sh)));
-            const uint32_t p23 = pack_bf16(__builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(v[2][w] >> sh)),
-                                           __builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(v[3][w] >> sh)));
-            const u32x2 x = {p01, p23};
+            const u32x2 x = {pack_bf16(nib(0, j), nib(1, j)), pack_bf16(nib(2, j), nib(3, j))};
             a[j] = __builtin_bit_cast(s16x4, x);
         }
     } else {
@@ -223,6 +269,34 @@ __device__ __forceinline__ void v_operands(const uint32_t (*v)[Geo<HD, MODE>::VW
 
 // ------------------------------------------------------------ the kernel
 
+// Tiles in flight per wave: enough bytes outstanding to cover the memory
+// latency with the waves a CU holds, within the register budget.
+template <int HD, int MODE>
+constexpr int attention_depth() {
+    return HD == 64 ? 4 : 2;
+}
+
+// Tiles per softmax round (rounds of two tiles measured no faster: the path
+// is bound by the memory requests in flight, not by the round's latency).
+template <int HD, int MODE>
+constexpr int attention_round() {
+    return 1;
+}
+
+// Whether rounds with no token to mask take a path of their own (at head_dim
+// 256 the second copy of the round costs more registers than it saves).
+template <int HD>
+constexpr bool attention_fast_path() {
+    return HD < 256;
+}
+
+// Waves per SIMD the register allocation must allow: one workgroup of eight
+// waves per CU.
+template <int HD>
+constexpr int attention_waves() {
+    return 2;
+}
+
 template <int HD, int MODE>
 struct Tile {
     uint32_t k[Geo<HD, MODE>::KW];
@@ -233,11 +307,39 @@ struct Tile {
 
 // Loads of tile tau of sequence b for KV head h.  Entries of the block table
 // that do not name a block of the layer read block 0 instead and are masked.
+// Per-lane byte offsets inside a block, fixed for a wave (KV head h, lane
+// r, q4): the tile's first position adds a wave-uniform term, so the loads
+// take a scalar base and a 32-bit lane offset.
+struct LaneOff {
+    uint32_t vsh;                  // right shift that moves a 2-byte V slice to bits 0..15
+    uint32_t k;                    // K slice of token r
+    uint32_t v[4];                 // V slices of tokens 4q4+i
+    uint32_t s[4];                 // (s_K, s_V) of tokens 4q4+i, from the scale trailer
+};
+
+template <int HD, int MODE>
+__device__ __forceinline__ LaneOff lane_offsets(const AttnArgs& a, int h, int r, int q4) {
+    using G = Geo<HD, MODE>;
+    const uint32_t hkv = static_cast<uint32_t>(a.hkv), uh = static_cast<uint32_t>(h);
+    LaneOff o;
+    o.vsh = G::VB == 2 ? 16u * static_cast<uint32_t>(r & 1) : 0u;
+    o.k = ((static_cast<uint32_t>(r) * hkv + uh) * 2) * G::RB + static_cast<uint32_t>(q4) * G::KB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t pos = static_cast<uint32_t>(4 * q4 + i);
+        o.v[i] = (((pos * hkv + uh) * 2 + 1) * G::RB + static_cast<uint32_t>(r) * G::VB) & ~static_cast<uint32_t>(G::VL - 1);
+        o.s[i] = static_cast<uint32_t>(a.code_bytes) + (pos * hkv + uh) * 8;
+    }
+    return o;
+}
+
+// Loads of tile tau of sequence b for KV head h.  Entries of the block table
+// that do not name a block of the layer read block 0 instead and are masked.
 // With blocks of 16 or more tokens a tile lies in one block, whose id (blk,
 // read by the caller one tile ahead) is the same for the whole wave.
 template <int HD, int MODE, bool SMALL_BS>
 __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt_row, int blk, int h, int tau, int r,
-                                          int q4, Tile<HD, MODE>& T) {
+                                          int q4, const LaneOff& lo, Tile<HD, MODE>& T) {
     using G = Geo<HD, MODE>;
     const int t0 = tau * kTile;
     const int bs_mask = (1 << a.bs_log2) - 1;
@@ -246,15 +348,22 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt_r
         // rejects negative ids)
         const bool ok = static_cast<uint32_t>(blk) < static_cast<uint32_t>(a.num_blocks);
         const uint32_t ublk = ok ? static_cast<uint32_t>(blk) : 0u;
+        const uint32_t pos0 = static_cast<uint32_t>(t0 & bs_mask);
+        // a buffer descriptor of the block: lane offsets in VGPRs, the tile's
+        // first row as a scalar offset, no 64-bit address arithmetic per lane
         const uint8_t* base = a.layer + static_cast<uint64_t>(ublk) * static_cast<uint64_t>(a.block_bytes);
-        const int pos0 = t0 & bs_mask;
-        load_n<G::KB, true>(T.k, base + (((pos0 + r) * a.hkv + h) * 2) * G::RB + q4 * G::KB);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(base), 0, static_cast<int>(a.block_bytes), kBufferDword3);
+        const int srow = static_cast<int>(pos0 * static_cast<uint32_t>(a.hkv) * (2 * G::RB));
+        buf_load<G::KB, kNonTemporal>(T.k, rs, lo.k, srow);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int pos = pos0 + 4 * q4 + i;
-            load_n<G::VB, true>(T.v[i], base + (((pos * a.hkv + h) * 2) + 1) * G::RB + r * G::VB);
-            if constexpr (G::DYN)
-                T.s[i] = *reinterpret_cast<const f32x2*>(base + a.code_bytes + (pos * a.hkv + h) * 8);
+            buf_load<G::VL, kNonTemporal>(T.v[i], rs, lo.v[i], srow);
+            if constexpr (G::DYN) {
+                uint32_t w[2];
+                buf_load<8, 0>(w, rs, lo.s[i], static_cast<int>(pos0 * static_cast<uint32_t>(a.hkv) * 8u));
+                T.s[i] = f32x2{__uint_as_float(w[0]), __uint_as_float(w[1])};
+            }
         }
         T.ok = ok ? 0xFu : 0u;
     } else {
@@ -262,8 +371,8 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt_r
         {
             const int t = t0 + r;
             int blk = bt_row[min(t >> a.bs_log2, last)];
-            blk = static_cast<uint64_t>(static_cast<int64_t>(blk)) < static_cast<uint64_t>(a.num_blocks) ? blk : 0;
-            const uint8_t* base = a.layer + static_cast<int64_t>(blk) * a.block_bytes;
+            blk = static_cast<uint32_t>(blk) < static_cast<uint32_t>(a.num_blocks) ? blk : 0;
+            const uint8_t* base = a.layer + static_cast<uint64_t>(static_cast<uint32_t>(blk)) * a.block_bytes;
             load_n<G::KB, true>(T.k, base + ((((t & bs_mask) * a.hkv) + h) * 2) * G::RB + q4 * G::KB);
         }
         uint32_t ok = 0;
@@ -271,12 +380,12 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt_r
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + 4 * q4 + i;
             int blk = bt_row[min(t >> a.bs_log2, last)];
-            const bool good = static_cast<uint64_t>(static_cast<int64_t>(blk)) < static_cast<uint64_t>(a.num_blocks);
+            const bool good = static_cast<uint32_t>(blk) < static_cast<uint32_t>(a.num_blocks);
             blk = good ? blk : 0;
             ok |= good ? (1u << i) : 0u;
-            const uint8_t* base = a.layer + static_cast<int64_t>(blk) * a.block_bytes;
+            const uint8_t* base = a.layer + static_cast<uint64_t>(static_cast<uint32_t>(blk)) * a.block_bytes;
             const int pos = t & bs_mask;
-            load_n<G::VB, true>(T.v[i], base + (((pos * a.hkv + h) * 2) + 1) * G::RB + r * G::VB);
+            load_n<G::VL, true>(T.v[i], base + ((((pos * a.hkv + h) * 2) + 1) * G::RB + r * G::VB) / G::VL * G::VL);
             if constexpr (G::DYN)
                 T.s[i] = *reinterpret_cast<const f32x2*>(base + a.code_bytes + (pos * a.hkv + h) * 8);
         }
@@ -306,56 +415,82 @@ struct State {
     float l;                       // this lane's share of the running sum
 };
 
-template <int HD, int MODE>
-__device__ __forceinline__ void tile_step(const Tile<HD, MODE>& T, State<HD, MODE>& st, const bf16x8* qb, int t0,
-                                          int len, int q4, float k_factor) {
+// One round of the online softmax over NT consecutive tiles (16 NT tokens):
+// the tiles' Q K^T products, one running-maximum update, then their P V
+// products.  MASK = false is the path of rounds whose tokens all lie below
+// len in blocks of the layer (a wave-uniform fact).
+template <int HD, int MODE, int NT, bool MASK>
+__device__ __forceinline__ void tile_round(const Tile<HD, MODE>* const* T, State<HD, MODE>& st, const bf16x8* qb,
+                                           int t0, int len, int q4, float k_factor, uint32_t vsh) {
     using G = Geo<HD, MODE>;
-    f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 sacc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) sacc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < G::KSTEPS; ++j)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(T.k, j), qb[j], sacc, 0, 0, 0);
-
-    float s[4];
-    bool valid[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        valid[i] = (t0 + 4 * q4 + i < len) && ((T.ok >> i) & 1u);
-        const float f = G::DYN ? T.s[i][0] * k_factor : k_factor;
-        s[i] = valid[i] ? sacc[i] * f : -INFINITY;
-    }
-    const float tmax = max_q4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+        for (int n = 0; n < NT; ++n)
+            sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(T[n]->k, j), qb[j], sacc[n], 0, 0, 0);
+
+    float s[NT][4];
+    bool valid[NT][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            valid[n][i] = !MASK || ((t0 + kTile * n + 4 * q4 + i < len) && ((T[n]->ok >> i) & 1u));
+            const float f = G::DYN ? T[n]->s[i][0] * k_factor : k_factor;
+            s[n][i] = valid[n][i] ? sacc[n][i] * f : -INFINITY;
+            tmax = fmaxf(tmax, s[n][i]);
+        }
+    tmax = max_q4(tmax);
     const float mnew = fmaxf(st.m, tmax);
     const float mref = mnew == -INFINITY ? 0.0f : mnew;
     const float alpha = __builtin_amdgcn_exp2f(st.m - mref);
-    float p[4];
+    float psum = 0.0f;
+    s16x4 b[NT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - mref);
-    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    for (int n = 0; n < NT; ++n) {
+        float p[4], pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(s[n][i] - mref);
+            pv[i] = valid[n][i] ? (G::DYN ? p[i] * (T[n]->s[i][1] * G::CODE_UNIT) : p[i]) : 0.0f;
+        }
+        psum += (p[0] + p[1]) + (p[2] + p[3]);
+        const u32x2 pb = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
+        b[n] = __builtin_bit_cast(s16x4, pb);
+    }
+    st.l = st.l * alpha + psum;
     st.m = mnew;
 
-    float pv[4];
+    s16x4 av[NT][G::J];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pv[i] = valid[i] ? (G::DYN ? p[i] * (T.s[i][1] * G::CODE_UNIT) : p[i]) : 0.0f;
-    const u32x2 pb = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
-    const s16x4 b = __builtin_bit_cast(s16x4, pb);
-
-    // masked tokens may hold any bytes (NaN codes included): zero them
-    uint32_t vz[4][G::VW];
+    for (int n = 0; n < NT; ++n) {
+        // masked tokens may hold any bytes (NaN codes included): zero them
+        uint32_t vz[4][G::VW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int w = 0; w < G::VW; ++w) vz[i][w] = valid[i] ? T.v[i][w] : 0u;
-    s16x4 av[G::J];
-    v_operands<HD, MODE>(vz, av);
-#pragma unroll
-    for (int j = 0; j < G::J; ++j) {
-        st.o[j] *= alpha;
-        st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], b, st.o[j], 0, 0, 0);
+            for (int w = 0; w < G::VW; ++w)
+                vz[i][w] = valid[n][i] ? (G::VB == 2 ? T[n]->v[i][w] >> vsh : T[n]->v[i][w]) : 0u;
+        v_operands<HD, MODE>(vz, av[n]);
     }
+    // once the running maxima settle, alpha is 1 in every lane: skip the rescale
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int j = 0; j < G::J; ++j) st.o[j] *= alpha;
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int j = 0; j < G::J; ++j)
+            st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[n][j], b[n], st.o[j], 0, 0, 0);
 }
 
 template <int HD, int MODE, bool SMALL_BS>
-__global__ void __launch_bounds__(512) attention_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attention_kernel(AttnArgs a) {
     using G = Geo<HD, MODE>;
     // Workgroup -> work item, spreading consecutive items over one XCD
     // (workgroups are dealt to the 8 XCDs round robin).
@@ -413,30 +548,57 @@ __global__ void __launch_bounds__(512) attention_kernel(AttnArgs a) {
 
     const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
     if (tbeg < tend) {
-        // Two tiles in flight: the next tile's loads are issued before the
-        // current tile's arithmetic.  An odd count ends on a fully masked
-        // tile (tokens at or past the split's end take no part), so the loop
-        // has no exit between a load and its use; loads past the end re-read
-        // the last tile, and the final prefetch is consumed at the exit.
+        // Rounds of NT tiles, D tiles in flight: while a round is computed,
+        // the loads of the next D - NT tiles are outstanding.  The loop runs
+        // whole passes of D tiles; tiles at or past the split's end are fully
+        // masked (they take no part) and their loads re-read the last tile,
+        // so no loop exit falls between a load and its use, and the
+        // prefetches still pending at the exit are consumed there.
+        constexpr int D = attention_depth<HD, MODE>();
+        constexpr int NT = attention_round<HD, MODE>();
+        static_assert(D % NT == 0 && D > NT, "whole rounds, at least one round in flight");
         const int lim = min(len, tend * kTile);
+        const int last = tend - 1;
         auto block_of = [&](int tau) { return SMALL_BS ? 0 : bt_row[(tau * kTile) >> a.bs_log2]; };
-        Tile<HD, MODE> ta, tb;
-        load_tile<HD, MODE, SMALL_BS>(a, bt_row, block_of(tbeg), h, tbeg, r, q4, ta);
-        int nb = block_of(min(tbeg + 1, tend - 1));
-        // (the scheduling barriers keep each prefetch ahead of the arithmetic)
-        for (int tau = tbeg; tau < tend; tau += 2) {
-            load_tile<HD, MODE, SMALL_BS>(a, bt_row, nb, h, min(tau + 1, tend - 1), r, q4, tb);
-            nb = block_of(min(tau + 2, tend - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            tile_step<HD, MODE>(ta, st, qb, tau * kTile, lim, q4, k_factor);
-            __builtin_amdgcn_sched_barrier(0);
-            load_tile<HD, MODE, SMALL_BS>(a, bt_row, nb, h, min(tau + 2, tend - 1), r, q4, ta);
-            nb = block_of(min(tau + 3, tend - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            tile_step<HD, MODE>(tb, st, qb, (tau + 1) * kTile, lim, q4, k_factor);
+        const LaneOff lo = lane_offsets<HD, MODE>(a, h, r, q4);
+        Tile<HD, MODE> t[D];
+        // (in tile order, so that the loop's waits for the oldest tile also
+        // hold on entry)
+#pragma unroll
+        for (int k = 0; k < D - NT; ++k) {
+            load_tile<HD, MODE, SMALL_BS>(a, bt_row, block_of(min(tbeg + k, last)), h, min(tbeg + k, last), r, q4,
+                                          lo, t[k]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        consume(ta);
+        int nb = block_of(min(tbeg + D - NT, last));
+        // (the scheduling barriers keep each prefetch ahead of the arithmetic)
+        for (int tau = tbeg; tau < tend; tau += D) {
+#pragma unroll
+            for (int k = 0; k < D; k += NT) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    load_tile<HD, MODE, SMALL_BS>(a, bt_row, nb, h, min(tau + k + D - NT + n, last), r, q4, lo,
+                                                  t[(k + D - NT + n) % D]);
+                    nb = block_of(min(tau + k + D - NT + n + 1, last));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const Tile<HD, MODE>* rt[NT];
+                bool all_ok = true;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    rt[n] = &t[k + n];
+                    all_ok = all_ok && t[k + n].ok != 0;
+                }
+                const int t0 = (tau + k) * kTile;
+                if (attention_fast_path<HD>() && !SMALL_BS && t0 + NT * kTile <= lim && all_ok)
+                    tile_round<HD, MODE, NT, false>(rt, st, qb, t0, lim, q4, k_factor, lo.vsh);
+                else
+                    tile_round<HD, MODE, NT, true>(rt, st, qb, t0, lim, q4, k_factor, lo.vsh);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < D - NT; ++k) consume(t[k]);
     }
 
     const float l = sum_q4(st.l);
@@ -555,7 +717,7 @@ AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_d
                         int32_t max_blocks, int32_t num_seqs) {
     AttnPlan pl{};
     int hpw = 1;
-    while (hpw < 8 && num_kv_heads % (2 * hpw) == 0) hpw *= 2;
+    while (hpw < kMaxHeadsPerWg && num_kv_heads % (2 * hpw) == 0) hpw *= 2;
     pl.heads_per_wg = hpw;
     const int group = num_q_heads / num_kv_heads;
     pl.qgroups = (group + 15) / 16;
