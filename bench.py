@@ -58,13 +58,36 @@ def algorithmic_bytes(mode, hd, hkv, bs, token_heads):
     return store, gather
 
 
-def kernel_source_hash():
-    """Hash of the sources the store and gather kernels are built from."""
+def kernel_source_hash(sources=None):
+    """Hash of the sources a kernel is built from (default: store and gather)."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in sources or KERNEL_SOURCES:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+ATTN_SOURCES = [os.path.join(ROOT, "quantized_fp8_int4_amd", "csrc", f)
+                for f in ("kvq_attention.hip", "kvq_device.h", "kvq_exact.h")]
+
+
+def attention_profile_paths(mode_name, hd):
+    base = f"attention_decode_{mode_name}_hd{hd}.md"
+    return (os.path.join(ROOT, "profiles", "kernel_trace_" + base), os.path.join(ROOT, "profiles", "traffic_" + base))
+
+
+def measured_attention_traffic(mode_name, hd):
+    """Per-launch HBM bytes of the attention kernel from the committed counter
+    summary, if it was taken on the current kernel source."""
+    path = attention_profile_paths(mode_name, hd)[1]
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"traffic_bytes_per_launch\[attention\]:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash(ATTN_SOURCES):
+        return None
+    return float(m_val.group(1))
 
 
 def measured_traffic():
@@ -104,6 +127,10 @@ def _counter_per_kernel(rows, counter):
             acc.setdefault("store", []).append(val)
         elif "gather_kernel" in name:
             acc.setdefault("gather", []).append(val)
+        elif "attention_kernel" in name:
+            acc.setdefault("attention", []).append(val)
+        elif "combine_kernel" in name:
+            acc.setdefault("combine", []).append(val)
         elif "copyBuffer" in name:
             copies.append(val)
     top = max(copies)
@@ -156,6 +183,66 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir):
     for k in ("store", "gather"):
         out.append(f"traffic_bytes_per_launch[{k}]: {fetch[k][0] * 1024.0 * f_scale + write[k][0] * 1024.0 * w_scale:.6g}")
     with open(PROFILE_TRAFFIC, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(lines + [""] + out))
+
+
+def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd):
+    """profiles/ summaries of the decode-attention workload from three
+    rocprofv3 runs of bench.py --workload attention (kernel trace with
+    --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, the latter two with
+    --calibrate-copy)."""
+    kt_path, tr_path = attention_profile_paths(mode_name, hd)
+    args_s = f"--workload attention --mode {mode_name} --head-dim {hd}"
+    stats = _read_csv(kt_dir, "kernel_stats.csv")
+    lines = [f"# Kernel trace: decode attention, 256 x 8192 tokens, 32 query / 8 KV heads, {mode_name}, head_dim {hd}", "",
+             "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(kt_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline",
+             "", "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r.get("Name") or r.get("KernelName") or ""
+        if "kvq" not in name:
+            continue
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    with open(kt_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    fetch = _counter_per_kernel(_read_csv(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    write = _counter_per_kernel(_read_csv(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    f_scale = COPY_BYTES / (fetch["copy"][0] * 1024.0)
+    w_scale = COPY_BYTES / (write["copy"][0] * 1024.0)
+    mode = {"fp8_per_token_head": 3, "int4_per_token_head": 4}[mode_name]
+    S, ctx, hkv, H, bs = 256, 8192, 8, 32, 16
+    # the profiled launches: 4 fused steps (lengths ctx + 1 .. ctx + 4) and 4
+    # attention-only passes at ctx + 4, 32 layers each: mean length ctx + 3.25
+    algo = attention_bytes(mode, hd, hkv, bs, H, S, int(S * (ctx + 3.25)))
+    flt = "--kernel-include-regex 'attention_kernel|combine_kernel|copyBuffer'"
+    out = [f"# HBM traffic per launch: decode attention, {mode_name}, head_dim {hd} (256 x ~8195 cached tokens, 8 KV heads)", "",
+           "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+           f"    rocprofv3 --pmc FETCH_SIZE {flt} --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(fetch_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
+           f"    rocprofv3 --pmc WRITE_SIZE {flt} --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(write_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
+           "",
+           f"Calibration: a {COPY_BYTES >> 20} MiB device-to-device copy reads FETCH_SIZE {fetch['copy'][0]:.0f} KiB and "
+           f"WRITE_SIZE {write['copy'][0]:.0f} KiB per dispatch; scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
+           "Algorithmic bytes per launch: every cached token's K and V codes and per-token scales once, the block-table "
+           "entries, the BF16 queries and outputs (the split partials the combine kernel reads are not counted).", "",
+           "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched bytes (scaled) | written bytes (scaled) | traffic | algorithmic | traffic / algorithmic |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    tot = 0.0
+    for k in ("attention", "combine"):
+        if k not in fetch:
+            continue
+        fb = fetch[k][0] * 1024.0 * f_scale
+        wb = write[k][0] * 1024.0 * w_scale
+        tot += fb + wb
+        a_s = f"{algo:.4g}" if k == "attention" else "-"
+        r_s = f"{(fb + wb) / algo:.3f}" if k == "attention" else "-"
+        out.append(f"| {k}_kernel | {fetch[k][1]} | {fetch[k][0]:.0f} | {write[k][0]:.0f} | {fb:.4g} | {wb:.4g} | "
+                   f"{fb + wb:.4g} | {a_s} | {r_s} |")
+    out += ["", f"kernel_source_sha256_16: {kernel_source_hash(ATTN_SOURCES)}",
+            f"traffic_bytes_per_launch[attention]: {tot:.6g}"]
+    with open(tr_path, "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(lines + [""] + out))
 
@@ -649,6 +736,12 @@ def run_other_workload(args, torch, kvq, W):
             if ev: ev[1].record(); ev[2].record()
         _, aevs = _timed(torch, attn_only, args.steps, 1)
         attn_s = sum(e[0].elapsed_time(e[1]) for e in aevs) / (args.steps * L) / 1e3
+        if args.calibrate_copy:
+            src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
         lens_last = D["lens_at"][-1].cpu().numpy()
         ntok = int(lens_last.sum())
         sb, _ = algorithmic_bytes(mode, hd, hkv, bs, S * hkv)
@@ -688,7 +781,7 @@ def run_other_workload(args, torch, kvq, W):
                "decode_tokens_per_s": round(S / sec, 1),
                "roofline": {"bound": "hbm", "kernel": "attention_kernel", "achieved": round(agbps, 1),
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(agbps / HBM_PEAK_GBPS, 4),
-                            "traffic": None},
+                            "traffic": measured_attention_traffic(args.mode, hd)},
                "cpu_baseline": cpu,
                "parity_vs_oracle_sampled": parity,
                "workspace_bytes": wsb, "cache_GiB": round(D["cache"].bytes["total"] / 2**30, 3)}
@@ -711,11 +804,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, copy 256 MiB device-to-device 3 times (reference for counter scaling)")
+    ap.add_argument("--summarize-attention-profiles", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the attention profiles/ summaries (for --mode and --head-dim) and exit")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from rocprofv3 csv output and exit")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles)
+        return
+    if args.summarize_attention_profiles:
+        summarize_attention_profiles(*args.summarize_attention_profiles, args.mode, args.head_dim)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
