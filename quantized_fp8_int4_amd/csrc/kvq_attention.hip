@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -67,6 +69,11 @@ struct Geo {
     static constexpr int KW = (KB + 3) / 4;
     static constexpr int VW = VL / 4;
     static constexpr bool DYN = dynamic_mode<MODE>();
+    // Staged reads: a tile's 16 K|V row pairs (2 * RB bytes each) read as
+    // whole 16-byte pieces, NC wave-wide loads of 1 KiB, then regrouped in LDS.
+    static constexpr int NC = 16 * 2 * RB / 1024;
+    static constexpr int LDS_ROW = 2 * RB + 16;       // padded row pair: conflict-free K slices
+    static constexpr int LDS_TILE = 16 * LDS_ROW;
     // INT4 codes widen to n / 16 (exact); the 16 goes back in with the scales.
     static constexpr float CODE_UNIT = MODE == KVQ_INT4_PER_TOKEN_HEAD ? 16.0f : 1.0f;
 };
@@ -283,6 +290,14 @@ constexpr int attention_round() {
     return 1;
 }
 
+// Whether a tile's K and V rows are read as whole lines and regrouped in LDS
+// (one L2 request per line) instead of straight into the MFMA operand lanes
+// (where the K and the V slices of a line are separate requests).
+template <int HD, int MODE>
+constexpr bool attention_staged() {
+    return Geo<HD, MODE>::NC >= 1 && Geo<HD, MODE>::NC <= 4 && HD <= 128;
+}
+
 // Whether rounds with no token to mask take a path of their own (at head_dim
 // 256 the second copy of the round costs more registers than it saves).
 template <int HD>
@@ -305,12 +320,22 @@ struct Tile {
     uint32_t ok;                   // bit i: token 4q+i's block names a block of the layer
 };
 
+// A tile read for LDS regrouping: this lane's whole 16-byte pieces of the
+// tile's 16 K|V row pairs, plus the same scales and mask as Tile.
+template <int HD, int MODE>
+struct RawTile {
+    uint32_t kv[4 * Geo<HD, MODE>::NC];
+    f32x2 s[4];
+    uint32_t ok;
+};
+
 // Loads of tile tau of sequence b for KV head h.  Entries of the block table
 // that do not name a block of the layer read block 0 instead and are masked.
 // Per-lane byte offsets inside a block, fixed for a wave (KV head h, lane
 // r, q4): the tile's first position adds a wave-uniform term, so the loads
 // take a scalar base and a 32-bit lane offset.
 struct LaneOff {
+    uint32_t kv[4];                // staged reads: the lane's 16-byte pieces of the tile's row pairs
     uint32_t vsh;                  // right shift that moves a 2-byte V slice to bits 0..15
     uint32_t k;                    // K slice of token r
     uint32_t v[4];                 // V slices of tokens 4q4+i
@@ -322,6 +347,13 @@ __device__ __forceinline__ LaneOff lane_offsets(const AttnArgs& a, int h, int r,
     using G = Geo<HD, MODE>;
     const uint32_t hkv = static_cast<uint32_t>(a.hkv), uh = static_cast<uint32_t>(h);
     LaneOff o;
+    const uint32_t lane = static_cast<uint32_t>(16 * q4 + r);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t g = static_cast<uint32_t>(c) * 1024u + lane * 16u;       // byte of the tile's row-pair image
+        const uint32_t tok = g / (2 * G::RB), off = g % (2 * G::RB);
+        o.kv[c] = (tok * hkv + uh) * (2 * G::RB) + off;
+    }
     o.vsh = G::VB == 2 ? 16u * static_cast<uint32_t>(r & 1) : 0u;
     o.k = ((static_cast<uint32_t>(r) * hkv + uh) * 2) * G::RB + static_cast<uint32_t>(q4) * G::KB;
 #pragma unroll
@@ -391,6 +423,70 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, const int32_t* bt_r
         }
         T.ok = ok;
     }
+}
+
+// Staged loads of tile tau (blocks of 16 or more tokens only).
+template <int HD, int MODE>
+__device__ __forceinline__ void load_raw(const AttnArgs& a, int blk, int tau, const LaneOff& lo, RawTile<HD, MODE>& T) {
+    using G = Geo<HD, MODE>;
+    const int t0 = tau * kTile;
+    const bool ok = static_cast<uint32_t>(blk) < static_cast<uint32_t>(a.num_blocks);
+    const uint32_t ublk = ok ? static_cast<uint32_t>(blk) : 0u;
+    const uint32_t pos0 = static_cast<uint32_t>(t0 & ((1 << a.bs_log2) - 1));
+    const uint8_t* base = a.layer + static_cast<uint64_t>(ublk) * static_cast<uint64_t>(a.block_bytes);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(base), 0, static_cast<int>(a.block_bytes), kBufferDword3);
+    const int srow = static_cast<int>(pos0 * static_cast<uint32_t>(a.hkv) * (2 * G::RB));
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) buf_load<16, kNonTemporal>(T.kv + 4 * c, rs, lo.kv[c], srow);
+    if constexpr (G::DYN) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t w[2];
+            buf_load<8, 0>(w, rs, lo.s[i], static_cast<int>(pos0 * static_cast<uint32_t>(a.hkv) * 8u));
+            T.s[i] = f32x2{__uint_as_float(w[0]), __uint_as_float(w[1])};
+        }
+    }
+    T.ok = ok ? 0xFu : 0u;
+}
+
+// The staged tile into the wave's LDS rows, then the K and V operand slices
+// back out of them (the same registers Tile holds when read directly).
+template <int HD, int MODE>
+__device__ __forceinline__ void unstage(const RawTile<HD, MODE>& R, uint8_t* lds, int r, int q4, Tile<HD, MODE>& T) {
+    using G = Geo<HD, MODE>;
+    const uint32_t lane = static_cast<uint32_t>(16 * q4 + r);
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) {
+        const uint32_t g = static_cast<uint32_t>(c) * 1024u + lane * 16u;
+        const uint32_t tok = g / (2 * G::RB), off = g % (2 * G::RB);
+        const u32x4 v = {R.kv[4 * c], R.kv[4 * c + 1], R.kv[4 * c + 2], R.kv[4 * c + 3]};
+        *reinterpret_cast<u32x4*>(lds + tok * G::LDS_ROW + off) = v;
+    }
+    const uint8_t* kp = lds + r * G::LDS_ROW + q4 * G::KB;
+#pragma unroll
+    for (int w = 0; w < G::KW; w += 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(kp + 4 * w);
+        T.k[w] = v[0];
+        T.k[w + 1] = v[1];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint8_t* vp = lds + (4 * q4 + i) * G::LDS_ROW + G::RB + ((r * G::VB) & ~(G::VL - 1));
+#pragma unroll
+        for (int w = 0; w < G::VW; ++w) T.v[i][w] = reinterpret_cast<const uint32_t*>(vp)[w];
+        T.s[i] = R.s[i];
+    }
+    T.ok = R.ok;
+}
+
+template <int HD, int MODE>
+__device__ __forceinline__ void consume(const RawTile<HD, MODE>& T) {
+#pragma unroll
+    for (int w = 0; w < 4 * Geo<HD, MODE>::NC; ++w) asm volatile("" ::"v"(T.kv[w]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if constexpr (Geo<HD, MODE>::DYN) asm volatile("" ::"v"(T.s[i][0]), "v"(T.s[i][1]));
 }
 
 // An empty use of every register of T, so that no load of T is moved past
@@ -561,13 +657,21 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
         const int last = tend - 1;
         auto block_of = [&](int tau) { return SMALL_BS ? 0 : bt_row[(tau * kTile) >> a.bs_log2]; };
         const LaneOff lo = lane_offsets<HD, MODE>(a, h, r, q4);
-        Tile<HD, MODE> t[D];
+        constexpr bool STAGE = attention_staged<HD, MODE>() && !SMALL_BS;
+        using InFlight = typename std::conditional<STAGE, RawTile<HD, MODE>, Tile<HD, MODE>>::type;
+        // each wave's own LDS rows for the regrouping of staged tiles
+        __shared__ __attribute__((aligned(16))) uint8_t lds_all[STAGE ? kMaxHeadsPerWg * Geo<HD, MODE>::LDS_TILE : 16];
+        uint8_t* lds = lds_all + (STAGE ? (threadIdx.x >> 6) * Geo<HD, MODE>::LDS_TILE : 0);
+        auto load = [&](int blk, int tau, InFlight& x) {
+            if constexpr (STAGE) load_raw<HD, MODE>(a, blk, tau, lo, x);
+            else load_tile<HD, MODE, SMALL_BS>(a, bt_row, blk, h, tau, r, q4, lo, x);
+        };
+        InFlight t[D];
         // (in tile order, so that the loop's waits for the oldest tile also
         // hold on entry)
 #pragma unroll
         for (int k = 0; k < D - NT; ++k) {
-            load_tile<HD, MODE, SMALL_BS>(a, bt_row, block_of(min(tbeg + k, last)), h, min(tbeg + k, last), r, q4,
-                                          lo, t[k]);
+            load(block_of(min(tbeg + k, last)), min(tbeg + k, last), t[k]);
             __builtin_amdgcn_sched_barrier(0);
         }
         int nb = block_of(min(tbeg + D - NT, last));
@@ -577,16 +681,21 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
             for (int k = 0; k < D; k += NT) {
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    load_tile<HD, MODE, SMALL_BS>(a, bt_row, nb, h, min(tau + k + D - NT + n, last), r, q4, lo,
-                                                  t[(k + D - NT + n) % D]);
+                    load(nb, min(tau + k + D - NT + n, last), t[(k + D - NT + n) % D]);
                     nb = block_of(min(tau + k + D - NT + n + 1, last));
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                Tile<HD, MODE> staged[STAGE ? NT : 1];
                 const Tile<HD, MODE>* rt[NT];
                 bool all_ok = true;
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    rt[n] = &t[k + n];
+                    if constexpr (STAGE) {
+                        unstage<HD, MODE>(t[k + n], lds, r, q4, staged[n]);
+                        rt[n] = &staged[n];
+                    } else {
+                        rt[n] = &t[k + n];
+                    }
                     all_ok = all_ok && t[k + n].ok != 0;
                 }
                 const int t0 = (tau + k) * kTile;
