@@ -51,7 +51,8 @@ typedef enum kvq_status {
     KVQ_ERR_MODE_MISMATCH = -2,    /* kvq_store mode differs from the layer's mode */
     KVQ_ERR_BUFFER_TOO_SMALL = -3, /* cache buffer smaller than kvq_cache_bytes().total */
     KVQ_ERR_UNSUPPORTED = -4,      /* geometry outside what the kernels handle */
-    KVQ_ERR_HIP = -5               /* a HIP launch or runtime call failed */
+    KVQ_ERR_HIP = -5,              /* a HIP launch or runtime call failed */
+    KVQ_ERR_NO_SPACE = -6          /* kvq_manager_append: no free block left */
 } kvq_status;
 
 /* Per-layer cache mode ("Per-tensor vs per-head FP8 KV cache scales",
@@ -299,6 +300,138 @@ KVQ_API kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const
                                         const int32_t* block_table, int32_t max_blocks_per_seq,
                                         const int32_t* seq_lens, int32_t num_seqs, float sm_scale, void* out,
                                         void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Capacity planning and the decode-time block manager (host code only)
+ * ---------------------------------------------------------------------- */
+
+/* Model geometry for planning: a cache geometry without block counts, plus
+ * each layer's retention.  All pointers are host memory, read during the call.
+ *  layer_mode    [num_layers] kvq_mode values
+ *  layer_window  [num_layers] 0 = full attention (the layer retains the whole
+ *                context); W > 0 = sliding window retaining at most the last
+ *                W positions, a multiple of block_size ("FP8 KV cache layer
+ *                skipping vs per-head scales", "Layer skipping follows
+ *                retained-token footprint")
+ * Other fields as in kvq_cache_config. */
+typedef struct kvq_model_config {
+    int32_t num_layers;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    const int32_t* layer_mode;
+    const int32_t* layer_window;
+} kvq_model_config;
+
+/* A capacity plan for sequences of one context length.
+ *  retained_positions  A: retained token-layer positions of one sequence,
+ *                      min(context, W) for a sliding layer, context otherwise
+ *  skipped_positions   S: the same sum over the BF16 (skipped) layers; the
+ *                      payload compression against all-BF16 is 2A / (A + S)
+ *                      when the quantized layers carry no per-token scales
+ *  sequence_bytes      one sequence's cache bytes: whole blocks of every
+ *                      layer, codes plus per-token scales
+ *  max_sequences       the most sequences of this context whose whole cache
+ *                      buffer (kvq_cache_bytes().total of the planned block
+ *                      counts: blocks, layer alignment, static scales) fits
+ *                      the pool
+ *  max_tokens          max_sequences * context
+ *  buffer_bytes        kvq_cache_bytes().total of the planned block counts */
+typedef struct kvq_plan {
+    int64_t retained_positions;
+    int64_t skipped_positions;
+    uint64_t sequence_bytes;
+    int64_t max_sequences;
+    int64_t max_tokens;
+    uint64_t buffer_bytes;
+} kvq_plan;
+
+/*
+ * kvq_plan_capacity -- how many sequences of `context` tokens fit a usable
+ * pool of pool_bytes, and the block count of every layer that holds them.
+ * "Per-token-head KV cache scale overhead", section "Convert bytes into block
+ * capacity" (bytes per token times the block size, rounded to whole blocks;
+ * the usable pool, after weights, activations and runtime reserves, divided
+ * by the rounded bytes); "FP8 KV cache layer skipping vs per-head scales",
+ * section "Layer skipping follows retained-token footprint" (a sliding layer
+ * retains at most its window; A and S).  The byte prices are the cache
+ * layout's own, so passing layer_num_blocks to kvq_create_cache with a
+ * buffer of buffer_bytes always fits the pool.
+ *   model             host, read only.
+ *   context           >= 1 tokens per sequence.
+ *   pool_bytes        the usable pool; the caller subtracts every reserve.
+ *   out               host, written on success.
+ *   layer_num_blocks  host [num_layers] or NULL: max_sequences times each
+ *                     layer's blocks per sequence.
+ *   Errors: KVQ_ERR_INVALID_ARG (null pointer, bad value, a window that is
+ *           not a multiple of block_size), KVQ_ERR_UNSUPPORTED (as
+ *           kvq_cache_bytes).
+ */
+KVQ_API kvq_status kvq_plan_capacity(const kvq_model_config* model, int64_t context, uint64_t pool_bytes,
+                                     kvq_plan* out, int64_t* layer_num_blocks);
+
+/* Opaque host handle: the blocks of a cache handed out to sequences. */
+typedef struct kvq_seq_manager kvq_seq_manager;
+
+/*
+ * kvq_manager_create -- a block manager over a cache geometry.  Layers with
+ * the same window form a group that shares block ids (each id names a block
+ * in every layer of the group, in that layer's own region), so every layer
+ * of a group must have the same block count.  A full-attention group gives
+ * each sequence a growing list of blocks; a sliding group gives it a ring of
+ * W / block_size blocks in which token t occupies position t mod W, so only
+ * the last W tokens are retained ("FP8 KV cache layer skipping vs per-head
+ * scales", "Layer skipping follows retained-token footprint").
+ *   model               host, read only (the windows define the groups).
+ *   layer_num_blocks    host [num_layers]: the cache's blocks per layer.
+ *   max_blocks_per_seq  block-table width: the longest sequence is
+ *                       max_blocks_per_seq * block_size tokens.
+ *   out                 receives the handle; free it with kvq_manager_destroy.
+ *   Errors: KVQ_ERR_INVALID_ARG.
+ * Not thread safe: one caller at a time per handle.
+ */
+KVQ_API kvq_status kvq_manager_create(const kvq_model_config* model, const int64_t* layer_num_blocks,
+                                      int32_t max_blocks_per_seq, kvq_seq_manager** out);
+KVQ_API kvq_status kvq_manager_destroy(kvq_seq_manager* m);
+
+/* kvq_manager_num_groups / kvq_manager_layer_group -- the number of layer
+ * groups, and the group of a layer (groups are numbered in order of their
+ * first layer).  Errors: KVQ_ERR_INVALID_ARG. */
+KVQ_API kvq_status kvq_manager_num_groups(const kvq_seq_manager* m, int32_t* num_groups);
+KVQ_API kvq_status kvq_manager_layer_group(const kvq_seq_manager* m, int32_t layer, int32_t* group);
+
+/*
+ * kvq_manager_append -- reserve n more tokens for sequence seq (an unknown
+ * id starts a new, empty sequence) and write the slot of every new token in
+ * every group: slots[g * n + i] is the kvq_store slot of token i for the
+ * layers of group g.  In a sliding group, a token that a later token of the
+ * same call displaces from the window gets slot -1 (kvq_store skips it), so
+ * the slots of one call never coincide.  Blocks come from the group's free
+ * list, lowest id first when none was released.
+ *   seq    >= 0.  n >= 0.  slots: host [num_groups * n].
+ *   Errors: KVQ_ERR_INVALID_ARG (bad argument, or the sequence would need
+ *           more than max_blocks_per_seq blocks), KVQ_ERR_NO_SPACE (a group
+ *           has no free block left).  On an error nothing changes.
+ */
+KVQ_API kvq_status kvq_manager_append(kvq_seq_manager* m, int32_t seq, int32_t n, int64_t* slots);
+
+/* kvq_manager_release -- return a sequence's blocks to the free lists.
+ * Errors: KVQ_ERR_INVALID_ARG (unknown sequence). */
+KVQ_API kvq_status kvq_manager_release(kvq_seq_manager* m, int32_t seq);
+
+/*
+ * kvq_manager_tables -- the block table and lengths of group `group` for the
+ * given sequences, ready for kvq_gather_dequant and kvq_decode_attention:
+ * block_table[i][j] is the j-th block of seqs[i] (-1 past its last block),
+ * seq_lens[i] its retained tokens (min(length, W) in a sliding group, whose
+ * tokens are in ring order, which attention does not depend on).
+ *   seqs        host [num_seqs] known sequence ids.
+ *   block_table host [num_seqs][max_blocks].  seq_lens: host [num_seqs].
+ *   Errors: KVQ_ERR_INVALID_ARG (unknown sequence, a table too narrow).
+ */
+KVQ_API kvq_status kvq_manager_tables(const kvq_seq_manager* m, int32_t group, const int32_t* seqs,
+                                      int32_t num_seqs, int32_t max_blocks, int32_t* block_table,
+                                      int32_t* seq_lens);
 
 /* kvq_status_string -- static description of a status code. */
 KVQ_API const char* kvq_status_string(kvq_status s);

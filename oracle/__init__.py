@@ -209,6 +209,37 @@ def attention_error_bound(g: Geometry, buf: np.ndarray, layer: int, q_bits, bloc
     floor = (lens.astype(np.float64)[:, None, None] + 16) * 2.0 ** -120 * max(1.0, float(static_v_max))
     return (2.0 ** -8 + 2.5 * eps[:, :, None]) * absv + 2.0 ** -8 * np.abs(ref) + floor
 
+def retained_positions(layer_windows, context: int):
+    """Retained token-layer positions of one sequence per layer: a
+    full-attention layer (window 0) retains the whole context, a sliding layer
+    at most its window ("FP8 KV cache layer skipping vs per-head scales",
+    "Layer skipping follows retained-token footprint")."""
+    return [min(int(context), int(w)) if int(w) > 0 else int(context) for w in layer_windows]
+
+
+def plan_capacity(bs: int, hkv: int, hd: int, layer_modes, layer_windows, context: int, pool_bytes: int) -> dict:
+    """Capacity plan from the pages: A and S ("Layer skipping follows
+    retained-token footprint"); each layer's retained positions rounded up to
+    whole blocks and priced with this module's own layout; the usable pool
+    divided by one sequence's bytes, stepped down until the whole buffer
+    (alignment and static scales included) fits ("Per-token-head KV cache
+    scale overhead", "Convert bytes into block capacity")."""
+    r = retained_positions(layer_windows, context)
+    A = sum(r)
+    S = sum(x for x, m in zip(r, layer_modes) if int(m) == BF16)
+    per_seq = [-(-x // bs) for x in r]
+    one = cache_bytes(Geometry(bs, hkv, hd, layer_modes, per_seq))
+    seq_bytes = one["payload"] + one["token_scales"]
+    n = int(pool_bytes) // seq_bytes
+
+    def total(k):
+        return cache_bytes(Geometry(bs, hkv, hd, layer_modes, [k * b for b in per_seq]))["total"]
+    while n > 0 and total(n) > pool_bytes:
+        n -= 1
+    return {"retained_positions": A, "skipped_positions": S, "sequence_bytes": seq_bytes, "max_sequences": n,
+            "max_tokens": n * int(context), "buffer_bytes": total(n) if n > 0 else 0,
+            "layer_num_blocks": [n * b for b in per_seq]}
+
 def calibrate_amax(keys_bits, values_bits, hkv: int, hd: int, amax=None) -> np.ndarray:
     """Per-(K/V, head) absolute maximum over a batch, float32 [2 * hkv]
     (K heads, then V heads); with amax given, the running maximum continues

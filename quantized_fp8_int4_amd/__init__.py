@@ -36,11 +36,14 @@ MODE_NAMES = {BF16: "bf16", FP8_PER_TENSOR: "fp8_per_tensor", FP8_PER_HEAD: "fp8
               FP8_PER_TOKEN_HEAD: "fp8_per_token_head", INT4_PER_TOKEN_HEAD: "int4_per_token_head"}
 
 # kvq_status
-OK, ERR_INVALID_ARG, ERR_MODE_MISMATCH, ERR_BUFFER_TOO_SMALL, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4, -5
+OK, ERR_INVALID_ARG, ERR_MODE_MISMATCH, ERR_BUFFER_TOO_SMALL, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_SPACE = \
+    0, -1, -2, -3, -4, -5, -6
 
 EXPORTED_SYMBOLS = ("kvq_cache_bytes", "kvq_create_cache", "kvq_destroy_cache", "kvq_store",
                     "kvq_gather_dequant", "kvq_calibrate_amax", "kvq_static_scales",
-                    "kvq_decode_attention_workspace", "kvq_decode_attention", "kvq_status_string")
+                    "kvq_decode_attention_workspace", "kvq_decode_attention", "kvq_plan_capacity",
+                    "kvq_manager_create", "kvq_manager_destroy", "kvq_manager_num_groups", "kvq_manager_layer_group",
+                    "kvq_manager_append", "kvq_manager_release", "kvq_manager_tables", "kvq_status_string")
 
 
 class _Config(ctypes.Structure):
@@ -48,6 +51,18 @@ class _Config(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("layer_mode", ctypes.POINTER(ctypes.c_int32)),
                 ("layer_num_blocks", ctypes.POINTER(ctypes.c_int64))]
+
+
+class _Model(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("layer_mode", ctypes.POINTER(ctypes.c_int32)),
+                ("layer_window", ctypes.POINTER(ctypes.c_int32))]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("retained_positions", ctypes.c_int64), ("skipped_positions", ctypes.c_int64),
+                ("sequence_bytes", ctypes.c_uint64), ("max_sequences", ctypes.c_int64),
+                ("max_tokens", ctypes.c_int64), ("buffer_bytes", ctypes.c_uint64)]
 
 
 class _Bytes(ctypes.Structure):
@@ -68,6 +83,14 @@ def _load_library():
     lib.kvq_static_scales.argtypes = [P, I32, ctypes.c_int, P]
     lib.kvq_decode_attention_workspace.argtypes = [P, I32, I32, I32, ctypes.POINTER(ctypes.c_uint64)]
     lib.kvq_decode_attention.argtypes = [P, I32, P, I32, P, I32, P, I32, ctypes.c_float, P, P, ctypes.c_uint64, P]
+    lib.kvq_plan_capacity.argtypes = [ctypes.POINTER(_Model), I64, ctypes.c_uint64, ctypes.POINTER(_Plan), P]
+    lib.kvq_manager_create.argtypes = [ctypes.POINTER(_Model), P, I32, ctypes.POINTER(P)]
+    lib.kvq_manager_destroy.argtypes = [P]
+    lib.kvq_manager_num_groups.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
+    lib.kvq_manager_layer_group.argtypes = [P, I32, ctypes.POINTER(ctypes.c_int32)]
+    lib.kvq_manager_append.argtypes = [P, I32, I32, P]
+    lib.kvq_manager_release.argtypes = [P, I32]
+    lib.kvq_manager_tables.argtypes = [P, I32, P, I32, I32, P, P]
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     for name in EXPORTED_SYMBOLS[:-1]:
@@ -245,6 +268,94 @@ def kvq_decode_attention(handle, layer: int, q: torch.Tensor, block_table: torch
                                      ctypes.c_void_p(op), ctypes.c_void_p(wp), wb, _stream_ptr(stream, q.device)),
            "kvq_decode_attention")
 
+
+@dataclass
+class ModelConfig:
+    """kvq_model_config: a cache geometry without block counts, plus each
+    layer's window (0 = full attention, W > 0 = sliding window of W tokens)."""
+    block_size: int
+    num_kv_heads: int
+    head_dim: int
+    layer_modes: Sequence[int]
+    layer_windows: Sequence[int]
+
+    def _c(self):
+        n = len(self.layer_modes)
+        modes = (ctypes.c_int32 * n)(*[int(m) for m in self.layer_modes])
+        wins = (ctypes.c_int32 * n)(*[int(w) for w in self.layer_windows])
+        m = _Model(n, int(self.block_size), int(self.num_kv_heads), int(self.head_dim),
+                   ctypes.cast(modes, ctypes.POINTER(ctypes.c_int32)), ctypes.cast(wins, ctypes.POINTER(ctypes.c_int32)))
+        return m, (modes, wins)
+
+    def cache_config(self, layer_num_blocks) -> CacheConfig:
+        return CacheConfig(self.block_size, self.num_kv_heads, self.head_dim, list(self.layer_modes),
+                           [int(b) for b in layer_num_blocks])
+
+
+def kvq_plan_capacity(model: ModelConfig, context: int, pool_bytes: int):
+    """Returns (plan dict, per-layer block counts) for sequences of `context`
+    tokens in a usable pool of pool_bytes."""
+    m, keep = model._c()
+    out = _Plan()
+    blocks = (ctypes.c_int64 * len(model.layer_modes))()
+    _check(_lib.kvq_plan_capacity(ctypes.byref(m), int(context), int(pool_bytes), ctypes.byref(out), blocks),
+           "kvq_plan_capacity")
+    plan = {k: int(getattr(out, k)) for k, _ in _Plan._fields_}
+    return plan, [int(b) for b in blocks]
+
+
+class SeqManager:
+    """The decode-time block manager (kvq_manager_*): slots for new tokens per
+    layer group, and block tables / lengths per group."""
+
+    def __init__(self, model: ModelConfig, layer_num_blocks, max_blocks_per_seq: int):
+        m, keep = model._c()
+        nb = (ctypes.c_int64 * len(layer_num_blocks))(*[int(b) for b in layer_num_blocks])
+        h = ctypes.c_void_p()
+        _check(_lib.kvq_manager_create(ctypes.byref(m), nb, int(max_blocks_per_seq), ctypes.byref(h)),
+               "kvq_manager_create")
+        self.handle = h
+        self.max_blocks_per_seq = int(max_blocks_per_seq)
+        g = ctypes.c_int32()
+        _check(_lib.kvq_manager_num_groups(self.handle, ctypes.byref(g)), "kvq_manager_num_groups")
+        self.num_groups = int(g.value)
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            _lib.kvq_manager_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def layer_group(self, layer: int) -> int:
+        g = ctypes.c_int32()
+        _check(_lib.kvq_manager_layer_group(self.handle, int(layer), ctypes.byref(g)), "kvq_manager_layer_group")
+        return int(g.value)
+
+    def append(self, seq: int, n: int):
+        """Slots (list per group, n int64 each) of n new tokens of sequence seq."""
+        buf = (ctypes.c_int64 * max(1, self.num_groups * int(n)))()
+        _check(_lib.kvq_manager_append(self.handle, int(seq), int(n), buf), "kvq_manager_append")
+        flat = list(buf)[: self.num_groups * int(n)]
+        return [flat[g * n: (g + 1) * n] for g in range(self.num_groups)]
+
+    def release(self, seq: int) -> None:
+        _check(_lib.kvq_manager_release(self.handle, int(seq)), "kvq_manager_release")
+
+    def tables(self, group: int, seqs, max_blocks=None):
+        """(block_table [len(seqs)][max_blocks], seq_lens [len(seqs)]) as lists."""
+        mb = int(max_blocks or self.max_blocks_per_seq)
+        ns = len(seqs)
+        sq = (ctypes.c_int32 * max(1, ns))(*[int(x) for x in seqs])
+        bt = (ctypes.c_int32 * max(1, ns * mb))()
+        sl = (ctypes.c_int32 * max(1, ns))()
+        _check(_lib.kvq_manager_tables(self.handle, int(group), sq, ns, mb, bt, sl), "kvq_manager_tables")
+        flat = list(bt)
+        return [flat[i * mb: (i + 1) * mb] for i in range(ns)], list(sl)[:ns]
 
 class Cache:
     """A cache buffer (zeroed torch uint8 tensor of kvq_cache_bytes().total

@@ -55,6 +55,7 @@ const char* kvq_status_string(kvq_status s) {
         case KVQ_ERR_BUFFER_TOO_SMALL: return "cache buffer smaller than kvq_cache_bytes().total";
         case KVQ_ERR_UNSUPPORTED: return "unsupported geometry";
         case KVQ_ERR_HIP: return "HIP runtime error";
+        case KVQ_ERR_NO_SPACE: return "no free block left";
         default: return "unknown status";
     }
 }

@@ -39,7 +39,7 @@ def test_library_exports_nothing_else(kvq):
 
 
 def test_status_strings(kvq):
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert kvq._lib.kvq_status_string(s)
     assert b"unknown" in kvq._lib.kvq_status_string(-99)
 
