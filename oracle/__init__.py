@@ -64,7 +64,7 @@ def _load():
     lib.orc_num_threads.restype = I32
     lib.orc_calibrate_amax.argtypes = [P, P, I64, I64, I64, P, I32]
     lib.orc_decode_attention.argtypes = [I32, I64, I64, I64, P, P, P, I32, P, I64, P, I64, P, I64,
-                                         ctypes.c_double, P, P]
+                                         ctypes.c_double, P, P, P]
     _lib = lib
     return lib
 
@@ -158,26 +158,43 @@ def gather(g: Geometry, buf: np.ndarray, layer: int, block_table, seq_lens):
 
 
 def decode_attention(g: Geometry, buf: np.ndarray, layer: int, q_bits, block_table, seq_lens,
-                     sm_scale: float, with_absv: bool = False):
+                     sm_scale: float, with_absv: bool = False, q_scales=None):
     """Attention of one query token per sequence over its cached tokens, from
     the dequantized cache values, all in double ("Per-tensor vs per-head FP8 KV
     cache scales", "Dynamic per-token-head scales add 3.125 percent": scales
     are read during attention).  q_bits: BF16 bits [num_seqs, H, hd].  Returns
-    out [num_seqs, H, hd] (float64) and, if asked, sum_t p_t |V^_t| alike."""
+    out [num_seqs, H, hd] (float64) and, if asked, sum_t p_t |V^_t| alike.
+    With q_scales ([H] static FP8 query scales, "FP8 KV cache layer skipping vs
+    per-head scales", "Per-head scales have fixed overhead"), each query
+    element is its E4M3 code under its head's scale, decoded back."""
     q = _c(q_bits, np.uint16)
     nseq, nqh = int(q.shape[0]), int(q.shape[1])
     bt = _c(block_table, np.int32)
     sl = _c(seq_lens, np.int32)
     out = np.zeros((nseq, nqh, g.hd), np.float64)
     absv = np.zeros_like(out) if with_absv else None
+    qs = None if q_scales is None else _c(q_scales, np.float32)
+    assert qs is None or (qs.size == nqh and (qs > 0).all())
     _load().orc_decode_attention(*g._args(), _ptr(buf), int(layer), _ptr(q), nqh, _ptr(bt), int(bt.shape[1]),
-                                 _ptr(sl), nseq, float(sm_scale), _ptr(out),
+                                 _ptr(sl), nseq, float(sm_scale), _ptr(qs) if qs is not None else None, _ptr(out),
                                  _ptr(absv) if absv is not None else None)
     return (out, absv) if with_absv else out
 
 
+def query_values(q_bits, q_scales=None) -> np.ndarray:
+    """Query elements as attention uses them (float64): BF16 values, or with
+    q_scales [H] their E4M3 codes under each head's scale, decoded back."""
+    q = _c(q_bits, np.uint16)
+    x = (q.astype(np.uint32) << 16).view(np.float32)
+    if q_scales is None:
+        return x.astype(np.float64)
+    s = _c(q_scales, np.float32).reshape(1, -1, 1)
+    codes = e4m3_encode(quotient(x, np.broadcast_to(s, x.shape)))
+    return e4m3_decode(codes).astype(np.float64) * s.astype(np.float64)
+
+
 def attention_error_bound(g: Geometry, buf: np.ndarray, layer: int, q_bits, block_table, seq_lens,
-                          sm_scale: float, ref, absv, static_v_max: float = 1.0):
+                          sm_scale: float, ref, absv, static_v_max: float = 1.0, q_scales=None):
     """Per-element bound on |o_kernel - o_exact| for an attention kernel that
     takes the dequantized-cache attention with FP32 accumulation, BF16
     softmax weights (times per-token V scales) in the value product and a
@@ -197,7 +214,7 @@ def attention_error_bound(g: Geometry, buf: np.ndarray, layer: int, q_bits, bloc
     group = nqh // g.hkv
     kb, _ = gather(g, buf, layer, bt, lens)
     kabs = np.abs((kb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)) * (1 + 2.0 ** -8)
-    qabs = np.abs((q.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    qabs = np.abs(query_values(q, q_scales))
     eps = np.zeros((q.shape[0], nqh))
     row0 = 0
     for i, n in enumerate(lens):

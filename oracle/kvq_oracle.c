@@ -501,6 +501,19 @@ static double orc_cached_value(int mode, const uint8_t* buf, int64_t layer_base,
     return (double)orc_e4m3_decode(src[i]) * s;
 }
 
+/* A query element as attention uses it: the BF16 value itself, or, with a
+ * static FP8 query scale sq > 0 (one per query head, "FP8 KV cache layer
+ * skipping vs per-head scales", "Per-head scales have fixed overhead"), its
+ * E4M3 code under that scale decoded back, exactly: decode(E4M3(RN32(q/sq)))
+ * times sq, the same encoding the cache applies to K and V. */
+static double orc_query_value(uint16_t qb, float sq)
+{
+    float x = orc_bf16_to_float(qb);
+    if (sq == 0.0f)
+        return (double)x;
+    return (double)orc_e4m3_decode(orc_e4m3_encode(orc_quotient(x, sq))) * (double)sq;
+}
+
 /*
  * Attention of one new query token per sequence over the sequence's cached
  * tokens, read through the block table ("Per-tensor vs per-head FP8 KV cache
@@ -509,7 +522,8 @@ static double orc_cached_value(int mode, const uint8_t* buf, int64_t layer_base,
  *   score_t = sm_scale * sum_d q[b][qh][d] * K^[t][d],  p = softmax(score),
  *   out[b][qh][d] = sum_t p_t * V^[t][d],
  * with K^, V^ the dequantized cache values, all in double.  q: BF16 bits
- * [num_seqs][H][hd]; out: double [num_seqs][H][hd].  Lengths are clamped to
+ * [num_seqs][H][hd]; q_scales: NULL (BF16 queries) or [H] positive static
+ * FP8 query scales; out: double [num_seqs][H][hd].  Lengths are clamped to
  * [0, max_blocks * bs]; a token whose block-table entry does not name a block
  * of the layer takes no part (no score, no weight), and a sequence with no
  * token left gives zeros.  Also returns sum_t p_t |V^[t][d]| in out_absv (for error
@@ -520,7 +534,7 @@ void orc_decode_attention(int num_layers, int64_t bs, int64_t hkv, int64_t hd,
                           const uint8_t* buf, int layer, const uint16_t* q, int64_t num_q_heads,
                           const int32_t* block_table, int64_t max_blocks,
                           const int32_t* seq_lens, int64_t num_seqs, double sm_scale,
-                          double* out, double* out_absv)
+                          const float* q_scales, double* out, double* out_absv)
 {
     int64_t layer_base[num_layers > 0 ? num_layers : 1];
     int64_t static_base[num_layers > 0 ? num_layers : 1];
@@ -549,7 +563,7 @@ void orc_decode_attention(int num_layers, int64_t bs, int64_t hkv, int64_t hd,
                 }
                 double acc = 0.0;
                 for (int64_t i = 0; i < hd; ++i)
-                    acc += (double)orc_bf16_to_float(q[(b * num_q_heads + qh) * hd + i]) *
+                    acc += orc_query_value(q[(b * num_q_heads + qh) * hd + i], q_scales ? q_scales[qh] : 0.0f) *
                            orc_cached_value(mode, buf, layer_base[layer], static_base[layer], bs, hkv, hd,
                                             blk, pos, h, 0, i);
                 score[t] = acc * sm_scale;

@@ -94,3 +94,32 @@ def test_attention_skips_blocks_outside_the_layer(orc):
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
     bt[0, :] = -1
     assert not orc.decode_attention(g, buf, 0, _bits(q), bt, lens, 0.2).any()
+
+
+@pytest.mark.parametrize("mode", [W.FP8_PER_TENSOR, W.FP8_PER_TOKEN_HEAD])
+def test_fp8_query_attention_matches_numpy(orc, mode):
+    """With static FP8 query scales each query element is its E4M3 code under
+    its head's scale, decoded back; here built from numpy float32 division and
+    torch's float8_e4m3fn cast, independently of the oracle's codec."""
+    hkv, hd, group = 2, 64, 4
+    g, buf, st = _setup(orc, mode, hkv, hd)
+    lens = st.seq_lens
+    q = torch.randn((len(lens), hkv * group, hd), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    qf = q.float().numpy()
+    sq = (np.abs(qf).max(axis=(0, 2)) / np.float32(448.0)).astype(np.float32) * np.float32(1.5)   # some saturate
+    quo = (qf / sq[None, :, None]).astype(np.float32)
+    qhat = _brute._e4m3(quo.reshape(-1)).reshape(quo.shape)
+    qhat = torch.from_numpy(qhat).view(torch.float8_e4m3fn).double().numpy() * sq[None, :, None].astype(np.float64)
+    out = orc.decode_attention(g, buf, 0, _bits(q), st.block_table.numpy(), lens, 0.125, q_scales=sq)
+    kh, vh = _brute.dequant_f64(buf, g.bs, hkv, hd, [mode], [12], 0, st.block_table.numpy(), lens)
+    ref = _numpy_attention(qhat, kh, vh, lens, group, 0.125)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(orc.query_values(_bits(q), sq), qhat)
+    # a scale so large that every code is zero: uniform weights, the mean of V
+    zero = orc.decode_attention(g, buf, 0, _bits(q), st.block_table.numpy(), lens, 0.125,
+                                q_scales=np.full(hkv * group, 3e38, np.float32))
+    row0 = 0
+    for b, n in enumerate(lens):
+        if n:
+            assert np.allclose(zero[b], np.repeat(vh[row0: row0 + n].mean(axis=0), group, axis=0), rtol=1e-13, atol=1e-13)
+        row0 += n
