@@ -706,10 +706,21 @@ def run_other_workload(args, torch, kvq, W):
         ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
         ct = __import__("ctypes")
 
+        q_scales, q_scales_h = None, None
+        if args.q_fp8:
+            # static per-query-head scales calibrated on the first step's queries
+            amax = torch.zeros(2 * H, dtype=torch.float32, device=dev)
+            kvq.kvq_calibrate_amax(qs[0], qs[0], amax)
+            q_scales_h = kvq.kvq_static_scales(amax, H, kvq.FP8_PER_HEAD)[:H]
+            q_scales = torch.tensor(q_scales_h, dtype=torch.float32, device=dev)
+        attn_fn = kvq._lib.kvq_decode_attention_fp8q if args.q_fp8 else kvq._lib.kvq_decode_attention
+
         def attn_args(l, i):
-            return (D["cache"].handle, l, ct.c_void_p(qs[i].data_ptr()), H, ct.c_void_p(D["bt"].data_ptr()), maxb,
-                    ct.c_void_p(D["lens_at"][i].data_ptr()), S, ct.c_float(sm_scale), ct.c_void_p(out.data_ptr()),
-                    ct.c_void_p(ws.data_ptr()), wsb, Lc.stream)
+            qpart = (ct.c_void_p(qs[i].data_ptr()),) + ((ct.c_void_p(q_scales.data_ptr()),) if args.q_fp8 else ())
+            return (D["cache"].handle, l) + qpart + (H, ct.c_void_p(D["bt"].data_ptr()), maxb,
+                                                     ct.c_void_p(D["lens_at"][i].data_ptr()), S, ct.c_float(sm_scale),
+                                                     ct.c_void_p(out.data_ptr()), ct.c_void_p(ws.data_ptr()), wsb,
+                                                     Lc.stream)
         counter = {"i": 0}
 
         def step(ev):
@@ -720,7 +731,7 @@ def run_other_workload(args, torch, kvq, W):
             if ev: ev[0].record()
             for l in range(L):
                 Lc.store(sa[l])
-                st_ = kvq._lib.kvq_decode_attention(*aa[l])
+                st_ = attn_fn(*aa[l])
                 if st_ != 0:
                     raise kvq.KVQError(st_, "kvq_decode_attention")
             if ev: ev[1].record(); ev[2].record()
@@ -732,7 +743,7 @@ def run_other_workload(args, torch, kvq, W):
         def attn_only(ev):
             if ev: ev[0].record()
             for a in last:
-                kvq._lib.kvq_decode_attention(*a)
+                attn_fn(*a)
             if ev: ev[1].record(); ev[2].record()
         _, aevs = _timed(torch, attn_only, args.steps, 1)
         attn_s = sum(e[0].elapsed_time(e[1]) for e in aevs) / (args.steps * L) / 1e3
@@ -756,9 +767,11 @@ def run_other_workload(args, torch, kvq, W):
             bt_h = D["st"].block_table.numpy()
             qb = _bits(torch, qs[-1])[pick]
             t0 = time.perf_counter()
-            ref, absv = oracle.decode_attention(g, host, 0, qb, bt_h[pick], lens_last[pick], sm_scale, with_absv=True)
+            ref, absv = oracle.decode_attention(g, host, 0, qb, bt_h[pick], lens_last[pick], sm_scale, with_absv=True,
+                                                q_scales=q_scales_h)
             csec = time.perf_counter() - t0
-            tol = oracle.attention_error_bound(g, host, 0, qb, bt_h[pick], lens_last[pick], sm_scale, ref, absv)
+            tol = oracle.attention_error_bound(g, host, 0, qb, bt_h[pick], lens_last[pick], sm_scale, ref, absv,
+                                               q_scales=q_scales_h)
             got = (_bits(torch, out[pick]).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
             parity = bool((np.abs(got - ref) <= tol).all())
             sample_tok = int(lens_last[pick].sum())
@@ -773,15 +786,17 @@ def run_other_workload(args, torch, kvq, W):
                "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True,
                "scaling": "weak", "vs_baseline": None, "dtype": "fp8/int4 codes, bf16 MFMA, f32 accumulate",
                "data": "synthetic",
-               "config": {"workload": D["desc"] + f", {H} query heads, fused append + attention per layer",
+               "config": {"workload": D["desc"] + f", {H} query heads, fused append + attention per layer"
+                                                  + (", FP8 queries (static per-head scales)" if args.q_fp8 else ""),
                           "layers": L, "num_seqs": S, "context": D["ctx"], "num_kv_heads": hkv,
-                          "num_q_heads": H, "head_dim": hd, "block_size": bs, "mode": args.mode},
+                          "num_q_heads": H, "head_dim": hd, "block_size": bs, "mode": args.mode,
+                          "queries": "fp8" if args.q_fp8 else "bf16"},
                "attention_us": round(attn_s * 1e6, 2), "attention_GBps": round(agbps, 1),
                "step_ms_events": round(step_s * 1e3, 4),
                "decode_tokens_per_s": round(S / sec, 1),
                "roofline": {"bound": "hbm", "kernel": "attention_kernel", "achieved": round(agbps, 1),
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(agbps / HBM_PEAK_GBPS, 4),
-                            "traffic": measured_attention_traffic(args.mode, hd)},
+                            "traffic": None if args.q_fp8 else measured_attention_traffic(args.mode, hd)},
                "cpu_baseline": cpu,
                "parity_vs_oracle_sampled": parity,
                "workspace_bytes": wsb, "cache_GiB": round(D["cache"].bytes["total"] / 2**30, 3)}
@@ -798,6 +813,7 @@ def main():
                     help="gqa32 is the headline line; the others measure the remaining shapes")
     ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128], help="decode and attention workloads")
     ap.add_argument("--q-per-kv", type=int, default=4, help="attention workload: query heads per KV head")
+    ap.add_argument("--q-fp8", action="store_true", help="attention workload: FP8 queries (kvq_decode_attention_fp8q)")
     ap.add_argument("--mode", default="fp8_per_token_head",
                     choices=["fp8_per_token_head", "fp8_per_tensor", "fp8_per_head", "int4_per_token_head", "bf16"])
     ap.add_argument("--cpu-layers", type=int, default=16, help="layers of one step timed on the CPU oracle")

@@ -301,6 +301,31 @@ KVQ_API kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const
                                         const int32_t* seq_lens, int32_t num_seqs, float sm_scale, void* out,
                                         void* workspace, uint64_t workspace_bytes, void* stream);
 
+/*
+ * kvq_decode_attention_fp8q -- kvq_decode_attention with FP8 queries: each
+ * query element is encoded to E4M3 under a static scale of its query head,
+ * the way the cache encodes K and V (E4M3(RN32(q / s)), nearest even,
+ * saturating at 448), and the Q K^T products run on the FP8 codes directly.
+ * This is the per-attention-head calibration's one Q scale per query head
+ * ("Per-tensor vs per-head FP8 KV cache scales", "Per-tensor vs per-head FP8
+ * KV cache scales"; "FP8 KV cache layer skipping vs per-head scales", "Per-head
+ * scales have fixed overhead": H query scales beside 2 * Hkv K and V scales);
+ * a per-tensor Q scale is H equal values.  kvq_calibrate_amax over the
+ * queries and kvq_static_scales give such scales.
+ *   q_scales   device FP32 [num_q_heads], 4-byte aligned, positive and finite
+ *              (not checked: other values give undefined results, never a
+ *              memory fault).
+ *   Other arguments, workspace and results as kvq_decode_attention, with the
+ *   queries' decoded FP8 values in place of the BF16 ones.
+ *   Errors: as kvq_decode_attention; KVQ_ERR_INVALID_ARG for a null
+ *           q_scales; KVQ_ERR_UNSUPPORTED for a BF16 or INT4 layer.
+ */
+KVQ_API kvq_status kvq_decode_attention_fp8q(const kvq_cache* c, int32_t layer, const void* q, const float* q_scales,
+                                             int32_t num_q_heads, const int32_t* block_table,
+                                             int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                                             float sm_scale, void* out, void* workspace, uint64_t workspace_bytes,
+                                             void* stream);
+
 /* ------------------------------------------------------------------------
  * Capacity planning and the decode-time block manager (host code only)
  * ---------------------------------------------------------------------- */

@@ -41,7 +41,8 @@ OK, ERR_INVALID_ARG, ERR_MODE_MISMATCH, ERR_BUFFER_TOO_SMALL, ERR_UNSUPPORTED, E
 
 EXPORTED_SYMBOLS = ("kvq_cache_bytes", "kvq_create_cache", "kvq_destroy_cache", "kvq_store",
                     "kvq_gather_dequant", "kvq_calibrate_amax", "kvq_static_scales",
-                    "kvq_decode_attention_workspace", "kvq_decode_attention", "kvq_plan_capacity",
+                    "kvq_decode_attention_workspace", "kvq_decode_attention", "kvq_decode_attention_fp8q",
+                    "kvq_plan_capacity",
                     "kvq_manager_create", "kvq_manager_destroy", "kvq_manager_num_groups", "kvq_manager_layer_group",
                     "kvq_manager_append", "kvq_manager_release", "kvq_manager_tables", "kvq_status_string")
 
@@ -83,6 +84,8 @@ def _load_library():
     lib.kvq_static_scales.argtypes = [P, I32, ctypes.c_int, P]
     lib.kvq_decode_attention_workspace.argtypes = [P, I32, I32, I32, ctypes.POINTER(ctypes.c_uint64)]
     lib.kvq_decode_attention.argtypes = [P, I32, P, I32, P, I32, P, I32, ctypes.c_float, P, P, ctypes.c_uint64, P]
+    lib.kvq_decode_attention_fp8q.argtypes = [P, I32, P, P, I32, P, I32, P, I32, ctypes.c_float, P, P,
+                                              ctypes.c_uint64, P]
     lib.kvq_plan_capacity.argtypes = [ctypes.POINTER(_Model), I64, ctypes.c_uint64, ctypes.POINTER(_Plan), P]
     lib.kvq_manager_create.argtypes = [ctypes.POINTER(_Model), P, I32, ctypes.POINTER(P)]
     lib.kvq_manager_destroy.argtypes = [P]
@@ -242,11 +245,12 @@ def kvq_decode_attention_workspace(handle, num_q_heads: int, max_blocks_per_seq:
 
 def kvq_decode_attention(handle, layer: int, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                          sm_scale: float, out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-                         stream=None) -> None:
+                         stream=None, q_scales: Optional[torch.Tensor] = None) -> None:
     """q: bf16 [num_seqs, H, hd] on the device; block_table int32 [num_seqs,
     max_blocks]; seq_lens int32 [num_seqs]; out: bf16 [num_seqs, H, hd];
     workspace: a device tensor of at least kvq_decode_attention_workspace()
-    bytes (None when that is 0)."""
+    bytes (None when that is 0).  q_scales: float32 [H] on the device for FP8
+    queries (kvq_decode_attention_fp8q), else None."""
     num_seqs = int(seq_lens.numel())
     if num_seqs == 0:
         return
@@ -263,10 +267,19 @@ def kvq_decode_attention(handle, layer: int, q: torch.Tensor, block_table: torch
         if workspace.device.type != "cuda" or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous device tensor")
         wp, wb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(_lib.kvq_decode_attention(handle, int(layer), ctypes.c_void_p(qp), int(q.shape[1]), ctypes.c_void_p(bt),
-                                     int(block_table.shape[1]), ctypes.c_void_p(sl), num_seqs, float(sm_scale),
-                                     ctypes.c_void_p(op), ctypes.c_void_p(wp), wb, _stream_ptr(stream, q.device)),
-           "kvq_decode_attention")
+    if q_scales is None:
+        _check(_lib.kvq_decode_attention(handle, int(layer), ctypes.c_void_p(qp), int(q.shape[1]), ctypes.c_void_p(bt),
+                                         int(block_table.shape[1]), ctypes.c_void_p(sl), num_seqs, float(sm_scale),
+                                         ctypes.c_void_p(op), ctypes.c_void_p(wp), wb, _stream_ptr(stream, q.device)),
+               "kvq_decode_attention")
+        return
+    sp = _dev(q_scales, torch.float32, "q_scales")
+    if q_scales.numel() != q.shape[1]:
+        raise ValueError("q_scales must hold one scale per query head")
+    _check(_lib.kvq_decode_attention_fp8q(handle, int(layer), ctypes.c_void_p(qp), ctypes.c_void_p(sp), int(q.shape[1]),
+                                          ctypes.c_void_p(bt), int(block_table.shape[1]), ctypes.c_void_p(sl), num_seqs,
+                                          float(sm_scale), ctypes.c_void_p(op), ctypes.c_void_p(wp), wb,
+                                          _stream_ptr(stream, q.device)), "kvq_decode_attention_fp8q")
 
 
 @dataclass
@@ -398,13 +411,15 @@ class Cache:
         kvq_gather_dequant(self.handle, layer, block_table, seq_lens, out[0], out[1], stream)
         return out
 
-    def decode_attention(self, layer, q, block_table, seq_lens, sm_scale, out=None, workspace=None, stream=None):
+    def decode_attention(self, layer, q, block_table, seq_lens, sm_scale, out=None, workspace=None, stream=None,
+                         q_scales=None):
         """Fused decode attention over one layer; returns bf16 [num_seqs, H, hd].
-        Allocates the workspace with torch when none is given."""
+        Allocates the workspace with torch when none is given.  q_scales
+        (float32 [H] on the device) selects FP8 queries."""
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
             nbytes = kvq_decode_attention_workspace(self.handle, q.shape[1], block_table.shape[1], seq_lens.numel())
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device) if nbytes else None
-        kvq_decode_attention(self.handle, layer, q, block_table, seq_lens, sm_scale, out, workspace, stream)
+        kvq_decode_attention(self.handle, layer, q, block_table, seq_lens, sm_scale, out, workspace, stream, q_scales)
         return out

@@ -214,10 +214,14 @@ kvq_status kvq_decode_attention_workspace(const kvq_cache* c, int32_t num_q_head
     return KVQ_OK;
 }
 
-kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q, int32_t num_q_heads,
-                                const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                                int32_t num_seqs, float sm_scale, void* out, void* workspace,
-                                uint64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kvq_status decode_attention(const kvq_cache* c, int32_t layer, const void* q, const float* q_scales,
+                            int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t num_seqs, float sm_scale, void* out, void* workspace,
+                            uint64_t workspace_bytes, void* stream) {
     if (!c || layer < 0 || layer >= c->layout.num_layers || num_seqs < 0) return KVQ_ERR_INVALID_ARG;
     if (num_seqs == 0) return KVQ_OK;
     const kvq_status st = attention_args(c, num_q_heads, max_blocks_per_seq, num_seqs);
@@ -231,6 +235,8 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
     if (kvq::has_static_scales(lmode) && c->static_values[layer].empty()) return KVQ_ERR_INVALID_ARG;
     if (L.block_bytes[layer] % 16 != 0) return KVQ_ERR_UNSUPPORTED;
     if (L.block_bytes[layer] >= (uint64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
+    if (q_scales && (lmode == KVQ_BF16 || lmode == KVQ_INT4_PER_TOKEN_HEAD)) return KVQ_ERR_UNSUPPORTED;
+    if (q_scales && (reinterpret_cast<uintptr_t>(q_scales) & 3u)) return KVQ_ERR_INVALID_ARG;
     const kvq::AttnPlan plan =
         kvq::attention_plan(L.block_size, L.num_kv_heads, L.head_dim, num_q_heads, max_blocks_per_seq, num_seqs);
     if (plan.grid >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
@@ -241,6 +247,7 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
     a.layer = c->dev + L.layer_base[layer];
     a.static_scales = reinterpret_cast<const float*>(c->dev + L.static_base[layer]);
     a.q = q;
+    a.q_scales = q_scales;
     a.block_table = block_table;
     a.seq_lens = seq_lens;
     a.out = out;
@@ -257,9 +264,31 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
     a.mode = lmode;
     a.sm_scale = sm_scale;
     if (log_enabled())
-        std::fprintf(stderr, "[kvq] attention layer=%d mode=%s hd=%d seqs=%d H=%d splits=%d tiles/split=%d\n", layer,
-                     mode_name(lmode), L.head_dim, num_seqs, num_q_heads, plan.splits, plan.tiles_per_split);
+        std::fprintf(stderr, "[kvq] attention layer=%d mode=%s hd=%d seqs=%d H=%d q=%s splits=%d tiles/split=%d\n",
+                     layer, mode_name(lmode), L.head_dim, num_seqs, num_q_heads, q_scales ? "fp8" : "bf16",
+                     plan.splits, plan.tiles_per_split);
     return kvq::launch_attention(a, plan, stream) == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q, int32_t num_q_heads,
+                                const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                int32_t num_seqs, float sm_scale, void* out, void* workspace,
+                                uint64_t workspace_bytes, void* stream) {
+    return decode_attention(c, layer, q, nullptr, num_q_heads, block_table, max_blocks_per_seq, seq_lens, num_seqs,
+                            sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_attention_fp8q(const kvq_cache* c, int32_t layer, const void* q, const float* q_scales,
+                                     int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, int32_t num_seqs, float sm_scale, void* out,
+                                     void* workspace, uint64_t workspace_bytes, void* stream) {
+    if (!q_scales) return KVQ_ERR_INVALID_ARG;
+    return decode_attention(c, layer, q, q_scales, num_q_heads, block_table, max_blocks_per_seq, seq_lens, num_seqs,
+                            sm_scale, out, workspace, workspace_bytes, stream);
 }
 
 kvq_status kvq_calibrate_amax(const void* keys, const void* values, int64_t num_tokens, int32_t num_kv_heads,

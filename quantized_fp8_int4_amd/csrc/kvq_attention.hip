@@ -82,6 +82,7 @@ struct AttnArgs {
     const uint8_t* layer;          // layer base
     const float* statics;          // layer's static scale table (static modes)
     const uint16_t* q;             // BF16 [num_seqs][H][hd]
+    const float* q_scales;         // [H] static FP8 query scales (FP8-query kernels)
     const int32_t* block_table;    // [num_seqs][max_blocks]
     const int32_t* seq_lens;       // [num_seqs]
     uint16_t* out;                 // BF16 [num_seqs][H][hd]      (one split)
@@ -511,22 +512,67 @@ struct State {
     float l;                       // this lane's share of the running sum
 };
 
+// The lane's query slice as the Q K^T B operand: BF16 values, or (QF8) the
+// FP8 E4M3 codes of the query under its head's static scale.
+template <int HD, bool QF8>
+struct QOperand {
+    bf16x8 b[HD / 32];
+};
+template <int HD>
+struct QOperand<HD, true> {
+    uint32_t c[HD / 16];           // hd/4 codes, 4 per dword, in slice order
+};
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Q K^T of one tile: with BF16 queries the codes are widened to BF16 and go
+// through the 16x16x32 BF16 product; with FP8 queries the FP8 codes of both
+// go straight into the FP8 products (16x16x128 at head_dim 128 and 256,
+// 16x16x32 at 64), whose products are exact, as the BF16 ones are.  Both
+// operands hold the same contiguous slice of dims in every lane, so the
+// hardware's order of k within a lane does not matter.
+template <int HD, int MODE, bool QF8>
+__device__ __forceinline__ f32x4 qk_product(const uint32_t* k, const QOperand<HD, QF8>& q) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (!QF8) {
+#pragma unroll
+        for (int j = 0; j < HD / 32; ++j)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(k, j), q.b[j], acc, 0, 0, 0);
+    } else if constexpr (HD == 64) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const long a = static_cast<long>((static_cast<uint64_t>(k[2 * j + 1]) << 32) | k[2 * j]);
+            const long b = static_cast<long>((static_cast<uint64_t>(q.c[2 * j + 1]) << 32) | q.c[2 * j]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, acc, 0, 0, 0);
+        }
+    } else {
+        // format 0 (E4M3) for both operands, block scales 2^0 (E8M0 127)
+#pragma unroll
+        for (int j = 0; j < HD / 128; ++j) {
+            const i32x8 a = {static_cast<int>(k[8 * j]), static_cast<int>(k[8 * j + 1]), static_cast<int>(k[8 * j + 2]),
+                             static_cast<int>(k[8 * j + 3]), static_cast<int>(k[8 * j + 4]), static_cast<int>(k[8 * j + 5]),
+                             static_cast<int>(k[8 * j + 6]), static_cast<int>(k[8 * j + 7])};
+            const i32x8 b = {static_cast<int>(q.c[8 * j]), static_cast<int>(q.c[8 * j + 1]), static_cast<int>(q.c[8 * j + 2]),
+                             static_cast<int>(q.c[8 * j + 3]), static_cast<int>(q.c[8 * j + 4]), static_cast<int>(q.c[8 * j + 5]),
+                             static_cast<int>(q.c[8 * j + 6]), static_cast<int>(q.c[8 * j + 7])};
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+        }
+    }
+    return acc;
+}
+
 // One round of the online softmax over NT consecutive tiles (16 NT tokens):
 // the tiles' Q K^T products, one running-maximum update, then their P V
 // products.  MASK = false is the path of rounds whose tokens all lie below
 // len in blocks of the layer (a wave-uniform fact).
-template <int HD, int MODE, int NT, bool MASK>
-__device__ __forceinline__ void tile_round(const Tile<HD, MODE>* const* T, State<HD, MODE>& st, const bf16x8* qb,
-                                           int t0, int len, int q4, float k_factor, uint32_t vsh) {
+template <int HD, int MODE, int NT, bool MASK, bool QF8>
+__device__ __forceinline__ void tile_round(const Tile<HD, MODE>* const* T, State<HD, MODE>& st,
+                                           const QOperand<HD, QF8>& qo, int t0, int len, int q4, float k_factor,
+                                           uint32_t vsh) {
     using G = Geo<HD, MODE>;
     f32x4 sacc[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) sacc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < G::KSTEPS; ++j)
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-            sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(T[n]->k, j), qb[j], sacc[n], 0, 0, 0);
+    for (int n = 0; n < NT; ++n) sacc[n] = qk_product<HD, MODE, QF8>(T[n]->k, qo);
 
     float s[NT][4];
     bool valid[NT][4];
@@ -585,7 +631,7 @@ __device__ __forceinline__ void tile_round(const Tile<HD, MODE>* const* T, State
             st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[n][j], b[n], st.o[j], 0, 0, 0);
 }
 
-template <int HD, int MODE, bool SMALL_BS>
+template <int HD, int MODE, bool SMALL_BS, bool QF8>
 __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attention_kernel(AttnArgs a) {
     using G = Geo<HD, MODE>;
     // Workgroup -> work item, spreading consecutive items over one XCD
@@ -615,18 +661,32 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
     const int gi = qg * 16 + r;
     const bool qvalid = gi < a.group;
     const int qh = h * a.group + (qvalid ? gi : 0);
-    bf16x8 qb[G::KSTEPS];
+    QOperand<HD, QF8> qo;
+    float q_factor = 1.0f;
     {
         const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.num_q_heads + qh) * HD + q4 * (HD / 4);
+        if constexpr (!QF8) {
 #pragma unroll
-        for (int j = 0; j < G::KSTEPS; ++j) {
-            const uint4 v = qvalid ? ld16<false>(qp + 8 * j) : make_uint4(0, 0, 0, 0);
-            const u32x4 w = {v.x, v.y, v.z, v.w};
-            qb[j] = __builtin_bit_cast(bf16x8, w);
+            for (int j = 0; j < G::KSTEPS; ++j) {
+                const uint4 v = qvalid ? ld16<false>(qp + 8 * j) : make_uint4(0, 0, 0, 0);
+                const u32x4 w = {v.x, v.y, v.z, v.w};
+                qo.b[j] = __builtin_bit_cast(bf16x8, w);
+            }
+        } else {
+            // E4M3(RN32(q / s_q)), saturating, exactly as the cache encodes K
+            q_factor = qvalid ? a.q_scales[qh] : 1.0f;
+            const RowQ rq = row_prep(q_factor);
+#pragma unroll
+            for (int j = 0; j < HD / 32; ++j) {
+                const uint4 v = qvalid ? ld16<false>(qp + 8 * j) : make_uint4(0, 0, 0, 0);
+                const uint2 c = encode_fp8<true, true>(v, rq);
+                qo.c[2 * j] = c.x;
+                qo.c[2 * j + 1] = c.y;
+            }
         }
     }
 
-    float k_factor = a.c * G::CODE_UNIT;
+    float k_factor = a.c * G::CODE_UNIT * q_factor;
     float v_factor = 1.0f;
     if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
         k_factor *= a.statics[0];
@@ -700,9 +760,9 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
                 }
                 const int t0 = (tau + k) * kTile;
                 if (attention_fast_path<HD>() && !SMALL_BS && t0 + NT * kTile <= lim && all_ok)
-                    tile_round<HD, MODE, NT, false>(rt, st, qb, t0, lim, q4, k_factor, lo.vsh);
+                    tile_round<HD, MODE, NT, false, QF8>(rt, st, qo, t0, lim, q4, k_factor, lo.vsh);
                 else
-                    tile_round<HD, MODE, NT, true>(rt, st, qb, t0, lim, q4, k_factor, lo.vsh);
+                    tile_round<HD, MODE, NT, true, QF8>(rt, st, qo, t0, lim, q4, k_factor, lo.vsh);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -805,8 +865,16 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
 
 template <int HD, int MODE>
 void launch_attention_v(const AttnArgs& p, int threads, bool small_bs, hipStream_t st) {
-    if (small_bs) hipLaunchKernelGGL((attention_kernel<HD, MODE, true>), dim3(p.total_wg), dim3(threads), 0, st, p);
-    else hipLaunchKernelGGL((attention_kernel<HD, MODE, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
+    const bool qf8 = p.q_scales != nullptr;
+    if constexpr (MODE == KVQ_FP8_PER_TENSOR || MODE == KVQ_FP8_PER_HEAD || MODE == KVQ_FP8_PER_TOKEN_HEAD) {
+        if (qf8) {
+            if (small_bs) hipLaunchKernelGGL((attention_kernel<HD, MODE, true, true>), dim3(p.total_wg), dim3(threads), 0, st, p);
+            else hipLaunchKernelGGL((attention_kernel<HD, MODE, false, true>), dim3(p.total_wg), dim3(threads), 0, st, p);
+            return;
+        }
+    }
+    if (small_bs) hipLaunchKernelGGL((attention_kernel<HD, MODE, true, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
+    else hipLaunchKernelGGL((attention_kernel<HD, MODE, false, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
 }
 
 template <int HD>
@@ -857,6 +925,7 @@ int launch_attention(const AttnLaunch& a, const AttnPlan& pl, void* stream) {
     p.layer = a.layer;
     p.statics = a.static_scales;
     p.q = static_cast<const uint16_t*>(a.q);
+    p.q_scales = a.q_scales;
     p.block_table = a.block_table;
     p.seq_lens = a.seq_lens;
     p.out = static_cast<uint16_t*>(a.out);

@@ -114,6 +114,7 @@ struct AttnLaunch {
     const uint8_t* layer;
     const float* static_scales;
     const void* q;
+    const float* q_scales;         // device [H] static FP8 query scales, or null for BF16 queries
     const int32_t* block_table;
     const int32_t* seq_lens;
     void* out;

@@ -80,26 +80,27 @@ class Scenario:
         self.q = torch.randn((len(self.lens), hkv * group, hd), generator=gq).to(torch.bfloat16)
         self.sm_scale = 1.0 / math.sqrt(hd)
 
-    def run_gpu(self, bt=None, lens=None):
+    def run_gpu(self, bt=None, lens=None, q_scales=None):
         bt = self.bt if bt is None else bt
         lens = self.lens if lens is None else lens
+        qs = None if q_scales is None else torch.as_tensor(q_scales, dtype=torch.float32).to(DEV)
         out = self.cache.decode_attention(0, self.q.to(DEV), torch.as_tensor(bt, dtype=torch.int32).to(DEV),
                                           torch.as_tensor(np.asarray(lens), dtype=torch.int32).to(DEV),
-                                          self.sm_scale)
+                                          self.sm_scale, q_scales=qs)
         torch.cuda.synchronize()
         return _f64(_bits(out))
 
-    def reference(self, rows=None, bt=None, lens=None):
+    def reference(self, rows=None, bt=None, lens=None, q_scales=None):
         """Oracle output, weighted |V| sums and the tolerance, for sequences rows."""
         bt = self.bt if bt is None else bt
         lens = np.asarray(self.lens if lens is None else lens)
         rows = np.arange(len(lens)) if rows is None else np.asarray(rows)
         qb = _bits(self.q)[rows]
         ref, absv = self.orc.decode_attention(self.g, self.img, 0, qb, bt[rows], lens[rows], self.sm_scale,
-                                              with_absv=True)
+                                              with_absv=True, q_scales=q_scales)
         v_big = 1.0 if self.scales is None else float(self.scales[len(self.scales) // 2:].max())
         tol = self.orc.attention_error_bound(self.g, self.img, 0, qb, bt[rows], lens[rows], self.sm_scale, ref, absv,
-                                             v_big)
+                                             v_big, q_scales=q_scales)
         return ref, tol
 
     def check(self, out, ref, tol, what):
@@ -286,3 +287,50 @@ def test_attention_layer_without_blocks_gives_zeros(kvq, orc):
             assert not out.any()
     finally:
         cache.close()
+
+
+def _query_scales(q, shrink):
+    """Static per-query-head scales amax/448 of the queries, divided by shrink
+    (shrink > 1 makes the largest elements saturate at 448)."""
+    amax = q.float().abs().amax(dim=(0, 2)).numpy().astype(np.float32)
+    return (amax / np.float32(448.0) / np.float32(shrink)).astype(np.float32)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("mode", [W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD])
+@pytest.mark.parametrize("shrink", [1.0, 4.0])
+def test_fp8_query_attention(kvq, orc, mode, hd, shrink):
+    """FP8 queries under static per-query-head scales, on the FP8 products."""
+    what = f"fp8 query mode {W.MODE_NAMES[mode]} hd {hd} shrink {shrink}"
+    _flush(f"[attention] {what}")
+    sc = Scenario(kvq, orc, mode=mode, hd=hd, hkv=2, bs=16, lens=RAGGED, group=4, seed=100 + hd + mode)
+    try:
+        qs = _query_scales(sc.q, shrink)
+        out = sc.run_gpu(q_scales=qs)
+        ref, tol = sc.reference(q_scales=qs)
+        sc.check(out, ref, tol, what)
+        # the queries really are quantized: against BF16 queries the result moves
+        plain, _ = sc.reference()
+        assert np.abs(ref - plain).max() > 0
+    finally:
+        sc.close()
+
+
+def test_fp8_query_decode_workload_sampled(kvq, orc):
+    """FP8 queries on the full decode shape (256 x 8192-8207 tokens, 32/8 heads,
+    head_dim 128, per-token-head FP8), eight sequences against the oracle."""
+    _flush("[attention] fp8 query decode 256 x 8192 (sampled)")
+    g = torch.Generator().manual_seed(21)
+    lens = (8192 + torch.randint(0, 16, (256,), generator=g)).tolist()
+    k, v = (t.cpu() for t in W.normal_kv(sum(lens), 8, 128, seed=22, device=DEV))
+    sc = Scenario(kvq, orc, mode=W.FP8_PER_TOKEN_HEAD, hd=128, hkv=8, bs=16, lens=lens, group=4, seed=23,
+                  extra_blocks=0, kv=(k, v))
+    del k, v
+    try:
+        qs = _query_scales(sc.q, 1.0)
+        out = sc.run_gpu(q_scales=qs)
+        rows = [0, 5, 99, 128, 201, 255, 17, 64]
+        ref, tol = sc.reference(rows=rows, q_scales=qs)
+        sc.check(out[rows], ref, tol, "fp8 query decode sampled")
+    finally:
+        sc.close()

@@ -222,3 +222,22 @@ def test_attention_argument_checks(kvq):
         assert kvq._lib.kvq_decode_attention_workspace(h, 4, 64, 2, None) == kvq.ERR_INVALID_ARG
     finally:
         kvq.kvq_destroy_cache(h)
+
+
+
+def test_fp8_query_attention_argument_checks(kvq):
+    cfg = _cfg(kvq, [kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD, kvq.BF16], hd=128)
+    h = _handle(kvq, cfg)
+
+    def call(layer, qs=FAKE_DEV, nseq=1):
+        return kvq._lib.kvq_decode_attention_fp8q(h, layer, ctypes.c_void_p(FAKE_DEV), ctypes.c_void_p(qs), 4,
+                                                  ctypes.c_void_p(FAKE_DEV), 4, ctypes.c_void_p(FAKE_DEV), nseq,
+                                                  0.125, ctypes.c_void_p(FAKE_DEV), None, 0, None)
+    try:
+        assert call(0, qs=0) == kvq.ERR_INVALID_ARG                 # FP8 queries need their scales
+        assert call(0, qs=FAKE_DEV + 2) == kvq.ERR_INVALID_ARG      # 4-byte aligned
+        assert call(1) == kvq.ERR_UNSUPPORTED                       # INT4 layer
+        assert call(2) == kvq.ERR_UNSUPPORTED                       # BF16 layer
+        assert call(0, nseq=0) == kvq.OK                            # no-op
+    finally:
+        kvq.kvq_destroy_cache(h)
