@@ -604,6 +604,78 @@ def run_other_workload(args, torch, kvq, W):
                       step_bytes / sec / 1e9, sec * 1e3, sb, gb, store_s, gather_s, cpu, bool(parity),
                       {"sliding_store_us": round(slide_store_s * 1e6, 2), "sliding_gather_us": round(slide_gather_s * 1e6, 2),
                        "cache_MiB": round(cache.bytes["total"] / 2**20, 3)})
+    elif name == "itl":
+        # Attention-only inter-token latency against context, gpt-oss-20b shape
+        # (24 layers alternating sliding W=128 and full, 64 query / 8 KV heads,
+        # head_dim 64), batch 1: the three cache variants the pages' latency
+        # study compares (all BF16, all FP8 with per-tensor scale 1.0, FP8 with
+        # the sliding layers kept BF16); the slope is ms per context token.
+        L, hkv, hd, bs, Wn, H = 24, 8, 64, 16, 128, 64
+        ctxs = [8192, 16384, 32768]
+        variants = {"bf16": (kvq.BF16, kvq.BF16), "fp8": (kvq.FP8_PER_TENSOR, kvq.FP8_PER_TENSOR),
+                    "fp8_skip_sliding": (kvq.FP8_PER_TENSOR, kvq.BF16)}
+        ct = __import__("ctypes")
+        sm = 1.0 / math.sqrt(hd)
+        slopes, times = {}, {}
+        for vname, (full_mode, slide_mode) in variants.items():
+            ts = []
+            for T in ctxs:
+                sliding = [W.gptoss_layer_is_sliding(l) for l in range(L)]
+                modes = [slide_mode if sl_ else full_mode for sl_ in sliding]
+                nbs = [Wn // bs if sl_ else T // bs for sl_ in sliding]
+                cache = kvq.Cache(kvq.CacheConfig(bs, hkv, hd, modes, nbs), device=dev)
+                full_slots = torch.arange(T, dtype=torch.int64, device=dev)
+                ring = W.ring_slots(T, Wn, device=dev)
+                for l in range(L):
+                    k, v = W.normal_kv(T, hkv, hd, seed=9000 + l, device=dev)
+                    sc = [1.0, 1.0] if modes[l] == kvq.FP8_PER_TENSOR else None
+                    cache.store(l, k, v, ring if sliding[l] else full_slots, sc)
+                bt_full = torch.arange(T // bs, dtype=torch.int32, device=dev).view(1, -1)
+                bt_ring = W.ring_block_table(Wn, bs, device=dev)
+                sl_full = torch.tensor([T], dtype=torch.int32, device=dev)
+                sl_ring = torch.tensor([Wn], dtype=torch.int32, device=dev)
+                q = W.normal_kv(1, H, hd, seed=9999, device=dev)[0]
+                out = torch.empty_like(q)
+                ws_n = max(kvq.kvq_decode_attention_workspace(cache.handle, H, T // bs, 1), 16)
+                ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+                stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+                aa = []
+                for l in range(L):
+                    bt, sl_ = (bt_ring, sl_ring) if sliding[l] else (bt_full, sl_full)
+                    aa.append((cache.handle, l, ct.c_void_p(q.data_ptr()), H, ct.c_void_p(bt.data_ptr()),
+                               int(bt.shape[1]), ct.c_void_p(sl_.data_ptr()), 1, ct.c_float(sm),
+                               ct.c_void_p(out.data_ptr()), ct.c_void_p(ws.data_ptr()), ws_n, stream))
+
+                def step(ev):
+                    if ev: ev[0].record()
+                    for a in aa:
+                        st_ = kvq._lib.kvq_decode_attention(*a)
+                        if st_ != 0:
+                            raise kvq.KVQError(st_, "kvq_decode_attention")
+                    if ev: ev[1].record(); ev[2].record()
+                _, evs = _timed(torch, step, args.steps, args.warmup)
+                ts.append(sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps)     # ms per decode step
+                del cache
+                torch.cuda.empty_cache()
+            n = len(ctxs)
+            mx, my = sum(ctxs) / n, sum(ts) / n
+            slope = sum((x - mx) * (y - my) for x, y in zip(ctxs, ts)) / sum((x - mx) ** 2 for x in ctxs)
+            slopes[vname] = slope
+            times[vname] = [round(t, 5) for t in ts]
+            log(f"[bench] itl {vname}: {times[vname]} ms at {ctxs} tokens, slope {slope:.3e} ms/token")
+        res = {"metric": "attention-only inter-token latency slope (ms per context token), gpt-oss-20b shape, batch 1",
+               "value": round(slopes["fp8_skip_sliding"], 12), "unit": "ms/token", "n_gpus": 1, "steps": args.steps,
+               "warmup": args.warmup, "ms_per_step": times["fp8_skip_sliding"][-1], "higher_is_better": False,
+               "scaling": "weak", "vs_baseline": None, "dtype": "fp8/bf16 codes, bf16 MFMA, f32 accumulate",
+               "data": "synthetic",
+               "config": {"workload": "gpt-oss-20b shape: 24 layers alternating sliding (W=128) and full, 64 query / "
+                                      "8 KV heads, head_dim 64, one sequence; decode attention of all 24 layers",
+                          "contexts": ctxs, "variants": list(variants)},
+               "slopes_ms_per_token": {k: float(f"{v:.4g}") for k, v in slopes.items()},
+               "step_ms": times,
+               "pages_h100_full_model_slopes_ms_per_token": {"bf16": 8.94e-06, "fp8": 7.14e-06,
+                                                              "fp8_skip_sliding": 6.34e-06},
+               "roofline": None, "cpu_baseline": None, "parity_vs_oracle_sampled": None}
     elif name == "calib":
         # on-the-fly calibration over the GQA-32 prefill: one amax pass per layer
         spec = W.WORKLOADS["gqa32"]
@@ -809,7 +881,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa32",
-                    choices=["gqa32", "long80", "gptoss", "decode", "attention", "calib"],
+                    choices=["gqa32", "long80", "gptoss", "decode", "attention", "itl", "calib"],
                     help="gqa32 is the headline line; the others measure the remaining shapes")
     ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128], help="decode and attention workloads")
     ap.add_argument("--q-per-kv", type=int, default=4, help="attention workload: query heads per KV head")

@@ -54,6 +54,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kTile = 16;                 // tokens per tile
 constexpr int kMaxHeadsPerWg = 8;        // waves (KV heads) per attention workgroup
 constexpr int kMaxAttnThreads = 64 * kMaxHeadsPerWg;
+// Splits per sequence never exceed the target wave count, so the wide
+// combine's LDS weight table holds them all.
+constexpr int kMaxSplits = 4096;
+constexpr int kWideCombineSplits = 16;       // from here on the combine spreads the splits
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int HD, int MODE>
@@ -863,6 +867,65 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     }
 }
 
+// The same combine with the splits spread over a workgroup, one workgroup
+// per (sequence, query head): for long single sequences, whose few rows
+// each carry hundreds of splits, a serial walk over the splits would leave
+// the combine latency-bound.  The weights go through LDS; each thread sums a
+// strided share of the splits for one dim, and the shares are added in LDS.
+constexpr int kWideCombineThreads = 256;
+
+template <int HD>
+__global__ void __launch_bounds__(kWideCombineThreads) combine_wide_kernel(CombineArgs a) {
+    constexpr int T = kWideCombineThreads;
+    constexpr int G = T / HD;          // split groups per dim
+    __shared__ float wts[kMaxSplits];
+    __shared__ float red[T];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int b = static_cast<int>(row / a.num_q_heads);
+    const int len = max(0, min(a.seq_lens[b], a.max_len));
+    const int ntiles = (len + kTile - 1) / kTile;
+    const int nsp = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+    const float* ml = a.part_ml + row * a.splits * 2;
+
+    float mx = -INFINITY;
+    for (int s = tid; s < nsp; s += T) mx = fmaxf(mx, ml[2 * s]);
+    red[tid] = mx;
+    __syncthreads();
+    for (int k = T / 2; k > 0; k >>= 1) {
+        if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
+        __syncthreads();
+    }
+    const float M = red[0];
+    __syncthreads();
+    float lsum = 0.0f;
+    for (int s = tid; s < nsp; s += T) {
+        const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[2 * s] - M);
+        wts[s] = w;
+        lsum += w * ml[2 * s + 1];
+    }
+    red[tid] = lsum;
+    __syncthreads();
+    for (int k = T / 2; k > 0; k >>= 1) {
+        if (tid < k) red[tid] += red[tid + k];
+        __syncthreads();
+    }
+    const float L = red[0];
+    __syncthreads();
+    const int d = tid % HD, grp = tid / HD;
+    float acc = 0.0f;
+    for (int s = grp; s < nsp; s += G) acc += wts[s] * a.part_o[(row * a.splits + s) * HD + d];
+    red[tid] = acc;
+    __syncthreads();
+    if (grp == 0) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) sum += red[g * HD + d];
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        a.out[row * HD + d] = static_cast<uint16_t>(pack_bf16(sum * inv, 0.0f) & 0xFFFFu);
+    }
+}
+
 template <int HD, int MODE>
 void launch_attention_v(const AttnArgs& p, int threads, bool small_bs, hipStream_t st) {
     const bool qf8 = p.q_scales != nullptr;
@@ -900,10 +963,13 @@ AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_d
     pl.qgroups = (group + 15) / 16;
     const int64_t units = static_cast<int64_t>(num_seqs) * (num_kv_heads / hpw) * pl.qgroups;
     const int64_t max_tiles = (static_cast<int64_t>(max_blocks) * block_size + kTile - 1) / kTile;
-    // About 4096 waves fill the chip with a few waves per SIMD; a split keeps
-    // at least 8 tiles so that the partial results stay small next to the
-    // cache bytes it reads.
-    constexpr int64_t kTargetWaves = 4096, kMinTilesPerSplit = 8;
+    // About 1024 waves in all (measured best against 4096 and 2048: a wave
+    // streams best over a long tile range, and fewer splits write fewer
+    // partials); a split keeps at least 8 tiles.  A long single sequence gets
+    // up to 1024 / heads_per_wg splits; a large batch gets one split, and the
+    // kernel then writes the output itself.
+    constexpr int64_t kTargetWaves = 1024, kMinTilesPerSplit = 8;
+    static_assert(kTargetWaves <= kMaxSplits, "the wide combine holds every split's weight");
     const int64_t want = (kTargetWaves / hpw + units - 1) / units;
     const int64_t cap = (max_tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
     int64_t splits = want < cap ? want : cap;
@@ -968,6 +1034,15 @@ int launch_attention(const AttnLaunch& a, const AttnPlan& pl, void* stream) {
     c.splits = pl.splits;
     c.tiles_per_split = pl.tiles_per_split;
     c.max_len = p.max_len;
+    if (pl.splits >= kWideCombineSplits) {
+        const uint32_t grid = static_cast<uint32_t>(c.rows);
+        switch (a.head_dim) {
+            case 64: hipLaunchKernelGGL(combine_wide_kernel<64>, dim3(grid), dim3(kWideCombineThreads), 0, st, c); break;
+            case 128: hipLaunchKernelGGL(combine_wide_kernel<128>, dim3(grid), dim3(kWideCombineThreads), 0, st, c); break;
+            default: hipLaunchKernelGGL(combine_wide_kernel<256>, dim3(grid), dim3(kWideCombineThreads), 0, st, c); break;
+        }
+        return static_cast<int>(hipGetLastError());
+    }
     const uint32_t grid = static_cast<uint32_t>((c.rows + 3) / 4);
     switch (a.head_dim) {
         case 64: hipLaunchKernelGGL(combine_kernel<64>, dim3(grid), dim3(256), 0, st, c); break;

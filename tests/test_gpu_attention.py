@@ -334,3 +334,21 @@ def test_fp8_query_decode_workload_sampled(kvq, orc):
         sc.check(out[rows], ref, tol, "fp8 query decode sampled")
     finally:
         sc.close()
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.BF16, W.INT4_PER_TOKEN_HEAD])
+def test_attention_one_long_sequence(kvq, orc, mode, hd):
+    """Batch 1: a single long sequence split into dozens of ranges, merged by
+    the workgroup-wide combine; one range's blocks are outside the layer."""
+    what = f"one long sequence mode {W.MODE_NAMES[mode]} hd {hd}"
+    _flush(f"[attention] {what}")
+    sc = Scenario(kvq, orc, mode=mode, hd=hd, hkv=2, bs=16, lens=[6001], group=8, seed=130 + hd + mode)
+    try:
+        bt = sc.bt.copy()
+        bt[0, 40:48] = -1                    # 128 tokens of one split range take no part
+        out = sc.run_gpu(bt=bt)
+        ref, tol = sc.reference(bt=bt)
+        sc.check(out, ref, tol, what)
+    finally:
+        sc.close()
