@@ -409,8 +409,12 @@ def _decode_setup(args, torch, kvq, W, dev):
     L, hkv, bs, S, ctx = spec["num_layers"], spec["hkv"], spec["block_size"], spec["num_seqs"], spec["context"]
     hd = args.head_dim
     mode = {v: k for k, v in W.MODE_NAMES.items()}[args.mode]
-    if mode not in (kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD):
-        raise SystemExit("decode workloads: --mode fp8_per_token_head or int4_per_token_head")
+    if args.workload == "decode" and mode not in (kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD):
+        raise SystemExit("decode workload: --mode fp8_per_token_head or int4_per_token_head")
+    if args.layers:
+        L = int(args.layers)
+    # static layers: uncalibrated scale 1.0 (the pages' per-tensor default)
+    scales = {kvq.FP8_PER_TENSOR: [1.0, 1.0], kvq.FP8_PER_HEAD: [1.0] * (2 * hkv)}.get(mode)
     # the workload's 513 blocks per sequence hold 8192 + 16 tokens; room is
     # added for every appended step this run takes
     maxb = ctx // bs + 1 + (args.warmup + args.steps) // bs
@@ -428,7 +432,7 @@ def _decode_setup(args, torch, kvq, W, dev):
     for l in range(L):
         for c0 in range(0, S * ctx, chunk):
             k, v = W.normal_kv(chunk, hkv, hd, seed=5000 + 1000 * l + c0 // chunk, device=dev)
-            Lc.store(Lc.store_args(l, k, v, slots[c0: c0 + chunk], mode))
+            Lc.store(Lc.store_args(l, k, v, slots[c0: c0 + chunk], mode, scales if c0 == 0 else None))
         torch.cuda.synchronize()
     steps_slots = []
     for _ in range(args.warmup + args.steps):
@@ -437,6 +441,7 @@ def _decode_setup(args, torch, kvq, W, dev):
     lens_at = [torch.tensor([ctx + s_ + 1] * S, dtype=torch.int32, device=dev)
                for s_ in range(args.warmup + args.steps)]
     return {"L": L, "S": S, "hkv": hkv, "hd": hd, "bs": bs, "ctx": ctx, "mode": mode, "nb": nb, "cache": cache,
+            "scales": scales,
             "st": st, "slots": slots, "chunk": chunk, "Lc": Lc, "steps_slots": steps_slots, "kdec": kdec,
             "vdec": vdec, "lens_at": lens_at, "bt": st.block_table.to(dev),
             "desc": spec["desc"] + f", head_dim {hd}, {args.mode}"}
@@ -445,17 +450,19 @@ def _decode_setup(args, torch, kvq, W, dev):
 def _decode_oracle_layer(D, torch, W, oracle):
     """The oracle's own image of the last layer after every step: its store
     of the same seeded prefill chunks and appended tokens."""
+    import numpy as np
     l = D["L"] - 1
     g = oracle.Geometry(D["bs"], D["hkv"], D["hd"], [D["mode"]], [D["nb"]])
     host = oracle.new_cache(g)
     slots = D["slots"].cpu().numpy()
     dev = D["slots"].device
+    sc = None if D["scales"] is None else np.array(D["scales"], np.float32)
     for c0 in range(0, D["S"] * D["ctx"], D["chunk"]):
         k, v = W.normal_kv(D["chunk"], D["hkv"], D["hd"], seed=5000 + 1000 * l + c0 // D["chunk"], device=dev)
-        oracle.store(g, host, 0, _bits(torch, k), _bits(torch, v), slots[c0: c0 + D["chunk"]])
+        oracle.store(g, host, 0, _bits(torch, k), _bits(torch, v), slots[c0: c0 + D["chunk"]], sc)
     kb, vb = _bits(torch, D["kdec"]), _bits(torch, D["vdec"])
     for ss in D["steps_slots"]:
-        oracle.store(g, host, 0, kb, vb, ss.cpu().numpy())
+        oracle.store(g, host, 0, kb, vb, ss.cpu().numpy(), sc)
     return g, host
 
 
@@ -883,7 +890,8 @@ def main():
     ap.add_argument("--workload", default="gqa32",
                     choices=["gqa32", "long80", "gptoss", "decode", "attention", "itl", "calib"],
                     help="gqa32 is the headline line; the others measure the remaining shapes")
-    ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128], help="decode and attention workloads")
+    ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128, 256], help="decode and attention workloads")
+    ap.add_argument("--layers", type=int, default=0, help="attention workload: layers (default: the workload's 32)")
     ap.add_argument("--q-per-kv", type=int, default=4, help="attention workload: query heads per KV head")
     ap.add_argument("--q-fp8", action="store_true", help="attention workload: FP8 queries (kvq_decode_attention_fp8q)")
     ap.add_argument("--mode", default="fp8_per_token_head",

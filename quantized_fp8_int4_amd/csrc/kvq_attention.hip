@@ -58,6 +58,7 @@ constexpr int kMaxAttnThreads = 64 * kMaxHeadsPerWg;
 // combine's LDS weight table holds them all.
 constexpr int kMaxSplits = 4096;
 constexpr int kWideCombineSplits = 16;       // from here on the combine spreads the splits
+constexpr int kMaxStagedPieces = 8;          // 16-byte pieces per lane of a staged tile (8 KiB)
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int HD, int MODE>
@@ -297,10 +298,11 @@ constexpr int attention_round() {
 
 // Whether a tile's K and V rows are read as whole lines and regrouped in LDS
 // (one L2 request per line) instead of straight into the MFMA operand lanes
-// (where the K and the V slices of a line are separate requests).
+// (where the K and the V slices of a line are separate requests): every
+// case whose tile of row pairs is 1 to 8 KiB, i.e. all but BF16 at head_dim 256.
 template <int HD, int MODE>
 constexpr bool attention_staged() {
-    return Geo<HD, MODE>::NC >= 1 && Geo<HD, MODE>::NC <= 4 && HD <= 128;
+    return Geo<HD, MODE>::NC >= 1 && Geo<HD, MODE>::NC <= kMaxStagedPieces;
 }
 
 // Whether rounds with no token to mask take a path of their own (at head_dim
@@ -334,13 +336,11 @@ struct RawTile {
     uint32_t ok;
 };
 
-// Loads of tile tau of sequence b for KV head h.  Entries of the block table
-// that do not name a block of the layer read block 0 instead and are masked.
 // Per-lane byte offsets inside a block, fixed for a wave (KV head h, lane
 // r, q4): the tile's first position adds a wave-uniform term, so the loads
 // take a scalar base and a 32-bit lane offset.
 struct LaneOff {
-    uint32_t kv[4];                // staged reads: the lane's 16-byte pieces of the tile's row pairs
+    uint32_t kv[kMaxStagedPieces]; // staged reads: the lane's 16-byte pieces of the tile's row pairs
     uint32_t vsh;                  // right shift that moves a 2-byte V slice to bits 0..15
     uint32_t k;                    // K slice of token r
     uint32_t v[4];                 // V slices of tokens 4q4+i
@@ -354,7 +354,7 @@ __device__ __forceinline__ LaneOff lane_offsets(const AttnArgs& a, int h, int r,
     LaneOff o;
     const uint32_t lane = static_cast<uint32_t>(16 * q4 + r);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < (G::NC < kMaxStagedPieces ? G::NC : kMaxStagedPieces); ++c) {
         const uint32_t g = static_cast<uint32_t>(c) * 1024u + lane * 16u;       // byte of the tile's row-pair image
         const uint32_t tok = g / (2 * G::RB), off = g % (2 * G::RB);
         o.kv[c] = (tok * hkv + uh) * (2 * G::RB) + off;
