@@ -186,15 +186,6 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// The low INT4 nibble of byte B of x -> n / 16 as FP32, exact.  Written as
-// byte extracts so that the conversion reads the byte through an SDWA operand
-// select instead of a separate shift.
-template <int B>
-__device__ __forceinline__ float int4_over16(uint32_t x) {
-    const uint32_t b = B == 0 ? x : (B == 3 ? x >> 24 : (x >> (8 * B)) & 0xFFu);
-    return __builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(b));
-}
-
 // K step j of the lane's K slice -> 8 BF16 A-operand values (dims 8j .. 8j+7
 // of the slice).
 template <int HD, int MODE>

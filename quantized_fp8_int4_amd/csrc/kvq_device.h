@@ -80,21 +80,28 @@ __device__ __forceinline__ RowQ row_prep(float s) {
     return q;
 }
 
-// RN(|x| / s) for |x| >= 0.  CLAMP bounds y for static scales, whose
-// quotients may overflow; any y >= 2^20 saturates both formats anyway.
+// RN(x / s), sign included.  y = RN(x r) is within an ulp of the quotient;
+// the residual d = y s - x is exact in one FMA, and q = RN(y - d r) is the
+// correctly rounded quotient (Markstein).  Every step is odd in x, so the
+// result is the sign of x times RN(|x| / s).  Writing the residual as y s - x,
+// not x - y s, keeps the sign of zero: x = -0 gives y = -0, d = +0 and
+// q = -0 + -0 = -0 (and s = 0, where r = 0, gives q = x * 0).  CLAMP bounds y
+// for static scales, whose quotients may overflow; any |y| >= 2^20 saturates
+// both formats anyway.
 template <bool PRESCALE, bool CLAMP>
 __device__ __forceinline__ float quotient(float x, const RowQ& q) {
-    float ax = fabsf(x);
-    if constexpr (PRESCALE) ax *= q.f;
-    float y = ax * q.r;
-    if constexpr (CLAMP) y = fminf(y, 0x1p20f);
-    const float e = fmaf(-y, q.s, ax);
-    return fmaf(e, q.r, y);
+    if constexpr (PRESCALE) x *= q.f;
+    float y = x * q.r;
+    if constexpr (CLAMP) y = __builtin_amdgcn_fmed3f(y, -0x1p20f, 0x1p20f);
+    const float d = fmaf(y, q.s, -x);
+    return fmaf(-d, q.r, y);
 }
 
-// 8 BF16 values -> 8 E4M3FN codes.  The magnitude is clamped to 448 and
-// converted (round to nearest even); the sign bits of the inputs are then
-// copied into the code bytes, so zero and tiny quotients keep their sign.
+// 8 BF16 values -> 8 E4M3FN codes.  The conversion rounds to nearest even and
+// keeps the sign of zero and of quotients too small for E4M3.  Static scales
+// (CLAMP) clamp the quotient to [-448, 448] first.  Dynamic scales need no
+// clamp: s = RN(a / 448) >= (a / 448)(1 - 2^-24), so |q| <= RN(448 (1 + 2^-23))
+// = 448 + 2^-15, which the conversion rounds to 448 like any value below 464.
 template <bool PRESCALE, bool CLAMP>
 __device__ __forceinline__ uint2 encode_fp8(const uint4& w, const RowQ& q) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -102,37 +109,59 @@ __device__ __forceinline__ uint2 encode_fp8(const uint4& w, const RowQ& q) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const uint32_t w0 = ws[2 * i], w1 = ws[2 * i + 1];
-        const float q0 = fminf(quotient<PRESCALE, CLAMP>(bf16_lo(w0), q), 448.0f);
-        const float q1 = fminf(quotient<PRESCALE, CLAMP>(bf16_hi(w0), q), 448.0f);
-        const float q2 = fminf(quotient<PRESCALE, CLAMP>(bf16_lo(w1), q), 448.0f);
-        const float q3 = fminf(quotient<PRESCALE, CLAMP>(bf16_hi(w1), q), 448.0f);
+        float q0 = quotient<PRESCALE, CLAMP>(bf16_lo(w0), q);
+        float q1 = quotient<PRESCALE, CLAMP>(bf16_hi(w0), q);
+        float q2 = quotient<PRESCALE, CLAMP>(bf16_lo(w1), q);
+        float q3 = quotient<PRESCALE, CLAMP>(bf16_hi(w1), q);
+        if constexpr (CLAMP) {
+            q0 = __builtin_amdgcn_fmed3f(q0, -448.0f, 448.0f);
+            q1 = __builtin_amdgcn_fmed3f(q1, -448.0f, 448.0f);
+            q2 = __builtin_amdgcn_fmed3f(q2, -448.0f, 448.0f);
+            q3 = __builtin_amdgcn_fmed3f(q3, -448.0f, 448.0f);
+        }
         int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
         pk = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, pk, true);
-        // high byte of each BF16 (bit 7 = sign) -> byte lanes 0..3
-        const uint32_t sign = __builtin_amdgcn_perm(w1, w0, 0x07050301u) & 0x80808080u;
-        out[i] = static_cast<uint32_t>(pk) | sign;
+        out[i] = static_cast<uint32_t>(pk);
     }
     return make_uint2(out[0], out[1]);
 }
 
 // 8 BF16 values -> 8 two's-complement nibbles, element 2j in the low nibble
-// of byte j.  Adding 1.5 * 2^23 rounds the signed quotient to the nearest
-// integer, ties to even, and leaves that integer in the low mantissa bits.
-// Dynamic INT4 quotients are at most a / RN(a / 7) < 7.5 in magnitude, so the
-// rounded value already lies in [-7, 7] and the clamp to [-8, 7] is a no-op.
+// of byte j.  Dynamic INT4 quotients are at most a / RN(a / 7) < 7.5 in
+// magnitude, so n = rint_even(q) lies in [-7, 7] and no clamp is needed.
+// t = RN(q + 2^23 + 8) = 2^23 + 8 + n exactly (one rounding, to an integer,
+// ties to even): its bit pattern is the exponent of 2^23, zeros, and n + 8
+// in bits 0..3.  Shifted left by 8 or more, only that nibble survives (bit 23,
+// the exponent's lowest bit, is 0).  Element 1 (shift 4) uses
+// RN(1024 q + 2^33 + 2^13) instead, whose exponent field has its five lowest
+// bits clear.  The nibbles n + 8 are then flipped to two's complement with
+// one XOR by 8.
 template <bool PRESCALE>
 __device__ __forceinline__ uint32_t encode_int4(const uint4& w, const RowQ& q) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
     uint32_t acc = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const uint32_t xb = (e & 1) ? (ws[e >> 1] & 0xFFFF0000u) : (ws[e >> 1] << 16);
-        const float mag = quotient<PRESCALE, false>(__uint_as_float(xb), q);
-        const float sq = __uint_as_float((__float_as_uint(mag) & 0x7FFFFFFFu) | (xb & 0x80000000u));
-        const float t = sq + 12582912.0f;
-        acc |= (__float_as_uint(t) & 0xFu) << (4 * e);
+        const float x = (e & 1) ? bf16_hi(ws[e >> 1]) : bf16_lo(ws[e >> 1]);
+        const float qe = quotient<PRESCALE, false>(x, q);
+        if (e == 0) {
+            acc = __float_as_uint(qe + 0x1.00001p23f) & 0xFu;
+        } else if (e == 1) {
+            acc |= __float_as_uint(fmaf(qe, 1024.0f, 0x1.00001p33f)) << 4;
+        } else {
+            acc |= __float_as_uint(qe + 0x1.00001p23f) << (4 * e);
+        }
     }
-    return acc;
+    return acc ^ 0x88888888u;
+}
+
+// The low INT4 nibble of byte B of x -> n / 16 as FP32, exact
+// (v_cvt_off_f32_i4).  Written as byte extracts so that the conversion reads
+// the byte through an SDWA operand select instead of a separate shift.
+template <int B>
+__device__ __forceinline__ float int4_over16(uint32_t x) {
+    const uint32_t b = B == 0 ? x : (B == 3 ? x >> 24 : (x >> (8 * B)) & 0xFFu);
+    return __builtin_amdgcn_cvt_off_f32_i4(static_cast<int>(b));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {

@@ -16,7 +16,7 @@
 //
 // Exactness.  The stored quotient must be the correctly rounded FP32 x / s.
 // Each row computes r = RN(1/s) once (rcp_exact); each element then
-// takes y = RN(|x| r), e = fma(-y, s, |x|) (exact), q = fma(e, r, y), which is
+// takes y = RN(x r), d = fma(y, s, -x) (exact), q = fma(-d, r, y), which is
 // the correctly rounded quotient when r is the correctly rounded reciprocal
 // and nothing is subnormal (P. Markstein, "Computation of elementary
 // functions on the IBM RISC System/6000 processor", IBM J. R&D 34(1), 1990;
@@ -24,8 +24,8 @@
 // Systems", 2002).  Rows whose scale lies outside [2^-64, 2^64] scale both x
 // and s by the same power of two first, which leaves the quotient unchanged
 // and keeps s and r normal.  Quotients small enough to be subnormal encode to
-// zero in both formats, so their rounding does not matter; the sign is taken
-// from x, never from the quotient.
+// zero in both formats, so their rounding does not matter; the steps are odd
+// in x and keep the sign of x on a zero quotient.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -393,14 +393,28 @@ __global__ __launch_bounds__(TPB) void gather_kernel(GatherArgs p) {
 #pragma unroll
             for (int d = 0; d < DW; ++d) o[d] = cw[u][d];
         } else if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+            // Byte e holds elements 2e (low nibble) and 2e+1.  While 16 s is
+            // finite, (n / 16)(16 s) is the same real number as n s, so it
+            // rounds alike; waves holding a larger scale widen n itself.
+            if (__builtin_amdgcn_ballot_w64(s > 0x1p120f) == 0) {
+                const float s16 = s * 16.0f;
 #pragma unroll
-            for (int d = 0; d < DW; ++d) {
+                for (int d = 0; d < DW; ++d) {
+                    const uint32_t w = cw[u][d], hi = __builtin_amdgcn_alignbit(w, w, 4);
+                    o[4 * d + 0] = pack_bf16(int4_over16<0>(w) * s16, int4_over16<0>(hi) * s16);
+                    o[4 * d + 1] = pack_bf16(int4_over16<1>(w) * s16, int4_over16<1>(hi) * s16);
+                    o[4 * d + 2] = pack_bf16(int4_over16<2>(w) * s16, int4_over16<2>(hi) * s16);
+                    o[4 * d + 3] = pack_bf16(int4_over16<3>(w) * s16, int4_over16<3>(hi) * s16);
+                }
+            } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // byte e holds elements 2e (low nibble) and 2e+1
-                    const float a = static_cast<float>(static_cast<int32_t>(cw[u][d] << (28 - 8 * e)) >> 28);
-                    const float bb = static_cast<float>(static_cast<int32_t>(cw[u][d] << (24 - 8 * e)) >> 28);
-                    o[4 * d + e] = pack_bf16(a * s, bb * s);
+                for (int d = 0; d < DW; ++d) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float a = static_cast<float>(static_cast<int32_t>(cw[u][d] << (28 - 8 * e)) >> 28);
+                        const float bb = static_cast<float>(static_cast<int32_t>(cw[u][d] << (24 - 8 * e)) >> 28);
+                        o[4 * d + e] = pack_bf16(a * s, bb * s);
+                    }
                 }
             }
         } else {
@@ -432,16 +446,15 @@ __global__ void write_static_kernel(float* dst, StaticValues vals, int n) {
 
 // Default tuning, chosen by measurement on MI355X (32768 tokens x 8 KV heads
 // per call): 8 lanes per row, so every load instruction reads whole 128-byte
-// lines of each row; more rows per lane for INT4 at head_dim 128 and for BF16
-// (little arithmetic to hide latency behind); non-temporal streams for data
+// lines of each row; more rows per lane for BF16 (no arithmetic to hide
+// latency behind); non-temporal streams for data
 // that one call touches once.  The
 // gather moves 8 code bytes (FP8) or 4 (INT4) per thread chunk, so each
 // wave-wide store writes 1 KiB of contiguous BF16 output.
 template <int HD, int MODE>
 struct Tune {
     static constexpr int store_epl = HD / 8;
-    static constexpr int store_rpl = (MODE == KVQ_BF16) ? (HD == 64 ? 4 : 2)
-                                   : ((MODE == KVQ_INT4_PER_TOKEN_HEAD && HD == 128) ? 2 : 1);
+    static constexpr int store_rpl = (MODE == KVQ_BF16) ? (HD == 64 ? 4 : 2) : 1;
     static constexpr bool store_nt_load = true;
     static constexpr bool store_nt_store = true;
     static constexpr bool store_contig = false;
