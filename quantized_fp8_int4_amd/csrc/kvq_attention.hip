@@ -593,7 +593,7 @@ __device__ __forceinline__ void tile_round(const Tile<HD, MODE>* const* T, State
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             p[i] = __builtin_amdgcn_exp2f(s[n][i] - mref);
-            pv[i] = valid[n][i] ? (G::DYN ? p[i] * (T[n]->s[i][1] * G::CODE_UNIT) : p[i]) : 0.0f;
+            pv[i] = valid[n][i] ? (G::DYN ? p[i] * T[n]->s[i][1] : p[i]) : 0.0f;
         }
         psum += (p[0] + p[1]) + (p[2] + p[3]);
         const u32x2 pb = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
@@ -681,8 +681,10 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
         }
     }
 
+    // INT4 operands are n / 16 (v_cvt_off_f32_i4): the factor 16 is applied
+    // once to the scores' factor and once to the output, never per token
     float k_factor = a.c * G::CODE_UNIT * q_factor;
-    float v_factor = 1.0f;
+    float v_factor = G::CODE_UNIT;
     if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
         k_factor *= a.statics[0];
         v_factor = a.statics[1];

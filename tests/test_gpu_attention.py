@@ -175,6 +175,25 @@ def test_attention_heavy_tails(kvq, orc):
          group=4, seed=60, kv=(k, v))
 
 
+@pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_attention_extreme_value_scales(kvq, orc, mode, hd):
+    """V rows whose absmax is near the BF16 maximum (scales above 2^124, whose
+    16-fold overflows FP32), FP32-subnormal and BF16-subnormal ones, among
+    ordinary rows; short sequences keep the weighted sums of the huge rows
+    finite in FP32."""
+    lens = [1, 5, 16]
+    n = sum(lens)
+    g = torch.Generator().manual_seed(140 + hd + mode)
+    k = torch.randn((n, 2, hd), generator=g)
+    v = torch.randn((n, 2, hd), generator=g)
+    kinds = torch.randint(0, 4, (n, 2), generator=g)
+    target = torch.tensor([1.0, 3.0e38, 1.0e-38, 2.0 ** -130])[kinds]
+    v = v / v.abs().amax(dim=-1, keepdim=True) * target[..., None]
+    _run(kvq, orc, f"extreme V scales mode {W.MODE_NAMES[mode]} hd {hd}", mode=mode, hd=hd, hkv=2, bs=16,
+         lens=lens, group=4, seed=140 + hd, kv=(k.to(torch.bfloat16), v.to(torch.bfloat16)))
+
+
 @pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.BF16, W.FP8_PER_HEAD])
 def test_attention_skips_blocks_outside_the_layer(kvq, orc, mode):
     """Table entries that are negative or past the layer's blocks drop their
