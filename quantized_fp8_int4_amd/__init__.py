@@ -72,7 +72,7 @@ class _Bytes(ctypes.Structure):
 
 def _load_library():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libkvq.so is not built ({LIB_PATH}); run `python -m quantized_fp8_int4_amd.build`")
+        raise ImportError(f"libkvq.so is not built ({LIB_PATH}); run `python quantized_fp8_int4_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.kvq_cache_bytes.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Bytes)]

@@ -1,6 +1,6 @@
 """Build the gfx950 shared library libkvq.so in-tree with hipcc.
 
-    python -m quantized_fp8_int4_amd.build
+    python quantized_fp8_int4_amd/build.py
 
 Flags: IEEE single precision on the device (no fast-math, FP32 denormals kept,
 no mul-add contraction: the kernels place every fused multiply-add
