@@ -256,14 +256,17 @@ __device__ __forceinline__ int64_t wave_sum(int64_t v) {
     return v;
 }
 
+// Codes are read once per call: 8- and 16-byte chunks are loaded
+// non-temporally (+1.7% at FP8 head_dim 128); 4-byte chunks are not, which
+// measured up to 19% slower in that form.
 template <int N>
 __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&w)[N]) {
     if constexpr (N == 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p);
-        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
     } else if constexpr (N == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
-        w[0] = v.x; w[1] = v.y;
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        w[0] = v[0]; w[1] = v[1];
     } else {
         w[0] = *reinterpret_cast<const uint32_t*>(p);
     }
