@@ -41,6 +41,18 @@ def test_calibrate_amax_matches_oracle(kvq, orc, hd, hkv):
     assert (amax.cpu() == 0).all()
 
 
+def test_calibrate_amax_many_rows(kvq, orc):
+    """Enough rows (40001 tokens x 8 KV heads) that every workgroup loops
+    over several row groups, with a ragged last group."""
+    print("[calib] many rows", flush=True)
+    k, v = W.gqa_kv(40001, 8, 128, seed=75)
+    amax = torch.empty((16,), dtype=torch.float32, device=DEV)
+    kvq.kvq_calibrate_amax(k.to(DEV), v.to(DEV), amax, accumulate=False)
+    ref = orc.calibrate_amax(_bits(k), _bits(v), 8, 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(amax.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("mode", [W.FP8_PER_TENSOR, W.FP8_PER_HEAD], ids=["per_tensor", "per_head"])
 def test_calibrated_static_layout_end_to_end(kvq, orc, mode):
     """Warmup batches -> device amax -> static scales -> store and gather of a
