@@ -280,11 +280,14 @@ constexpr int attention_depth() {
     return HD == 64 ? 4 : 2;
 }
 
-// Tiles per softmax round (rounds of two tiles measured no faster: the path
-// is bound by the memory requests in flight, not by the round's latency).
-template <int HD, int MODE>
+// Tiles per softmax round: one, or two when their columns are packed (PACK:
+// a query group of at most 8 heads fills at most half of the 16 MFMA
+// columns, so two tiles' scores share one set of lanes and one softmax).
+// Rounds of two unpacked tiles measured no faster: the path is then bound by
+// the memory requests in flight, not by the round's latency.
+template <int HD, int MODE, bool PACK>
 constexpr int attention_round() {
-    return 1;
+    return PACK ? 2 : 1;
 }
 
 // Whether a tile's K and V rows are read as whole lines and regrouped in LDS
@@ -560,47 +563,92 @@ __device__ __forceinline__ f32x4 qk_product(const uint32_t* k, const QOperand<HD
 // the tiles' Q K^T products, one running-maximum update, then their P V
 // products.  MASK = false is the path of rounds whose tokens all lie below
 // len in blocks of the layer (a wave-uniform fact).
-template <int HD, int MODE, int NT, bool MASK, bool QF8>
+template <int HD, int MODE, int NT, bool MASK, bool QF8, bool PACK>
 __device__ __forceinline__ void tile_round(const Tile<HD, MODE>* const* T, State<HD, MODE>& st,
-                                           const QOperand<HD, QF8>& qo, int t0, int len, int q4, float k_factor,
-                                           uint32_t vsh) {
+                                           const QOperand<HD, QF8>& qo, int t0, int len, int r, int q4,
+                                           float k_factor, uint32_t vsh) {
     using G = Geo<HD, MODE>;
     f32x4 sacc[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) sacc[n] = qk_product<HD, MODE, QF8>(T[n]->k, qo);
 
-    float s[NT][4];
     bool valid[NT][4];
-    float tmax = -INFINITY;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
             valid[n][i] = !MASK || ((t0 + kTile * n + 4 * q4 + i < len) && ((T[n]->ok >> i) & 1u));
-            const float f = G::DYN ? T[n]->s[i][0] * k_factor : k_factor;
-            s[n][i] = valid[n][i] ? sacc[n][i] * f : -INFINITY;
-            tmax = fmaxf(tmax, s[n][i]);
-        }
-    tmax = max_q4(tmax);
-    const float mnew = fmaxf(st.m, tmax);
-    const float mref = mnew == -INFINITY ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - mref);
-    float psum = 0.0f;
+
+    float alpha;
     s16x4 b[NT];
+    if constexpr (PACK) {
+        static_assert(NT == 2, "two tiles share the 16 columns");
+        // Lanes r < 8 hold tile 0's columns; lanes r >= 8 hold tile 1's,
+        // whose column c moves from lane c to lane c + 8 (DPP row_shr:8).
+        // Each score, weight and sum is the one the unpacked round computes;
+        // only the lanes of unused columns are no longer spent on them.
+        const bool hi = r >= 8;
+        float s[4], fv[4];
+        bool vl[4];
+        float lmax = -INFINITY;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
+        for (int i = 0; i < 4; ++i) {
+            const float s1 = __uint_as_float(dpp<0x118>(__float_as_uint(sacc[1][i])));
+            vl[i] = hi ? valid[1][i] : valid[0][i];
+            const float f = G::DYN ? (hi ? T[1]->s[i][0] : T[0]->s[i][0]) * k_factor : k_factor;
+            fv[i] = G::DYN ? (hi ? T[1]->s[i][1] : T[0]->s[i][1]) : 1.0f;
+            s[i] = vl[i] ? (hi ? s1 : sacc[0][i]) * f : -INFINITY;
+            lmax = fmaxf(lmax, s[i]);
+        }
+        float tmax = max_q4(lmax);
+        tmax = fmaxf(tmax, __uint_as_float(dpp<0x128>(__float_as_uint(tmax))));   // row_ror:8: both tiles
+        const float mnew = fmaxf(st.m, tmax);
+        const float mref = mnew == -INFINITY ? 0.0f : mnew;
+        alpha = __builtin_amdgcn_exp2f(st.m - mref);
         float p[4], pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(s[n][i] - mref);
-            pv[i] = valid[n][i] ? (G::DYN ? p[i] * T[n]->s[i][1] : p[i]) : 0.0f;
+            p[i] = __builtin_amdgcn_exp2f(s[i] - mref);
+            pv[i] = vl[i] ? (G::DYN ? p[i] * fv[i] : p[i]) : 0.0f;
         }
-        psum += (p[0] + p[1]) + (p[2] + p[3]);
+        st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        st.m = mnew;
         const u32x2 pb = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
-        b[n] = __builtin_bit_cast(s16x4, pb);
+        b[0] = __builtin_bit_cast(s16x4, pb);
+        // tile 1's weights back to their columns (DPP row_shl:8)
+        const u32x2 pb1 = {dpp<0x108>(pb[0]), dpp<0x108>(pb[1])};
+        b[1] = __builtin_bit_cast(s16x4, pb1);
+    } else {
+        float s[NT][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float f = G::DYN ? T[n]->s[i][0] * k_factor : k_factor;
+                s[n][i] = valid[n][i] ? sacc[n][i] * f : -INFINITY;
+                tmax = fmaxf(tmax, s[n][i]);
+            }
+        tmax = max_q4(tmax);
+        const float mnew = fmaxf(st.m, tmax);
+        const float mref = mnew == -INFINITY ? 0.0f : mnew;
+        alpha = __builtin_amdgcn_exp2f(st.m - mref);
+        float psum = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            float p[4], pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(s[n][i] - mref);
+                pv[i] = valid[n][i] ? (G::DYN ? p[i] * T[n]->s[i][1] : p[i]) : 0.0f;
+            }
+            psum += (p[0] + p[1]) + (p[2] + p[3]);
+            const u32x2 pb = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
+            b[n] = __builtin_bit_cast(s16x4, pb);
+        }
+        st.l = st.l * alpha + psum;
+        st.m = mnew;
     }
-    st.l = st.l * alpha + psum;
-    st.m = mnew;
 
     s16x4 av[NT][G::J];
 #pragma unroll
@@ -626,7 +674,7 @@ __device__ __forceinline__ void tile_round(const Tile<HD, MODE>* const* T, State
             st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[n][j], b[n], st.o[j], 0, 0, 0);
 }
 
-template <int HD, int MODE, bool SMALL_BS, bool QF8>
+template <int HD, int MODE, bool SMALL_BS, bool QF8, bool PACK>
 __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attention_kernel(AttnArgs a) {
     using G = Geo<HD, MODE>;
     // Workgroup -> work item, spreading consecutive items over one XCD
@@ -692,6 +740,12 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
         k_factor *= a.statics[h];
         v_factor = a.statics[a.hkv + h];
     }
+    if constexpr (PACK) {
+        // lanes r >= 8 score column r - 8 (of the round's second tile): they
+        // take that column's factor, which differs per column with FP8 queries
+        const float kf = __uint_as_float(dpp<0x118>(__float_as_uint(k_factor)));
+        if (r >= 8) k_factor = kf;
+    }
 
     State<HD, MODE> st;
 #pragma unroll
@@ -708,7 +762,7 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
         // so no loop exit falls between a load and its use, and the
         // prefetches still pending at the exit are consumed there.
         constexpr int D = attention_depth<HD, MODE>();
-        constexpr int NT = attention_round<HD, MODE>();
+        constexpr int NT = attention_round<HD, MODE, PACK>();
         static_assert(D % NT == 0 && D > NT, "whole rounds, at least one round in flight");
         const int lim = min(len, tend * kTile);
         const int last = tend - 1;
@@ -757,9 +811,9 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
                 }
                 const int t0 = (tau + k) * kTile;
                 if (attention_fast_path<HD>() && !SMALL_BS && t0 + NT * kTile <= lim && all_ok)
-                    tile_round<HD, MODE, NT, false, QF8>(rt, st, qo, t0, lim, q4, k_factor, lo.vsh);
+                    tile_round<HD, MODE, NT, false, QF8, PACK>(rt, st, qo, t0, lim, r, q4, k_factor, lo.vsh);
                 else
-                    tile_round<HD, MODE, NT, true, QF8>(rt, st, qo, t0, lim, q4, k_factor, lo.vsh);
+                    tile_round<HD, MODE, NT, true, QF8, PACK>(rt, st, qo, t0, lim, r, q4, k_factor, lo.vsh);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -767,7 +821,8 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
         for (int k = 0; k < D - NT; ++k) consume(t[k]);
     }
 
-    const float l = sum_q4(st.l);
+    float l = sum_q4(st.l);
+    if constexpr (PACK) l += __uint_as_float(dpp<0x128>(__float_as_uint(l)));   // + the other tile's lanes
     // lane holds dims J*(4*q4 + i) + j, i < 4, j < J: hd/4 contiguous dims
     const int64_t row = static_cast<int64_t>(b) * a.num_q_heads + qh;
     if (a.splits == 1) {
@@ -919,18 +974,34 @@ __global__ void __launch_bounds__(kWideCombineThreads) combine_wide_kernel(Combi
     }
 }
 
+// Packed softmax rounds (two tiles per set of columns) where the query group
+// leaves at least half of the columns free: at head_dim 64, where the
+// per-tile softmax is the largest share of the instructions.
+template <int HD>
+constexpr bool attention_packs() {
+    return HD == 64;
+}
+
+template <int HD, int MODE, bool QF8>
+void launch_attention_q(const AttnArgs& p, int threads, bool small_bs, hipStream_t st) {
+    if (small_bs)
+        hipLaunchKernelGGL((attention_kernel<HD, MODE, true, QF8, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
+    else if (attention_packs<HD>() && p.group <= 8)
+        hipLaunchKernelGGL((attention_kernel<HD, MODE, false, QF8, attention_packs<HD>()>), dim3(p.total_wg),
+                           dim3(threads), 0, st, p);
+    else
+        hipLaunchKernelGGL((attention_kernel<HD, MODE, false, QF8, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
+}
+
 template <int HD, int MODE>
 void launch_attention_v(const AttnArgs& p, int threads, bool small_bs, hipStream_t st) {
-    const bool qf8 = p.q_scales != nullptr;
     if constexpr (MODE == KVQ_FP8_PER_TENSOR || MODE == KVQ_FP8_PER_HEAD || MODE == KVQ_FP8_PER_TOKEN_HEAD) {
-        if (qf8) {
-            if (small_bs) hipLaunchKernelGGL((attention_kernel<HD, MODE, true, true>), dim3(p.total_wg), dim3(threads), 0, st, p);
-            else hipLaunchKernelGGL((attention_kernel<HD, MODE, false, true>), dim3(p.total_wg), dim3(threads), 0, st, p);
+        if (p.q_scales != nullptr) {
+            launch_attention_q<HD, MODE, true>(p, threads, small_bs, st);
             return;
         }
     }
-    if (small_bs) hipLaunchKernelGGL((attention_kernel<HD, MODE, true, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
-    else hipLaunchKernelGGL((attention_kernel<HD, MODE, false, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
+    launch_attention_q<HD, MODE, false>(p, threads, small_bs, st);
 }
 
 template <int HD>

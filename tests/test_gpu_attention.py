@@ -145,10 +145,11 @@ def test_attention_single_split(kvq, orc, mode):
          lens=[0, 1, 7, 16, 33, 100], group=4, seed=20 + mode)
 
 
-@pytest.mark.parametrize("group", [1, 2, 8, 16, 20, 33])
-def test_attention_query_groups(kvq, orc, group):
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("group", [1, 2, 8, 9, 16, 20, 33])
+def test_attention_query_groups(kvq, orc, group, hd):
     """Query heads per KV head below, at and above one 16-wide MFMA column block."""
-    _run(kvq, orc, f"group {group}", mode=W.FP8_PER_TOKEN_HEAD, hd=128, hkv=2, bs=16, lens=[5, 70, 200],
+    _run(kvq, orc, f"group {group} hd {hd}", mode=W.FP8_PER_TOKEN_HEAD, hd=hd, hkv=2, bs=16, lens=[5, 70, 200],
          group=group, seed=30 + group)
 
 
