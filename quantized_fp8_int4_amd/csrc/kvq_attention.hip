@@ -761,7 +761,8 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
         // masked (they take no part) and their loads re-read the last tile,
         // so no loop exit falls between a load and its use, and the
         // prefetches still pending at the exit are consumed there.
-        constexpr int D = attention_depth<HD, MODE>();
+        // a packed round at head_dim 128 keeps four tiles in flight
+        constexpr int D = (PACK && HD == 128) ? 4 : attention_depth<HD, MODE>();
         constexpr int NT = attention_round<HD, MODE, PACK>();
         static_assert(D % NT == 0 && D > NT, "whole rounds, at least one round in flight");
         const int lim = min(len, tend * kTile);
@@ -976,18 +977,20 @@ __global__ void __launch_bounds__(kWideCombineThreads) combine_wide_kernel(Combi
 
 // Packed softmax rounds (two tiles per set of columns) where the query group
 // leaves at least half of the columns free: at head_dim 64, where the
-// per-tile softmax is the largest share of the instructions.
-template <int HD>
+// per-tile softmax is the largest share of the instructions, and for INT4 at
+// head_dim 128, whose widening makes it the most VALU-heavy case (+3.5%
+// there; FP8 at head_dim 128 measured 0.7% slower).
+template <int HD, int MODE>
 constexpr bool attention_packs() {
-    return HD == 64;
+    return HD == 64 || (HD == 128 && MODE == KVQ_INT4_PER_TOKEN_HEAD);
 }
 
 template <int HD, int MODE, bool QF8>
 void launch_attention_q(const AttnArgs& p, int threads, bool small_bs, hipStream_t st) {
     if (small_bs)
         hipLaunchKernelGGL((attention_kernel<HD, MODE, true, QF8, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
-    else if (attention_packs<HD>() && p.group <= 8)
-        hipLaunchKernelGGL((attention_kernel<HD, MODE, false, QF8, attention_packs<HD>()>), dim3(p.total_wg),
+    else if (attention_packs<HD, MODE>() && p.group <= 8)
+        hipLaunchKernelGGL((attention_kernel<HD, MODE, false, QF8, attention_packs<HD, MODE>()>), dim3(p.total_wg),
                            dim3(threads), 0, st, p);
     else
         hipLaunchKernelGGL((attention_kernel<HD, MODE, false, QF8, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
