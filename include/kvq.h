@@ -307,9 +307,9 @@ KVQ_API kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const
  * the way the cache encodes K and V (E4M3(RN32(q / s)), nearest even,
  * saturating at 448), and the Q K^T products run on the FP8 codes directly.
  * This is the per-attention-head calibration's one Q scale per query head
- * ("Per-tensor vs per-head FP8 KV cache scales", "Per-tensor vs per-head FP8
- * KV cache scales"; "FP8 KV cache layer skipping vs per-head scales", "Per-head
- * scales have fixed overhead": H query scales beside 2 * Hkv K and V scales);
+ * ("Per-tensor vs per-head FP8 KV cache scales", the section of the same
+ * name; "FP8 KV cache layer skipping vs per-head scales", "Per-head scales
+ * have fixed overhead": H query scales beside 2 * Hkv K and V scales);
  * a per-tensor Q scale is H equal values.  kvq_calibrate_amax over the
  * queries and kvq_static_scales give such scales.
  *   q_scales   device FP32 [num_q_heads], 4-byte aligned, positive and finite
