@@ -58,6 +58,31 @@ def algorithmic_bytes(mode, hd, hkv, bs, token_heads):
     return store, gather
 
 
+def copy_ceiling(torch, nbytes, reps=10, pairs=8):
+    """Practical ceiling for a launch that moves 2 * nbytes: device-to-device
+    copies of nbytes (read once, written once) over `pairs` rotating buffer
+    pairs, so that the 256 MB Infinity Cache holds none of them; HIP events on
+    the current stream."""
+    n = (int(nbytes) + 15) // 16 * 16
+    bufs = [(torch.empty(n, dtype=torch.uint8, device="cuda"), torch.empty(n, dtype=torch.uint8, device="cuda"))
+            for _ in range(pairs)]
+    for src, dst in bufs:
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for src, dst in bufs:
+            dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / (reps * pairs)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes_per_copy": 2 * n, "us": round(sec * 1e6, 2), "GBps": round(2 * n / sec / 1e9, 1),
+            "frac_of_peak": round(2 * n / sec / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def kernel_source_hash(sources=None):
     """Hash of the sources a kernel is built from (default: store and gather)."""
     h = hashlib.sha256()
@@ -996,6 +1021,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # context: plain copies moving the same bytes as one store launch
+    ceiling = copy_ceiling(torch, store_bytes / 2)
+    ceiling["store_vs_copy"] = round(store_gbps / ceiling["GBps"], 4)
+    ceiling["gather_vs_copy"] = round(gather_gbps / ceiling["GBps"], 4)
+    log(f"[bench] copy ceiling: {ceiling['GBps']:.0f} GB/s for {ceiling['bytes_per_copy'] / 1e6:.1f} MB per copy")
+
     traffic = measured_traffic()
     cpu = None
     parity = None
@@ -1036,6 +1067,7 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else traffic.get(dominant)},
         "cpu_baseline": cpu,
+        "copy_ceiling": ceiling,
         "parity_vs_oracle_sampled": parity,
     }
     print(json.dumps(result), flush=True)
