@@ -169,7 +169,8 @@ KVQ_API kvq_status kvq_destroy_cache(kvq_cache* c);
  *                  slot, or one >= the layer's blocks * block_size, is not
  *                  stored (ring buffers of sliding layers use -1 for tokens
  *                  outside the window).  Two tokens with the same slot in one
- *                  call race (undefined which one lands).
+ *                  call race (undefined which one lands); the Python
+ *                  binding's Cache.check_slots finds them, off this path.
  *   mode           must equal the layer's mode (else KVQ_ERR_MODE_MISMATCH).
  *   scales         host FP32.  KVQ_FP8_PER_TENSOR: [sK, sV].
  *                  KVQ_FP8_PER_HEAD: [sK[0..H), sV[0..H)].  Other modes: NULL.

@@ -399,6 +399,18 @@ class Cache:
     def store(self, layer, keys, values, slot_mapping, scales=None, stream=None):
         kvq_store(self.handle, layer, keys, values, slot_mapping, self.cfg.layer_modes[layer], scales, stream)
 
+    def check_slots(self, layer, slot_mapping) -> int:
+        """Debug check of a store's slot_mapping, off the store path: raises
+        ValueError when two tokens name the same slot of the layer (kvq_store
+        leaves which one lands undefined); returns how many tokens the store
+        will skip (negative slots or slots past the layer's blocks)."""
+        s = slot_mapping.detach().to(torch.int64).flatten()
+        nslots = int(self.cfg.layer_num_blocks[layer]) * int(self.cfg.block_size)
+        kept = s[(s >= 0) & (s < nslots)]
+        if torch.unique(kept).numel() != kept.numel():
+            raise ValueError(f"layer {layer}: slot_mapping names a slot more than once")
+        return int(s.numel() - kept.numel())
+
     def gather_dequant(self, layer, block_table, seq_lens, total_tokens=None, out=None, stream=None):
         """Returns (keys, values) bf16 [sum(seq_lens), Hkv, hd].  Pass
         total_tokens (or out) to avoid reading seq_lens back to the host."""

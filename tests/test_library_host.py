@@ -241,3 +241,19 @@ def test_fp8_query_attention_argument_checks(kvq):
         assert call(0, nseq=0) == kvq.OK                            # no-op
     finally:
         kvq.kvq_destroy_cache(h)
+
+
+def test_check_slots_debug_helper(kvq):
+    """The binding's debug check of a slot mapping: duplicates among stored
+    slots raise; skipped tokens (negative or past the layer) are counted."""
+    import types
+    import torch
+    cfg = _cfg(kvq, [kvq.FP8_PER_TOKEN_HEAD])
+    fake = types.SimpleNamespace(cfg=cfg)
+    nslots = cfg.layer_num_blocks[0] * cfg.block_size
+    ok = torch.tensor([0, 5, -1, nslots, nslots - 1, -7], dtype=torch.int64)
+    assert kvq.Cache.check_slots(fake, 0, ok) == 3
+    with pytest.raises(ValueError):
+        kvq.Cache.check_slots(fake, 0, torch.tensor([3, 4, 3], dtype=torch.int64))
+    # repeated skipped slots are no duplicates: they are never written
+    assert kvq.Cache.check_slots(fake, 0, torch.tensor([-1, -1, nslots + 2, nslots + 2], dtype=torch.int64)) == 4
