@@ -31,14 +31,14 @@ def _numpy_attention(q, kh, vh, lens, group, sm_scale):
     return out
 
 
-def _setup(orc, mode, hkv=2, hd=64, bs=16, nblocks=12, lens=(37, 0, 80), seed=0):
+def _setup(orc, mode, hkv=2, hd=64, bs=16, nblocks=12, lens=(37, 0, 80), seed=0, gen=W.gqa_kv):
     g = orc.Geometry(bs, hkv, hd, [mode], [nblocks])
     buf = orc.new_cache(g)
     st = W.DecodeState(len(lens), bs, nblocks, 6, seed=seed)
     slots = []
     for b, n in enumerate(lens):
         slots += st.append(b, n)
-    k, v = W.gqa_kv(len(slots), hkv, hd, seed=seed + 1)
+    k, v = gen(len(slots), hkv, hd, seed=seed + 1)
     sc = None
     if mode == W.FP8_PER_TENSOR:
         sc = np.array([0.05, 0.04], np.float32)
@@ -123,3 +123,57 @@ def test_fp8_query_attention_matches_numpy(orc, mode):
         if n:
             assert np.allclose(zero[b], np.repeat(vh[row0: row0 + n].mean(axis=0), group, axis=0), rtol=1e-13, atol=1e-13)
         row0 += n
+
+
+@pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD, W.BF16, W.FP8_PER_HEAD])
+def test_error_bound_is_not_vacuous(orc, mode):
+    """The tolerance the GPU attention tests use catches plausible mistakes,
+    planted here in the oracle's own inputs: at the short lengths of those
+    tests, dropping a sequence's last token, or giving a token the V row of
+    its neighbour, moves some output element of that sequence beyond the
+    bound; so does doubling a token's V scale in the per-token-head modes.
+    N(0, 1) rows keep every token's softmax weight near 1/len (a token of
+    negligible weight can take any value without any tolerance noticing)."""
+    hkv, hd, bs = 2, 64, 16
+    g, buf, st = _setup(orc, mode, hkv=hkv, hd=hd, bs=bs, lens=(5, 17, 33), gen=W.normal_kv)
+    bt = st.block_table.numpy()
+    lens = np.array(st.seq_lens, np.int32)
+    q = torch.randn((3, 4 * hkv, hd), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    qb = _bits(q)
+    sm = 1.0 / np.sqrt(hd)
+    v_big = 1.0 if mode != W.FP8_PER_HEAD else 0.06
+    ref, absv = orc.decode_attention(g, buf, 0, qb, bt, lens, sm, with_absv=True)
+    tol = orc.attention_error_bound(g, buf, 0, qb, bt, lens, sm, ref, absv, v_big)
+
+    def caught(wrong, rows):
+        return all((np.abs(wrong[b] - ref[b]) > tol[b]).any() for b in rows)
+
+    # a dropped token
+    assert caught(orc.decode_attention(g, buf, 0, qb, bt, lens - 1, sm), range(3))
+
+    # token 0 of each sequence takes the V row of token 1 (head 0), laid out as
+    # block = codes[bs][hkv][K, V][row bytes] then, per-token-head, scales[bs][hkv][K, V]
+    hb = {W.BF16: 2 * hd, W.INT4_PER_TOKEN_HEAD: hd // 2}.get(mode, hd)
+    dyn = mode in (W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD)
+    code_bytes = bs * hkv * 2 * hb
+    block_bytes = code_bytes + (bs * hkv * 8 if dyn else 0)
+    lb, _, _ = orc.layer_offsets(g)
+    planted = buf.copy()
+    for b in range(3):
+        base = int(lb[0]) + int(bt[b, 0]) * block_bytes
+        v0 = base + hb                                   # (pos 0, head 0) V row
+        v1 = base + (1 * hkv + 0) * 2 * hb + hb          # (pos 1, head 0) V row
+        planted[v0: v0 + hb] = buf[v1: v1 + hb]
+        if dyn:
+            s0 = base + code_bytes + 4
+            s1 = base + code_bytes + (1 * hkv) * 8 + 4
+            planted[s0: s0 + 4] = buf[s1: s1 + 4]
+    assert caught(orc.decode_attention(g, planted, 0, qb, bt, lens, sm), range(3))
+
+    if dyn:
+        doubled = buf.copy()
+        for b in range(3):
+            s0 = int(lb[0]) + int(bt[b, 0]) * block_bytes + code_bytes + 4
+            sv = doubled[s0: s0 + 4].view(np.float32)
+            doubled[s0: s0 + 4] = (sv * np.float32(2.0)).view(np.uint8)
+        assert caught(orc.decode_attention(g, doubled, 0, qb, bt, lens, sm), range(3))
