@@ -295,6 +295,51 @@ def test_decode_append_reduced(kvq, orc, mode, hd):
     pair.cache.close()
 
 
+@pytest.mark.parametrize("mode,hd", [(W.FP8_PER_TOKEN_HEAD, 128), (W.INT4_PER_TOKEN_HEAD, 64)],
+                         ids=["fp8_per_token_head-128", "int4_per_token_head-64"])
+def test_decode_layer_full_size(kvq, orc, mode, hd):
+    """Decode shape at full size, one layer, in the benchmark's launch
+    configuration: 256 sequences prefilled with 8192 tokens each in store
+    calls of 32768 tokens, blocks popped from a random free list, then two
+    steps appending one token per sequence (the first opens a new block for
+    every sequence); every cache byte compared, and the full-context gather
+    compared on eight sampled sequences."""
+    _flush(f"[decode-full] mode={W.MODE_NAMES[mode]} hd={hd}")
+    S, ctx, bs, hkv, chunk = 256, 8192, 16, 8, 32768
+    maxb = ctx // bs + 1
+    nblocks = S * maxb
+    st = W.DecodeState(S, bs, nblocks, maxb, seed=5000)
+    slots = []
+    for b in range(S):
+        slots += st.append(b, ctx)
+    slots = torch.tensor(slots, dtype=torch.int64)
+    pair = Pair(kvq, orc, bs, hkv, hd, [mode], [nblocks])
+    for c0 in range(0, S * ctx, chunk):
+        k, v = W.normal_kv(chunk, hkv, hd, seed=5000 + c0 // chunk, device=DEV)
+        pair.store(0, k, v, slots[c0: c0 + chunk])
+    for step in range(2):
+        sl = torch.tensor([st.append(b, 1)[0] for b in range(S)], dtype=torch.int64)
+        k, v = W.normal_kv(S, hkv, hd, seed=6000 + step, device=DEV)
+        pair.store(0, k, v, sl)
+    pair.assert_buffers_equal()
+    lens = np.array(st.seq_lens, np.int32)
+    bt = st.block_table.numpy()
+    total = int(lens.sum())
+    ok = torch.empty((total, hkv, hd), dtype=torch.bfloat16, device=DEV)
+    ov = torch.empty_like(ok)
+    pair.cache.gather_dequant(0, torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV), out=(ok, ov))
+    torch.cuda.synchronize()
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    pick = np.random.default_rng(7).choice(S, 8, replace=False)
+    for b in pick:
+        rk, rv = orc.gather(pair.g, pair.host, 0, bt[b: b + 1], lens[b: b + 1])
+        r0, n = int(starts[b]), int(lens[b])
+        assert np.array_equal(_bits(ok[r0: r0 + n]), rk), f"keys of sequence {b}"
+        assert np.array_equal(_bits(ov[r0: r0 + n]), rv), f"values of sequence {b}"
+    del ok, ov
+    pair.cache.close()
+
+
 def test_long80_layer_full_size(kvq, orc):
     """80-layer long-context shape, one layer: a single 131072-token sequence,
     heads alternating N(0,1) and Student-t(3), per-token-head FP8, full
