@@ -332,6 +332,15 @@ def cpu_baseline(S, torch, W, n_layers):
     for layer in range(n_layers):
         gathered.append(oracle.gather(g, host, layer, bt, lens))
     secs = time.perf_counter() - t0
+    # the same oracle on one core, one layer (its store again is idempotent)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    sc = S["scales"][0]
+    oracle.store(g, host, 0, ins[0][0], ins[0][1], slots, None if sc is None else np.asarray(sc, np.float32))
+    oracle.gather(g, host, 0, bt, lens)
+    secs_one = time.perf_counter() - t1
+    oracle.set_num_threads(threads)
     lb, _, _ = oracle.layer_offsets(g)
     import quantized_fp8_int4_amd as kvq
     sigma = 8 if S["mode"] in (kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD) else 0
@@ -343,7 +352,19 @@ def cpu_baseline(S, torch, W, n_layers):
         dk = S["outs"][layer][0].cpu().view(torch.int16).numpy().view(np.uint16)
         dv = S["outs"][layer][1].cpu().view(torch.int16).numpy().view(np.uint16)
         ok = ok and np.array_equal(dk, gathered[layer][0]) and np.array_equal(dv, gathered[layer][1])
-    return secs, oracle.num_threads(), ok
+    return secs, threads, ok, secs_one
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), for the baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 class Launcher:
@@ -1029,15 +1050,19 @@ def main():
 
     traffic = measured_traffic()
     cpu = None
+    cpu_one = None
     parity = None
     if not args.no_cpu_baseline:
         nl = max(1, min(args.cpu_layers, L))
         log(f"[bench] cpu baseline: oracle on {nl} layers (store + gather)")
-        secs, cores, parity = cpu_baseline(S, torch, W, nl)
+        secs, cores, parity, secs_one = cpu_baseline(S, torch, W, nl)
         cpu = {"value": round(nl * (store_bytes + gather_bytes) / secs / 1e9, 3), "unit": "GB/s",
                "cores": cores, "kind": "oracle",
                "sample": f"{nl} of {L} layers of one step (store then gather of {S['n']} tokens each), "
                          f"{secs:.2f} s wall"}
+        cpu_one = {"value": round((store_bytes + gather_bytes) / secs_one / 1e9, 3), "unit": "GB/s", "cores": 1,
+                   "sample": f"1 layer (store then gather), {secs_one:.2f} s wall", "cpu_model": cpu_model(),
+                   "host_cores_visible": len(os.sched_getaffinity(0))}
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -1067,6 +1092,7 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else traffic.get(dominant)},
         "cpu_baseline": cpu,
+        "cpu_single_core": cpu_one,
         "copy_ceiling": ceiling,
         "parity_vs_oracle_sampled": parity,
     }

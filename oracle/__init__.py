@@ -62,6 +62,8 @@ def _load():
     lib.orc_dequant_fp8_n.argtypes = [P, P, P, I64]
     lib.orc_dynamic_scale_n.argtypes = [P, ctypes.c_double, P, I64]
     lib.orc_num_threads.restype = I32
+    lib.orc_set_num_threads.argtypes = [I32]
+    lib.orc_set_num_threads.restype = None
     lib.orc_calibrate_amax.argtypes = [P, P, I64, I64, I64, P, I32]
     lib.orc_decode_attention.argtypes = [I32, I64, I64, I64, P, P, P, I32, P, I64, P, I64, P, I64,
                                          ctypes.c_double, P, P, P]
@@ -327,3 +329,8 @@ def dequant_fp8(codes, s) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from here on (used to time it)."""
+    _load().orc_set_num_threads(int(n))

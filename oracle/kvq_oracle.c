@@ -646,3 +646,14 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads of the oracle's parallel loops from here on (timing only). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
