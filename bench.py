@@ -670,6 +670,7 @@ def run_other_workload(args, torch, kvq, W):
         ct = __import__("ctypes")
         sm = 1.0 / math.sqrt(hd)
         slopes, times = {}, {}
+        itl_parity = None
         for vname, (full_mode, slide_mode) in variants.items():
             ts = []
             for T in ctxs:
@@ -708,6 +709,25 @@ def run_other_workload(args, torch, kvq, W):
                     if ev: ev[1].record(); ev[2].record()
                 _, evs = _timed(torch, step, args.steps, args.warmup)
                 ts.append(sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps)     # ms per decode step
+                if T == ctxs[0] and not args.no_cpu_baseline:
+                    # oracle check of the first sliding and the first full layer
+                    ok_layers = []
+                    for l in (0, 1):
+                        bt, sl_ = (bt_ring, sl_ring) if sliding[l] else (bt_full, sl_full)
+                        o_l = cache.decode_attention(l, q, bt, sl_, sm)
+                        g1 = oracle.Geometry(bs, hkv, hd, [modes[l]], [nbs[l]])
+                        img = oracle.new_cache(g1)
+                        k, v = W.normal_kv(T, hkv, hd, seed=9000 + l, device=dev)
+                        sc = np.array([1.0, 1.0], np.float32) if modes[l] == kvq.FP8_PER_TENSOR else None
+                        oracle.store(g1, img, 0, _bits(torch, k), _bits(torch, v),
+                                     (ring if sliding[l] else full_slots).cpu().numpy(), sc)
+                        qb = _bits(torch, q.view(1, H, hd))
+                        btn, sln = bt.cpu().numpy(), sl_.cpu().numpy()
+                        ref, absv = oracle.decode_attention(g1, img, 0, qb, btn, sln, sm, with_absv=True)
+                        tol = oracle.attention_error_bound(g1, img, 0, qb, btn, sln, sm, ref, absv, 1.0)
+                        got = o_l.float().cpu().numpy().reshape(ref.shape).astype(np.float64)
+                        ok_layers.append(bool((np.abs(got - ref) <= tol).all()))
+                    itl_parity = all(ok_layers) if itl_parity is None else (itl_parity and all(ok_layers))
                 del cache
                 torch.cuda.empty_cache()
             n = len(ctxs)
@@ -728,7 +748,7 @@ def run_other_workload(args, torch, kvq, W):
                "step_ms": times,
                "pages_h100_full_model_slopes_ms_per_token": {"bf16": 8.94e-06, "fp8": 7.14e-06,
                                                               "fp8_skip_sliding": 6.34e-06},
-               "roofline": None, "cpu_baseline": None, "parity_vs_oracle_sampled": None}
+               "roofline": None, "cpu_baseline": None, "parity_vs_oracle_sampled": itl_parity}
     elif name == "calib":
         # on-the-fly calibration over the GQA-32 prefill: one amax pass per layer
         spec = W.WORKLOADS["gqa32"]
