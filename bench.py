@@ -275,6 +275,8 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd):
 def setup(args, torch, kvq, W):
     spec = W.WORKLOADS["gqa32"]
     L, hkv, hd, bs = spec["num_layers"], spec["hkv"], spec["hd"], spec["block_size"]
+    # a tensor-parallel shard stores only its own KV heads for the same tokens
+    hkv //= getattr(args, "tp", 1)
     nseq, slen = spec["num_seqs"], spec["seq_len"]
     n = nseq * slen
     mode = {v: k for k, v in W.MODE_NAMES.items()}[args.mode]
@@ -957,6 +959,8 @@ def main():
                     choices=["gqa32", "long80", "gptoss", "decode", "attention", "itl", "calib"],
                     help="gqa32 is the headline line; the others measure the remaining shapes")
     ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128, 256], help="decode and attention workloads")
+    ap.add_argument("--tp", type=int, default=1, choices=[1, 2, 4, 8],
+                    help="gqa32 workload: one tensor-parallel shard's share, 8/TP KV heads per GPU")
     ap.add_argument("--layers", type=int, default=0, help="attention workload: layers (default: the workload's 32)")
     ap.add_argument("--q-per-kv", type=int, default=4, help="attention workload: query heads per KV head")
     ap.add_argument("--q-fp8", action="store_true", help="attention workload: FP8 queries (kvq_decode_attention_fp8q)")
@@ -1068,7 +1072,8 @@ def main():
     ceiling["gather_vs_copy"] = round(gather_gbps / ceiling["GBps"], 4)
     log(f"[bench] copy ceiling: {ceiling['GBps']:.0f} GB/s for {ceiling['bytes_per_copy'] / 1e6:.1f} MB per copy")
 
-    traffic = measured_traffic()
+    # the committed counters were taken on the default shape and mode only
+    traffic = measured_traffic() if (args.mode == "fp8_per_token_head" and args.tp == 1) else None
     cpu = None
     cpu_one = None
     parity = None
@@ -1096,10 +1101,12 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "gqa32: 32 layers, 8 KV heads, head_dim 128, block 16, prefill of 8 x 4096 "
+        "config": {"workload": (f"gqa32 tensor-parallel shard (TP {args.tp}): 32 layers, {S['hkv']} of 8 KV heads per GPU, "
+                                if args.tp > 1 else "gqa32: 32 layers, 8 KV heads, ")
+                               + "head_dim 128, block 16, prefill of 8 x 4096 "
                                f"tokens per layer call, store + gather_dequant of every layer, {args.mode}",
                    "mode": args.mode, "layers": L, "tokens_per_layer_call": S["n"], "num_kv_heads": S["hkv"],
-                   "head_dim": S["hd"], "block_size": S["bs"]},
+                   "head_dim": S["hd"], "block_size": S["bs"], "tp": args.tp},
         "store_GBps": round(store_gbps, 1),
         "gather_GBps": round(gather_gbps, 1),
         "store_frac_of_peak": round(store_gbps / HBM_PEAK_GBPS, 4),

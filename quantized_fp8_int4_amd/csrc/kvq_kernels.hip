@@ -558,6 +558,16 @@ int launch_store_m(const StoreLaunch& a, void* stream) {
 template <int HD, int MODE>
 int launch_gather_t(const GatherLaunch& a, void* stream) {
     using T = Tune<HD, MODE>;
+    // A block that half a workgroup already covers (few KV heads, as on a
+    // tensor-parallel shard) takes half the chunks per thread, so no lane
+    // repeats another lane's chunk.  The grid is the same: one part per block.
+    const int64_t chunks = static_cast<int64_t>(a.block_size) * a.num_kv_heads * 2 *
+                           static_cast<int64_t>(row_bytes(a.mode, HD) / T::gather_cb);
+    if constexpr (T::gather_u % 2 == 0) {
+        if (2 * chunks <= static_cast<int64_t>(T::gather_tpb) * T::gather_u)
+            return launch_gather_v<HD, MODE, T::gather_cb, T::gather_u / 2, T::gather_nt_store, T::gather_lds_scales,
+                                   T::gather_tpb>(a, stream);
+    }
     return launch_gather_v<HD, MODE, T::gather_cb, T::gather_u, T::gather_nt_store, T::gather_lds_scales,
                            T::gather_tpb>(a, stream);
 }
