@@ -250,6 +250,29 @@ def test_gqa32_layer_full_size(kvq, orc, mode):
     pair.cache.close()
 
 
+@pytest.mark.parametrize("tp,mode", [(8, W.FP8_PER_TOKEN_HEAD), (8, W.INT4_PER_TOKEN_HEAD), (2, W.FP8_PER_TOKEN_HEAD)],
+                         ids=["tp8-fp8_per_token_head", "tp8-int4_per_token_head", "tp2-fp8_per_token_head"])
+def test_gqa32_shard_layer_full_size(kvq, orc, tp, mode):
+    """One tensor-parallel shard's share of a GQA-32 layer call, as the
+    benchmark's --tp runs it: 8 / tp KV heads, 8 sequences x 4096 tokens,
+    head_dim 128, permuted block table.  At one KV head a block fills half a
+    gather workgroup, which then takes half the chunks per thread.  Every cache
+    byte and every gathered value compared."""
+    cfgw = W.WORKLOADS["gqa32"]
+    layer, hkv = 3, 8 // tp
+    _flush(f"[gqa32 shard] tp={tp} hkv={hkv} mode={W.MODE_NAMES[mode]} layer={layer}")
+    n = cfgw["num_seqs"] * cfgw["seq_len"]
+    nblocks = n // 16
+    k, v = W.gqa_kv(n, hkv, 128, seed=1000 + layer, device=DEV)
+    bt = W.permuted_block_table(cfgw["num_seqs"], cfgw["seq_len"] // 16, nblocks, seed=1000)
+    slots = W.slots_from_block_table(bt, [cfgw["seq_len"]] * cfgw["num_seqs"], 16)
+    pair = Pair(kvq, orc, 16, hkv, 128, [mode], [nblocks])
+    pair.store(0, k.cpu(), v.cpu(), slots)
+    pair.assert_buffers_equal()
+    pair.gather_and_compare(0, bt.numpy(), [cfgw["seq_len"]] * cfgw["num_seqs"])
+    pair.cache.close()
+
+
 def test_gptoss_sliding_and_full_layers(kvq, orc):
     """gpt-oss shape: a sliding layer kept BF16 in a 128-slot ring buffer and a
     full layer in per-token-head FP8, head_dim 64, 32768 tokens."""
