@@ -212,13 +212,14 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir):
     print("\n".join(lines + [""] + out))
 
 
-def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd):
+def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, layers=0):
     """profiles/ summaries of the decode-attention workload from three
     rocprofv3 runs of bench.py --workload attention (kernel trace with
     --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, the latter two with
-    --calibrate-copy)."""
+    --calibrate-copy); layers > 0 when the runs took --layers (a cache of
+    32 layers that would not fit in HBM)."""
     kt_path, tr_path = attention_profile_paths(mode_name, hd)
-    args_s = f"--workload attention --mode {mode_name} --head-dim {hd}"
+    args_s = f"--workload attention --mode {mode_name} --head-dim {hd}" + (f" --layers {layers}" if layers else "")
     stats = _read_csv(kt_dir, "kernel_stats.csv")
     lines = [f"# Kernel trace: decode attention, 256 x 8192 tokens, 32 query / 8 KV heads, {mode_name}, head_dim {hd}", "",
              "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
@@ -237,7 +238,8 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd):
     write = _counter_per_kernel(_read_csv(write_dir, "counter_collection.csv"), "WRITE_SIZE")
     f_scale = COPY_BYTES / (fetch["copy"][0] * 1024.0)
     w_scale = COPY_BYTES / (write["copy"][0] * 1024.0)
-    mode = {"fp8_per_token_head": 3, "int4_per_token_head": 4}[mode_name]
+    mode = {"bf16": 0, "fp8_per_tensor": 1, "fp8_per_head": 2, "fp8_per_token_head": 3,
+            "int4_per_token_head": 4}[mode_name]
     S, ctx, hkv, H, bs = 256, 8192, 8, 32, 16
     # the profiled launches: 4 fused steps (lengths ctx + 1 .. ctx + 4) and 4
     # attention-only passes at ctx + 4, 32 layers each: mean length ctx + 3.25
@@ -455,6 +457,8 @@ def _decode_setup(args, torch, kvq, W, dev):
     every decode step the run will take."""
     spec = W.WORKLOADS["decode"]
     L, hkv, bs, S, ctx = spec["num_layers"], spec["hkv"], spec["block_size"], spec["num_seqs"], spec["context"]
+    # a tensor-parallel shard holds only its own KV heads (and their query heads)
+    hkv //= args.tp
     hd = args.head_dim
     mode = {v: k for k, v in W.MODE_NAMES.items()}[args.mode]
     if args.workload == "decode" and mode not in (kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD):
@@ -492,7 +496,8 @@ def _decode_setup(args, torch, kvq, W, dev):
             "scales": scales,
             "st": st, "slots": slots, "chunk": chunk, "Lc": Lc, "steps_slots": steps_slots, "kdec": kdec,
             "vdec": vdec, "lens_at": lens_at, "bt": st.block_table.to(dev),
-            "desc": spec["desc"] + f", head_dim {hd}, {args.mode}"}
+            "desc": spec["desc"] + f", head_dim {hd}, {args.mode}"
+                    + (f"; tensor-parallel shard (TP {args.tp}): {hkv} of 8 KV heads per GPU" if args.tp > 1 else "")}
 
 
 def _decode_oracle_layer(D, torch, W, oracle):
@@ -943,7 +948,7 @@ def run_other_workload(args, torch, kvq, W):
                "decode_tokens_per_s": round(S / sec, 1),
                "roofline": {"bound": "hbm", "kernel": "attention_kernel", "achieved": round(agbps, 1),
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(agbps / HBM_PEAK_GBPS, 4),
-                            "traffic": None if args.q_fp8 else measured_attention_traffic(args.mode, hd)},
+                            "traffic": None if (args.q_fp8 or args.tp > 1) else measured_attention_traffic(args.mode, hd)},
                "cpu_baseline": cpu,
                "parity_vs_oracle_sampled": parity,
                "workspace_bytes": wsb, "cache_GiB": round(D["cache"].bytes["total"] / 2**30, 3)}
@@ -960,7 +965,8 @@ def main():
                     help="gqa32 is the headline line; the others measure the remaining shapes")
     ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128, 256], help="decode and attention workloads")
     ap.add_argument("--tp", type=int, default=1, choices=[1, 2, 4, 8],
-                    help="gqa32 workload: one tensor-parallel shard's share, 8/TP KV heads per GPU")
+                    help="gqa32, decode and attention workloads: one tensor-parallel shard's share, "
+                         "8/TP KV heads per GPU")
     ap.add_argument("--layers", type=int, default=0, help="attention workload: layers (default: the workload's 32)")
     ap.add_argument("--q-per-kv", type=int, default=4, help="attention workload: query heads per KV head")
     ap.add_argument("--q-fp8", action="store_true", help="attention workload: FP8 queries (kvq_decode_attention_fp8q)")
@@ -979,7 +985,7 @@ def main():
         summarize_profiles(*args.summarize_profiles)
         return
     if args.summarize_attention_profiles:
-        summarize_attention_profiles(*args.summarize_attention_profiles, args.mode, args.head_dim)
+        summarize_attention_profiles(*args.summarize_attention_profiles, args.mode, args.head_dim, args.layers)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -58,7 +58,7 @@ constexpr int kMaxAttnThreads = 64 * kMaxHeadsPerWg;
 // combine's LDS weight table holds them all.
 constexpr int kMaxSplits = 4096;
 constexpr int kWideCombineSplits = 16;       // from here on the combine spreads the splits
-constexpr int kMaxStagedPieces = 8;          // 16-byte pieces per lane of a staged tile (8 KiB)
+constexpr int kMaxStagedPieces = 16;         // 16-byte pieces per lane of a staged tile (16 KiB)
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int HD, int MODE>
@@ -77,6 +77,9 @@ struct Geo {
     // Staged reads: a tile's 16 K|V row pairs (2 * RB bytes each) read as
     // whole 16-byte pieces, NC wave-wide loads of 1 KiB, then regrouped in LDS.
     static constexpr int NC = 16 * 2 * RB / 1024;
+    // A 1 KiB piece is exactly one token's row pair (BF16 at head_dim 256):
+    // piece c of every lane lies one token further, a wave-uniform step.
+    static constexpr bool PIECE_IS_ROW = 2 * RB == 1024;
     static constexpr int LDS_ROW = 2 * RB + 16;       // padded row pair: conflict-free K slices
     static constexpr int LDS_TILE = 16 * LDS_ROW;
     // INT4 codes widen to n / 16 (exact); the 16 goes back in with the scales.
@@ -293,7 +296,7 @@ constexpr int attention_round() {
 // Whether a tile's K and V rows are read as whole lines and regrouped in LDS
 // (one L2 request per line) instead of straight into the MFMA operand lanes
 // (where the K and the V slices of a line are separate requests): every
-// case whose tile of row pairs is 1 to 8 KiB, i.e. all but BF16 at head_dim 256.
+// case, whose tiles of row pairs are 1 to 16 KiB.
 template <int HD, int MODE>
 constexpr bool attention_staged() {
     return Geo<HD, MODE>::NC >= 1 && Geo<HD, MODE>::NC <= kMaxStagedPieces;
@@ -348,7 +351,7 @@ __device__ __forceinline__ LaneOff lane_offsets(const AttnArgs& a, int h, int r,
     LaneOff o;
     const uint32_t lane = static_cast<uint32_t>(16 * q4 + r);
 #pragma unroll
-    for (int c = 0; c < (G::NC < kMaxStagedPieces ? G::NC : kMaxStagedPieces); ++c) {
+    for (int c = 0; c < (G::PIECE_IS_ROW ? 1 : (G::NC < kMaxStagedPieces ? G::NC : kMaxStagedPieces)); ++c) {
         const uint32_t g = static_cast<uint32_t>(c) * 1024u + lane * 16u;       // byte of the tile's row-pair image
         const uint32_t tok = g / (2 * G::RB), off = g % (2 * G::RB);
         o.kv[c] = (tok * hkv + uh) * (2 * G::RB) + off;
@@ -437,7 +440,12 @@ __device__ __forceinline__ void load_raw(const AttnArgs& a, int blk, int tau, co
         const_cast<uint8_t*>(base), 0, static_cast<int>(a.block_bytes), kBufferDword3);
     const int srow = static_cast<int>(pos0 * static_cast<uint32_t>(a.hkv) * (2 * G::RB));
 #pragma unroll
-    for (int c = 0; c < G::NC; ++c) buf_load<16, kNonTemporal>(T.kv + 4 * c, rs, lo.kv[c], srow);
+    for (int c = 0; c < G::NC; ++c) {
+        if constexpr (G::PIECE_IS_ROW)
+            buf_load<16, kNonTemporal>(T.kv + 4 * c, rs, lo.kv[0], srow + c * a.hkv * 1024);
+        else
+            buf_load<16, kNonTemporal>(T.kv + 4 * c, rs, lo.kv[c], srow);
+    }
     if constexpr (G::DYN) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -449,10 +457,9 @@ __device__ __forceinline__ void load_raw(const AttnArgs& a, int blk, int tau, co
     T.ok = ok ? 0xFu : 0u;
 }
 
-// The staged tile into the wave's LDS rows, then the K and V operand slices
-// back out of them (the same registers Tile holds when read directly).
+// The staged tile into the wave's LDS rows.
 template <int HD, int MODE>
-__device__ __forceinline__ void unstage(const RawTile<HD, MODE>& R, uint8_t* lds, int r, int q4, Tile<HD, MODE>& T) {
+__device__ __forceinline__ void stage_write(const RawTile<HD, MODE>& R, uint8_t* lds, int r, int q4) {
     using G = Geo<HD, MODE>;
     const uint32_t lane = static_cast<uint32_t>(16 * q4 + r);
 #pragma unroll
@@ -462,6 +469,15 @@ __device__ __forceinline__ void unstage(const RawTile<HD, MODE>& R, uint8_t* lds
         const u32x4 v = {R.kv[4 * c], R.kv[4 * c + 1], R.kv[4 * c + 2], R.kv[4 * c + 3]};
         *reinterpret_cast<u32x4*>(lds + tok * G::LDS_ROW + off) = v;
     }
+}
+
+// The K and V operand slices back out of the wave's LDS rows (the same
+// registers Tile holds when read directly), with the raw tile's scales and
+// mask.
+template <int HD, int MODE>
+__device__ __forceinline__ void stage_read(const RawTile<HD, MODE>& R, const uint8_t* lds, int r, int q4,
+                                           Tile<HD, MODE>& T) {
+    using G = Geo<HD, MODE>;
     const uint8_t* kp = lds + r * G::LDS_ROW + q4 * G::KB;
 #pragma unroll
     for (int w = 0; w < G::KW; w += 2) {
@@ -477,6 +493,21 @@ __device__ __forceinline__ void unstage(const RawTile<HD, MODE>& R, uint8_t* lds
         T.s[i] = R.s[i];
     }
     T.ok = R.ok;
+}
+
+template <int HD, int MODE>
+__device__ __forceinline__ void unstage(const RawTile<HD, MODE>& R, uint8_t* lds, int r, int q4, Tile<HD, MODE>& T) {
+    stage_write<HD, MODE>(R, lds, r, q4);
+    stage_read<HD, MODE>(R, lds, r, q4, T);
+}
+
+// Staged tiles of 16 KiB (BF16 at head_dim 256) are written to LDS before the
+// next tile's loads are issued: the raw registers of the tile in hand are then
+// free when the next tile's loads take theirs, so one raw tile, not two, is
+// live beside the operands.  Smaller tiles issue the next loads first.
+template <int HD, int MODE>
+constexpr bool attention_late_prefetch() {
+    return Geo<HD, MODE>::NC > 8;
 }
 
 template <int HD, int MODE>
@@ -771,9 +802,11 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
         const LaneOff lo = lane_offsets<HD, MODE>(a, h, r, q4);
         constexpr bool STAGE = attention_staged<HD, MODE>() && !SMALL_BS;
         using InFlight = typename std::conditional<STAGE, RawTile<HD, MODE>, Tile<HD, MODE>>::type;
-        // each wave's own LDS rows for the regrouping of staged tiles
-        __shared__ __attribute__((aligned(16))) uint8_t lds_all[STAGE ? kMaxHeadsPerWg * Geo<HD, MODE>::LDS_TILE : 16];
-        uint8_t* lds = lds_all + (STAGE ? (threadIdx.x >> 6) * Geo<HD, MODE>::LDS_TILE : 0);
+        // each wave's own LDS rows for the regrouping of staged tiles, in
+        // dynamic LDS sized by the launch for the workgroup's waves (a
+        // workgroup of fewer KV heads then leaves room for more workgroups)
+        extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+        uint8_t* lds = lds_dyn + (STAGE ? (threadIdx.x >> 6) * Geo<HD, MODE>::LDS_TILE : 0);
         auto load = [&](int blk, int tau, InFlight& x) {
             if constexpr (STAGE) load_raw<HD, MODE>(a, blk, tau, lo, x);
             else load_tile<HD, MODE, SMALL_BS>(a, bt_row, blk, h, tau, r, q4, lo, x);
@@ -791,6 +824,9 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
         for (int tau = tbeg; tau < tend; tau += D) {
 #pragma unroll
             for (int k = 0; k < D; k += NT) {
+                constexpr bool LATE = STAGE && attention_late_prefetch<HD, MODE>();
+                static_assert(!LATE || NT == 1, "a late prefetch stages one tile per round");
+                if constexpr (LATE) stage_write<HD, MODE>(t[k], lds, r, q4);
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
                     load(nb, min(tau + k + D - NT + n, last), t[(k + D - NT + n) % D]);
@@ -802,7 +838,10 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
                 bool all_ok = true;
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    if constexpr (STAGE) {
+                    if constexpr (LATE) {
+                        stage_read<HD, MODE>(t[k + n], lds, r, q4, staged[n]);
+                        rt[n] = &staged[n];
+                    } else if constexpr (STAGE) {
                         unstage<HD, MODE>(t[k + n], lds, r, q4, staged[n]);
                         rt[n] = &staged[n];
                     } else {
@@ -987,13 +1026,15 @@ constexpr bool attention_packs() {
 
 template <int HD, int MODE, bool QF8>
 void launch_attention_q(const AttnArgs& p, int threads, bool small_bs, hipStream_t st) {
+    // staged tiles: one LDS tile image per wave of the workgroup
+    const unsigned lds = attention_staged<HD, MODE>() ? static_cast<unsigned>(threads / 64) * Geo<HD, MODE>::LDS_TILE : 0u;
     if (small_bs)
         hipLaunchKernelGGL((attention_kernel<HD, MODE, true, QF8, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
     else if (attention_packs<HD, MODE>() && p.group <= 8)
         hipLaunchKernelGGL((attention_kernel<HD, MODE, false, QF8, attention_packs<HD, MODE>()>), dim3(p.total_wg),
-                           dim3(threads), 0, st, p);
+                           dim3(threads), lds, st, p);
     else
-        hipLaunchKernelGGL((attention_kernel<HD, MODE, false, QF8, false>), dim3(p.total_wg), dim3(threads), 0, st, p);
+        hipLaunchKernelGGL((attention_kernel<HD, MODE, false, QF8, false>), dim3(p.total_wg), dim3(threads), lds, st, p);
 }
 
 template <int HD, int MODE>
