@@ -678,6 +678,7 @@ def run_other_workload(args, torch, kvq, W):
         sm = 1.0 / math.sqrt(hd)
         slopes, times = {}, {}
         itl_parity = None
+        ocpu_s, ocpu_b = 0.0, 0           # oracle attention: seconds and algorithmic bytes
         for vname, (full_mode, slide_mode) in variants.items():
             ts = []
             for T in ctxs:
@@ -730,7 +731,10 @@ def run_other_workload(args, torch, kvq, W):
                                      (ring if sliding[l] else full_slots).cpu().numpy(), sc)
                         qb = _bits(torch, q.view(1, H, hd))
                         btn, sln = bt.cpu().numpy(), sl_.cpu().numpy()
+                        c0 = time.perf_counter()
                         ref, absv = oracle.decode_attention(g1, img, 0, qb, btn, sln, sm, with_absv=True)
+                        ocpu_s += time.perf_counter() - c0
+                        ocpu_b += attention_bytes(modes[l], hd, hkv, bs, H, 1, int(sln[0]))
                         tol = oracle.attention_error_bound(g1, img, 0, qb, btn, sln, sm, ref, absv, 1.0)
                         got = o_l.float().cpu().numpy().reshape(ref.shape).astype(np.float64)
                         ok_layers.append(bool((np.abs(got - ref) <= tol).all()))
@@ -743,6 +747,22 @@ def run_other_workload(args, torch, kvq, W):
             slopes[vname] = slope
             times[vname] = [round(t, 5) for t in ts]
             log(f"[bench] itl {vname}: {times[vname]} ms at {ctxs} tokens, slope {slope:.3e} ms/token")
+        # one decode step of the FP8 variant with BF16 sliding layers at the
+        # longest context: 12 full layers of T tokens, 12 rings of W tokens
+        T = ctxs[-1]
+        step_b = 12 * attention_bytes(kvq.FP8_PER_TENSOR, hd, hkv, bs, H, 1, T) + \
+            12 * attention_bytes(kvq.BF16, hd, hkv, bs, H, 1, Wn)
+        ach = step_b / (times["fp8_skip_sliding"][-1] / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": f"attention_kernel + combine_kernel, a step of {L} layers at {T} tokens "
+                                          "(fp8_skip_sliding)",
+                "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
+        cpu = None
+        if ocpu_s > 0:
+            cpu = {"value": round(ocpu_b / ocpu_s / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+                   "kind": "oracle",
+                   "sample": f"fp64 attention of the first sliding and the first full layer at {ctxs[0]} tokens, "
+                             f"each variant, {ocpu_s:.2f} s wall"}
         res = {"metric": "attention-only inter-token latency slope (ms per context token), gpt-oss-20b shape, batch 1",
                "value": round(slopes["fp8_skip_sliding"], 12), "unit": "ms/token", "n_gpus": 1, "steps": args.steps,
                "warmup": args.warmup, "ms_per_step": times["fp8_skip_sliding"][-1], "higher_is_better": False,
@@ -755,7 +775,7 @@ def run_other_workload(args, torch, kvq, W):
                "step_ms": times,
                "pages_h100_full_model_slopes_ms_per_token": {"bf16": 8.94e-06, "fp8": 7.14e-06,
                                                               "fp8_skip_sliding": 6.34e-06},
-               "roofline": None, "cpu_baseline": None, "parity_vs_oracle_sampled": itl_parity}
+               "roofline": roof, "cpu_baseline": cpu, "parity_vs_oracle_sampled": itl_parity}
     elif name == "calib":
         # on-the-fly calibration over the GQA-32 prefill: one amax pass per layer
         spec = W.WORKLOADS["gqa32"]
