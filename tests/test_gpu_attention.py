@@ -160,6 +160,15 @@ def test_attention_kv_heads(kvq, orc, hkv):
          group=2, seed=40 + hkv)
 
 
+@pytest.mark.parametrize("hkv", [1, 8])
+def test_attention_bf16_hd256_staged_tiles(kvq, orc, hkv):
+    """BF16 at head_dim 256: 16 KiB tiles staged through LDS one per wave, with
+    one (a tensor-parallel shard) and eight waves per workgroup; lengths that
+    end inside, at and past whole tiles, several splits."""
+    _run(kvq, orc, f"bf16 hd 256 hkv {hkv}", mode=W.BF16, hd=256, hkv=hkv, bs=16, lens=[3, 16, 50, 300, 515],
+         group=4, seed=60 + hkv)
+
+
 @pytest.mark.parametrize("bs", [1, 2, 4, 8, 32, 128])
 @pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD, W.BF16])
 def test_attention_block_sizes(kvq, orc, mode, bs):
