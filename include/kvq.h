@@ -168,7 +168,10 @@ KVQ_API kvq_status kvq_destroy_cache(kvq_cache* c);
  *                  slot / block_size, position slot % block_size.  A negative
  *                  slot, or one >= the layer's blocks * block_size, is not
  *                  stored (ring buffers of sliding layers use -1 for tokens
- *                  outside the window).  Two tokens with the same slot in one
+ *                  outside the window).  A skipped token's K and V are still
+ *                  read (all loads are issued before any slot is examined):
+ *                  hand a sliding layer only the tokens of its window when
+ *                  most of a call would be skipped.  Two tokens with the same slot in one
  *                  call race (undefined which one lands); the Python
  *                  binding's Cache.check_slots finds them, off this path.
  *   mode           must equal the layer's mode (else KVQ_ERR_MODE_MISMATCH).
