@@ -195,6 +195,27 @@ def query_values(q_bits, q_scales=None) -> np.ndarray:
     return e4m3_decode(codes).astype(np.float64) * s.astype(np.float64)
 
 
+def _token_key_scales(g: Geometry, buf: np.ndarray, layer: int, bt: np.ndarray, lens: np.ndarray) -> np.ndarray:
+    """FP32 K scale of every token-head a gather of a per-token-head layer
+    reads, [sum(lens), hkv] in the gather's order, from the scale trailer of
+    this module's own block layout; 0 for tokens whose block is not in the
+    layer."""
+    lb, _, _ = layer_offsets(g)
+    rb = g.hd // 2 if int(g.modes[layer]) == INT4_PER_TOKEN_HEAD else g.hd
+    code_bytes = g.bs * g.hkv * 2 * rb
+    block_bytes = code_bytes + g.bs * g.hkv * 8
+    out = np.zeros((int(lens.sum()), g.hkv))
+    row = 0
+    for i, n in enumerate(lens):
+        for t in range(int(n)):
+            blk = int(bt[i, t // g.bs])
+            if 0 <= blk < int(g.nblocks[layer]):
+                base = int(lb[layer]) + blk * block_bytes + code_bytes + (t % g.bs) * g.hkv * 8
+                out[row] = buf[base: base + g.hkv * 8].view(np.float32).reshape(g.hkv, 2)[:, 0]
+            row += 1
+    return out
+
+
 def attention_error_bound(g: Geometry, buf: np.ndarray, layer: int, q_bits, block_table, seq_lens,
                           sm_scale: float, ref, absv, static_v_max: float = 1.0, q_scales=None):
     """Per-element bound on |o_kernel - o_exact| for an attention kernel that
@@ -202,13 +223,18 @@ def attention_error_bound(g: Geometry, buf: np.ndarray, layer: int, q_bits, bloc
     softmax weights (times per-token V scales) in the value product and a
     BF16 output:
       (2^-8 + 2.5 eps_S) * sum_t p_t |V^_t| + 2^-8 |o| + (n + 16) 2^-120 max(1, s_V)
-    eps_S = (hd + 4) 2^-24 max_t sum_d |K^_t[d] q[d]| * sm_scale bounds the
-    score error of an FP32 dot product of hd exact products (a score error e
-    moves each weight by a factor within exp(+-2e)); 2^-8 covers the BF16
-    rounding of the weights (2^-9) and of the output (2^-9) plus FP32
-    accumulation and rescaling over fewer than 2^11 tiles; the last term is
-    the FP32 underflow floor (products below 2^-126 may be lost).  ref and
-    absv are this module's decode_attention results for the same inputs."""
+    eps_S = (hd + 4) 2^-24 max_t (sum_d |K^_t[d] q[d]| + b_t) * sm_scale bounds
+    the score error of an FP32 dot product of hd exact products (a score
+    error e moves each weight by a factor within exp(+-2e)).  b_t is 0 except
+    in INT4 layers, whose keys enter the products biased, as n + 8, with the
+    FP32 sum (8 / 16) sum(q) subtracted through the initial accumulator:
+    the biased terms, the subtracted sum and that sum's own rounding add at
+    most 24 s_t sum_d |q[d]| (s_t the token's K scale) to what the rounding
+    acts on.  2^-8 covers the BF16 rounding of the weights (2^-9) and of the
+    output (2^-9) plus FP32 accumulation and rescaling over fewer than 2^11
+    tiles; the last term is the FP32 underflow floor (products below 2^-126
+    may be lost).  ref and absv are this module's decode_attention results
+    for the same inputs."""
     q = _c(q_bits, np.uint16)
     bt = _c(block_table, np.int32)
     lens = np.clip(_c(seq_lens, np.int64), 0, int(bt.shape[1]) * g.bs)
@@ -217,13 +243,18 @@ def attention_error_bound(g: Geometry, buf: np.ndarray, layer: int, q_bits, bloc
     kb, _ = gather(g, buf, layer, bt, lens)
     kabs = np.abs((kb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)) * (1 + 2.0 ** -8)
     qabs = np.abs(query_values(q, q_scales))
+    biased = int(g.modes[layer]) == INT4_PER_TOKEN_HEAD
+    ks = _token_key_scales(g, buf, layer, bt, lens) if biased else None
     eps = np.zeros((q.shape[0], nqh))
     row0 = 0
     for i, n in enumerate(lens):
         if n:
             kk = kabs[row0: row0 + n]
             for qh in range(nqh):
-                eps[i, qh] = (g.hd + 4) * 2.0 ** -24 * (kk[:, qh // group, :] @ qabs[i, qh]).max() * sm_scale
+                dot = kk[:, qh // group, :] @ qabs[i, qh]
+                if biased:
+                    dot = dot + 24.0 * ks[row0: row0 + n, qh // group] * qabs[i, qh].sum()
+                eps[i, qh] = (g.hd + 4) * 2.0 ** -24 * dot.max() * sm_scale
         row0 += int(n)
     floor = (lens.astype(np.float64)[:, None, None] + 16) * 2.0 ** -120 * max(1.0, float(static_v_max))
     return (2.0 ** -8 + 2.5 * eps[:, :, None]) * absv + 2.0 ** -8 * np.abs(ref) + floor

@@ -198,14 +198,22 @@ __device__ __forceinline__ bf16x8 k_operand(const uint32_t* k, int j) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = k[4 * j + e];
     } else if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
-        // elements 2b and 2b+1 are the low and high nibbles of byte b; hi is
-        // w rotated right by 4 (a rotate, so that the byte extracts below are
-        // not folded back into bit-field extracts of w)
-        const uint32_t w = k[j], hi = __builtin_amdgcn_alignbit(w, w, 4);
-        o[0] = pack_bf16(int4_over16<0>(w), int4_over16<0>(hi));
-        o[1] = pack_bf16(int4_over16<1>(w), int4_over16<1>(hi));
-        o[2] = pack_bf16(int4_over16<2>(w), int4_over16<2>(hi));
-        o[3] = pack_bf16(int4_over16<3>(w), int4_over16<3>(hi));
+        // Biased keys: a nibble n (two's complement) XOR 8 is n + 8 in 0..15,
+        // and alone in its byte it is the E4M3 code of (n + 8) 2^-9 (codes
+        // 0x00..0x0F are m 2^-9 exactly: the subnormal step runs on through
+        // the first binade); converted with the scale 2^5 it is (n + 8) / 16,
+        // exact in BF16.  Element 2b is the low nibble of byte b, 2b + 1 the
+        // high one, so the dwords hold elements (0, 2), (4, 6), (1, 3), (5, 7)
+        // of the code dword; the query operand is permuted alike
+        // (int4_query_order) and the bias (8 / 16) sum(q) leaves through the
+        // product's initial accumulator (int4_key_bias).
+        const uint32_t w = k[j];
+        const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;
+        const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 32.0f, false));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 32.0f, true));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 32.0f, false));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 32.0f, true));
     } else {
         o[0] = fp8x2_to_bf16x2<false>(k[2 * j]);
         o[1] = fp8x2_to_bf16x2<true>(k[2 * j]);
@@ -561,8 +569,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // operands hold the same contiguous slice of dims in every lane, so the
 // hardware's order of k within a lane does not matter.
 template <int HD, int MODE, bool QF8>
-__device__ __forceinline__ f32x4 qk_product(const uint32_t* k, const QOperand<HD, QF8>& q) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+__device__ __forceinline__ f32x4 qk_product(const uint32_t* k, const QOperand<HD, QF8>& q, f32x4 acc) {
     if constexpr (!QF8) {
 #pragma unroll
         for (int j = 0; j < HD / 32; ++j)
@@ -590,18 +597,44 @@ __device__ __forceinline__ f32x4 qk_product(const uint32_t* k, const QOperand<HD
     return acc;
 }
 
+// The BF16 query slice in the order of the biased INT4 key operand: each k
+// step's elements (0, 1, ..., 7) become (0, 2, 4, 6, 1, 3, 5, 7).
+template <int HD>
+__device__ __forceinline__ void int4_query_order(QOperand<HD, false>& q) {
+#pragma unroll
+    for (int j = 0; j < HD / 32; ++j) {
+        const u32x4 w = __builtin_bit_cast(u32x4, q.b[j]);
+        const u32x4 o = {__builtin_amdgcn_perm(w[1], w[0], 0x05040100u), __builtin_amdgcn_perm(w[3], w[2], 0x05040100u),
+                         __builtin_amdgcn_perm(w[1], w[0], 0x07060302u), __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)};
+        q.b[j] = __builtin_bit_cast(bf16x8, o);
+    }
+}
+
+// Minus the bias of the biased INT4 keys, (8 / 16) sum(q) for each query
+// column, through the same products with every key element 1/2: the initial
+// accumulator of each tile's Q K^T product.
+template <int HD>
+__device__ __forceinline__ f32x4 int4_key_bias(const QOperand<HD, false>& q) {
+    const u32x4 halves = {0x3F003F00u, 0x3F003F00u, 0x3F003F00u, 0x3F003F00u};   // BF16 0.5
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < HD / 32; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, halves), q.b[j], acc, 0, 0, 0);
+    return -acc;
+}
+
 // One round of the online softmax over NT consecutive tiles (16 NT tokens):
 // the tiles' Q K^T products, one running-maximum update, then their P V
 // products.  MASK = false is the path of rounds whose tokens all lie below
 // len in blocks of the layer (a wave-uniform fact).
 template <int HD, int MODE, int NT, bool MASK, bool QF8, bool PACK>
 __device__ __forceinline__ void tile_round(const Tile<HD, MODE>* const* T, State<HD, MODE>& st,
-                                           const QOperand<HD, QF8>& qo, int t0, int len, int r, int q4,
-                                           float k_factor, uint32_t vsh) {
+                                           const QOperand<HD, QF8>& qo, f32x4 qk_init, int t0, int len, int r,
+                                           int q4, float k_factor, uint32_t vsh) {
     using G = Geo<HD, MODE>;
     f32x4 sacc[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) sacc[n] = qk_product<HD, MODE, QF8>(T[n]->k, qo);
+    for (int n = 0; n < NT; ++n) sacc[n] = qk_product<HD, MODE, QF8>(T[n]->k, qo, qk_init);
 
     bool valid[NT][4];
 #pragma unroll
@@ -760,6 +793,13 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
         }
     }
 
+    // biased INT4 keys: the query in their element order, and the bias out
+    f32x4 qk_init = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD && !QF8) {
+        int4_query_order<HD>(qo);
+        qk_init = int4_key_bias<HD>(qo);
+    }
+
     // INT4 operands are n / 16 (v_cvt_off_f32_i4): the factor 16 is applied
     // once to the scores' factor and once to the output, never per token
     float k_factor = a.c * G::CODE_UNIT * q_factor;
@@ -851,9 +891,9 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
                 }
                 const int t0 = (tau + k) * kTile;
                 if (attention_fast_path<HD>() && !SMALL_BS && t0 + NT * kTile <= lim && all_ok)
-                    tile_round<HD, MODE, NT, false, QF8, PACK>(rt, st, qo, t0, lim, r, q4, k_factor, lo.vsh);
+                    tile_round<HD, MODE, NT, false, QF8, PACK>(rt, st, qo, qk_init, t0, lim, r, q4, k_factor, lo.vsh);
                 else
-                    tile_round<HD, MODE, NT, true, QF8, PACK>(rt, st, qo, t0, lim, r, q4, k_factor, lo.vsh);
+                    tile_round<HD, MODE, NT, true, QF8, PACK>(rt, st, qo, qk_init, t0, lim, r, q4, k_factor, lo.vsh);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }

@@ -77,6 +77,21 @@ def test_attention_special_cases(orc):
     assert np.array_equal(out2, out) and (absv >= np.abs(out) - 1e-12).all()
 
 
+@pytest.mark.parametrize("mode,qmax", [(W.INT4_PER_TOKEN_HEAD, 7.0), (W.FP8_PER_TOKEN_HEAD, 448.0)])
+def test_bound_reads_each_tokens_key_scale(orc, mode, qmax):
+    """The error bound's INT4 term takes every token's K scale from the cache
+    image; read back through the block table they are RN32(absmax / qmax) of
+    the stored rows, computed here with numpy float32 division."""
+    g, buf, st = _setup(orc, mode)
+    lens = np.array(st.seq_lens)
+    slots_k, _ = W.gqa_kv(int(lens.sum()), 2, 64, seed=1)
+    amax = slots_k.float().abs().amax(dim=2).numpy().astype(np.float32)
+    want = (amax / np.float32(qmax)).astype(np.float64)
+    got = orc._token_key_scales(g, buf, 0, st.block_table.numpy(), lens)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+
+
 def test_attention_skips_blocks_outside_the_layer(orc):
     """Tokens whose block-table entry is negative or past the layer's block
     count take no part; the rest is softmax attention over what remains."""
