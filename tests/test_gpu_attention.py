@@ -277,17 +277,20 @@ def test_attention_workspace_reuse_and_sizes(kvq, orc):
         sc.close()
 
 
-def test_attention_decode_workload_sampled(kvq, orc):
+@pytest.mark.parametrize("mode,hd", [(W.FP8_PER_TOKEN_HEAD, 128), (W.INT4_PER_TOKEN_HEAD, 128),
+                                     (W.INT4_PER_TOKEN_HEAD, 64)],
+                         ids=["fp8_per_token_head-128", "int4_per_token_head-128", "int4_per_token_head-64"])
+def test_attention_decode_workload_sampled(kvq, orc, mode, hd):
     """Full decode shape: 256 sequences of 8192-8207 cached tokens, 8 KV heads,
-    32 query heads, head_dim 128, per-token-head FP8, in the launch
-    configuration the benchmark times; eight sampled sequences against the
-    oracle."""
-    _flush("[attention] decode 256 x 8192 fp8_per_token_head (sampled)")
+    32 query heads, per-token-head FP8 at head_dim 128 and INT4 at 128 and 64,
+    in the launch configuration the benchmark times; eight sampled sequences
+    against the oracle."""
+    _flush(f"[attention] decode 256 x 8192 {W.MODE_NAMES[mode]} hd {hd} (sampled)")
     g = torch.Generator().manual_seed(11)
     lens = (8192 + torch.randint(0, 16, (256,), generator=g)).tolist()
     n = sum(lens)
-    k, v = (t.cpu() for t in W.normal_kv(n, 8, 128, seed=12, device=DEV))
-    sc = Scenario(kvq, orc, mode=W.FP8_PER_TOKEN_HEAD, hd=128, hkv=8, bs=16, lens=lens, group=4, seed=13,
+    k, v = (t.cpu() for t in W.normal_kv(n, 8, hd, seed=12, device=DEV))
+    sc = Scenario(kvq, orc, mode=mode, hd=hd, hkv=8, bs=16, lens=lens, group=4, seed=13,
                   extra_blocks=0, kv=(k, v))
     del k, v
     try:
