@@ -85,6 +85,31 @@ def build_hw_checks(verbose: bool = False) -> str:
     return HW_CHECK_LIB
 
 
+C_DEVICE_SRC = os.path.join(ROOT, "tests", "c_api", "device_roundtrip.c")
+C_DEVICE_EXE = os.path.join(ROOT, "tests", "c_api", "_build", "device_roundtrip")
+
+
+def build_c_tests(verbose: bool = False) -> str:
+    """The plain C99 GPU test program (HIP runtime C API + the library's C ABI),
+    compiled by gcc; it finds libkvq.so relative to itself."""
+    os.makedirs(os.path.dirname(C_DEVICE_EXE), exist_ok=True)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = C_DEVICE_EXE + ".tmp"
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", os.path.join(rocm, "include"), C_DEVICE_SRC,
+           "-L", BUILD_DIR, "-lkvq", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../../quantized_fp8_int4_amd/_build", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}",
+           "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on {C_DEVICE_SRC}:\n{r.stderr}")
+    os.replace(tmp, C_DEVICE_EXE)
+    return C_DEVICE_EXE
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
     print(build_hw_checks(verbose="-v" in sys.argv))
+    print(build_c_tests(verbose="-v" in sys.argv))
