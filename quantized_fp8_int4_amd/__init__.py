@@ -201,6 +201,8 @@ def kvq_gather_dequant(handle, layer: int, block_table: torch.Tensor, seq_lens: 
     sl = _dev(seq_lens, torch.int32, "seq_lens")
     ok = _dev(out_keys, torch.bfloat16, "out_keys")
     ov = _dev(out_values, torch.bfloat16, "out_values")
+    if out_keys.shape != out_values.shape:
+        raise ValueError("out_keys and out_values must have the same shape")
     if block_table.dim() != 2 or block_table.shape[0] != num_seqs:
         raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
     _check(_lib.kvq_gather_dequant(handle, int(layer), ctypes.c_void_p(bt), int(block_table.shape[1]),
@@ -396,7 +398,18 @@ class Cache:
         except Exception:
             pass
 
+    def _rows(self, name, t, first=None):
+        # the C ABI cannot see a device buffer's size: shapes are checked here,
+        # before any launch, so a wrong one never reaches a kernel
+        want = (self.cfg.num_kv_heads, self.cfg.head_dim)
+        if t.dim() != 3 or tuple(t.shape[1:]) != want or (first is not None and t.shape[0] != first):
+            lead = "N" if first is None else str(first)
+            raise ValueError(f"{name} must be [{lead}, {want[0]}, {want[1]}], got {tuple(t.shape)}")
+
     def store(self, layer, keys, values, slot_mapping, scales=None, stream=None):
+        n = int(slot_mapping.numel())
+        self._rows("keys", keys, n)
+        self._rows("values", values, n)
         kvq_store(self.handle, layer, keys, values, slot_mapping, self.cfg.layer_modes[layer], scales, stream)
 
     def check_slots(self, layer, slot_mapping) -> int:
@@ -413,8 +426,13 @@ class Cache:
 
     def gather_dequant(self, layer, block_table, seq_lens, total_tokens=None, out=None, stream=None):
         """Returns (keys, values) bf16 [sum(seq_lens), Hkv, hd].  Pass
-        total_tokens (or out) to avoid reading seq_lens back to the host."""
-        if out is None:
+        total_tokens (or out) to avoid reading seq_lens back to the host; it
+        must be at least the sum of the positive seq_lens, since the kernel
+        writes that many rows."""
+        if out is not None:
+            self._rows("out[0]", out[0])
+            self._rows("out[1]", out[1], int(out[0].shape[0]))
+        else:
             if total_tokens is None:
                 total_tokens = int(seq_lens.clamp(min=0).sum().item())
             shape = (int(total_tokens), self.cfg.num_kv_heads, self.cfg.head_dim)
@@ -428,6 +446,9 @@ class Cache:
         """Fused decode attention over one layer; returns bf16 [num_seqs, H, hd].
         Allocates the workspace with torch when none is given.  q_scales
         (float32 [H] on the device) selects FP8 queries."""
+        if q.dim() != 3 or q.shape[2] != self.cfg.head_dim or q.shape[1] % self.cfg.num_kv_heads:
+            raise ValueError(f"q must be [num_seqs, H, {self.cfg.head_dim}] with H a multiple of "
+                             f"{self.cfg.num_kv_heads}, got {tuple(q.shape)}")
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:

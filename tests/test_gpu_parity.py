@@ -377,6 +377,36 @@ def test_long80_layer_full_size(kvq, orc):
     pair.cache.close()
 
 
+def test_binding_rejects_wrong_shapes(kvq):
+    """The C ABI cannot see a device buffer's size, so the binding checks every
+    shape it knows against the cache geometry and raises before any launch."""
+    _flush("[binding shapes]")
+    cache = kvq.Cache(kvq.CacheConfig(16, 2, 64, [W.FP8_PER_TOKEN_HEAD], [4]), device=DEV)
+    try:
+        bf = dict(dtype=torch.bfloat16, device=DEV)
+        slots = torch.arange(10, dtype=torch.int64, device=DEV)
+        good = torch.zeros((10, 2, 64), **bf)
+        for k, v, sl in ((torch.zeros((10, 4, 64), **bf), good, slots),        # wrong KV heads
+                         (torch.zeros((10, 2, 128), **bf), good, slots),       # wrong head_dim
+                         (good, torch.zeros((9, 2, 64), **bf), slots),         # values short
+                         (good, good, slots[:8]),                              # slot count
+                         (good.view(10, 128), good, slots)):                   # flattened rows
+            with pytest.raises(ValueError):
+                cache.store(0, k, v, sl)
+        bt = torch.zeros((1, 4), dtype=torch.int32, device=DEV)
+        sl = torch.tensor([10], dtype=torch.int32, device=DEV)
+        with pytest.raises(ValueError):
+            cache.gather_dequant(0, bt, sl, out=(torch.zeros((10, 2, 32), **bf), torch.zeros((10, 2, 32), **bf)))
+        with pytest.raises(ValueError):
+            cache.gather_dequant(0, bt, sl, out=(good, torch.zeros((8, 2, 64), **bf)))
+        for q in (torch.zeros((1, 3, 64), **bf), torch.zeros((1, 4, 128), **bf)):
+            with pytest.raises(ValueError):
+                cache.decode_attention(0, q, bt, sl, 0.125)
+        torch.cuda.synchronize()
+    finally:
+        cache.close()
+
+
 def test_edge_cases(kvq, orc):
     """Zero tokens, zero sequences, a layer with no blocks, tokens beyond the
     block table, and repeated stores of the same tokens."""
