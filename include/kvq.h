@@ -209,6 +209,9 @@ KVQ_API kvq_status kvq_store(kvq_cache* c, int32_t layer, const void* keys, cons
  *                       t % block_size.
  *   A block-table entry outside [0, layer blocks) leaves its tokens' output
  *   rows unwritten, as do tokens beyond max_blocks_per_seq * block_size.
+ *   out_keys and out_values must be non-null whenever num_seqs > 0, also when
+ *   every length is 0 (the library cannot read seq_lens on the host); a
+ *   caller that knows the total is 0 may skip the call.
  *   A static-scale layer must have been stored to at least once.
  *   num_seqs == 0 is a no-op returning KVQ_OK.
  *   Errors: KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED (block bytes not a

@@ -203,6 +203,10 @@ def kvq_gather_dequant(handle, layer: int, block_table: torch.Tensor, seq_lens: 
     ov = _dev(out_values, torch.bfloat16, "out_values")
     if out_keys.shape != out_values.shape:
         raise ValueError("out_keys and out_values must have the same shape")
+    if out_keys.numel() == 0:
+        # outputs of zero rows: every sequence is empty, there is nothing to
+        # write (and an empty tensor has no device address to pass)
+        return
     if block_table.dim() != 2 or block_table.shape[0] != num_seqs:
         raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
     _check(_lib.kvq_gather_dequant(handle, int(layer), ctypes.c_void_p(bt), int(block_table.shape[1]),

@@ -126,6 +126,55 @@ def test_store_gather_parity_small(kvq, orc, mode, hd, hkv):
     pair.cache.close()
 
 
+def _random_geometry(seed):
+    rng = np.random.default_rng(9000 + seed)
+    bs = int(rng.choice([1, 2, 4, 32, 64, 128, 1024]))
+    hkv = int(rng.choice([1, 2, 3, 5, 8, 16]))
+    hd = int(rng.choice([64, 128, 256]))
+    mode = int(rng.choice(MODES))
+    if bs * hkv % 2 and mode in (W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD):
+        hkv += 1                      # such a block's scale trailer is not 16-byte sized
+    slots_total = max(64, int(rng.integers(64, 2048)) // bs * bs)
+    nblocks = max(1, slots_total // bs)
+    return rng, bs, hkv, hd, mode, nblocks
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_store_gather_random_geometries(kvq, orc, seed):
+    """Seeded random geometries beyond the fixed cases: block sizes 1 to 1024,
+    1 to 16 KV heads, every mode and head_dim, slots permuted with skipped and
+    out-of-range entries, block tables with entries outside the layer, ragged
+    lengths; every cache byte and gathered value against the oracle."""
+    rng, bs, hkv, hd, mode, nblocks = _random_geometry(seed)
+    nslots = nblocks * bs
+    n = int(rng.integers(1, min(nslots, 300) + 1))
+    _flush(f"[random {seed}] mode={W.MODE_NAMES[mode]} bs={bs} hkv={hkv} hd={hd} blocks={nblocks} tokens={n}")
+    pair = Pair(kvq, orc, bs, hkv, hd, [mode], [nblocks])
+    try:
+        k, v = _adversarial_kv(n, hkv, hd, seed=int(rng.integers(1 << 30)))
+        slots = rng.permutation(nslots)[:n].astype(np.int64)
+        drop = rng.random(n) < 0.05
+        slots[drop] = -1
+        far = rng.random(n) < 0.03
+        slots[far] = nslots + rng.integers(0, 50, int(far.sum()))
+        scales = None
+        if mode == W.FP8_PER_TENSOR:
+            scales = [float(rng.uniform(0.005, 0.05)), float(rng.uniform(0.005, 0.05))]
+        elif mode == W.FP8_PER_HEAD:
+            scales = list(rng.uniform(0.001, 0.05, 2 * hkv).astype(np.float32))
+        pair.store(0, k, v, torch.from_numpy(slots), scales)
+        pair.assert_buffers_equal()
+        nseq = int(rng.integers(1, 5))
+        maxb = int(rng.integers(1, min(nblocks, 12) + 1))
+        bt = rng.integers(0, nblocks, (nseq, maxb)).astype(np.int32)
+        bad = rng.random((nseq, maxb)) < 0.1
+        bt[bad] = rng.choice([-1, nblocks, nblocks + 7])
+        lens = [int(rng.integers(0, maxb * bs + 1)) for _ in range(nseq)]
+        pair.gather_and_compare(0, bt, lens)
+    finally:
+        pair.cache.close()
+
+
 def _exhaustive_rows(start, stride, seed):
     """Rows of 64 BF16 values: element 0 is a positive absmax a (every
     stride-th finite BF16 magnitude from start), the others enumerate every
