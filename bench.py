@@ -299,8 +299,11 @@ def setup(args, torch, kvq, W):
         if mode == kvq.FP8_PER_TENSOR:
             scales.append([1.0, 1.0])
         elif mode == kvq.FP8_PER_HEAD:
+            # calibrated on a separate draw by the library's own calibration
             kc, vc = W.gqa_kv(4096, hkv, hd, seed=2000 + layer, device=dev)
-            scales.append(W.static_scales_from_amax(W.calibration_amax(kc, vc)).tolist())
+            amax = torch.zeros(2 * hkv, dtype=torch.float32, device=dev)
+            kvq.kvq_calibrate_amax(kc, vc, amax)
+            scales.append(kvq.kvq_static_scales(amax, hkv, mode))
         else:
             scales.append(None)
     torch.cuda.synchronize()
@@ -389,7 +392,7 @@ class Launcher:
     def gather_args(self, layer, bt, sl, ok, ov):
         ct = self.ct
         return (self.h, layer, ct.c_void_p(bt.data_ptr()), int(bt.shape[1]), ct.c_void_p(sl.data_ptr()),
-                int(sl.numel()), ct.c_void_p(ok.data_ptr()), ct.c_void_p(ov.data_ptr()), self.stream)
+                int(sl.numel()), ct.c_void_p(ok.data_ptr()), ct.c_void_p(ov.data_ptr()), int(ok.shape[0]), self.stream)
 
     def store(self, a):
         st = self.lib.kvq_store(*a)
@@ -1042,7 +1045,7 @@ def main():
                            P(S["slots"].data_ptr()), S["n"], S["mode"], csc, stream))
         gather_args.append((handle, layer, P(S["bt_d"].data_ptr()), S["bt_d"].shape[1],
                             P(S["seq_lens"].data_ptr()), S["nseq"], P(S["outs"][layer][0].data_ptr()),
-                            P(S["outs"][layer][1].data_ptr()), stream))
+                            P(S["outs"][layer][1].data_ptr()), int(S["outs"][layer][0].shape[0]), stream))
 
     def step(ev=None):
         if ev is not None:

@@ -119,7 +119,8 @@ typedef struct kvq_cache kvq_cache;
  * "Layer skipping follows retained-token footprint".
  *   cfg  host, read only.  out: host, written on success.
  *   Errors: KVQ_ERR_INVALID_ARG (null pointer, bad value),
- *           KVQ_ERR_UNSUPPORTED (head_dim or block_size not supported).
+ *           KVQ_ERR_UNSUPPORTED (head_dim or block_size not supported, or
+ *           a layer whose block, codes and scales, is 2 GiB or more).
  *
  * Layout of the buffer: layers in order, each starting on a 256-byte
  * boundary; layer l is layer_num_blocks[l] blocks, each block
@@ -202,18 +203,24 @@ KVQ_API kvq_status kvq_store(kvq_cache* c, int32_t layer, const void* keys, cons
  *   seq_lens            device, int32 [num_seqs]: tokens of each sequence
  *                       (negative counts as 0); must not exceed
  *                       max_blocks_per_seq * block_size.
- *   out_keys, out_values device, BF16 [sum(seq_lens)][num_kv_heads][head_dim],
+ *   out_keys, out_values device, BF16 [out_rows][num_kv_heads][head_dim],
  *                       16-byte aligned; sequence b starts at row
- *                       sum(seq_lens[0..b)).  Token t of sequence b comes from
- *                       block block_table[b][t / block_size], position
+ *                       sum(seq_lens[0..b)) (positive lengths only).  Token t
+ *                       of sequence b comes from block
+ *                       block_table[b][t / block_size], position
  *                       t % block_size.
+ *   out_rows            rows (tokens) that out_keys and out_values each hold,
+ *                       >= 0.  A token whose output row is out_rows or beyond
+ *                       is not written, so an output shorter than
+ *                       sum(seq_lens) is never overrun; size it to the sum
+ *                       to receive every token.  out_keys and out_values may
+ *                       be NULL only when out_rows is 0 (nothing is written
+ *                       then).
  *   A block-table entry outside [0, layer blocks) leaves its tokens' output
  *   rows unwritten, as do tokens beyond max_blocks_per_seq * block_size.
- *   out_keys and out_values must be non-null whenever num_seqs > 0, also when
- *   every length is 0 (the library cannot read seq_lens on the host); a
- *   caller that knows the total is 0 may skip the call.
  *   A static-scale layer must have been stored to at least once.
- *   num_seqs == 0 is a no-op returning KVQ_OK.
+ *   num_seqs == 0 or out_rows == 0 is a no-op returning KVQ_OK (after the
+ *   argument checks).
  *   Errors: KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED (block bytes not a
  *           multiple of 16, i.e. an odd block_size * num_kv_heads with a
  *           per-token-head mode), KVQ_ERR_HIP.
@@ -221,7 +228,7 @@ KVQ_API kvq_status kvq_store(kvq_cache* c, int32_t layer, const void* keys, cons
 KVQ_API kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const int32_t* block_table,
                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
                               int32_t num_seqs, void* out_keys, void* out_values,
-                              void* stream);
+                              int64_t out_rows, void* stream);
 
 /*
  * kvq_calibrate_amax -- on-the-fly calibration for the static layouts: the

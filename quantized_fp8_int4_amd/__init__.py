@@ -79,7 +79,7 @@ def _load_library():
     lib.kvq_create_cache.argtypes = [ctypes.POINTER(_Config), P, ctypes.c_uint64, ctypes.POINTER(P)]
     lib.kvq_destroy_cache.argtypes = [P]
     lib.kvq_store.argtypes = [P, I32, P, P, P, I64, ctypes.c_int, P, P]
-    lib.kvq_gather_dequant.argtypes = [P, I32, P, I32, P, I32, P, P, P]
+    lib.kvq_gather_dequant.argtypes = [P, I32, P, I32, P, I32, P, P, I64, P]
     lib.kvq_calibrate_amax.argtypes = [P, P, I64, I32, I32, P, I32, P]
     lib.kvq_static_scales.argtypes = [P, I32, ctypes.c_int, P]
     lib.kvq_decode_attention_workspace.argtypes = [P, I32, I32, I32, ctypes.POINTER(ctypes.c_uint64)]
@@ -193,24 +193,24 @@ def kvq_store(handle, layer: int, keys: torch.Tensor, values: torch.Tensor, slot
 def kvq_gather_dequant(handle, layer: int, block_table: torch.Tensor, seq_lens: torch.Tensor,
                        out_keys: torch.Tensor, out_values: torch.Tensor, stream=None) -> None:
     """block_table: int32 [num_seqs, max_blocks] on the device; seq_lens: int32
-    [num_seqs] on the device; out_*: bf16 [sum(seq_lens), Hkv, hd] on the device."""
+    [num_seqs] on the device; out_*: bf16 [rows, Hkv, hd] on the device.  The
+    library writes at most `rows` token rows (out_keys.shape[0]): tokens past
+    them are dropped, never written out of bounds."""
     num_seqs = int(seq_lens.numel())
     if num_seqs == 0:
         return
+    if out_keys.dim() != 3 or out_keys.shape != out_values.shape:
+        raise ValueError("out_keys and out_values must both be [rows, num_kv_heads, head_dim]")
+    rows = int(out_keys.shape[0])
     bt = _dev(block_table, torch.int32, "block_table")
     sl = _dev(seq_lens, torch.int32, "seq_lens")
-    ok = _dev(out_keys, torch.bfloat16, "out_keys")
-    ov = _dev(out_values, torch.bfloat16, "out_values")
-    if out_keys.shape != out_values.shape:
-        raise ValueError("out_keys and out_values must have the same shape")
-    if out_keys.numel() == 0:
-        # outputs of zero rows: every sequence is empty, there is nothing to
-        # write (and an empty tensor has no device address to pass)
-        return
+    # an output of zero rows has no device address to pass (and gets no writes)
+    ok = _dev(out_keys, torch.bfloat16, "out_keys") if rows else 0
+    ov = _dev(out_values, torch.bfloat16, "out_values") if rows else 0
     if block_table.dim() != 2 or block_table.shape[0] != num_seqs:
         raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
     _check(_lib.kvq_gather_dequant(handle, int(layer), ctypes.c_void_p(bt), int(block_table.shape[1]),
-                                   ctypes.c_void_p(sl), num_seqs, ctypes.c_void_p(ok), ctypes.c_void_p(ov),
+                                   ctypes.c_void_p(sl), num_seqs, ctypes.c_void_p(ok), ctypes.c_void_p(ov), rows,
                                    _stream_ptr(stream, out_keys.device)), "kvq_gather_dequant")
 
 
@@ -430,12 +430,19 @@ class Cache:
 
     def gather_dequant(self, layer, block_table, seq_lens, total_tokens=None, out=None, stream=None):
         """Returns (keys, values) bf16 [sum(seq_lens), Hkv, hd].  Pass
-        total_tokens (or out) to avoid reading seq_lens back to the host; it
-        must be at least the sum of the positive seq_lens, since the kernel
-        writes that many rows."""
+        total_tokens (or out) to avoid reading seq_lens back to the host.  The
+        kernel writes at most as many token rows as the output holds; an out
+        shorter than total_tokens, or one of zero rows without total_tokens=0
+        (which states that every sequence is empty), is refused here, since
+        it would silently drop tokens."""
         if out is not None:
             self._rows("out[0]", out[0])
             self._rows("out[1]", out[1], int(out[0].shape[0]))
+            rows = int(out[0].shape[0])
+            if total_tokens is not None and rows < int(total_tokens):
+                raise ValueError(f"out holds {rows} rows, fewer than total_tokens={int(total_tokens)}")
+            if rows == 0 and total_tokens is None and int(seq_lens.numel()) > 0:
+                raise ValueError("out holds no rows: pass total_tokens=0 if every sequence is empty")
         else:
             if total_tokens is None:
                 total_tokens = int(seq_lens.clamp(min=0).sum().item())

@@ -154,11 +154,13 @@ kvq_status kvq_store(kvq_cache* c, int32_t layer, const void* keys, const void* 
 
 kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const int32_t* block_table,
                               int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
-                              void* out_keys, void* out_values, void* stream) {
+                              void* out_keys, void* out_values, int64_t out_rows, void* stream) {
     if (!c || layer < 0 || layer >= c->layout.num_layers || num_seqs < 0) return KVQ_ERR_INVALID_ARG;
     if (num_seqs == 0) return KVQ_OK;
-    if (max_blocks_per_seq < 1 || !block_table || !seq_lens || !out_keys || !out_values)
-        return KVQ_ERR_INVALID_ARG;
+    // out_rows beyond 2^46 rows (at least 8 PiB of output) cannot be a real buffer
+    if (out_rows < 0 || out_rows > (int64_t{1} << 46)) return KVQ_ERR_INVALID_ARG;
+    if (max_blocks_per_seq < 1 || !block_table || !seq_lens) return KVQ_ERR_INVALID_ARG;
+    if (out_rows > 0 && (!out_keys || !out_values)) return KVQ_ERR_INVALID_ARG;
     if (!aligned16(out_keys) || !aligned16(out_values)) return KVQ_ERR_INVALID_ARG;
     const kvq::Layout& L = c->layout;
     const int32_t lmode = L.mode[layer];
@@ -172,6 +174,7 @@ kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const int32_t* 
     a.seq_lens = seq_lens;
     a.out_keys = out_keys;
     a.out_values = out_values;
+    a.out_rows = out_rows;
     a.num_blocks = L.num_blocks[layer];
     a.block_bytes = L.block_bytes[layer];
     a.code_bytes = L.code_bytes[layer];
@@ -182,7 +185,7 @@ kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const int32_t* 
     a.head_dim = L.head_dim;
     a.mode = lmode;
     if (kvq::gather_grid(a) >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
-    if (L.num_blocks[layer] == 0) return KVQ_OK;
+    if (L.num_blocks[layer] == 0 || out_rows == 0) return KVQ_OK;
     if (log_enabled())
         std::fprintf(stderr, "[kvq] gather layer=%d mode=%s hd=%d seqs=%d max_blocks=%d\n", layer,
                      mode_name(lmode), L.head_dim, num_seqs, max_blocks_per_seq);

@@ -69,6 +69,7 @@ struct GatherLaunch {
     const int32_t* seq_lens;
     void* out_keys;
     void* out_values;
+    int64_t out_rows;              // token rows each output holds; rows past it are not written
     int64_t num_blocks;
     uint64_t block_bytes;
     uint64_t code_bytes;

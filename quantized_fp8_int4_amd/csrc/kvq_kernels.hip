@@ -238,6 +238,7 @@ struct GatherArgs {
     const int32_t* __restrict__ seq_lens;
     uint16_t* __restrict__ out_k;
     uint16_t* __restrict__ out_v;
+    int64_t out_th;           // token-head rows each output holds (out_rows * hkv)
     int64_t num_blocks;
     uint64_t block_bytes;
     uint32_t code_bytes;
@@ -383,6 +384,8 @@ __global__ __launch_bounds__(TPB) void gather_kernel(GatherArgs p) {
         off += (lane + 64u * k < b) ? max(lens[k], 0) : 0;
     off = wave_sum(off);
     const int64_t out_row0 = (off + t0) * p.hkv;
+    // Token-head rows of this block that still fit the output (may be <= 0).
+    const int64_t room = p.out_th - out_row0;
 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -429,9 +432,11 @@ __global__ __launch_bounds__(TPB) void gather_kernel(GatherArgs p) {
                 o[2 * d + 1] = pack_bf16(hi[0] * s, hi[1] * s);
             }
         }
+        if (static_cast<int64_t>(row >> 1) < room) {
 #pragma unroll
-        for (int q = 0; q < ODW / 4; ++q)
-            st16<NTS>(outp + 8 * q, make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]));
+            for (int q = 0; q < ODW / 4; ++q)
+                st16<NTS>(outp + 8 * q, make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]));
+        }
     }
 }
 
@@ -505,6 +510,7 @@ GatherArgs make_gather_args(const GatherLaunch& a) {
     p.seq_lens = a.seq_lens;
     p.out_k = static_cast<uint16_t*>(a.out_keys);
     p.out_v = static_cast<uint16_t*>(a.out_values);
+    p.out_th = a.out_rows * a.num_kv_heads;
     p.num_blocks = a.num_blocks;
     p.block_bytes = a.block_bytes;
     p.code_bytes = static_cast<uint32_t>(a.code_bytes);

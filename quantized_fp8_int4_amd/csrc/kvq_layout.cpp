@@ -75,6 +75,8 @@ kvq_status build_layout(const kvq_cache_config* cfg, Layout* out) {
             return KVQ_ERR_UNSUPPORTED;
         const uint64_t code = bs * hkv * 2 * row_bytes(m, cfg->head_dim);
         const uint64_t trailer = has_token_scales(m) ? bs * hkv * 2 * 4 : 0;
+        // the kernels address a block's bytes with 32-bit offsets
+        if (code + trailer >= (uint64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
         off = align_up(off, kLayerAlign);
         L.mode.push_back(m);
         L.num_blocks.push_back(nb);

@@ -115,7 +115,7 @@ int main(void) {
         HIP_OK(hipMemcpy(dv, hv, sizeof hv, hipMemcpyHostToDevice));
         if (kvq_store(cache, layer, dk, dv, (const int64_t*)dslots, NTOK, (kvq_mode)modes[layer], NULL, NULL) != KVQ_OK ||
             kvq_gather_dequant(cache, layer, (const int32_t*)dtable, NBLK, (const int32_t*)dlen, 1, dok, dov,
-                               NULL) != KVQ_OK) {
+                               NTOK, NULL) != KVQ_OK) {
             fprintf(stderr, "store/gather of layer %d\n", layer);
             return 1;
         }

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import workloads as W
+from tests import _calib as C
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -61,11 +62,7 @@ class Scenario:
         k, v = kv if kv is not None else W.gqa_kv(n, hkv, hd, seed=seed + 1)
         self.scales = None
         if mode in (W.FP8_PER_TENSOR, W.FP8_PER_HEAD):
-            per_head = W.static_scales_from_amax(W.calibration_amax(k, v))
-            if mode == W.FP8_PER_TENSOR:
-                amax = W.calibration_amax(k, v).amax(dim=1, keepdim=True)
-                per_head = W.static_scales_from_amax(amax)
-            self.scales = per_head.numpy().astype(np.float32)
+            self.scales = C.oracle_static_scales(orc, k, v, mode)
         if n:
             orc.store(self.g, self.img, 0, _bits(k), _bits(v), np.array(slots, np.int64), self.scales)
         elif self.scales is not None:

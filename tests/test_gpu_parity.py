@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import workloads as W
+from tests import _calib as C
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -38,9 +39,13 @@ class Pair:
         self.host = orc.new_cache(self.g)
         assert self.host.size == self.cache.bytes["total"]
 
-    def store(self, layer, k, v, slots, scales=None):
+    def store(self, layer, k, v, slots, scales=None, orc_scales=None):
+        """Store on both sides; orc_scales (default: scales) are the oracle's
+        own static scales where each side derives them itself."""
         self.cache.store(layer, k.to(DEV), v.to(DEV), slots.to(DEV), scales)
-        sc = None if scales is None else np.asarray(scales, np.float32)
+        if orc_scales is None:
+            orc_scales = scales
+        sc = None if orc_scales is None else np.asarray(orc_scales, np.float32)
         self.orc.store(self.g, self.host, layer, _bits(k), _bits(v), slots.cpu().numpy(), sc)
 
     def assert_buffers_equal(self):
@@ -58,7 +63,7 @@ class Pair:
                torch.zeros(shape, dtype=torch.bfloat16, device=DEV))
         bt = torch.as_tensor(np.asarray(block_table), dtype=torch.int32).to(DEV)
         sl = torch.as_tensor(np.asarray(seq_lens), dtype=torch.int32).to(DEV)
-        self.cache.gather_dequant(layer, bt, sl, out=out)
+        self.cache.gather_dequant(layer, bt, sl, total_tokens=total, out=out)
         ko, vo = self.orc.gather(self.g, self.host, layer, np.asarray(block_table), np.asarray(seq_lens))
         for name, d, o in (("keys", out[0], ko), ("values", out[1], vo)):
             db = _bits(d)
@@ -286,14 +291,17 @@ def test_gqa32_layer_full_size(kvq, orc, mode):
     k, v = W.gqa_kv(n, 8, 128, seed=1000 + layer, device=DEV)
     bt = W.permuted_block_table(cfgw["num_seqs"], cfgw["seq_len"] // 16, nblocks, seed=1000)
     slots = W.slots_from_block_table(bt, [cfgw["seq_len"]] * cfgw["num_seqs"], 16)
-    scales = None
+    scales = orc_scales = None
     if mode == W.FP8_PER_TENSOR:
         scales = [1.0, 1.0]
     elif mode == W.FP8_PER_HEAD:
+        # calibrated on a separate draw, by each side's own calibration
         kc, vc = W.gqa_kv(4096, 8, 128, seed=2000 + layer, device=DEV)
-        scales = W.static_scales_from_amax(W.calibration_amax(kc, vc)).tolist()
+        scales = C.hip_static_scales(kvq, kc, vc, mode)
+        orc_scales = C.oracle_static_scales(orc, kc, vc, mode)
+        assert np.array_equal(np.asarray(scales, np.float32).view(np.uint32), orc_scales.view(np.uint32))
     pair = Pair(kvq, orc, 16, 8, 128, [mode], [nblocks])
-    pair.store(0, k.cpu(), v.cpu(), slots, scales)
+    pair.store(0, k.cpu(), v.cpu(), slots, scales, orc_scales)
     pair.assert_buffers_equal()
     pair.gather_and_compare(0, bt.numpy(), [cfgw["seq_len"]] * cfgw["num_seqs"])
     pair.cache.close()

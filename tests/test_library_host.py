@@ -101,9 +101,9 @@ def _store(kvq, h, layer, n, mode, scales=None, keys=FAKE_DEV, values=FAKE_DEV, 
                               n, mode, sc, None)
 
 
-def _gather(kvq, h, layer, nseq, maxb=4, out=FAKE_DEV):
+def _gather(kvq, h, layer, nseq, maxb=4, out=FAKE_DEV, rows=64):
     return kvq._lib.kvq_gather_dequant(h, layer, ctypes.c_void_p(FAKE_DEV), maxb, ctypes.c_void_p(FAKE_DEV),
-                                       nseq, ctypes.c_void_p(out), ctypes.c_void_p(out), None)
+                                       nseq, ctypes.c_void_p(out), ctypes.c_void_p(out), rows, None)
 
 
 def test_store_argument_checks(kvq):
@@ -134,6 +134,11 @@ def test_store_argument_checks(kvq):
         assert _gather(kvq, h, 0, 1, out=FAKE_DEV + 2) == kvq.ERR_INVALID_ARG
         assert _gather(kvq, h, 9, 1) == kvq.ERR_INVALID_ARG
         assert _gather(kvq, h, 0, 1 << 20, maxb=1 << 12) == kvq.ERR_UNSUPPORTED
+        # output capacity: negative or absurd row counts, null outputs with rows
+        assert _gather(kvq, h, 0, 1, rows=-1) == kvq.ERR_INVALID_ARG
+        assert _gather(kvq, h, 0, 1, rows=(1 << 46) + 1) == kvq.ERR_INVALID_ARG
+        assert _gather(kvq, h, 0, 1, out=0) == kvq.ERR_INVALID_ARG
+        assert _gather(kvq, h, 0, 1, out=0, rows=0) == kvq.OK                     # nothing to write: no launch
     finally:
         kvq.kvq_destroy_cache(h)
 

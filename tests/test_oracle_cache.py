@@ -8,6 +8,7 @@ import torch
 
 import workloads as W
 from tests import _brute
+from tests import _calib as C
 from tests._golden import load as load_golden
 
 MODES = [W.BF16, W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD]
@@ -206,8 +207,7 @@ def test_round_trip_error_bound(orc, mode):
     kb, vb = _bits(k), _bits(v)
     sc = None
     if mode == W.FP8_PER_HEAD:
-        amax = W.calibration_amax(k, v)
-        sc = W.static_scales_from_amax(amax).numpy()
+        sc = C.oracle_static_scales(orc, k, v, mode)
     g, buf = _store_rows(orc, mode, kb, vb, hkv, hd, sc)
     ko, vo = orc.gather(g, buf, 0, np.arange(n, dtype=np.int32)[None, :], np.array([n], np.int32))
     for x, xo, c in ((k, ko, 0), (v, vo, 1)):

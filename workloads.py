@@ -2,8 +2,13 @@
 side and the HIP side of every test and benchmark.
 
 This module draws numbers and lays out indices.  It holds none of the
-method's arithmetic: no absmax, no scale, no quantization and no layout
-addressing.  Everything is returned as torch tensors on the requested device;
+method's arithmetic: no per-token-head absmax, no scale, no calibration, no
+quantization and no layout addressing.  (The tiny draw rescales each head of
+its FP32 sample to a chosen maximum before the BF16 cast; that shapes the
+input, as the pages' range example does, and no result of the method comes
+from it.)  Static scales for the static layouts are derived by each side's
+own calibration (the library's kvq_calibrate_amax, the oracle's
+calibrate_amax).  Everything is returned as torch tensors on the requested device;
 callers copy to the host when the oracle needs them.
 
 The shapes follow the pages' own geometries: the 32-layer, 8-KV-head,
@@ -96,21 +101,6 @@ def heavy_tail_kv(n_tokens, hkv, hd, seed, device="cpu"):
         odd = (torch.arange(hkv, device=device) % 2 == 1).view(1, hkv, 1)
         out.append(torch.where(odd, t3, z).to(torch.bfloat16))
     return out[0], out[1]
-
-
-def calibration_amax(k_cal: torch.Tensor, v_cal: torch.Tensor) -> torch.Tensor:
-    """Absolute maximum per (K/V, head) of a calibration draw, float32 [2, hkv].
-    Calibration is an offline step outside the store/gather path; its output is
-    an input (the static scales) to both sides."""
-    ka = k_cal.float().abs().amax(dim=(0, 2))
-    va = v_cal.float().abs().amax(dim=(0, 2))
-    return torch.stack([ka, va]).cpu()
-
-
-def static_scales_from_amax(amax: torch.Tensor, qmax: float = 448.0) -> torch.Tensor:
-    """Stand-in for an offline calibration tool: scale = amax / qmax in float32,
-    flattened [K heads..., V heads...]."""
-    return (amax.to(torch.float32) / torch.tensor(qmax, dtype=torch.float32)).reshape(-1)
 
 
 # --------------------------------------------------------------------------
