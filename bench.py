@@ -58,29 +58,90 @@ def algorithmic_bytes(mode, hd, hkv, bs, token_heads):
     return store, gather
 
 
-def copy_ceiling(torch, nbytes, reps=10, pairs=8):
-    """Practical ceiling for a launch that moves 2 * nbytes: device-to-device
-    copies of nbytes (read once, written once) over `pairs` rotating buffer
-    pairs, so that the 256 MB Infinity Cache holds none of them; HIP events on
-    the current stream."""
-    n = (int(nbytes) + 15) // 16 * 16
-    bufs = [(torch.empty(n, dtype=torch.uint8, device="cuda"), torch.empty(n, dtype=torch.uint8, device="cuda"))
-            for _ in range(pairs)]
-    for src, dst in bufs:
-        dst.copy_(src)
+CEILING_LIB = os.path.join(ROOT, "ceiling", "_build", "libkvq_ceiling.so")
+
+
+def _ceiling_lib():
+    """The bench-only ceiling kernels (ceiling/copy_ceiling.hip, built by
+    __graft_entry__.build()); not part of libkvq.so."""
+    import ctypes
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(CEILING_LIB)
+    P = ctypes.c_void_p
+    lib.ceil_linear_copy.argtypes = [P, P, ctypes.c_uint64, P]
+    lib.ceil_store_pattern.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P]
+    return lib
+
+
+def _time_launches(torch, launches, reps, warmup=2):
+    """Mean seconds per launch of a list of launch closures, run back to back
+    `reps` times on the current stream between HIP events on that stream."""
+    for _ in range(warmup):
+        for f in launches:
+            f()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        for src, dst in bufs:
-            dst.copy_(src)
+        for f in launches:
+            f()
     e1.record()
     torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) / 1e3 / (reps * pairs)
-    del bufs
+    return e0.elapsed_time(e1) / 1e3 / (reps * len(launches))
+
+
+def _rate(nbytes, sec):
+    gbps = nbytes / sec / 1e9
+    return {"bytes": int(nbytes), "us": round(sec * 1e6, 2), "GBps": round(gbps, 1),
+            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def linear_copy_ceiling(torch, nbytes, buffers, reps):
+    """A non-temporal linear copy moving nbytes per launch (nbytes / 2 read,
+    nbytes / 2 written), rotating over `buffers` source/destination pairs so
+    that the 256 MB Infinity Cache holds none of them."""
+    import ctypes
+    lib = _ceiling_lib()
+    half = (int(nbytes) // 2 + 15) // 16 * 16
+    pairs = [(torch.empty(half, dtype=torch.uint8, device="cuda"), torch.empty(half, dtype=torch.uint8, device="cuda"))
+             for _ in range(buffers)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def mk(src, dst):
+        def f():
+            if lib.ceil_linear_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), half, stream):
+                raise RuntimeError("ceil_linear_copy failed")
+        return f
+    sec = _time_launches(torch, [mk(s_, d_) for s_, d_ in pairs], reps)
+    del pairs
     torch.cuda.empty_cache()
-    return {"bytes_per_copy": 2 * n, "us": round(sec * 1e6, 2), "GBps": round(2 * n / sec / 1e9, 1),
-            "frac_of_peak": round(2 * n / sec / 1e9 / HBM_PEAK_GBPS, 4)}
+    return _rate(2 * half, sec)
+
+
+def store_pattern_ceiling(torch, I, LA, slots, reps, out_buf):
+    """The store's exact loads and stores (every layer's own K/V, the given
+    slots, the layer's code rows and scale trailer) with no arithmetic,
+    written to a scratch buffer laid out like the layout's cache."""
+    import ctypes
+    lib = _ceiling_lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rb = row_bytes(LA["mode"], I["hd"])
+    sc = 8 if LA["dynamic"] else 0
+
+    def mk(layer):
+        base = out_buf.data_ptr() + LA["layer_base"][layer]
+        k, v = I["keys"][layer], I["values"][layer]
+
+        def f():
+            if lib.ceil_store_pattern(ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                      ctypes.c_void_p(slots.data_ptr()), ctypes.c_void_p(base), I["n"], I["hkv"],
+                                      I["hd"], rb, sc, I["bs"], I["nblocks"], stream):
+                raise RuntimeError("ceil_store_pattern failed")
+        return f
+    sec = _time_launches(torch, [mk(l) for l in range(I["L"])], reps)
+    return _rate(LA["store_bytes"], sec)
 
 
 def kernel_source_hash(sources=None):
@@ -274,91 +335,190 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, la
     print("\n".join(lines + [""] + out))
 
 
-def setup(args, torch, kvq, W):
+GQA32_LAYOUTS = ("fp8_per_token_head", "fp8_per_tensor", "fp8_per_head", "int4_per_token_head")
+
+
+def gqa32_inputs(args, torch, W):
+    """The GQA-32 step's inputs, shared by every layout: each layer's own
+    BF16 K/V (seed 1000 + layer), one permuted block table and its slots, and
+    each layer's own BF16 output pair."""
     spec = W.WORKLOADS["gqa32"]
     L, hkv, hd, bs = spec["num_layers"], spec["hkv"], spec["hd"], spec["block_size"]
     # a tensor-parallel shard stores only its own KV heads for the same tokens
     hkv //= getattr(args, "tp", 1)
     nseq, slen = spec["num_seqs"], spec["seq_len"]
     n = nseq * slen
-    mode = {v: k for k, v in W.MODE_NAMES.items()}[args.mode]
     nblocks = n // bs
     dev = torch.device("cuda", 0)
-    cfg = kvq.CacheConfig(bs, hkv, hd, [mode] * L, [nblocks] * L)
-    cache = kvq.Cache(cfg, device=dev)
     bt = W.permuted_block_table(nseq, slen // bs, nblocks, seed=1000)
     slots = W.slots_from_block_table(bt, [slen] * nseq, bs).to(dev)
-    bt_d = bt.to(dev)
-    seq_lens = torch.full((nseq,), slen, dtype=torch.int32, device=dev)
-    keys, values, outs, scales = [], [], [], []
+    keys, values, outs = [], [], []
     for layer in range(L):
         k, v = W.gqa_kv(n, hkv, hd, seed=1000 + layer, device=dev)
         keys.append(k)
         values.append(v)
         outs.append((torch.empty_like(k), torch.empty_like(v)))
+    torch.cuda.synchronize()
+    return dict(L=L, hkv=hkv, hd=hd, bs=bs, n=n, nseq=nseq, slen=slen, nblocks=nblocks, bt=bt, bt_d=bt.to(dev),
+                slots=slots, identity_slots=torch.arange(n, dtype=torch.int64, device=dev),
+                seq_lens=torch.full((nseq,), slen, dtype=torch.int32, device=dev), keys=keys, values=values, outs=outs)
+
+
+def gqa32_layout(torch, kvq, W, I, mode_name):
+    """One layout's cache over the shared inputs: per-tensor scale 1.0 (the
+    uncalibrated case), per-head scales calibrated by the library
+    (kvq_calibrate_amax + kvq_static_scales) on a separate draw (seed 2000 +
+    layer), and the pre-marshalled store and gather calls of every layer."""
+    import ctypes
+    mode = {v: k for k, v in W.MODE_NAMES.items()}[mode_name]
+    L, hkv, hd, bs, nblocks = I["L"], I["hkv"], I["hd"], I["bs"], I["nblocks"]
+    dev = I["keys"][0].device
+    cache = kvq.Cache(kvq.CacheConfig(bs, hkv, hd, [mode] * L, [nblocks] * L), device=dev)
+    scales = []
+    for layer in range(L):
         if mode == kvq.FP8_PER_TENSOR:
             scales.append([1.0, 1.0])
         elif mode == kvq.FP8_PER_HEAD:
-            # calibrated on a separate draw by the library's own calibration
             kc, vc = W.gqa_kv(4096, hkv, hd, seed=2000 + layer, device=dev)
             amax = torch.zeros(2 * hkv, dtype=torch.float32, device=dev)
             kvq.kvq_calibrate_amax(kc, vc, amax)
             scales.append(kvq.kvq_static_scales(amax, hkv, mode))
         else:
             scales.append(None)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
+    sa, ga = [], []
+    for layer in range(L):
+        sc = scales[layer]
+        csc = None if sc is None else (ctypes.c_float * len(sc))(*[float(x) for x in sc])
+        sa.append((cache.handle, layer, P(I["keys"][layer].data_ptr()), P(I["values"][layer].data_ptr()),
+                   P(I["slots"].data_ptr()), I["n"], mode, csc, stream))
+        ga.append((cache.handle, layer, P(I["bt_d"].data_ptr()), I["bt_d"].shape[1], P(I["seq_lens"].data_ptr()),
+                   I["nseq"], P(I["outs"][layer][0].data_ptr()), P(I["outs"][layer][1].data_ptr()),
+                   int(I["outs"][layer][0].shape[0]), stream))
+    return dict(layout_geometry(kvq, W, I, mode_name), cache=cache, scales=scales, store_args=sa, gather_args=ga)
+
+
+def layout_geometry(kvq, W, I, mode_name):
+    """A layout's mode, layer bases in the cache buffer (256-byte aligned
+    layers of equal size) and algorithmic bytes per launch."""
+    mode = {v: k for k, v in W.MODE_NAMES.items()}[mode_name]
+    L, hkv, hd, bs, nblocks = I["L"], I["hkv"], I["hd"], I["bs"], I["nblocks"]
+    dynamic = mode in (kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD)
+    block_bytes = bs * hkv * (2 * row_bytes(mode, hd) + (8 if dynamic else 0))
+    layer_bytes = (nblocks * block_bytes + 255) // 256 * 256
+    store_b, gather_b = algorithmic_bytes(mode, hd, hkv, bs, I["n"] * hkv)
+    return dict(mode=mode, name=mode_name, dynamic=dynamic, layer_base=[l * layer_bytes for l in range(L)],
+                store_bytes=store_b, gather_bytes=gather_b)
+
+
+def time_layout(torch, kvq, LA, steps, warmup):
+    """W untimed warmup steps, then exactly K timed steps of every layer's
+    store followed by every layer's gather; HIP events on the launch stream
+    bracket each step's stores and gathers.  Returns seconds per store launch,
+    per gather launch and per step (wall clock, synchronized on both sides)."""
+    lib = kvq._lib
+    sa, ga = LA["store_args"], LA["gather_args"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        for a in sa:
+            st = lib.kvq_store(*a)
+            if st != 0:
+                raise kvq.KVQError(st, "kvq_store")
+        if ev is not None:
+            ev[1].record()
+        for a in ga:
+            st = lib.kvq_gather_dequant(*a)
+            if st != 0:
+                raise kvq.KVQError(st, "kvq_gather_dequant")
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
-    return dict(L=L, hkv=hkv, hd=hd, bs=bs, n=n, nseq=nseq, slen=slen, mode=mode, nblocks=nblocks,
-                cfg=cfg, cache=cache, bt=bt, bt_d=bt_d, slots=slots, seq_lens=seq_lens, keys=keys,
-                values=values, outs=outs, scales=scales)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    n = steps * len(sa)
+    store_s = sum(e[0].elapsed_time(e[1]) for e in evs) / n / 1e3
+    gather_s = sum(e[1].elapsed_time(e[2]) for e in evs) / n / 1e3
+    return store_s, gather_s, wall
 
 
-def cpu_baseline(S, torch, W, n_layers):
-    """The oracle, as it stands, on the first n_layers layers of the same step
-    (store then gather), on this host's cores; also checks those layers' cache
-    bytes and gathered values against the GPU's."""
+def oracle_scales(torch, W, I, LA, layer):
+    """The oracle side's static scales of one layer, by the oracle's own
+    calibration of the same draw: calibrate_amax, then RN32(amax / 448) in
+    numpy float32 (per-tensor: of the maximum over heads); the library's
+    scales must equal them bit for bit."""
+    import numpy as np
+    import oracle
+    import quantized_fp8_int4_amd as kvq
+    if LA["mode"] == kvq.FP8_PER_TENSOR:
+        return np.array([1.0, 1.0], np.float32)
+    if LA["mode"] != kvq.FP8_PER_HEAD:
+        return None
+    hkv, hd = I["hkv"], I["hd"]
+    kc, vc = W.gqa_kv(4096, hkv, hd, seed=2000 + layer, device="cpu")
+    a = oracle.calibrate_amax(_bits(torch, kc), _bits(torch, vc), hkv, hd)
+    s = (a / np.float32(448.0)).astype(np.float32)
+    s[s == 0] = np.float32(np.finfo(np.float32).smallest_subnormal)
+    return s
+
+
+def oracle_leg(torch, W, I, LA, layers, single_core=False):
+    """The oracle, as it stands, on the given layers of the same step (store
+    then gather of each), on this host's cores; checks those layers' cache
+    bytes and gathered values against the GPU's.  Returns (seconds, threads,
+    parity, seconds of one layer on one core or None)."""
     import numpy as np
     import oracle
 
     oracle.build(force=False)
-    g = oracle.Geometry(S["bs"], S["hkv"], S["hd"], [S["mode"]] * S["L"], [S["nblocks"]] * S["L"])
+    L, hkv, hd, bs, nb = I["L"], I["hkv"], I["hd"], I["bs"], I["nblocks"]
+    g = oracle.Geometry(bs, hkv, hd, [LA["mode"]] * L, [nb] * L)
     host = oracle.new_cache(g)
-    slots = S["slots"].cpu().numpy()
-    bt = S["bt"].numpy()
-    lens = np.full(S["nseq"], S["slen"], np.int32)
-    ins = []
-    for layer in range(n_layers):
-        kb = S["keys"][layer].cpu().view(torch.int16).numpy().view(np.uint16)
-        vb = S["values"][layer].cpu().view(torch.int16).numpy().view(np.uint16)
-        ins.append((kb, vb))
+    slots = I["slots"].cpu().numpy()
+    bt = I["bt"].numpy()
+    lens = np.full(I["nseq"], I["slen"], np.int32)
+    ins = {l: (_bits(torch, I["keys"][l]), _bits(torch, I["values"][l])) for l in layers}
+    osc = {l: oracle_scales(torch, W, I, LA, l) for l in layers}
+    ok = True
+    for l in layers:
+        if osc[l] is not None:
+            ok = ok and bool(np.array_equal(np.asarray(LA["scales"][l], np.float32).view(np.uint32),
+                                            osc[l].view(np.uint32)))
     t0 = time.perf_counter()
-    gathered = []
-    for layer in range(n_layers):
-        sc = S["scales"][layer]
-        oracle.store(g, host, layer, ins[layer][0], ins[layer][1], slots,
-                     None if sc is None else np.asarray(sc, np.float32))
-    for layer in range(n_layers):
-        gathered.append(oracle.gather(g, host, layer, bt, lens))
+    gathered = {}
+    for l in layers:
+        oracle.store(g, host, l, ins[l][0], ins[l][1], slots, osc[l])
+    for l in layers:
+        gathered[l] = oracle.gather(g, host, l, bt, lens)
     secs = time.perf_counter() - t0
-    # the same oracle on one core, one layer (its store again is idempotent)
     threads = oracle.num_threads()
-    oracle.set_num_threads(1)
-    t1 = time.perf_counter()
-    sc = S["scales"][0]
-    oracle.store(g, host, 0, ins[0][0], ins[0][1], slots, None if sc is None else np.asarray(sc, np.float32))
-    oracle.gather(g, host, 0, bt, lens)
-    secs_one = time.perf_counter() - t1
-    oracle.set_num_threads(threads)
+    secs_one = None
+    if single_core:
+        l = layers[0]
+        oracle.set_num_threads(1)
+        t1 = time.perf_counter()
+        oracle.store(g, host, l, ins[l][0], ins[l][1], slots, osc[l])
+        oracle.gather(g, host, l, bt, lens)
+        secs_one = time.perf_counter() - t1
+        oracle.set_num_threads(threads)
     lb, _, _ = oracle.layer_offsets(g)
-    import quantized_fp8_int4_amd as kvq
-    sigma = 8 if S["mode"] in (kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD) else 0
-    layer_bytes = S["nblocks"] * S["bs"] * S["hkv"] * (2 * row_bytes(S["mode"], S["hd"]) + sigma)
-    end = int(lb[n_layers - 1]) + layer_bytes
-    dev_buf = S["cache"].buffer[:end].cpu().numpy()
-    ok = bool(np.array_equal(dev_buf, host[:end]))
-    for layer in range(n_layers):
-        dk = S["outs"][layer][0].cpu().view(torch.int16).numpy().view(np.uint16)
-        dv = S["outs"][layer][1].cpu().view(torch.int16).numpy().view(np.uint16)
-        ok = ok and np.array_equal(dk, gathered[layer][0]) and np.array_equal(dv, gathered[layer][1])
+    lbytes = int(lb[1] - lb[0]) if L > 1 else host.size
+    dev = LA["cache"].buffer
+    for l in layers:
+        lo = int(lb[l])
+        ok = ok and bool(np.array_equal(dev[lo: lo + lbytes].cpu().numpy(), host[lo: lo + lbytes]))
+        ok = ok and bool(np.array_equal(_bits(torch, I["outs"][l][0]), gathered[l][0]))
+        ok = ok and bool(np.array_equal(_bits(torch, I["outs"][l][1]), gathered[l][1]))
     return secs, threads, ok, secs_one
 
 
@@ -997,6 +1157,9 @@ def main():
                     choices=["fp8_per_token_head", "fp8_per_tensor", "fp8_per_head", "int4_per_token_head", "bf16"])
     ap.add_argument("--cpu-layers", type=int, default=16, help="layers of one step timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="gqa32: time only the --mode layout (default: also the other three layouts of the target)")
+    ap.add_argument("--no-ceiling", action="store_true", help="gqa32: skip the bandwidth-ceiling kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, copy 256 MiB device-to-device 3 times (reference for counter scaling)")
     ap.add_argument("--summarize-attention-profiles", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -1025,68 +1188,96 @@ def main():
         run_other_workload(args, torch, kvq, W)
         return
 
+    run_gqa32(args, torch, kvq, W)
+
+
+def run_gqa32(args, torch, kvq, W):
+    """The headline line: the GQA-32 step in the --mode layout (default
+    per-token-head FP8), and beside it every other layout of the target (FP8
+    per-tensor, FP8 static per-head, INT4 per-token-head) on the same inputs,
+    each with its oracle check; the store's bandwidth ceilings (a linear
+    non-temporal copy, the store's own access pattern without arithmetic)."""
     log("[bench] setting up gqa32 inputs on the device")
-    S = setup(args, torch, kvq, W)
-    L, cache = S["L"], S["cache"]
-    token_heads = S["n"] * S["hkv"]
-    store_bytes, gather_bytes = algorithmic_bytes(S["mode"], S["hd"], S["hkv"], S["bs"], token_heads)
+    I = gqa32_inputs(args, torch, W)
+    L = I["L"]
+    order = [args.mode] + ([m for m in GQA32_LAYOUTS if m != args.mode] if not args.headline_only else [])
+    layouts, head = {}, None
+    cpu = cpu_one = None
+    for name in order:
+        LA = gqa32_layout(torch, kvq, W, I, name)
+        store_s, gather_s, wall = time_layout(torch, kvq, LA, args.steps, args.warmup)
+        sg, gg = LA["store_bytes"] / store_s / 1e9, LA["gather_bytes"] / gather_s / 1e9
+        log(f"[bench] {name}: {wall * 1e3:.3f} ms/step; store {store_s * 1e6:.2f} us ({sg:.0f} GB/s), "
+            f"gather {gather_s * 1e6:.2f} us ({gg:.0f} GB/s)")
+        rec = {"store_us": round(store_s * 1e6, 2), "store_GBps": round(sg, 1),
+               "store_frac_of_peak": round(sg / HBM_PEAK_GBPS, 4), "gather_us": round(gather_s * 1e6, 2),
+               "gather_GBps": round(gg, 1), "gather_frac_of_peak": round(gg / HBM_PEAK_GBPS, 4),
+               "store_bytes_per_launch": int(LA["store_bytes"]), "gather_bytes_per_launch": int(LA["gather_bytes"])}
+        if name == args.mode:
+            head = dict(LA=LA, store_s=store_s, gather_s=gather_s, wall=wall)
+        # the oracle's check of this layout, while the outputs hold its gather
+        if args.no_cpu_baseline:
+            rec["parity_vs_oracle_sampled"] = None
+        elif name == args.mode:
+            nl = max(1, min(args.cpu_layers, L))
+            log(f"[bench] cpu baseline: oracle on {nl} layers (store + gather)")
+            secs, cores, parity, secs_one = oracle_leg(torch, W, I, LA, list(range(nl)), single_core=True)
+            cpu = {"value": round(nl * (LA["store_bytes"] + LA["gather_bytes"]) / secs / 1e9, 3), "unit": "GB/s",
+                   "cores": cores, "kind": "oracle",
+                   "sample": f"{nl} of {L} layers of one step (store then gather of {I['n']} tokens each), "
+                             f"{secs:.2f} s wall"}
+            cpu_one = {"value": round((LA["store_bytes"] + LA["gather_bytes"]) / secs_one / 1e9, 3), "unit": "GB/s",
+                       "cores": 1, "sample": f"1 layer (store then gather), {secs_one:.2f} s wall",
+                       "cpu_model": cpu_model(), "host_cores_visible": len(os.sched_getaffinity(0))}
+            rec["parity_vs_oracle_sampled"] = parity
+            rec["parity_layers"] = nl
+        else:
+            sample = [0, L - 1]
+            _, _, parity, _ = oracle_leg(torch, W, I, LA, sample)
+            rec["parity_vs_oracle_sampled"] = parity
+            rec["parity_layers"] = len(sample)
+        layouts[name] = rec
+        if name != args.mode:
+            LA["cache"].close()
+            del LA
+            torch.cuda.empty_cache()
 
-    # Launch arguments prepared once, so the host stays far ahead of the GPU
-    # and every kernel starts as soon as the previous one ends.
-    import ctypes
-    lib, handle = kvq._lib, cache.handle
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    P = ctypes.c_void_p
-    store_args, gather_args = [], []
-    for layer in range(L):
-        sc = S["scales"][layer]
-        csc = None if sc is None else (ctypes.c_float * len(sc))(*[float(x) for x in sc])
-        store_args.append((handle, layer, P(S["keys"][layer].data_ptr()), P(S["values"][layer].data_ptr()),
-                           P(S["slots"].data_ptr()), S["n"], S["mode"], csc, stream))
-        gather_args.append((handle, layer, P(S["bt_d"].data_ptr()), S["bt_d"].shape[1],
-                            P(S["seq_lens"].data_ptr()), S["nseq"], P(S["outs"][layer][0].data_ptr()),
-                            P(S["outs"][layer][1].data_ptr()), int(S["outs"][layer][0].shape[0]), stream))
+    # Ceilings: what the memory system gives the store's bytes with no
+    # arithmetic, on the same inputs, rotating over all 32 layers.
+    LA = head["LA"]
+    ceilings = {}
+    if not args.no_ceiling:
+        out_buf = torch.empty(LA["cache"].bytes["total"], dtype=torch.uint8, device=I["keys"][0].device)
+        reps = max(3, args.steps)
+        ceilings["store_pattern_permuted_slots"] = store_pattern_ceiling(torch, I, LA, I["slots"], reps, out_buf)
+        ceilings["store_pattern_identity_slots"] = store_pattern_ceiling(torch, I, LA, I["identity_slots"], reps,
+                                                                         out_buf)
+        ceilings["linear_nt_copy"] = linear_copy_ceiling(torch, LA["store_bytes"], 16, reps)
+        for name in layouts:
+            if name == args.mode:
+                continue
+            pc = store_pattern_ceiling(torch, I, layout_geometry(kvq, W, I, name), I["slots"], reps, out_buf)
+            layouts[name]["store_pattern_ceiling_GBps"] = pc["GBps"]
+            layouts[name]["store_vs_pattern_ceiling"] = round(layouts[name]["store_GBps"] / pc["GBps"], 4)
+        del out_buf
+        torch.cuda.empty_cache()
+        pc = ceilings["store_pattern_permuted_slots"]
+        layouts[args.mode]["store_pattern_ceiling_GBps"] = pc["GBps"]
+        layouts[args.mode]["store_vs_pattern_ceiling"] = round(layouts[args.mode]["store_GBps"] / pc["GBps"], 4)
+        log(f"[bench] ceilings: store pattern {pc['GBps']:.0f} GB/s (permuted slots), "
+            f"{ceilings['store_pattern_identity_slots']['GBps']:.0f} (identity), "
+            f"linear copy {ceilings['linear_nt_copy']['GBps']:.0f}")
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        for a in store_args:
-            st = lib.kvq_store(*a)
-            if st != 0:
-                raise kvq.KVQError(st, "kvq_store")
-        if ev is not None:
-            ev[1].record()
-        for a in gather_args:
-            st = lib.kvq_gather_dequant(*a)
-            if st != 0:
-                raise kvq.KVQError(st, "kvq_gather_dequant")
-        if ev is not None:
-            ev[2].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
-
-    # HIP events on the launch stream bracket each step's 32 stores and 32 gathers.
-    all_events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(all_events[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    avg_store_s = sum(ev[0].elapsed_time(ev[1]) for ev in all_events) / (args.steps * L) / 1e3
-    avg_gather_s = sum(ev[1].elapsed_time(ev[2]) for ev in all_events) / (args.steps * L) / 1e3
-    ms_per_step = wall / args.steps * 1e3
+    store_s, gather_s, wall = head["store_s"], head["gather_s"], head["wall"]
+    store_bytes, gather_bytes = LA["store_bytes"], LA["gather_bytes"]
     step_bytes = L * (store_bytes + gather_bytes)
-    value = step_bytes / (wall / args.steps) / 1e9
-    store_gbps = store_bytes / avg_store_s / 1e9
-    gather_gbps = gather_bytes / avg_gather_s / 1e9
-    dominant = "store" if avg_store_s >= avg_gather_s else "gather"
+    value = step_bytes / wall / 1e9
+    store_gbps, gather_gbps = store_bytes / store_s / 1e9, gather_bytes / gather_s / 1e9
+    dominant = "store" if store_s >= gather_s else "gather"
     dom_gbps = store_gbps if dominant == "store" else gather_gbps
-    log(f"[bench] {ms_per_step:.3f} ms/step; store {avg_store_s * 1e6:.1f} us ({store_gbps:.0f} GB/s), "
-        f"gather {avg_gather_s * 1e6:.1f} us ({gather_gbps:.0f} GB/s)")
+    if ceilings:
+        ceilings["store_vs_pattern_ceiling"] = round(store_gbps / ceilings["store_pattern_permuted_slots"]["GBps"], 4)
+        ceilings["store_vs_linear_copy"] = round(store_gbps / ceilings["linear_nt_copy"]["GBps"], 4)
 
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -1095,28 +1286,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    # context: plain copies moving the same bytes as one store launch
-    ceiling = copy_ceiling(torch, store_bytes / 2)
-    ceiling["store_vs_copy"] = round(store_gbps / ceiling["GBps"], 4)
-    ceiling["gather_vs_copy"] = round(gather_gbps / ceiling["GBps"], 4)
-    log(f"[bench] copy ceiling: {ceiling['GBps']:.0f} GB/s for {ceiling['bytes_per_copy'] / 1e6:.1f} MB per copy")
-
     # the committed counters were taken on the default shape and mode only
     traffic = measured_traffic() if (args.mode == "fp8_per_token_head" and args.tp == 1) else None
-    cpu = None
-    cpu_one = None
-    parity = None
-    if not args.no_cpu_baseline:
-        nl = max(1, min(args.cpu_layers, L))
-        log(f"[bench] cpu baseline: oracle on {nl} layers (store + gather)")
-        secs, cores, parity, secs_one = cpu_baseline(S, torch, W, nl)
-        cpu = {"value": round(nl * (store_bytes + gather_bytes) / secs / 1e9, 3), "unit": "GB/s",
-               "cores": cores, "kind": "oracle",
-               "sample": f"{nl} of {L} layers of one step (store then gather of {S['n']} tokens each), "
-                         f"{secs:.2f} s wall"}
-        cpu_one = {"value": round((store_bytes + gather_bytes) / secs_one / 1e9, 3), "unit": "GB/s", "cores": 1,
-                   "sample": f"1 layer (store then gather), {secs_one:.2f} s wall", "cpu_model": cpu_model(),
-                   "host_cores_visible": len(os.sched_getaffinity(0))}
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -1124,33 +1295,34 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(wall * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": (f"gqa32 tensor-parallel shard (TP {args.tp}): 32 layers, {S['hkv']} of 8 KV heads per GPU, "
+        "config": {"workload": (f"gqa32 tensor-parallel shard (TP {args.tp}): 32 layers, {I['hkv']} of 8 KV heads per GPU, "
                                 if args.tp > 1 else "gqa32: 32 layers, 8 KV heads, ")
                                + "head_dim 128, block 16, prefill of 8 x 4096 "
                                f"tokens per layer call, store + gather_dequant of every layer, {args.mode}",
-                   "mode": args.mode, "layers": L, "tokens_per_layer_call": S["n"], "num_kv_heads": S["hkv"],
-                   "head_dim": S["hd"], "block_size": S["bs"], "tp": args.tp},
+                   "mode": args.mode, "layers": L, "tokens_per_layer_call": I["n"], "num_kv_heads": I["hkv"],
+                   "head_dim": I["hd"], "block_size": I["bs"], "tp": args.tp},
         "store_GBps": round(store_gbps, 1),
         "gather_GBps": round(gather_gbps, 1),
         "store_frac_of_peak": round(store_gbps / HBM_PEAK_GBPS, 4),
         "gather_frac_of_peak": round(gather_gbps / HBM_PEAK_GBPS, 4),
-        "store_us": round(avg_store_s * 1e6, 2),
-        "gather_us": round(avg_gather_s * 1e6, 2),
-        "cached_tokens_per_s": round(S["n"] / (L * avg_store_s), 1),
+        "store_us": round(store_s * 1e6, 2),
+        "gather_us": round(gather_s * 1e6, 2),
+        "cached_tokens_per_s": round(I["n"] / (L * store_s), 1),
         "algorithmic_bytes_per_step": int(step_bytes),
         "roofline": {"bound": "hbm", "kernel": f"{dominant}_kernel", "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else traffic.get(dominant)},
         "cpu_baseline": cpu,
         "cpu_single_core": cpu_one,
-        "copy_ceiling": ceiling,
-        "parity_vs_oracle_sampled": parity,
+        "parity_vs_oracle_sampled": layouts[args.mode]["parity_vs_oracle_sampled"],
+        "layouts": layouts,
+        "ceilings": ceilings,
     }
     print(json.dumps(result), flush=True)
 

@@ -109,7 +109,27 @@ def build_c_tests(verbose: bool = False) -> str:
     return C_DEVICE_EXE
 
 
+CEILING_SRC = os.path.join(ROOT, "ceiling", "copy_ceiling.hip")
+CEILING_LIB = os.path.join(ROOT, "ceiling", "_build", "libkvq_ceiling.so")
+
+
+def build_ceiling(verbose: bool = False) -> str:
+    """The benchmark's bandwidth-ceiling kernels (a separate library, never
+    loaded by libkvq.so or the binding)."""
+    os.makedirs(os.path.dirname(CEILING_LIB), exist_ok=True)
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-shared", CEILING_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {CEILING_SRC}:\n{r.stderr}")
+    os.replace(tmp, CEILING_LIB)
+    return CEILING_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
     print(build_hw_checks(verbose="-v" in sys.argv))
     print(build_c_tests(verbose="-v" in sys.argv))
+    print(build_ceiling(verbose="-v" in sys.argv))

@@ -43,3 +43,22 @@ def test_attention_bytes_of_one_launch():
     assert bench.attention_bytes(FP8_PTH, 128, 8, 16, 32, 2, 40) == 40 * 8 * (256 + 8) + 3 * 4 + 2 * 32 * 128 * 4
     # INT4 at head_dim 64 halves the rows: 32 code bytes each, the same 8 scale bytes
     assert bench.attention_bytes(INT4_PTH, 64, 8, 16, 32, 1, 16) == 16 * 8 * (64 + 8) + 4 + 32 * 64 * 4
+
+
+@pytest.mark.parametrize("name", ["fp8_per_token_head", "fp8_per_tensor", "fp8_per_head", "int4_per_token_head"])
+def test_layout_geometry_matches_the_cache_layout(orc, name):
+    """The layer bases the store-pattern ceiling writes at are the cache
+    layout's (the oracle's own offsets), and its last layer ends inside a
+    buffer of kvq_cache_bytes().total, so the ceiling kernel stays in bounds."""
+    import quantized_fp8_int4_amd as kvq
+    import workloads as W
+    spec = W.WORKLOADS["gqa32"]
+    L, hkv, hd, bs = spec["num_layers"], spec["hkv"], spec["hd"], spec["block_size"]
+    n = spec["num_seqs"] * spec["seq_len"]
+    I = dict(L=L, hkv=hkv, hd=hd, bs=bs, n=n, nblocks=n // bs)
+    geo = bench.layout_geometry(kvq, W, I, name)
+    g = orc.Geometry(bs, hkv, hd, [geo["mode"]] * L, [n // bs] * L)
+    assert [int(x) for x in orc.layer_offsets(g)[0]] == geo["layer_base"]
+    block = bs * hkv * (2 * bench.row_bytes(geo["mode"], hd) + (8 if geo["dynamic"] else 0))
+    total = kvq.kvq_cache_bytes(kvq.CacheConfig(bs, hkv, hd, [geo["mode"]] * L, [n // bs] * L))["total"]
+    assert geo["layer_base"][-1] + (n // bs) * block <= total

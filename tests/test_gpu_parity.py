@@ -375,15 +375,18 @@ def test_decode_append_reduced(kvq, orc, mode, hd):
     pair.cache.close()
 
 
-@pytest.mark.parametrize("mode,hd", [(W.FP8_PER_TOKEN_HEAD, 128), (W.INT4_PER_TOKEN_HEAD, 64)],
-                         ids=["fp8_per_token_head-128", "int4_per_token_head-64"])
+@pytest.mark.parametrize("mode,hd", [(W.FP8_PER_TOKEN_HEAD, 128), (W.INT4_PER_TOKEN_HEAD, 128),
+                                     (W.FP8_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 64)],
+                         ids=["fp8_per_token_head-128", "int4_per_token_head-128", "fp8_per_token_head-64",
+                              "int4_per_token_head-64"])
 def test_decode_layer_full_size(kvq, orc, mode, hd):
     """Decode shape at full size, one layer, in the benchmark's launch
     configuration: 256 sequences prefilled with 8192 tokens each in store
     calls of 32768 tokens, blocks popped from a random free list, then two
     steps appending one token per sequence (the first opens a new block for
-    every sequence); every cache byte compared, and the full-context gather
-    compared on eight sampled sequences."""
+    every sequence); every cache byte compared, and the full-context gather of
+    all 256 sequences (one launch) compared with the oracle's, 64 sequences at
+    a time."""
     _flush(f"[decode-full] mode={W.MODE_NAMES[mode]} hd={hd}")
     S, ctx, bs, hkv, chunk = 256, 8192, 16, 8, 32768
     maxb = ctx // bs + 1
@@ -407,15 +410,20 @@ def test_decode_layer_full_size(kvq, orc, mode, hd):
     total = int(lens.sum())
     ok = torch.empty((total, hkv, hd), dtype=torch.bfloat16, device=DEV)
     ov = torch.empty_like(ok)
-    pair.cache.gather_dequant(0, torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV), out=(ok, ov))
+    pair.cache.gather_dequant(0, torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV),
+                              total_tokens=total, out=(ok, ov))
     torch.cuda.synchronize()
-    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
-    pick = np.random.default_rng(7).choice(S, 8, replace=False)
-    for b in pick:
-        rk, rv = orc.gather(pair.g, pair.host, 0, bt[b: b + 1], lens[b: b + 1])
-        r0, n = int(starts[b]), int(lens[b])
-        assert np.array_equal(_bits(ok[r0: r0 + n]), rk), f"keys of sequence {b}"
-        assert np.array_equal(_bits(ov[r0: r0 + n]), rv), f"values of sequence {b}"
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    for b0 in range(0, S, 64):
+        rk, rv = orc.gather(pair.g, pair.host, 0, bt[b0: b0 + 64], lens[b0: b0 + 64])
+        r0, r1 = int(starts[b0]), int(starts[b0 + 64])
+        for name, d, o in (("keys", ok, rk), ("values", ov, rv)):
+            db = _bits(d[r0:r1])
+            if not np.array_equal(db, o):
+                bad = np.argwhere(db != o)
+                pytest.fail(f"{name} of sequences {b0}..{b0 + 63}: {len(bad)} elements differ, first at "
+                            f"row {r0 + bad[0][0]}")
+        del rk, rv
     del ok, ov
     pair.cache.close()
 
@@ -432,6 +440,79 @@ def test_long80_layer_full_size(kvq, orc):
     pair.assert_buffers_equal()
     pair.gather_and_compare(0, np.arange(T // 16, dtype=np.int32)[None, :], [T])
     pair.cache.close()
+
+
+@pytest.mark.parametrize("num_seqs", [300, 1100])
+@pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD, W.FP8_PER_HEAD, W.BF16],
+                         ids=["fp8_per_token_head", "int4_per_token_head", "fp8_per_head", "bf16"])
+def test_gather_many_sequences(kvq, orc, num_seqs, mode):
+    """One gather over more than 256 sequences, so the sequence offsets of
+    most workgroups are summed past the first 256 lengths: ragged lengths 0 to
+    40, some negative, block tables with entries outside the layer; every
+    gathered value against the oracle."""
+    _flush(f"[many-seqs] num_seqs={num_seqs} mode={W.MODE_NAMES[mode]}")
+    bs, hkv, hd, nblocks = 16, 2, 128, 96
+    rng = np.random.default_rng(num_seqs * 10 + mode)
+    pair = Pair(kvq, orc, bs, hkv, hd, [mode], [nblocks])
+    try:
+        n = nblocks * bs
+        k, v = W.gqa_kv(n, hkv, hd, seed=int(rng.integers(1 << 30)))
+        scales = orc_scales = None
+        if mode == W.FP8_PER_HEAD:
+            scales = C.hip_static_scales(kvq, k.to(DEV), v.to(DEV), mode)
+            orc_scales = C.oracle_static_scales(orc, k, v, mode)
+        pair.store(0, k, v, torch.from_numpy(rng.permutation(n).astype(np.int64)), scales, orc_scales)
+        pair.assert_buffers_equal()
+        maxb = 3
+        bt = rng.integers(0, nblocks, (num_seqs, maxb)).astype(np.int32)
+        bad = rng.random((num_seqs, maxb)) < 0.05
+        bt[bad] = rng.choice([-1, nblocks, nblocks + 1000])
+        lens = rng.integers(0, 41, num_seqs).astype(np.int32)
+        neg = rng.random(num_seqs) < 0.05
+        lens[neg] = -rng.integers(1, 30, int(neg.sum()))
+        lens[0], lens[255], lens[256], lens[-1] = 40, 0, -5, 33
+        pair.gather_and_compare(0, bt, lens)
+    finally:
+        pair.cache.close()
+
+
+def test_gather_short_output_is_never_overrun(kvq, orc):
+    """An output shorter than the sequences' total receives exactly its
+    leading rows, and the bytes just past it (a guard region of the same
+    allocation) stay untouched; an output of zero rows receives nothing."""
+    _flush("[short output]")
+    bs, hkv, hd, nblocks = 16, 2, 64, 8
+    pair = Pair(kvq, orc, bs, hkv, hd, [W.FP8_PER_TOKEN_HEAD], [nblocks])
+    try:
+        n = nblocks * bs
+        k, v = W.normal_kv(n, hkv, hd, seed=77)
+        pair.store(0, k, v, torch.arange(n, dtype=torch.int64))
+        bt = np.arange(nblocks, dtype=np.int32).reshape(2, 4)
+        lens = np.array([60, 50], np.int32)
+        rk, rv = orc.gather(pair.g, pair.host, 0, bt, lens)
+        guard = 0x7FC1                                  # a BF16 NaN pattern the gather never writes
+        for short in (0, 1, 37, 59, 60, 83, 109):
+            big_k = torch.full((110 + 16, hkv, hd), guard, dtype=torch.int16, device=DEV)
+            big_v = big_k.clone()
+            ok = big_k.view(torch.bfloat16)[:short]
+            ov = big_v.view(torch.bfloat16)[:short]
+            kvq.kvq_gather_dequant(pair.cache.handle, 0, torch.from_numpy(bt).to(DEV),
+                                   torch.from_numpy(lens).to(DEV), ok, ov)
+            torch.cuda.synchronize()
+            for big, ref in ((big_k, rk), (big_v, rv)):
+                hb = big.cpu().numpy().view(np.uint16)
+                assert np.array_equal(hb[:short], ref[:short]), f"rows below {short}"
+                assert (hb[short:] == guard).all(), f"guard past {short} rows written"
+        # the binding refuses a zero-row or short output unless the total is stated
+        e = torch.empty((0, hkv, hd), dtype=torch.bfloat16, device=DEV)
+        with pytest.raises(ValueError):
+            pair.cache.gather_dequant(0, torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV), out=(e, e))
+        with pytest.raises(ValueError):
+            s = torch.empty((50, hkv, hd), dtype=torch.bfloat16, device=DEV)
+            pair.cache.gather_dequant(0, torch.from_numpy(bt).to(DEV), torch.from_numpy(lens).to(DEV),
+                                      total_tokens=110, out=(s, s))
+    finally:
+        pair.cache.close()
 
 
 def test_binding_rejects_wrong_shapes(kvq):

@@ -230,6 +230,17 @@ def test_attention_argument_checks(kvq):
 
 
 
+def test_blocks_of_2gib_or_more_are_unsupported(kvq):
+    """The kernels address a block with 32-bit offsets, so a layer whose
+    block (codes and scale trailer) reaches 2^31 bytes is refused."""
+    ok = kvq.CacheConfig(1024, 1024, 256, [kvq.BF16], [1])            # 2^30-byte blocks
+    assert kvq.kvq_cache_bytes(ok)["total"] == 1 << 30
+    for hkv, mode in ((2048, kvq.BF16), (4096, kvq.FP8_PER_TOKEN_HEAD), (8192, kvq.INT4_PER_TOKEN_HEAD)):
+        with pytest.raises(kvq.KVQError) as e:
+            kvq.kvq_cache_bytes(kvq.CacheConfig(1024, hkv, 256, [mode], [1]))
+        assert e.value.status == kvq.ERR_UNSUPPORTED
+
+
 def test_fp8_query_attention_argument_checks(kvq):
     cfg = _cfg(kvq, [kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD, kvq.BF16], hd=128)
     h = _handle(kvq, cfg)
