@@ -340,6 +340,33 @@ KVQ_API kvq_status kvq_decode_attention_fp8q(const kvq_cache* c, int32_t layer, 
                                              float sm_scale, void* out, void* workspace, uint64_t workspace_bytes,
                                              void* stream);
 
+/* Bytes of the fixed device array that holds kvq_decode_attention_noalloc's
+ * split partials (one copy per GPU, kept until the process ends). */
+#define KVQ_ATTENTION_SCRATCH_BYTES (32ull << 20)
+
+/*
+ * kvq_decode_attention_noalloc -- kvq_decode_attention for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels, plan and
+ * results, with the split partials kept in a fixed device array of
+ * KVQ_ATTENTION_SCRATCH_BYTES instead of a caller workspace.  Nothing is
+ * allocated by the call; the array's device address is looked up once per
+ * GPU, on the first call made with that GPU current.
+ *   Arguments, results and errors as kvq_decode_attention without
+ *   workspace / workspace_bytes; KVQ_ERR_UNSUPPORTED also when the call
+ *   shape needs more than KVQ_ATTENTION_SCRATCH_BYTES of partials
+ *   (kvq_decode_attention_workspace reports the need; shapes with one split
+ *   need none).
+ *   All calls on one GPU share its array, and the partials of a call are
+ *   live until that call's work on its stream has finished: calls that
+ *   overlap on one GPU (other streams, other threads, other handles) race
+ *   and give undefined results.  Calls on different GPUs do not interact.
+ */
+KVQ_API kvq_status kvq_decode_attention_noalloc(const kvq_cache* c, int32_t layer, const void* q,
+                                                int32_t num_q_heads, const int32_t* block_table,
+                                                int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                                int32_t num_seqs, float sm_scale, void* out, void* stream);
+
 /* ------------------------------------------------------------------------
  * Capacity planning and the decode-time block manager (host code only)
  * ---------------------------------------------------------------------- */

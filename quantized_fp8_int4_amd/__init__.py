@@ -42,6 +42,7 @@ OK, ERR_INVALID_ARG, ERR_MODE_MISMATCH, ERR_BUFFER_TOO_SMALL, ERR_UNSUPPORTED, E
 EXPORTED_SYMBOLS = ("kvq_cache_bytes", "kvq_create_cache", "kvq_destroy_cache", "kvq_store",
                     "kvq_gather_dequant", "kvq_calibrate_amax", "kvq_static_scales",
                     "kvq_decode_attention_workspace", "kvq_decode_attention", "kvq_decode_attention_fp8q",
+                    "kvq_decode_attention_noalloc",
                     "kvq_plan_capacity",
                     "kvq_manager_create", "kvq_manager_destroy", "kvq_manager_num_groups", "kvq_manager_layer_group",
                     "kvq_manager_append", "kvq_manager_release", "kvq_manager_tables", "kvq_status_string")
@@ -86,6 +87,7 @@ def _load_library():
     lib.kvq_decode_attention.argtypes = [P, I32, P, I32, P, I32, P, I32, ctypes.c_float, P, P, ctypes.c_uint64, P]
     lib.kvq_decode_attention_fp8q.argtypes = [P, I32, P, P, I32, P, I32, P, I32, ctypes.c_float, P, P,
                                               ctypes.c_uint64, P]
+    lib.kvq_decode_attention_noalloc.argtypes = [P, I32, P, I32, P, I32, P, I32, ctypes.c_float, P, P]
     lib.kvq_plan_capacity.argtypes = [ctypes.POINTER(_Model), I64, ctypes.c_uint64, ctypes.POINTER(_Plan), P]
     lib.kvq_manager_create.argtypes = [ctypes.POINTER(_Model), P, I32, ctypes.POINTER(P)]
     lib.kvq_manager_destroy.argtypes = [P]
@@ -286,6 +288,32 @@ def kvq_decode_attention(handle, layer: int, q: torch.Tensor, block_table: torch
                                           ctypes.c_void_p(bt), int(block_table.shape[1]), ctypes.c_void_p(sl), num_seqs,
                                           float(sm_scale), ctypes.c_void_p(op), ctypes.c_void_p(wp), wb,
                                           _stream_ptr(stream, q.device)), "kvq_decode_attention_fp8q")
+
+
+# Bytes of the fixed device array behind kvq_decode_attention_noalloc.
+ATTENTION_SCRATCH_BYTES = 32 << 20
+
+
+def kvq_decode_attention_noalloc(handle, layer: int, q: torch.Tensor, block_table: torch.Tensor,
+                                 seq_lens: torch.Tensor, sm_scale: float, out: torch.Tensor, stream=None) -> None:
+    """kvq_decode_attention without a workspace: the library keeps the split
+    partials in a fixed per-GPU device array and allocates nothing.  Calls
+    that overlap on one GPU share that array and race."""
+    num_seqs = int(seq_lens.numel())
+    if num_seqs == 0:
+        return
+    qp = _dev(q, torch.bfloat16, "q")
+    op = _dev(out, torch.bfloat16, "out")
+    bt = _dev(block_table, torch.int32, "block_table")
+    sl = _dev(seq_lens, torch.int32, "seq_lens")
+    if q.dim() != 3 or q.shape[0] != num_seqs or out.shape != q.shape:
+        raise ValueError("q and out must be [num_seqs, num_q_heads, head_dim]")
+    if block_table.dim() != 2 or block_table.shape[0] != num_seqs:
+        raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
+    _check(_lib.kvq_decode_attention_noalloc(handle, int(layer), ctypes.c_void_p(qp), int(q.shape[1]),
+                                             ctypes.c_void_p(bt), int(block_table.shape[1]), ctypes.c_void_p(sl),
+                                             num_seqs, float(sm_scale), ctypes.c_void_p(op),
+                                             _stream_ptr(stream, q.device)), "kvq_decode_attention_noalloc")
 
 
 @dataclass

@@ -224,7 +224,7 @@ namespace {
 kvq_status decode_attention(const kvq_cache* c, int32_t layer, const void* q, const float* q_scales,
                             int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks_per_seq,
                             const int32_t* seq_lens, int32_t num_seqs, float sm_scale, void* out, void* workspace,
-                            uint64_t workspace_bytes, void* stream) {
+                            uint64_t workspace_bytes, void* stream, bool fixed_scratch = false) {
     if (!c || layer < 0 || layer >= c->layout.num_layers || num_seqs < 0) return KVQ_ERR_INVALID_ARG;
     if (num_seqs == 0) return KVQ_OK;
     const kvq_status st = attention_args(c, num_q_heads, max_blocks_per_seq, num_seqs);
@@ -243,8 +243,21 @@ kvq_status decode_attention(const kvq_cache* c, int32_t layer, const void* q, co
     const kvq::AttnPlan plan =
         kvq::attention_plan(L.block_size, L.num_kv_heads, L.head_dim, num_q_heads, max_blocks_per_seq, num_seqs);
     if (plan.grid >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
-    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    if (fixed_scratch) {
+        // The allocation-free variant: split partials go to this device's
+        // fixed array, looked up (never allocated) after every other check.
+        if (plan.workspace_bytes > KVQ_ATTENTION_SCRATCH_BYTES) {
+            if (log_enabled())
+                std::fprintf(stderr, "[kvq] attention_noalloc: %llu bytes of split partials exceed the fixed %llu\n",
+                             static_cast<unsigned long long>(plan.workspace_bytes),
+                             static_cast<unsigned long long>(KVQ_ATTENTION_SCRATCH_BYTES));
+            return KVQ_ERR_UNSUPPORTED;
+        }
+        workspace = nullptr;
+        if (plan.workspace_bytes > 0 && kvq::attention_scratch(&workspace) != 0) return KVQ_ERR_HIP;
+    } else if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes)) {
         return KVQ_ERR_BUFFER_TOO_SMALL;
+    }
 
     kvq::AttnLaunch a;
     a.layer = c->dev + L.layer_base[layer];
@@ -283,6 +296,14 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
                                 uint64_t workspace_bytes, void* stream) {
     return decode_attention(c, layer, q, nullptr, num_q_heads, block_table, max_blocks_per_seq, seq_lens, num_seqs,
                             sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* c, int32_t layer, const void* q, int32_t num_q_heads,
+                                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                                        const int32_t* seq_lens, int32_t num_seqs, float sm_scale, void* out,
+                                        void* stream) {
+    return decode_attention(c, layer, q, nullptr, num_q_heads, block_table, max_blocks_per_seq, seq_lens, num_seqs,
+                            sm_scale, out, nullptr, 0, stream, /*fixed_scratch=*/true);
 }
 
 kvq_status kvq_decode_attention_fp8q(const kvq_cache* c, int32_t layer, const void* q, const float* q_scales,

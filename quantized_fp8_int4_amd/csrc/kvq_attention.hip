@@ -37,6 +37,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -1100,6 +1101,37 @@ void launch_attention_hd(const AttnArgs& p, int mode, int threads, bool small_bs
 }
 
 }  // namespace
+
+// Split partials of the allocation-free entry point live in this fixed
+// device array instead of a caller workspace.  Each GPU holds its own copy
+// (allocated with the code object, kept until the process ends); host code
+// never passes `scratch` itself to a kernel: the name is only a host-side
+// stand-in for the symbol, and its device address comes from
+// hipGetSymbolAddress once per device (attention_scratch below).
+static __device__ __align__(256) uint8_t scratch[KVQ_ATTENTION_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+int attention_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (dev < 0 || dev >= kMaxScratchDevices) return static_cast<int>(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return static_cast<int>(e);
+        if (!p) return static_cast<int>(hipErrorInvalidSymbol);
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return 0;
+}
 
 AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t num_q_heads,
                         int32_t max_blocks, int32_t num_seqs) {

@@ -133,5 +133,9 @@ struct AttnLaunch {
     float sm_scale;
 };
 int launch_attention(const AttnLaunch& a, const AttnPlan& plan, void* stream);
+// Device address of this device's fixed split-partial array
+// (KVQ_ATTENTION_SCRATCH_BYTES), looked up on the device's first call; 0 on
+// success, else the hipError_t value.
+int attention_scratch(void** ptr);
 
 }  // namespace kvq

@@ -241,6 +241,42 @@ def test_blocks_of_2gib_or_more_are_unsupported(kvq):
         assert e.value.status == kvq.ERR_UNSUPPORTED
 
 
+def test_noalloc_attention_argument_checks(kvq):
+    """The allocation-free attention checks everything before any HIP call,
+    and refuses a call shape whose split partials exceed its fixed array."""
+    cfg = _cfg(kvq, [kvq.FP8_PER_TOKEN_HEAD, kvq.FP8_PER_TENSOR], hd=128)
+    h = _handle(kvq, cfg)
+
+    def call(layer, nseq=1, H=4, maxb=4, q=FAKE_DEV, out=FAKE_DEV, sm=0.125):
+        return kvq._lib.kvq_decode_attention_noalloc(h, layer, ctypes.c_void_p(q), H, ctypes.c_void_p(FAKE_DEV),
+                                                     maxb, ctypes.c_void_p(FAKE_DEV), nseq, sm,
+                                                     ctypes.c_void_p(out), None)
+    try:
+        assert call(2) == kvq.ERR_INVALID_ARG                 # layer out of range
+        assert call(0, nseq=0) == kvq.OK                      # no-op, no HIP call
+        assert call(0, nseq=-1) == kvq.ERR_INVALID_ARG
+        assert call(0, H=3) == kvq.ERR_INVALID_ARG
+        assert call(0, q=0) == kvq.ERR_INVALID_ARG
+        assert call(0, out=FAKE_DEV + 2) == kvq.ERR_INVALID_ARG
+        assert call(0, sm=float("nan")) == kvq.ERR_INVALID_ARG
+        assert call(1) == kvq.ERR_INVALID_ARG                 # static layer never stored
+        assert call(0, maxb=1 << 27) == kvq.ERR_UNSUPPORTED
+    finally:
+        kvq.kvq_destroy_cache(h)
+    # 1023 sequences of one KV head with 16 query heads at head_dim 256 take
+    # two splits each: 1023 * 16 * 2 * 258 * 4 bytes of partials, above 32 MiB
+    big = kvq.CacheConfig(16, 1, 256, [kvq.FP8_PER_TOKEN_HEAD], [4])
+    h = _handle(kvq, big)
+    try:
+        need = kvq.kvq_decode_attention_workspace(h, 16, 16, 1023)
+        assert need == 1023 * 16 * 2 * 258 * 4 > kvq.ATTENTION_SCRATCH_BYTES
+        assert kvq._lib.kvq_decode_attention_noalloc(h, 0, ctypes.c_void_p(FAKE_DEV), 16, ctypes.c_void_p(FAKE_DEV),
+                                                     16, ctypes.c_void_p(FAKE_DEV), 1023, 0.0625,
+                                                     ctypes.c_void_p(FAKE_DEV), None) == kvq.ERR_UNSUPPORTED
+    finally:
+        kvq.kvq_destroy_cache(h)
+
+
 def test_fp8_query_attention_argument_checks(kvq):
     cfg = _cfg(kvq, [kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD, kvq.BF16], hd=128)
     h = _handle(kvq, cfg)
