@@ -119,8 +119,9 @@ typedef struct kvq_cache kvq_cache;
  * "Layer skipping follows retained-token footprint".
  *   cfg  host, read only.  out: host, written on success.
  *   Errors: KVQ_ERR_INVALID_ARG (null pointer, bad value),
- *           KVQ_ERR_UNSUPPORTED (head_dim or block_size not supported, or
- *           a layer whose block, codes and scales, is 2 GiB or more).
+ *           KVQ_ERR_UNSUPPORTED (head_dim or block_size not supported, a
+ *           layer whose block, codes and scales, is 2 GiB or more, or a
+ *           buffer beyond 2^62 bytes).
  *
  * Layout of the buffer: layers in order, each starting on a 256-byte
  * boundary; layer l is layer_num_blocks[l] blocks, each block

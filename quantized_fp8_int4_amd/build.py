@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(BUILD_DIR, "libkvq.so")
 SOURCES = ["kvq_kernels.hip", "kvq_calib.hip", "kvq_attention.hip", "kvq_api.cpp", "kvq_layout.cpp",
-           "kvq_planner.cpp"]
+           "kvq_planner.cpp", "kvq_launch_geometry.cpp"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [

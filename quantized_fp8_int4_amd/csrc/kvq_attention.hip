@@ -52,12 +52,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 16;                 // tokens per tile
-constexpr int kMaxHeadsPerWg = 8;        // waves (KV heads) per attention workgroup
+constexpr int kTile = kAttnTile;
+constexpr int kMaxHeadsPerWg = kAttnMaxHeadsPerWg;
 constexpr int kMaxAttnThreads = 64 * kMaxHeadsPerWg;
-// Splits per sequence never exceed the target wave count, so the wide
-// combine's LDS weight table holds them all.
-constexpr int kMaxSplits = 4096;
+constexpr int kMaxSplits = kAttnMaxSplits;
 constexpr int kWideCombineSplits = 16;       // from here on the combine spreads the splits
 constexpr int kMaxStagedPieces = 16;         // 16-byte pieces per lane of a staged tile (16 KiB)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -1131,38 +1129,6 @@ int attention_scratch(void** ptr) {
     }
     *ptr = g_scratch_ptr[dev];
     return 0;
-}
-
-AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t num_q_heads,
-                        int32_t max_blocks, int32_t num_seqs) {
-    AttnPlan pl{};
-    int hpw = 1;
-    while (hpw < kMaxHeadsPerWg && num_kv_heads % (2 * hpw) == 0) hpw *= 2;
-    pl.heads_per_wg = hpw;
-    const int group = num_q_heads / num_kv_heads;
-    pl.qgroups = (group + 15) / 16;
-    const int64_t units = static_cast<int64_t>(num_seqs) * (num_kv_heads / hpw) * pl.qgroups;
-    const int64_t max_tiles = (static_cast<int64_t>(max_blocks) * block_size + kTile - 1) / kTile;
-    // About 1024 waves in all (measured best against 4096 and 2048: a wave
-    // streams best over a long tile range, and fewer splits write fewer
-    // partials); a split keeps at least 8 tiles.  A long single sequence gets
-    // up to 1024 / heads_per_wg splits; a large batch gets one split, and the
-    // kernel then writes the output itself.
-    constexpr int64_t kTargetWaves = 1024, kMinTilesPerSplit = 8;
-    static_assert(kTargetWaves <= kMaxSplits, "the wide combine holds every split's weight");
-    const int64_t want = (kTargetWaves / hpw + units - 1) / units;
-    const int64_t cap = (max_tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
-    int64_t splits = want < cap ? want : cap;
-    if (splits < 1) splits = 1;
-    int64_t tps = (max_tiles + splits - 1) / splits;
-    if (tps < 1) tps = 1;
-    splits = (max_tiles + tps - 1) / tps;
-    if (splits < 1) splits = 1;
-    pl.splits = static_cast<int32_t>(splits);
-    pl.tiles_per_split = static_cast<int32_t>(tps);
-    pl.grid = units * splits;
-    pl.workspace_bytes = splits > 1 ? static_cast<uint64_t>(num_seqs) * num_q_heads * splits * (head_dim + 2) * 4 : 0;
-    return pl;
 }
 
 int launch_attention(const AttnLaunch& a, const AttnPlan& pl, void* stream) {

@@ -84,7 +84,28 @@ struct GatherLaunch {
 // Each returns 0 on a successful enqueue, else the hipError_t value.
 int launch_store(const StoreLaunch& a, void* stream);
 int launch_gather(const GatherLaunch& a, void* stream);
-// Workgroups launch_gather would use (to reject grids of 2^31 or more).
+
+// Gather tuning, chosen by measurement on MI355X (32768 tokens x 8 KV heads
+// per call), shared by the kernel dispatch and the host's grid arithmetic:
+// cb code bytes per thread chunk (8 FP8, 4 INT4, 16 BF16: every wave-wide
+// 16-byte store writes 1 KiB of contiguous BF16), u chunks per thread, tpb
+// threads per workgroup (INT4 from head_dim 128 on: 512 threads of 4 chunks,
+// +1.4% at 128 and +3.4% at 256; 5.5% slower at 64, where 256 threads of 8
+// chunks stay).
+struct GatherTune {
+    int cb;
+    int u;
+    int tpb;
+};
+constexpr GatherTune gather_tune(int hd, int mode) {
+    return (mode == KVQ_INT4_PER_TOKEN_HEAD && hd >= 128)
+               ? GatherTune{4, 4, 512}
+               : GatherTune{mode == KVQ_BF16 ? 16 : (mode == KVQ_INT4_PER_TOKEN_HEAD ? 4 : 8),
+                            (hd == 64 || mode == KVQ_INT4_PER_TOKEN_HEAD || mode == KVQ_BF16) ? 8 : 4, 256};
+}
+// Workgroups per logical block: parts of up to tpb * u chunks of cb bytes.
+int64_t gather_parts(int64_t block_size, int64_t hkv, uint64_t hb, int cb, int u, int tpb);
+// Workgroups launch_gather uses (to reject grids of 2^31 or more).
 int64_t gather_grid(const GatherLaunch& a);
 int launch_write_static(float* dst, const float* values, int n, void* stream);
 
@@ -99,7 +120,12 @@ struct CalibLaunch {
 };
 int launch_calibrate(const CalibLaunch& a, void* stream);
 
-// ---- decode attention (kvq_attention.hip) ------------------------------
+// ---- decode attention (kvq_attention.hip; plan in kvq_launch_geometry.cpp)
+constexpr int kAttnTile = 16;          // tokens per attention tile
+constexpr int kAttnMaxHeadsPerWg = 8;  // waves (KV heads) per attention workgroup
+// Splits per sequence never exceed the plan's target wave count, so the wide
+// combine's LDS weight table holds them all.
+constexpr int kAttnMaxSplits = 4096;
 struct AttnPlan {
     int32_t splits;                // tile ranges per sequence
     int32_t tiles_per_split;       // 16-token tiles per range

@@ -452,13 +452,11 @@ __global__ void write_static_kernel(float* dst, StaticValues vals, int n) {
 
 // --------------------------------------------------------------- dispatch
 
-// Default tuning, chosen by measurement on MI355X (32768 tokens x 8 KV heads
-// per call): 8 lanes per row, so every load instruction reads whole 128-byte
-// lines of each row; more rows per lane for BF16 (no arithmetic to hide
-// latency behind); non-temporal streams for data
-// that one call touches once.  The
-// gather moves 8 code bytes (FP8) or 4 (INT4) per thread chunk, so each
-// wave-wide store writes 1 KiB of contiguous BF16 output.
+// Default store tuning, chosen by measurement on MI355X (32768 tokens x 8 KV
+// heads per call): 8 lanes per row, so every load instruction reads whole
+// 128-byte lines of each row; more rows per lane for BF16 (no arithmetic to
+// hide latency behind); non-temporal streams for data that one call touches
+// once.  The gather's tuning is shared with the host (gather_tune).
 template <int HD, int MODE>
 struct Tune {
     static constexpr int store_epl = HD / 8;
@@ -467,14 +465,11 @@ struct Tune {
     static constexpr bool store_nt_store = true;
     static constexpr bool store_contig = false;
     static constexpr int store_tpb = 256;
-    static constexpr int gather_cb = (MODE == KVQ_BF16) ? 16 : (MODE == KVQ_INT4_PER_TOKEN_HEAD ? 4 : 8);
-    // INT4 from head_dim 128 on: 512 threads of 4 chunks (+1.4% at 128, +3.4%
-    // at 256; 5.5% slower at 64, where 256 threads of 8 chunks stay)
-    static constexpr bool gather_wide = MODE == KVQ_INT4_PER_TOKEN_HEAD && HD >= 128;
-    static constexpr int gather_u = gather_wide ? 4 : ((HD == 64 || MODE == KVQ_INT4_PER_TOKEN_HEAD || MODE == KVQ_BF16) ? 8 : 4);
+    static constexpr int gather_cb = gather_tune(HD, MODE).cb;
+    static constexpr int gather_u = gather_tune(HD, MODE).u;
     static constexpr bool gather_nt_store = true;
     static constexpr bool gather_lds_scales = true;
-    static constexpr int gather_tpb = gather_wide ? 512 : 256;
+    static constexpr int gather_tpb = gather_tune(HD, MODE).tpb;
 };
 
 StoreArgs make_store_args(const StoreLaunch& a) {
@@ -494,12 +489,6 @@ StoreArgs make_store_args(const StoreLaunch& a) {
     p.hkv_shift = dm.shift;
     p.bs_log2 = static_cast<uint32_t>(a.bs_log2);
     return p;
-}
-
-int64_t gather_parts(int64_t block_size, int64_t hkv, uint64_t hb, int cb, int u, int tpb) {
-    const int64_t chunks = block_size * hkv * 2 * static_cast<int64_t>(hb / cb);
-    const int64_t per = static_cast<int64_t>(tpb) * u;
-    return (chunks + per - 1) / per;
 }
 
 GatherArgs make_gather_args(const GatherLaunch& a) {
@@ -587,33 +576,7 @@ int launch_gather_m(const GatherLaunch& a, void* stream) {
     }
 }
 
-template <int HD, int MODE>
-int64_t gather_grid_t(const GatherLaunch& a) {
-    using T = Tune<HD, MODE>;
-    return static_cast<int64_t>(a.num_seqs) * a.max_blocks *
-           gather_parts(a.block_size, a.num_kv_heads, row_bytes(a.mode, HD), T::gather_cb, T::gather_u, T::gather_tpb);
-}
-
-template <int MODE>
-int64_t gather_grid_m(const GatherLaunch& a) {
-    switch (a.head_dim) {
-        case 64: return gather_grid_t<64, MODE>(a);
-        case 128: return gather_grid_t<128, MODE>(a);
-        default: return gather_grid_t<256, MODE>(a);
-    }
-}
-
 }  // namespace
-
-int64_t gather_grid(const GatherLaunch& a) {
-    switch (a.mode) {
-        case KVQ_BF16: return gather_grid_m<KVQ_BF16>(a);
-        case KVQ_FP8_PER_TENSOR: return gather_grid_m<KVQ_FP8_PER_TENSOR>(a);
-        case KVQ_FP8_PER_HEAD: return gather_grid_m<KVQ_FP8_PER_HEAD>(a);
-        case KVQ_FP8_PER_TOKEN_HEAD: return gather_grid_m<KVQ_FP8_PER_TOKEN_HEAD>(a);
-        default: return gather_grid_m<KVQ_INT4_PER_TOKEN_HEAD>(a);
-    }
-}
 
 int launch_store(const StoreLaunch& a, void* stream) {
     switch (a.mode) {

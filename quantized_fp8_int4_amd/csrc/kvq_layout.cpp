@@ -84,6 +84,8 @@ kvq_status build_layout(const kvq_cache_config* cfg, Layout* out) {
         L.code_bytes.push_back(code);
         L.block_bytes.push_back(code + trailer);
         off += static_cast<uint64_t>(nb) * (code + trailer);
+        // (each term is below 2^62: nb <= 2^31 blocks of < 2^31 bytes)
+        if (off > (uint64_t{1} << 62)) return KVQ_ERR_UNSUPPORTED;
         payload += static_cast<uint64_t>(nb) * code;
         tok += static_cast<uint64_t>(nb) * trailer;
     }
