@@ -72,6 +72,8 @@ def _ceiling_lib():
     lib.ceil_linear_copy.argtypes = [P, P, ctypes.c_uint64, P]
     lib.ceil_store_pattern.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P]
+    I32 = ctypes.c_int32
+    lib.ceil_gather_pattern.argtypes = [P, P, I32, P, I32, P, P, I32, I32, I32, I32, I32, ctypes.c_int64, P]
     return lib
 
 
@@ -96,6 +98,32 @@ def _rate(nbytes, sec):
     gbps = nbytes / sec / 1e9
     return {"bytes": int(nbytes), "us": round(sec * 1e6, 2), "GBps": round(gbps, 1),
             "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def gather_pattern_ceiling(torch, I, LA, bt, reps, cache_buf):
+    """The gather's exact loads and stores (block table, sequence offsets,
+    code chunks and row scales of the layout's blocks, every layer's BF16
+    output rows) with no arithmetic, reading a buffer laid out like the
+    layout's cache."""
+    import ctypes
+    lib = _ceiling_lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rb = row_bytes(LA["mode"], I["hd"])
+    sc = 8 if LA["dynamic"] else 0
+
+    def mk(layer):
+        base = cache_buf.data_ptr() + LA["layer_base"][layer]
+        ok, ov = I["outs"][layer]
+
+        def f():
+            if lib.ceil_gather_pattern(ctypes.c_void_p(base), ctypes.c_void_p(bt.data_ptr()), bt.shape[1],
+                                       ctypes.c_void_p(I["seq_lens"].data_ptr()), I["nseq"],
+                                       ctypes.c_void_p(ok.data_ptr()), ctypes.c_void_p(ov.data_ptr()), I["hkv"],
+                                       I["hd"], rb, sc, I["bs"], I["nblocks"], stream):
+                raise RuntimeError("ceil_gather_pattern failed")
+        return f
+    sec = _time_launches(torch, [mk(l) for l in range(I["L"])], reps)
+    return _rate(LA["gather_bytes"], sec)
 
 
 def linear_copy_ceiling(torch, nbytes, buffers, reps):
@@ -409,7 +437,7 @@ def layout_geometry(kvq, W, I, mode_name):
     layer_bytes = (nblocks * block_bytes + 255) // 256 * 256
     store_b, gather_b = algorithmic_bytes(mode, hd, hkv, bs, I["n"] * hkv)
     return dict(mode=mode, name=mode_name, dynamic=dynamic, layer_base=[l * layer_bytes for l in range(L)],
-                store_bytes=store_b, gather_bytes=gather_b)
+                layers_bytes=L * layer_bytes, store_bytes=store_b, gather_bytes=gather_b)
 
 
 def time_layout(torch, kvq, LA, steps, warmup):
@@ -465,7 +493,9 @@ def oracle_scales(torch, W, I, LA, layer):
     if LA["mode"] != kvq.FP8_PER_HEAD:
         return None
     hkv, hd = I["hkv"], I["hd"]
-    kc, vc = W.gqa_kv(4096, hkv, hd, seed=2000 + layer, device="cpu")
+    # the same draw as the library's calibration (drawn on the device, as all
+    # inputs are; the CPU generator's stream differs), copied to the host
+    kc, vc = W.gqa_kv(4096, hkv, hd, seed=2000 + layer, device=I["keys"][0].device)
     a = oracle.calibrate_amax(_bits(torch, kc), _bits(torch, vc), hkv, hd)
     s = (a / np.float32(448.0)).astype(np.float32)
     s[s == 0] = np.float32(np.finfo(np.float32).smallest_subnormal)
@@ -821,12 +851,32 @@ def run_other_workload(args, torch, kvq, W):
         cpu = {"value": round((sb + gb + ssb + sgb) / csec / 1e9, 3), "unit": "GB/s",
                "cores": oracle.num_threads(), "kind": "oracle",
                "sample": f"one full and one sliding layer of the {L} (store + gather), {csec:.2f} s wall"}
+        extra = {"sliding_store_us": round(slide_store_s * 1e6, 2), "sliding_gather_us": round(slide_gather_s * 1e6, 2),
+                 "cache_MiB": round(cache.bytes["total"] / 2**20, 3)}
+        if not args.no_ceiling:
+            # the full layers' own access patterns without arithmetic, at the
+            # same launch size (32768 tokens x 8 KV heads x head_dim 64)
+            nbf = T // bs
+            lbytes = (nbf * bs * hkv * (2 * hd + 8) + 255) // 256 * 256
+            Ifull = dict(L=len(full), hkv=hkv, hd=hd, bs=bs, n=T, nblocks=nbf, nseq=1, seq_lens=sl_full,
+                         keys=[ins[l][0] for l in full], values=[ins[l][1] for l in full],
+                         outs=[outs[l] for l in full])
+            geo = dict(mode=kvq.FP8_PER_TOKEN_HEAD, dynamic=True, layer_base=[i * lbytes for i in range(len(full))],
+                       store_bytes=sb, gather_bytes=gb)
+            sbuf = torch.zeros(len(full) * lbytes, dtype=torch.uint8, device=dev)
+            reps = max(3, args.steps)
+            spc = store_pattern_ceiling(torch, Ifull, geo, full_slots, reps, sbuf)
+            gpc = gather_pattern_ceiling(torch, Ifull, geo, bt_full, reps, sbuf)
+            del sbuf
+            extra["ceilings"] = {"store_pattern": spc, "gather_pattern": gpc,
+                                 "store_vs_pattern_ceiling": round(sb / store_s / 1e9 / spc["GBps"], 4),
+                                 "gather_vs_pattern_ceiling": round(gb / gather_s / 1e9 / gpc["GBps"], 4)}
+            log(f"[bench] gptoss full-layer ceilings: store pattern {spc['GBps']:.0f} GB/s, "
+                f"gather pattern {gpc['GBps']:.0f} GB/s")
         res = _result(args, {"workload": spec["desc"], "layers": L, "tokens": T, "window": Wn,
                              "num_kv_heads": hkv, "head_dim": hd, "block_size": bs,
                              "mode": "full: fp8_per_token_head, sliding: bf16 ring"},
-                      step_bytes / sec / 1e9, sec * 1e3, sb, gb, store_s, gather_s, cpu, bool(parity),
-                      {"sliding_store_us": round(slide_store_s * 1e6, 2), "sliding_gather_us": round(slide_gather_s * 1e6, 2),
-                       "cache_MiB": round(cache.bytes["total"] / 2**20, 3)})
+                      step_bytes / sec / 1e9, sec * 1e3, sb, gb, store_s, gather_s, cpu, bool(parity), extra)
     elif name == "itl":
         # Attention-only inter-token latency against context, gpt-oss-20b shape
         # (24 layers alternating sliding W=128 and full, 64 query / 8 KV heads,
@@ -1247,26 +1297,36 @@ def run_gqa32(args, torch, kvq, W):
     LA = head["LA"]
     ceilings = {}
     if not args.no_ceiling:
-        out_buf = torch.empty(LA["cache"].bytes["total"], dtype=torch.uint8, device=I["keys"][0].device)
+        geos = {name: layout_geometry(kvq, W, I, name) for name in layouts}
+        dev = I["keys"][0].device
+        out_buf = torch.zeros(max(g["layers_bytes"] for g in geos.values()), dtype=torch.uint8, device=dev)
         reps = max(3, args.steps)
-        ceilings["store_pattern_permuted_slots"] = store_pattern_ceiling(torch, I, LA, I["slots"], reps, out_buf)
-        ceilings["store_pattern_identity_slots"] = store_pattern_ceiling(torch, I, LA, I["identity_slots"], reps,
+        ident_bt = torch.arange(I["nblocks"], dtype=torch.int32, device=dev).view(I["nseq"], -1)
+        hg = geos[args.mode]
+        ceilings["store_pattern_permuted_slots"] = store_pattern_ceiling(torch, I, hg, I["slots"], reps, out_buf)
+        ceilings["store_pattern_identity_slots"] = store_pattern_ceiling(torch, I, hg, I["identity_slots"], reps,
                                                                          out_buf)
+        ceilings["gather_pattern_permuted_blocks"] = gather_pattern_ceiling(torch, I, hg, I["bt_d"], reps, out_buf)
+        ceilings["gather_pattern_identity_blocks"] = gather_pattern_ceiling(torch, I, hg, ident_bt, reps, out_buf)
         ceilings["linear_nt_copy"] = linear_copy_ceiling(torch, LA["store_bytes"], 16, reps)
-        for name in layouts:
+        for name, g in geos.items():
             if name == args.mode:
-                continue
-            pc = store_pattern_ceiling(torch, I, layout_geometry(kvq, W, I, name), I["slots"], reps, out_buf)
+                pc = ceilings["store_pattern_permuted_slots"]
+                gc = ceilings["gather_pattern_permuted_blocks"]
+            else:
+                pc = store_pattern_ceiling(torch, I, g, I["slots"], reps, out_buf)
+                gc = gather_pattern_ceiling(torch, I, g, I["bt_d"], reps, out_buf)
             layouts[name]["store_pattern_ceiling_GBps"] = pc["GBps"]
             layouts[name]["store_vs_pattern_ceiling"] = round(layouts[name]["store_GBps"] / pc["GBps"], 4)
+            layouts[name]["gather_pattern_ceiling_GBps"] = gc["GBps"]
+            layouts[name]["gather_vs_pattern_ceiling"] = round(layouts[name]["gather_GBps"] / gc["GBps"], 4)
         del out_buf
         torch.cuda.empty_cache()
-        pc = ceilings["store_pattern_permuted_slots"]
-        layouts[args.mode]["store_pattern_ceiling_GBps"] = pc["GBps"]
-        layouts[args.mode]["store_vs_pattern_ceiling"] = round(layouts[args.mode]["store_GBps"] / pc["GBps"], 4)
-        log(f"[bench] ceilings: store pattern {pc['GBps']:.0f} GB/s (permuted slots), "
-            f"{ceilings['store_pattern_identity_slots']['GBps']:.0f} (identity), "
-            f"linear copy {ceilings['linear_nt_copy']['GBps']:.0f}")
+        log("[bench] ceilings: store pattern {:.0f} GB/s (permuted slots), {:.0f} (identity); gather pattern "
+            "{:.0f} (permuted blocks), {:.0f} (identity); linear copy {:.0f}".format(
+                *(ceilings[k]["GBps"] for k in ("store_pattern_permuted_slots", "store_pattern_identity_slots",
+                                                "gather_pattern_permuted_blocks", "gather_pattern_identity_blocks",
+                                                "linear_nt_copy"))))
 
     store_s, gather_s, wall = head["store_s"], head["gather_s"], head["wall"]
     store_bytes, gather_bytes = LA["store_bytes"], LA["gather_bytes"]
@@ -1277,6 +1337,8 @@ def run_gqa32(args, torch, kvq, W):
     dom_gbps = store_gbps if dominant == "store" else gather_gbps
     if ceilings:
         ceilings["store_vs_pattern_ceiling"] = round(store_gbps / ceilings["store_pattern_permuted_slots"]["GBps"], 4)
+        ceilings["gather_vs_pattern_ceiling"] = round(
+            gather_gbps / ceilings["gather_pattern_permuted_blocks"]["GBps"], 4)
         ceilings["store_vs_linear_copy"] = round(store_gbps / ceilings["linear_nt_copy"]["GBps"], 4)
 
     if args.calibrate_copy:

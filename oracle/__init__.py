@@ -195,11 +195,12 @@ def query_values(q_bits, q_scales=None) -> np.ndarray:
     return e4m3_decode(codes).astype(np.float64) * s.astype(np.float64)
 
 
-def _token_key_scales(g: Geometry, buf: np.ndarray, layer: int, bt: np.ndarray, lens: np.ndarray) -> np.ndarray:
-    """FP32 K scale of every token-head a gather of a per-token-head layer
-    reads, [sum(lens), hkv] in the gather's order, from the scale trailer of
-    this module's own block layout; 0 for tokens whose block is not in the
-    layer."""
+def _token_key_scales(g: Geometry, buf: np.ndarray, layer: int, bt: np.ndarray, lens: np.ndarray,
+                      which: int = 0) -> np.ndarray:
+    """FP32 K (which = 0) or V (which = 1) scale of every token-head a gather
+    of a per-token-head layer reads, [sum(lens), hkv] in the gather's order,
+    from the scale trailer of this module's own block layout; 0 for tokens
+    whose block is not in the layer."""
     lb, _, _ = layer_offsets(g)
     rb = g.hd // 2 if int(g.modes[layer]) == INT4_PER_TOKEN_HEAD else g.hd
     code_bytes = g.bs * g.hkv * 2 * rb
@@ -211,7 +212,7 @@ def _token_key_scales(g: Geometry, buf: np.ndarray, layer: int, bt: np.ndarray, 
             blk = int(bt[i, t // g.bs])
             if 0 <= blk < int(g.nblocks[layer]):
                 base = int(lb[layer]) + blk * block_bytes + code_bytes + (t % g.bs) * g.hkv * 8
-                out[row] = buf[base: base + g.hkv * 8].view(np.float32).reshape(g.hkv, 2)[:, 0]
+                out[row] = buf[base: base + g.hkv * 8].view(np.float32).reshape(g.hkv, 2)[:, which]
             row += 1
     return out
 
@@ -232,9 +233,15 @@ def attention_error_bound(g: Geometry, buf: np.ndarray, layer: int, q_bits, bloc
     most 24 s_t sum_d |q[d]| (s_t the token's K scale) to what the rounding
     acts on.  2^-8 covers the BF16 rounding of the weights (2^-9) and of the
     output (2^-9) plus FP32 accumulation and rescaling over fewer than 2^11
-    tiles; the last term is the FP32 underflow floor (products below 2^-126
-    may be lost).  ref and absv are this module's decode_attention results
-    for the same inputs."""
+    tiles (2^-9); the last term is the FP32 underflow floor (products below
+    2^-126 may be lost).  INT4 layers' values enter the value product biased
+    too, as (n + 8) / 16, with (8 / 16) sum_t P'_t (the same BF16 weights)
+    accumulated beside them and subtracted at the end: the weights' rounding
+    cancels between the two, and the FP32 accumulation and rescaling (2^-9
+    relative, as above) act on sum_t p_t s_t (|n_t| + 16) / 16 in units of
+    the code (s_t the token's V scale), which adds at most
+    2^-9 * 16 * sum_t p_t s_t <= 2^-5 max_t s_t to each element.  ref and
+    absv are this module's decode_attention results for the same inputs."""
     q = _c(q_bits, np.uint16)
     bt = _c(block_table, np.int32)
     lens = np.clip(_c(seq_lens, np.int64), 0, int(bt.shape[1]) * g.bs)
@@ -245,7 +252,9 @@ def attention_error_bound(g: Geometry, buf: np.ndarray, layer: int, q_bits, bloc
     qabs = np.abs(query_values(q, q_scales))
     biased = int(g.modes[layer]) == INT4_PER_TOKEN_HEAD
     ks = _token_key_scales(g, buf, layer, bt, lens) if biased else None
+    vs = _token_key_scales(g, buf, layer, bt, lens, which=1) if biased else None
     eps = np.zeros((q.shape[0], nqh))
+    vbias = np.zeros((q.shape[0], nqh))
     row0 = 0
     for i, n in enumerate(lens):
         if n:
@@ -254,10 +263,11 @@ def attention_error_bound(g: Geometry, buf: np.ndarray, layer: int, q_bits, bloc
                 dot = kk[:, qh // group, :] @ qabs[i, qh]
                 if biased:
                     dot = dot + 24.0 * ks[row0: row0 + n, qh // group] * qabs[i, qh].sum()
+                    vbias[i, qh] = 2.0 ** -5 * vs[row0: row0 + n, qh // group].max()
                 eps[i, qh] = (g.hd + 4) * 2.0 ** -24 * dot.max() * sm_scale
         row0 += int(n)
     floor = (lens.astype(np.float64)[:, None, None] + 16) * 2.0 ** -120 * max(1.0, float(static_v_max))
-    return (2.0 ** -8 + 2.5 * eps[:, :, None]) * absv + 2.0 ** -8 * np.abs(ref) + floor
+    return ((2.0 ** -8 + 2.5 * eps[:, :, None]) * absv + 2.0 ** -8 * np.abs(ref) + vbias[:, :, None] + floor)
 
 def retained_positions(layer_windows, context: int):
     """Retained token-layer positions of one sequence per layer: a

@@ -242,28 +242,7 @@ __device__ __forceinline__ void v_operands(const uint32_t (*v)[Geo<HD, MODE>::VW
             a[j + 1] = __builtin_bit_cast(s16x4, y);
         }
     } else if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
-        // dim j of a token: nibble j % 8 of dword j / 8, i.e. the low (j even)
-        // or high (j odd) nibble of byte (j % 8) / 2
-        constexpr int VW = Geo<HD, MODE>::VW;
-        uint32_t hv[4][VW];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int w = 0; w < VW; ++w) hv[i][w] = __builtin_amdgcn_alignbit(v[i][w], v[i][w], 4);
-        auto nib = [&](int i, int j) -> float {
-            const uint32_t x = (j & 1) ? hv[i][j / 8] : v[i][j / 8];
-            switch ((j % 8) / 2) {
-                case 0: return int4_over16<0>(x);
-                case 1: return int4_over16<1>(x);
-                case 2: return int4_over16<2>(x);
-                default: return int4_over16<3>(x);
-            }
-        };
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const u32x2 x = {pack_bf16(nib(0, j), nib(1, j)), pack_bf16(nib(2, j), nib(3, j))};
-            a[j] = __builtin_bit_cast(s16x4, x);
-        }
+        static_assert(MODE != KVQ_INT4_PER_TOKEN_HEAD, "INT4 values widen in v_operands_int4");
     } else {
 #pragma unroll
         for (int j = 0; j < J; j += 2) {
@@ -279,6 +258,51 @@ __device__ __forceinline__ void v_operands(const uint32_t (*v)[Geo<HD, MODE>::VW
             a[j + 1] = __builtin_bit_cast(s16x4, y);
         }
     }
+}
+
+// INT4 V operands, biased like the keys: the lane's slice of a token is J
+// dims, dim j the low (j even) or high (j odd) nibble of slice byte j / 2.
+// One byte permute interleaves two tokens' byte pair p (dims 4p .. 4p+3):
+// [t0.B2p, t1.B2p, t0.B2p+1, t1.B2p+1]; XOR 8 per nibble makes n + 8 in
+// 0..15, and split into low and high nibbles each byte is the E4M3 code of
+// (n + 8) 2^-9, which the scaled conversion (2^5) turns into (n + 8) / 16,
+// exact in BF16.  So a pair of conversions gives one operand half: two
+// tokens of one dim.  The bias (8 / 16) sum_t P'_t leaves through its own
+// MFMA (int4_value_bias) and a subtraction at the end.  Every biased code is
+// finite, so masked tokens need no zeroing: their weight is 0.  vsel picks
+// the lane's byte pair from a token dword (2-byte slices at head_dim 64).
+template <int HD>
+__device__ __forceinline__ void v_operands_int4(const uint32_t (*v)[Geo<HD, KVQ_INT4_PER_TOKEN_HEAD>::VW],
+                                                uint32_t vsel, s16x4* a) {
+    using G = Geo<HD, KVQ_INT4_PER_TOKEN_HEAD>;
+#pragma unroll
+    for (int p = 0; p < G::J / 4; ++p) {
+        const int w = G::VB == 2 ? 0 : p / 2;
+        const uint32_t sel = G::VB == 2 ? vsel : ((p & 1) ? 0x07030602u : 0x05010400u);
+        const uint32_t x01 = __builtin_amdgcn_perm(v[1][w], v[0][w], sel) ^ 0x88888888u;
+        const uint32_t x23 = __builtin_amdgcn_perm(v[3][w], v[2][w], sel) ^ 0x88888888u;
+        const uint32_t lo01 = x01 & 0x0F0F0F0Fu, hi01 = (x01 >> 4) & 0x0F0F0F0Fu;
+        const uint32_t lo23 = x23 & 0x0F0F0F0Fu, hi23 = (x23 >> 4) & 0x0F0F0F0Fu;
+        const u32x2 d0 = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo01, 32.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo23, 32.0f, false))};
+        const u32x2 d1 = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi01, 32.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi23, 32.0f, false))};
+        const u32x2 d2 = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo01, 32.0f, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo23, 32.0f, true))};
+        const u32x2 d3 = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi01, 32.0f, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi23, 32.0f, true))};
+        a[4 * p] = __builtin_bit_cast(s16x4, d0);
+        a[4 * p + 1] = __builtin_bit_cast(s16x4, d1);
+        a[4 * p + 2] = __builtin_bit_cast(s16x4, d2);
+        a[4 * p + 3] = __builtin_bit_cast(s16x4, d3);
+    }
+}
+
+// The value bias of one tile: (8 / 16) sum_t P'_t for each query column, in
+// every row of the accumulator, through the P V product with every value 1/2.
+__device__ __forceinline__ f32x4 int4_value_bias(s16x4 b, f32x4 acc) {
+    const u32x2 halves = {0x3F003F00u, 0x3F003F00u};   // BF16 0.5
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, halves), b, acc, 0, 0, 0);
 }
 
 // ------------------------------------------------------------ the kernel
@@ -346,6 +370,7 @@ struct RawTile {
 struct LaneOff {
     uint32_t kv[kMaxStagedPieces]; // staged reads: the lane's 16-byte pieces of the tile's row pairs
     uint32_t vsh;                  // right shift that moves a 2-byte V slice to bits 0..15
+    uint32_t vsel;                 // byte-permute selector of the lane's 2-byte V slice (INT4 at head_dim 64)
     uint32_t k;                    // K slice of token r
     uint32_t v[4];                 // V slices of tokens 4q4+i
     uint32_t s[4];                 // (s_K, s_V) of tokens 4q4+i, from the scale trailer
@@ -364,6 +389,7 @@ __device__ __forceinline__ LaneOff lane_offsets(const AttnArgs& a, int h, int r,
         o.kv[c] = (tok * hkv + uh) * (2 * G::RB) + off;
     }
     o.vsh = G::VB == 2 ? 16u * static_cast<uint32_t>(r & 1) : 0u;
+    o.vsel = (r & 1) ? 0x07030602u : 0x05010400u;
     o.k = ((static_cast<uint32_t>(r) * hkv + uh) * 2) * G::RB + static_cast<uint32_t>(q4) * G::KB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -544,6 +570,7 @@ __device__ __forceinline__ void consume(const Tile<HD, MODE>& T) {
 template <int HD, int MODE>
 struct State {
     f32x4 o[Geo<HD, MODE>::J];     // O^T[dim slot 4q+i][head r], one per 16-dim tile
+    f32x4 vb;                      // INT4: (8 / 16) sum_t P'_t of head r, the bias of the biased values
     float m;                       // running maximum of head r (log2 domain)
     float l;                       // this lane's share of the running sum
 };
@@ -629,7 +656,7 @@ __device__ __forceinline__ f32x4 int4_key_bias(const QOperand<HD, false>& q) {
 template <int HD, int MODE, int NT, bool MASK, bool QF8, bool PACK>
 __device__ __forceinline__ void tile_round(const Tile<HD, MODE>* const* T, State<HD, MODE>& st,
                                            const QOperand<HD, QF8>& qo, f32x4 qk_init, int t0, int len, int r,
-                                           int q4, float k_factor, uint32_t vsh) {
+                                           int q4, float k_factor, uint32_t vsh, uint32_t vsel) {
     using G = Geo<HD, MODE>;
     f32x4 sacc[NT];
 #pragma unroll
@@ -713,28 +740,36 @@ __device__ __forceinline__ void tile_round(const Tile<HD, MODE>* const* T, State
         st.m = mnew;
     }
 
+    constexpr bool I4 = MODE == KVQ_INT4_PER_TOKEN_HEAD;
     s16x4 av[NT][G::J];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-        // masked tokens may hold any bytes (NaN codes included): zero them
-        uint32_t vz[4][G::VW];
+        if constexpr (I4) {
+            v_operands_int4<HD>(T[n]->v, vsel, av[n]);
+        } else {
+            // masked tokens may hold any bytes (NaN codes included): zero them
+            uint32_t vz[4][G::VW];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int w = 0; w < G::VW; ++w)
-                vz[i][w] = valid[n][i] ? (G::VB == 2 ? T[n]->v[i][w] >> vsh : T[n]->v[i][w]) : 0u;
-        v_operands<HD, MODE>(vz, av[n]);
+                for (int w = 0; w < G::VW; ++w)
+                    vz[i][w] = valid[n][i] ? (G::VB == 2 ? T[n]->v[i][w] >> vsh : T[n]->v[i][w]) : 0u;
+            v_operands<HD, MODE>(vz, av[n]);
+        }
     }
     // once the running maxima settle, alpha is 1 in every lane: skip the rescale
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
         for (int j = 0; j < G::J; ++j) st.o[j] *= alpha;
+        if constexpr (I4) st.vb *= alpha;
     }
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+    for (int n = 0; n < NT; ++n) {
 #pragma unroll
         for (int j = 0; j < G::J; ++j)
             st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[n][j], b[n], st.o[j], 0, 0, 0);
+        if constexpr (I4) st.vb = int4_value_bias(b[n], st.vb);
+    }
 }
 
 template <int HD, int MODE, bool SMALL_BS, bool QF8, bool PACK>
@@ -820,6 +855,7 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
     State<HD, MODE> st;
 #pragma unroll
     for (int j = 0; j < G::J; ++j) st.o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    st.vb = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     st.m = -INFINITY;
     st.l = 0.0f;
 
@@ -890,9 +926,11 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
                 }
                 const int t0 = (tau + k) * kTile;
                 if (attention_fast_path<HD>() && !SMALL_BS && t0 + NT * kTile <= lim && all_ok)
-                    tile_round<HD, MODE, NT, false, QF8, PACK>(rt, st, qo, qk_init, t0, lim, r, q4, k_factor, lo.vsh);
+                    tile_round<HD, MODE, NT, false, QF8, PACK>(rt, st, qo, qk_init, t0, lim, r, q4, k_factor, lo.vsh,
+                                                               lo.vsel);
                 else
-                    tile_round<HD, MODE, NT, true, QF8, PACK>(rt, st, qo, qk_init, t0, lim, r, q4, k_factor, lo.vsh);
+                    tile_round<HD, MODE, NT, true, QF8, PACK>(rt, st, qo, qk_init, t0, lim, r, q4, k_factor, lo.vsh,
+                                                              lo.vsel);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -902,6 +940,11 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
 
     float l = sum_q4(st.l);
     if constexpr (PACK) l += __uint_as_float(dpp<0x128>(__float_as_uint(l)));   // + the other tile's lanes
+    if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+        // the biased values' excess, the same in every dim of head r
+#pragma unroll
+        for (int j = 0; j < G::J; ++j) st.o[j] -= st.vb;
+    }
     // lane holds dims J*(4*q4 + i) + j, i < 4, j < J: hd/4 contiguous dims
     const int64_t row = static_cast<int64_t>(b) * a.num_q_heads + qh;
     if (a.splits == 1) {

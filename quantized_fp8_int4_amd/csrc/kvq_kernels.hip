@@ -273,6 +273,72 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&w)[N]) {
     }
 }
 
+// Decode the loaded chunks of one gather thread and store them as BF16 at
+// their packed output rows; BOUNDED skips rows at or past `room`.
+template <int HD, int MODE, int CB, int U, bool NTS, bool BOUNDED>
+__device__ __forceinline__ void gather_decode_store(const GatherArgs& p, const uint32_t (&cw)[U][CB / 4],
+                                                    const float (&sc)[U], const uint32_t (&chunk)[U],
+                                                    int64_t out_row0, int64_t room) {
+    constexpr uint32_t HB = row_bytes_of<MODE>(HD);
+    constexpr int DW = CB / 4;
+    constexpr uint32_t CPR = HB / CB;
+    constexpr int OUT_PER_DW = (MODE == KVQ_BF16) ? 1 : (MODE == KVQ_INT4_PER_TOKEN_HEAD ? 4 : 2);
+    constexpr int ODW = DW * OUT_PER_DW;
+    constexpr uint32_t EPC = ODW * 2;
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t row = chunk[u] / CPR;
+        const uint32_t col = chunk[u] % CPR;
+        uint16_t* const outp = ((row & 1u) ? p.out_v : p.out_k) +
+                               static_cast<uint64_t>(out_row0 + (row >> 1)) * HD + col * EPC;
+        const float s = sc[u];
+        uint32_t o[ODW];
+        if constexpr (MODE == KVQ_BF16) {
+#pragma unroll
+            for (int d = 0; d < DW; ++d) o[d] = cw[u][d];
+        } else if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+            // Byte e holds elements 2e (low nibble) and 2e+1.  While 16 s is
+            // finite, (n / 16)(16 s) is the same real number as n s, so it
+            // rounds alike; waves holding a larger scale widen n itself.
+            if (__builtin_amdgcn_ballot_w64(s > 0x1p120f) == 0) {
+                const float s16 = s * 16.0f;
+#pragma unroll
+                for (int d = 0; d < DW; ++d) {
+                    const uint32_t w = cw[u][d], hi = __builtin_amdgcn_alignbit(w, w, 4);
+                    o[4 * d + 0] = pack_bf16(int4_over16<0>(w) * s16, int4_over16<0>(hi) * s16);
+                    o[4 * d + 1] = pack_bf16(int4_over16<1>(w) * s16, int4_over16<1>(hi) * s16);
+                    o[4 * d + 2] = pack_bf16(int4_over16<2>(w) * s16, int4_over16<2>(hi) * s16);
+                    o[4 * d + 3] = pack_bf16(int4_over16<3>(w) * s16, int4_over16<3>(hi) * s16);
+                }
+            } else {
+#pragma unroll
+                for (int d = 0; d < DW; ++d) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float a = static_cast<float>(static_cast<int32_t>(cw[u][d] << (28 - 8 * e)) >> 28);
+                        const float bb = static_cast<float>(static_cast<int32_t>(cw[u][d] << (24 - 8 * e)) >> 28);
+                        o[4 * d + e] = pack_bf16(a * s, bb * s);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int d = 0; d < DW; ++d) {
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(cw[u][d]), false);
+                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(cw[u][d]), true);
+                o[2 * d] = pack_bf16(lo[0] * s, lo[1] * s);
+                o[2 * d + 1] = pack_bf16(hi[0] * s, hi[1] * s);
+            }
+        }
+        if (!BOUNDED || static_cast<int64_t>(row >> 1) < room) {
+#pragma unroll
+            for (int q = 0; q < ODW / 4; ++q)
+                st16<NTS>(outp + 8 * q, make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]));
+        }
+    }
+}
+
 // Sequences whose offset is summed without a loop: 64 lanes x kOffsetLoads.
 constexpr int kOffsetLoads = 4;
 
@@ -383,61 +449,19 @@ __global__ __launch_bounds__(TPB) void gather_kernel(GatherArgs p) {
     for (int k = 0; k < kOffsetLoads; ++k)
         off += (lane + 64u * k < b) ? max(lens[k], 0) : 0;
     off = wave_sum(off);
+    // (the same in every lane: made scalar, so that the fit test below is a
+    // wave-uniform branch)
+    off = static_cast<int64_t>(
+        (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(off >> 32)))) << 32) |
+        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(off))));
     const int64_t out_row0 = (off + t0) * p.hkv;
     // Token-head rows of this block that still fit the output (may be <= 0).
+    // A block that fits whole, the normal case, stores unconditionally.
     const int64_t room = p.out_th - out_row0;
-
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint32_t row = chunk[u] / CPR;
-        const uint32_t col = chunk[u] % CPR;
-        uint16_t* const outp = ((row & 1u) ? p.out_v : p.out_k) +
-                               static_cast<uint64_t>(out_row0 + (row >> 1)) * HD + col * EPC;
-        const float s = sc[u];
-        uint32_t o[ODW];
-        if constexpr (MODE == KVQ_BF16) {
-#pragma unroll
-            for (int d = 0; d < DW; ++d) o[d] = cw[u][d];
-        } else if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
-            // Byte e holds elements 2e (low nibble) and 2e+1.  While 16 s is
-            // finite, (n / 16)(16 s) is the same real number as n s, so it
-            // rounds alike; waves holding a larger scale widen n itself.
-            if (__builtin_amdgcn_ballot_w64(s > 0x1p120f) == 0) {
-                const float s16 = s * 16.0f;
-#pragma unroll
-                for (int d = 0; d < DW; ++d) {
-                    const uint32_t w = cw[u][d], hi = __builtin_amdgcn_alignbit(w, w, 4);
-                    o[4 * d + 0] = pack_bf16(int4_over16<0>(w) * s16, int4_over16<0>(hi) * s16);
-                    o[4 * d + 1] = pack_bf16(int4_over16<1>(w) * s16, int4_over16<1>(hi) * s16);
-                    o[4 * d + 2] = pack_bf16(int4_over16<2>(w) * s16, int4_over16<2>(hi) * s16);
-                    o[4 * d + 3] = pack_bf16(int4_over16<3>(w) * s16, int4_over16<3>(hi) * s16);
-                }
-            } else {
-#pragma unroll
-                for (int d = 0; d < DW; ++d) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float a = static_cast<float>(static_cast<int32_t>(cw[u][d] << (28 - 8 * e)) >> 28);
-                        const float bb = static_cast<float>(static_cast<int32_t>(cw[u][d] << (24 - 8 * e)) >> 28);
-                        o[4 * d + e] = pack_bf16(a * s, bb * s);
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int d = 0; d < DW; ++d) {
-                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(cw[u][d]), false);
-                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(cw[u][d]), true);
-                o[2 * d] = pack_bf16(lo[0] * s, lo[1] * s);
-                o[2 * d + 1] = pack_bf16(hi[0] * s, hi[1] * s);
-            }
-        }
-        if (static_cast<int64_t>(row >> 1) < room) {
-#pragma unroll
-            for (int q = 0; q < ODW / 4; ++q)
-                st16<NTS>(outp + 8 * q, make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]));
-        }
-    }
+    if (room >= static_cast<int64_t>(nrows / 2))
+        gather_decode_store<HD, MODE, CB, U, NTS, false>(p, cw, sc, chunk, out_row0, 0);
+    else
+        gather_decode_store<HD, MODE, CB, U, NTS, true>(p, cw, sc, chunk, out_row0, room);
 }
 
 // ---------------------------------------------------------- static table
