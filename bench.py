@@ -32,12 +32,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gqa32_fp8_per_token_head.md")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gqa32_all_layouts.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_fp8_int4_amd", "csrc", f)
                   for f in ("kvq_kernels.hip", "kvq_device.h", "kvq_exact.h")]
 METRIC = "kvq_store/gather GB/s and % of HBM peak; cached tokens/s (per-token-head FP8)"
 COPY_BYTES = 256 << 20
-PROFILE_KERNEL_TRACE = os.path.join(ROOT, "profiles", "kernel_trace_gqa32_fp8_per_token_head.md")
 
 
 def log(msg):
@@ -204,18 +203,33 @@ def measured_attention_traffic(mode_name, hd):
     return float(m_val.group(1))
 
 
-def measured_traffic():
-    """Per-launch HBM bytes of the dominant kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+def measured_traffic(path=PROFILE_TRAFFIC):
+    """Per-launch HBM bytes of each profiled kernel ("store/128/3": kind,
+    head_dim, mode) from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel source."""
+    if not os.path.exists(path):
         return None
-    text = open(PROFILE_TRAFFIC).read()
+    text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    m_val = re.search(r"traffic_bytes_per_launch\[(\w+)\]:\s*([0-9.eE+]+)", text)
     if not m_hash or m_hash.group(1) != kernel_source_hash():
         return None
-    vals = dict(re.findall(r"traffic_bytes_per_launch\[(\w+)\]:\s*([0-9.eE+]+)", text))
+    vals = dict(re.findall(r"traffic_bytes_per_launch\[([\w/]+)\]:\s*([0-9.eE+]+)", text))
     return {k: float(v) for k, v in vals.items()}
+
+
+def _kernel_key(name):
+    """(kind/head_dim/mode, short name) of a library or ceiling kernel's
+    demangled name, or None for other kernels."""
+    m = re.search(r"\b(store_kernel|gather_kernel|attention_kernel|combine_kernel|combine_wide_kernel|calib_kernel|"
+                  r"store_pattern_kernel|gather_pattern_kernel|linear_copy_kernel)(?:<([^>]*)>)?", name)
+    if not m:
+        return None
+    kind = m.group(1).replace("_kernel", "")
+    short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
+    targs = [t.strip() for t in (m.group(2) or "").split(",") if t.strip()]
+    # library kernels by head_dim and mode; the ceiling kernels by all their arguments
+    keep = targs[:2] if kind in ("store", "gather", "attention", "calib") else targs
+    return "/".join([kind] + keep), short
 
 
 def _read_csv(directory, suffix):
@@ -250,55 +264,6 @@ def _counter_per_kernel(rows, counter):
     top = max(copies)
     acc["copy"] = [v for v in copies if v >= 0.5 * top]
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
-
-
-def summarize_profiles(kt_dir, fetch_dir, write_dir):
-    """profiles/ summaries from three rocprofv3 runs of bench.py (kernel trace
-    with --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, the latter two with
-    --calibrate-copy).  Counter KiB are scaled by the copy kernel's reading of
-    a copy of known size."""
-    stats = _read_csv(kt_dir, "kernel_stats.csv")
-    lines = ["# Kernel trace: GQA-32 store + gather, per-token-head FP8", "",
-             "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
-             f"    rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(kt_dir))} -o run -- python3 $R/bench.py",
-             "", "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
-    for r in stats:
-        name = r.get("Name") or r.get("KernelName") or ""
-        if "kvq" not in name:
-            continue
-        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
-        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
-                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
-    with open(PROFILE_KERNEL_TRACE, "w") as f:
-        f.write("\n".join(lines) + "\n")
-
-    fetch = _counter_per_kernel(_read_csv(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
-    write = _counter_per_kernel(_read_csv(write_dir, "counter_collection.csv"), "WRITE_SIZE")
-    f_scale = COPY_BYTES / (fetch["copy"][0] * 1024.0)
-    w_scale = COPY_BYTES / (write["copy"][0] * 1024.0)
-    import quantized_fp8_int4_amd as kvq
-    store_b, gather_b = algorithmic_bytes(kvq.FP8_PER_TOKEN_HEAD, 128, 8, 16, 32768 * 8)
-    algo = {"store": store_b, "gather": gather_b}
-    out = ["# HBM traffic per launch: GQA-32 per-token-head FP8 (32768 tokens x 8 KV heads x head_dim 128)", "",
-           "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
-           f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(fetch_dir))} -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
-           f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(write_dir))} -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
-           "",
-           f"Calibration: a {COPY_BYTES >> 20} MiB device-to-device copy reads FETCH_SIZE {fetch['copy'][0]:.0f} KiB and "
-           f"WRITE_SIZE {write['copy'][0]:.0f} KiB per dispatch; scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
-           "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched bytes (scaled) | written bytes (scaled) | traffic | algorithmic | traffic / algorithmic |",
-           "|---|---|---|---|---|---|---|---|---|"]
-    for k in ("store", "gather"):
-        fb = fetch[k][0] * 1024.0 * f_scale
-        wb = write[k][0] * 1024.0 * w_scale
-        out.append(f"| {k}_kernel | {fetch[k][1]} | {fetch[k][0]:.0f} | {write[k][0]:.0f} | {fb:.4g} | {wb:.4g} | "
-                   f"{fb + wb:.4g} | {algo[k]:.4g} | {(fb + wb) / algo[k]:.3f} |")
-    out += ["", f"kernel_source_sha256_16: {kernel_source_hash()}"]
-    for k in ("store", "gather"):
-        out.append(f"traffic_bytes_per_launch[{k}]: {fetch[k][0] * 1024.0 * f_scale + write[k][0] * 1024.0 * w_scale:.6g}")
-    with open(PROFILE_TRAFFIC, "w") as f:
-        f.write("\n".join(out) + "\n")
-    print("\n".join(lines + [""] + out))
 
 
 def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, layers=0):
@@ -361,6 +326,83 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, la
     with open(tr_path, "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(lines + [""] + out))
+
+
+def summarize_kernels(kt_dir, fetch_dir, write_dir, tag, bytes_json, bench_args):
+    """profiles/kernel_trace_<tag>.md and profiles/traffic_<tag>.md from three
+    rocprofv3 runs of `bench.py <bench_args>` (kernel trace with --stats;
+    --pmc FETCH_SIZE; --pmc WRITE_SIZE, the counter runs with
+    --calibrate-copy), with each kernel's algorithmic bytes per launch from the
+    JSON the bench wrote with --launch-bytes-out.  Counter KiB are scaled by
+    what the same counters read for a 256 MiB device-to-device copy."""
+    import json as _json
+    stats = _read_csv(kt_dir, "kernel_stats.csv")
+    kt_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(kt_dir))} "
+              f"-o run -- python3 $R/bench.py {bench_args}")
+    lines = [f"# Kernel trace: {tag}", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+             f"    {kt_cmd}", "", "| kernel | calls | average (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r.get("Name") or r.get("KernelName") or ""
+        if _kernel_key(name) is None:
+            continue
+        lines.append(f"| {_kernel_key(name)[1]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{tag}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_kernel(rows, counter):
+        acc, names, copies = {}, {}, []
+        for r in rows:
+            if r.get("Counter_Name") != counter:
+                continue
+            val = float(r["Counter_Value"])
+            if "copyBuffer" in r["Kernel_Name"]:
+                copies.append(val)
+                continue
+            kk = _kernel_key(r["Kernel_Name"])
+            if kk is None:
+                continue
+            acc.setdefault(kk[0], []).append(val)
+            names[kk[0]] = kk[1]
+        top = max(copies)
+        copy = [v for v in copies if v >= 0.5 * top]
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}, names, sum(copy) / len(copy)
+
+    fetch, names, fcopy = per_kernel(_read_csv(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    write, _, wcopy = per_kernel(_read_csv(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    f_scale, w_scale = COPY_BYTES / (fcopy * 1024.0), COPY_BYTES / (wcopy * 1024.0)
+    algo = _json.load(open(bytes_json))
+    cmd = lambda c, d: (f"rocprofv3 --pmc {c} --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(d))} "
+                        f"-o run -- python3 $R/bench.py {bench_args} --calibrate-copy")
+    out = [f"# HBM traffic per launch: {tag}", "",
+           "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+           f"    {cmd('FETCH_SIZE', fetch_dir)}", f"    {cmd('WRITE_SIZE', write_dir)}", "",
+           f"Calibration: a {COPY_BYTES >> 20} MiB device-to-device copy reads FETCH_SIZE {fcopy:.0f} KiB and "
+           f"WRITE_SIZE {wcopy:.0f} KiB per dispatch; scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write).",
+           "", "Algorithmic bytes per launch are the bench's own (what each launch must move: no re-reads, no padding).",
+           "", "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched bytes (scaled) | written bytes (scaled) "
+               "| traffic | algorithmic | traffic / algorithmic |", "|---|---|---|---|---|---|---|---|---|"]
+    tail = ["", f"kernel_source_sha256_16: {kernel_source_hash()}"]
+    for k in sorted(fetch):
+        if k not in write:
+            continue
+        fb, wb = fetch[k][0] * 1024.0 * f_scale, write[k][0] * 1024.0 * w_scale
+        a = algo.get(k)
+        out.append(f"| {names[k]} | {fetch[k][1]} | {fetch[k][0]:.0f} | {write[k][0]:.0f} | {fb:.4g} | {wb:.4g} | "
+                   f"{fb + wb:.4g} | {'-' if a is None else f'{a:.4g}'} | {'-' if not a else f'{(fb + wb) / a:.3f}'} |")
+        tail.append(f"traffic_bytes_per_launch[{k}]: {fb + wb:.6g}")
+    with open(os.path.join(ROOT, "profiles", f"traffic_{tag}.md"), "w") as f:
+        f.write("\n".join(out + tail) + "\n")
+    print("\n".join(lines + [""] + out + tail))
+
+
+def write_launch_bytes(path, entries):
+    """The algorithmic bytes per launch of each kernel a run launched
+    ({"store/128/3": bytes, ...}), for summarize_kernels."""
+    if path:
+        with open(path, "w") as f:
+            json.dump({k: float(v) for k, v in entries.items()}, f, indent=1)
 
 
 GQA32_LAYOUTS = ("fp8_per_token_head", "fp8_per_tensor", "fp8_per_head", "int4_per_token_head")
@@ -721,6 +763,7 @@ def run_other_workload(args, torch, kvq, W):
     dev = torch.device("cuda", 0)
     oracle.build(force=False)
     name = args.workload
+    launch_bytes = {}
     if name == "long80":
         spec = W.WORKLOADS["long80"]
         L, hkv, hd, bs, T = spec["num_layers"], spec["hkv"], spec["hd"], spec["block_size"], spec["seq_len"]
@@ -748,6 +791,7 @@ def run_other_workload(args, torch, kvq, W):
         store_s = sum(e[0].elapsed_time(e[1]) for e in evs) / (args.steps * L) / 1e3
         gather_s = sum(e[1].elapsed_time(e[2]) for e in evs) / (args.steps * L) / 1e3
         sb, gb = algorithmic_bytes(mode, hd, hkv, bs, T * hkv)
+        launch_bytes.update({f"store/{hd}/{mode}": sb, f"gather/{hd}/{mode}": gb})
         # oracle: one layer, store + gather
         g = oracle.Geometry(bs, hkv, hd, [mode], [nb])
         host = oracle.new_cache(g)
@@ -827,6 +871,8 @@ def run_other_workload(args, torch, kvq, W):
         slide_gather_s = phase([(Lc.gather, ga[l]) for l in slide])
         sb, gb = algorithmic_bytes(kvq.FP8_PER_TOKEN_HEAD, hd, hkv, bs, T * hkv)
         ssb, sgb = algorithmic_bytes(kvq.BF16, hd, hkv, bs, Wn * hkv)
+        launch_bytes.update({f"store/{hd}/{kvq.FP8_PER_TOKEN_HEAD}": sb, f"gather/{hd}/{kvq.FP8_PER_TOKEN_HEAD}": gb,
+                             f"store/{hd}/{kvq.BF16}": ssb, f"gather/{hd}/{kvq.BF16}": sgb})
         step_bytes = len(full) * (sb + gb) + len(slide) * (ssb + sgb)
         g = oracle.Geometry(bs, hkv, hd, modes, nbs)
         host = oracle.new_cache(g)
@@ -1052,6 +1098,11 @@ def run_other_workload(args, torch, kvq, W):
         ntok = int(lens_last.sum())
         sb, _ = algorithmic_bytes(mode, hd, hkv, bs, S * hkv)
         _, gb = algorithmic_bytes(mode, hd, hkv, bs, ntok * hkv)
+        # every gather launch of the run (warmup steps included) reads its step's
+        # lengths; the store launches mix the prefill's 32768-token calls with
+        # the 256-token appends, so no single figure is theirs
+        mean_tok = sum(int(x.sum()) for x in D["lens_at"]) / len(D["lens_at"])
+        launch_bytes.update({f"gather/{hd}/{mode}": algorithmic_bytes(mode, hd, hkv, bs, mean_tok * hkv)[1]})
         # oracle sample: the oracle's own image of layer L-1 (its store of the
         # same seeded inputs), then its gather of 8 sequences, timed
         g, host = _decode_oracle_layer(D, torch, W, oracle)
@@ -1185,6 +1236,14 @@ def run_other_workload(args, torch, kvq, W):
                "cpu_baseline": cpu,
                "parity_vs_oracle_sampled": parity,
                "workspace_bytes": wsb, "cache_GiB": round(D["cache"].bytes["total"] / 2**30, 3)}
+    if args.calibrate_copy and name != "attention":
+        # the counter runs' reference: copies of a known size
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    write_launch_bytes(args.launch_bytes_out, launch_bytes)
     print(json.dumps(res), flush=True)
 
 
@@ -1210,15 +1269,18 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="gqa32: time only the --mode layout (default: also the other three layouts of the target)")
     ap.add_argument("--no-ceiling", action="store_true", help="gqa32: skip the bandwidth-ceiling kernels")
+    ap.add_argument("--launch-bytes-out", default="",
+                    help="write the algorithmic bytes per launch of each kernel run (JSON) for --summarize-kernels")
+    ap.add_argument("--summarize-kernels", nargs=6,
+                    metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "TAG", "LAUNCH_BYTES_JSON", "BENCH_ARGS"),
+                    help="write profiles/kernel_trace_TAG.md and traffic_TAG.md from rocprofv3 csv output and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, copy 256 MiB device-to-device 3 times (reference for counter scaling)")
     ap.add_argument("--summarize-attention-profiles", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the attention profiles/ summaries (for --mode and --head-dim) and exit")
-    ap.add_argument("--summarize-profiles", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="write the profiles/ summaries from rocprofv3 csv output and exit")
     args = ap.parse_args()
-    if args.summarize_profiles:
-        summarize_profiles(*args.summarize_profiles)
+    if args.summarize_kernels:
+        summarize_kernels(*args.summarize_kernels)
         return
     if args.summarize_attention_profiles:
         summarize_attention_profiles(*args.summarize_attention_profiles, args.mode, args.head_dim, args.layers)
@@ -1253,6 +1315,7 @@ def run_gqa32(args, torch, kvq, W):
     order = [args.mode] + ([m for m in GQA32_LAYOUTS if m != args.mode] if not args.headline_only else [])
     layouts, head = {}, None
     cpu = cpu_one = None
+    launch_bytes = {}
     for name in order:
         LA = gqa32_layout(torch, kvq, W, I, name)
         store_s, gather_s, wall = time_layout(torch, kvq, LA, args.steps, args.warmup)
@@ -1287,6 +1350,8 @@ def run_gqa32(args, torch, kvq, W):
             rec["parity_vs_oracle_sampled"] = parity
             rec["parity_layers"] = len(sample)
         layouts[name] = rec
+        launch_bytes[f"store/{I['hd']}/{LA['mode']}"] = LA["store_bytes"]
+        launch_bytes[f"gather/{I['hd']}/{LA['mode']}"] = LA["gather_bytes"]
         if name != args.mode:
             LA["cache"].close()
             del LA
@@ -1348,8 +1413,10 @@ def run_gqa32(args, torch, kvq, W):
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    # the committed counters were taken on the default shape and mode only
-    traffic = measured_traffic() if (args.mode == "fp8_per_token_head" and args.tp == 1) else None
+    write_launch_bytes(args.launch_bytes_out, launch_bytes)
+    # the committed counters were taken on the default shape only
+    traffic = measured_traffic() if args.tp == 1 else None
+    dom_key = f"{dominant}/{I['hd']}/{LA['mode']}"
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -1379,7 +1446,7 @@ def run_gqa32(args, torch, kvq, W):
         "algorithmic_bytes_per_step": int(step_bytes),
         "roofline": {"bound": "hbm", "kernel": f"{dominant}_kernel", "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None if traffic is None else traffic.get(dominant)},
+                     "traffic": None if traffic is None else traffic.get(dom_key)},
         "cpu_baseline": cpu,
         "cpu_single_core": cpu_one,
         "parity_vs_oracle_sampled": layouts[args.mode]["parity_vs_oracle_sampled"],
