@@ -985,6 +985,400 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
     }
 }
 
+// ------------------------------------------------------ the quad kernel
+//
+// Query groups of at most 4 heads fill at most 4 of the 16 MFMA columns of
+// a KV head's products, so the per-tile softmax would run on 12 idle
+// columns.  Here a wave serves a quad of 4 KV heads at once: column r is
+// query g = r % 4 of KV head h0 + r / 4.  The Q K^T product of a tile
+// accumulates the quad's 4 heads one after another into one accumulator,
+// each with its keys as the A operand and a query operand that holds only
+// that head's columns (the others zero: block diagonal), so every column
+// gets exactly its own head's scores; the P V product likewise takes each
+// head's values with the weights of that head's columns only.  The softmax
+// then runs once per tile for all 16 columns.
+//
+// The grid, the plan and the partial results are those of attention_kernel:
+// a workgroup still covers a run of heads_per_wg (4 or 8) KV heads of one
+// sequence over one split, with one wave per KV head; here its waves are
+// heads_per_wg / 4 quads times 4 waves, and the 4 waves of a quad take every
+// fourth tile of the split (interleaved, so the workgroup streams adjacent
+// tiles), then merge their (O, m, l) through LDS before the output.
+//
+// Used at head_dim 64 in the FP8 and INT4 modes (tiles of 4 or 8 KiB per
+// quad), with BF16 queries, blocks of at least 16 tokens and query groups
+// of at most 4.
+template <int HD, int MODE>
+struct QuadGeo {
+    using G = Geo<HD, MODE>;
+    static constexpr int QROW = 4 * 2 * G::RB;            // a position's K|V rows of the quad's 4 heads
+    static constexpr int NC = 16 * QROW / 1024;            // 16-byte pieces per lane of a tile
+    static constexpr int LDS_ROW = QROW + 16;
+    static constexpr int LDS_TILE = 16 * LDS_ROW;
+    static constexpr int MERGE = 64 * (2 + 4 * G::J) * 4;  // a wave's (m, l, O) for the merge
+    static constexpr int LDS_WAVE = LDS_TILE > MERGE ? LDS_TILE : MERGE;
+    static constexpr int D = NC <= 4 ? 3 : 2;              // tiles in flight per wave
+};
+
+template <int HD, int MODE>
+constexpr bool attention_quads() {
+    // (INT4 at head_dim 128 would fit 8 KiB tiles but spills registers)
+    return MODE != KVQ_BF16 && HD == 64 && QuadGeo<HD, MODE>::NC <= 8;
+}
+
+template <int HD, int MODE>
+struct QuadRaw {
+    uint32_t kv[4 * QuadGeo<HD, MODE>::NC];
+    f32x2 s[4];                    // (s_K, s_V) of tokens 4q+i, KV head h0 + r / 4
+    uint32_t ok;
+};
+
+struct QuadLaneOff {
+    uint32_t kv[8];                // the lane's 16-byte pieces of the tile's row image
+    uint32_t lds[8];               // ... and where they go in the wave's LDS rows
+    uint32_t s[4];                 // (s_K, s_V) of tokens 4q+i for the lane's column head
+};
+
+template <int HD, int MODE>
+__device__ __forceinline__ void quad_load(const AttnArgs& a, int blk, int tau, const QuadLaneOff& lo,
+                                          QuadRaw<HD, MODE>& T) {
+    using G = Geo<HD, MODE>;
+    using Q = QuadGeo<HD, MODE>;
+    const bool ok = static_cast<uint32_t>(blk) < static_cast<uint32_t>(a.num_blocks);
+    const uint32_t ublk = ok ? static_cast<uint32_t>(blk) : 0u;
+    const uint32_t pos0 = static_cast<uint32_t>((tau * kTile) & ((1 << a.bs_log2) - 1));
+    const uint8_t* base = a.layer + static_cast<uint64_t>(ublk) * static_cast<uint64_t>(a.block_bytes);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(base), 0, static_cast<int>(a.block_bytes), kBufferDword3);
+    const int srow = static_cast<int>(pos0 * static_cast<uint32_t>(a.hkv) * (2 * G::RB));
+#pragma unroll
+    for (int c = 0; c < Q::NC; ++c) buf_load<16, kNonTemporal>(T.kv + 4 * c, rs, lo.kv[c], srow);
+    if constexpr (G::DYN) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t w[2];
+            buf_load<8, 0>(w, rs, lo.s[i], static_cast<int>(pos0 * static_cast<uint32_t>(a.hkv) * 8u));
+            T.s[i] = f32x2{__uint_as_float(w[0]), __uint_as_float(w[1])};
+        }
+    }
+    T.ok = ok ? 0xFu : 0u;
+}
+
+template <int HD, int MODE>
+__device__ __forceinline__ void consume(const QuadRaw<HD, MODE>& T) {
+#pragma unroll
+    for (int w = 0; w < 4 * QuadGeo<HD, MODE>::NC; ++w) asm volatile("" ::"v"(T.kv[w]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if constexpr (Geo<HD, MODE>::DYN) asm volatile("" ::"v"(T.s[i][0]), "v"(T.s[i][1]));
+}
+
+// One tile of the quad: scores of all 16 columns, one softmax update, the
+// 4 heads' value products.  MASK = false: every token of the tile lies below
+// len in a block of the layer.
+template <int HD, int MODE, bool MASK>
+__device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uint8_t* lds, State<HD, MODE>& st,
+                                           const bf16x8 (*qb)[HD / 32], f32x4 qk_init, int t0, int len, int r,
+                                           int q4, float k_factor, uint32_t vsh, uint32_t vsel) {
+    using G = Geo<HD, MODE>;
+    using Q = QuadGeo<HD, MODE>;
+    constexpr bool I4 = MODE == KVQ_INT4_PER_TOKEN_HEAD;
+    // Q K^T, head by head into one accumulator
+    f32x4 sacc = qk_init;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        uint32_t k[G::KW];
+        const uint8_t* kp = lds + r * Q::LDS_ROW + h * 2 * G::RB + q4 * G::KB;
+#pragma unroll
+        for (int w = 0; w < G::KW; w += 2) {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(kp + 4 * w);
+            k[w] = v[0];
+            k[w + 1] = v[1];
+        }
+#pragma unroll
+        for (int j = 0; j < HD / 32; ++j)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(k, j), qb[h][j], sacc, 0, 0, 0);
+    }
+    bool valid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) valid[i] = !MASK || ((t0 + 4 * q4 + i < len) && ((R.ok >> i) & 1u));
+    float s[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float f = G::DYN ? R.s[i][0] * k_factor : k_factor;
+        s[i] = valid[i] ? sacc[i] * f : -INFINITY;
+        tmax = fmaxf(tmax, s[i]);
+    }
+    tmax = max_q4(tmax);
+    const float mnew = fmaxf(st.m, tmax);
+    const float mref = mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mref);
+    float p[4], pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(s[i] - mref);
+        pv[i] = valid[i] ? (G::DYN ? p[i] * R.s[i][1] : p[i]) : 0.0f;
+    }
+    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    st.m = mnew;
+    const u32x2 pb = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int j = 0; j < G::J; ++j) st.o[j] *= alpha;
+        if constexpr (I4) st.vb *= alpha;
+    }
+    // P V, head by head: head h's values with the weights of its columns only
+    const int hq = r >> 2;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        uint32_t v[4][G::VW];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint8_t* vp = lds + (4 * q4 + i) * Q::LDS_ROW + (2 * h + 1) * G::RB + ((r * G::VB) & ~(G::VL - 1));
+#pragma unroll
+            for (int w = 0; w < G::VW; ++w) {
+                const uint32_t x = reinterpret_cast<const uint32_t*>(vp)[w];
+                // masked tokens may hold any bytes (NaN codes included): zero
+                // them, except INT4, whose biased codes are all finite
+                v[i][w] = (I4 || valid[i]) ? x : 0u;
+            }
+        }
+        s16x4 av[G::J];
+        if constexpr (I4) {
+            v_operands_int4<HD>(v, vsel, av);
+        } else {
+            if constexpr (G::VB == 2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int w = 0; w < G::VW; ++w) v[i][w] >>= vsh;
+            }
+            v_operands<HD, MODE>(v, av);
+        }
+        const u32x2 pbh = {hq == h ? pb[0] : 0u, hq == h ? pb[1] : 0u};
+#pragma unroll
+        for (int j = 0; j < G::J; ++j)
+            st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[j], __builtin_bit_cast(s16x4, pbh), st.o[j], 0, 0, 0);
+    }
+    if constexpr (I4) st.vb = int4_value_bias(__builtin_bit_cast(s16x4, pb), st.vb);
+}
+
+template <int HD, int MODE>
+__global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_quad_kernel(AttnArgs a) {
+    using G = Geo<HD, MODE>;
+    using Q = QuadGeo<HD, MODE>;
+    // work item: as attention_kernel (qgroups is 1: groups of at most 4)
+    const uint32_t p = blockIdx.x;
+    const uint32_t xcd = p % 8u, slot = p / 8u;
+    const uint32_t per = a.total_wg / 8u, rem = a.total_wg % 8u;
+    uint32_t item = xcd * per + min(xcd, rem) + slot;
+    const int chunk = static_cast<int>(item % static_cast<uint32_t>(a.head_chunks));
+    item /= static_cast<uint32_t>(a.head_chunks);
+    const int split = static_cast<int>(item % static_cast<uint32_t>(a.splits));
+    const int b = static_cast<int>(item / static_cast<uint32_t>(a.splits));
+
+    // (scalar: the tile indices, block ids and buffer descriptors derived
+    // from it stay wave-uniform)
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int sr = wave & 3;                                   // the wave's share of the tiles
+    const int h0 = chunk * a.heads_per_wg + (wave >> 2) * 4;   // the quad's first KV head
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, q4 = lane >> 4;
+    const int hq = r >> 2, g = r & 3;
+    const int hk = h0 + hq;                                    // the column's KV head
+
+    const int len = max(0, min(a.seq_lens[b], a.max_len));
+    const int ntiles = (len + kTile - 1) / kTile;
+    const int tbeg = split * a.tiles_per_split;
+    const int tend = min(ntiles, tbeg + a.tiles_per_split);
+    if (a.splits > 1 && tbeg >= tend) return;      // (the whole workgroup) the combine reads only non-empty splits
+
+    const bool qvalid = g < a.group;
+    const int qh = hk * a.group + (qvalid ? g : 0);
+    QOperand<HD, false> qo;
+    {
+        const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.num_q_heads + qh) * HD + q4 * (HD / 4);
+#pragma unroll
+        for (int j = 0; j < HD / 32; ++j) {
+            const uint4 v = qvalid ? ld16<false>(qp + 8 * j) : make_uint4(0, 0, 0, 0);
+            const u32x4 w = {v.x, v.y, v.z, v.w};
+            qo.b[j] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+    f32x4 qk_init = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+        int4_query_order<HD>(qo);
+        qk_init = int4_key_bias<HD>(qo);
+    }
+    // block-diagonal query operands: head h's products see only its columns
+    bf16x8 qb[4][HD / 32];
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int j = 0; j < HD / 32; ++j) {
+            const u32x4 w = __builtin_bit_cast(u32x4, qo.b[j]);
+            const u32x4 z = {hq == h ? w[0] : 0u, hq == h ? w[1] : 0u, hq == h ? w[2] : 0u, hq == h ? w[3] : 0u};
+            qb[h][j] = __builtin_bit_cast(bf16x8, z);
+        }
+
+    float k_factor = a.c * G::CODE_UNIT;
+    float v_factor = G::CODE_UNIT;
+    if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
+        k_factor *= a.statics[0];
+        v_factor = a.statics[1];
+    } else if constexpr (MODE == KVQ_FP8_PER_HEAD) {
+        k_factor *= a.statics[hk];
+        v_factor = a.statics[a.hkv + hk];
+    }
+
+    State<HD, MODE> st;
+#pragma unroll
+    for (int j = 0; j < G::J; ++j) st.o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    st.vb = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    st.m = -INFINITY;
+    st.l = 0.0f;
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    uint8_t* const lds = lds_dyn + wave * Q::LDS_WAVE;
+    QuadLaneOff lo;
+    {
+        const uint32_t hkv = static_cast<uint32_t>(a.hkv), uh0 = static_cast<uint32_t>(h0);
+#pragma unroll
+        for (int c = 0; c < Q::NC; ++c) {
+            const uint32_t gb = static_cast<uint32_t>(c) * 1024u + static_cast<uint32_t>(lane) * 16u;
+            const uint32_t tok = gb / Q::QROW, off = gb % Q::QROW;
+            lo.kv[c] = (tok * hkv + uh0) * (2 * G::RB) + off;
+            lo.lds[c] = tok * Q::LDS_ROW + off;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            lo.s[i] = static_cast<uint32_t>(a.code_bytes) +
+                      ((static_cast<uint32_t>(4 * q4 + i) * hkv + static_cast<uint32_t>(hk)) * 8u);
+    }
+    const uint32_t vsh = G::VB == 2 ? 16u * static_cast<uint32_t>(r & 1) : 0u;
+    const uint32_t vsel = (r & 1) ? 0x07030602u : 0x05010400u;
+
+    const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+    const int first = tbeg + sr;
+    const int nt = first < tend ? (tend - first + 3) / 4 : 0;     // this wave's tiles: first, first + 4, ...
+    if (nt > 0) {
+        constexpr int D = Q::D;
+        const int lim = min(len, tend * kTile);
+        // tiles past the wave's last re-read the last (and are not used)
+        auto tile_of = [&](int k) { return first + 4 * min(k, nt - 1); };
+        auto block_of = [&](int k) { return bt_row[(tile_of(k) * kTile) >> a.bs_log2]; };
+        QuadRaw<HD, MODE> t[D];
+#pragma unroll
+        for (int k = 0; k < D - 1; ++k) {
+            quad_load<HD, MODE>(a, block_of(k), tile_of(k), lo, t[k]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        int nb = block_of(D - 1);
+        for (int k0 = 0; k0 < nt; k0 += D) {
+#pragma unroll
+            for (int kk = 0; kk < D; ++kk) {
+                const int k = k0 + kk;
+                quad_load<HD, MODE>(a, nb, tile_of(k + D - 1), lo, t[(kk + D - 1) % D]);
+                nb = block_of(k + D);
+                __builtin_amdgcn_sched_barrier(0);
+                if (k < nt) {
+                    // the tile into the wave's LDS rows, then its operands back out
+#pragma unroll
+                    for (int c = 0; c < Q::NC; ++c) {
+                        const u32x4 v = {t[kk].kv[4 * c], t[kk].kv[4 * c + 1], t[kk].kv[4 * c + 2], t[kk].kv[4 * c + 3]};
+                        *reinterpret_cast<u32x4*>(lds + lo.lds[c]) = v;
+                    }
+                    const int t0 = tile_of(k) * kTile;
+                    if (t0 + kTile <= lim && t[kk].ok != 0)
+                        quad_round<HD, MODE, false>(t[kk], lds, st, qb, qk_init, t0, lim, r, q4, k_factor, vsh, vsel);
+                    else
+                        quad_round<HD, MODE, true>(t[kk], lds, st, qb, qk_init, t0, lim, r, q4, k_factor, vsh, vsel);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < D - 1; ++k) consume(t[k]);
+    }
+
+    float l = sum_q4(st.l);
+    if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+#pragma unroll
+        for (int j = 0; j < G::J; ++j) st.o[j] -= st.vb;
+    }
+    // merge the quad's 4 waves: each writes (m, l, O) to its LDS, the first
+    // of the quad rescales and adds the others' to its own
+    __syncthreads();
+    float* const mine = reinterpret_cast<float*>(lds_dyn + wave * Q::LDS_WAVE);
+    mine[lane] = st.m;
+    mine[64 + lane] = l;
+#pragma unroll
+    for (int j = 0; j < G::J; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[(2 + 4 * j + i) * 64 + lane] = st.o[j][i];
+    __syncthreads();
+    if (sr != 0) return;
+    float m = st.m;
+#pragma unroll
+    for (int w = 1; w < 4; ++w) m = fmaxf(m, reinterpret_cast<const float*>(lds_dyn + (wave + w) * Q::LDS_WAVE)[lane]);
+    const float mref = m == -INFINITY ? 0.0f : m;
+    {
+        const float f0 = __builtin_amdgcn_exp2f(st.m - mref);
+        l *= f0;
+#pragma unroll
+        for (int j = 0; j < G::J; ++j) st.o[j] *= f0;
+    }
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+        const float* other = reinterpret_cast<const float*>(lds_dyn + (wave + w) * Q::LDS_WAVE);
+        const float f = __builtin_amdgcn_exp2f(other[lane] - mref);
+        l += f * other[64 + lane];
+#pragma unroll
+        for (int j = 0; j < G::J; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.o[j][i] += f * other[(2 + 4 * j + i) * 64 + lane];
+    }
+    st.m = m;
+    // lane holds dims J*(4*q4 + i) + j of query head qh, as attention_kernel
+    const int64_t row = static_cast<int64_t>(b) * a.num_q_heads + qh;
+    if (!qvalid) return;
+    if (a.splits == 1) {
+        const float inv = l > 0.0f ? v_factor / l : 0.0f;
+        uint16_t* op = a.out + row * HD + q4 * (HD / 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t w[G::J / 2];
+#pragma unroll
+            for (int j = 0; j < G::J; j += 2) w[j / 2] = pack_bf16(st.o[j][i] * inv, st.o[j + 1][i] * inv);
+            uint16_t* dst = op + i * G::J;
+            if constexpr (G::J >= 8) {
+#pragma unroll
+                for (int k = 0; k < G::J / 8; ++k) st16<false>(dst + 8 * k, make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]));
+            } else {
+                st8<false>(dst, make_uint2(w[0], w[1]));
+            }
+        }
+    } else {
+        const int64_t prow = row * a.splits + split;
+        float* op = a.part_o + prow * HD + q4 * (HD / 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < G::J; j += 4) {
+                const uint4 w = make_uint4(__float_as_uint(st.o[j][i] * v_factor), __float_as_uint(st.o[j + 1][i] * v_factor),
+                                           __float_as_uint(st.o[j + 2][i] * v_factor),
+                                           __float_as_uint(st.o[j + 3][i] * v_factor));
+                st16<false>(op + i * G::J + j, w);
+            }
+        }
+        if (q4 == 0) {
+            const u32x2 ml = {__float_as_uint(st.m), __float_as_uint(l)};
+            *reinterpret_cast<u32x2*>(a.part_ml + prow * 2) = ml;
+        }
+    }
+}
+
 // Combine of the splits' partial results: one wave per (sequence, query head).
 struct CombineArgs {
     const float* part_o;
@@ -1108,6 +1502,13 @@ constexpr bool attention_packs() {
 
 template <int HD, int MODE, bool QF8>
 void launch_attention_q(const AttnArgs& p, int threads, bool small_bs, hipStream_t st) {
+    if constexpr (!QF8 && attention_quads<HD, MODE>()) {
+        if (!small_bs && p.group <= 4 && p.heads_per_wg % 4 == 0) {
+            const unsigned qlds = static_cast<unsigned>(threads / 64) * QuadGeo<HD, MODE>::LDS_WAVE;
+            hipLaunchKernelGGL((attention_quad_kernel<HD, MODE>), dim3(p.total_wg), dim3(threads), qlds, st, p);
+            return;
+        }
+    }
     // staged tiles: one LDS tile image per wave of the workgroup
     const unsigned lds = attention_staged<HD, MODE>() ? static_cast<unsigned>(threads / 64) * Geo<HD, MODE>::LDS_TILE : 0u;
     if (small_bs)

@@ -275,13 +275,14 @@ def test_attention_workspace_reuse_and_sizes(kvq, orc):
 
 
 @pytest.mark.parametrize("mode,hd", [(W.FP8_PER_TOKEN_HEAD, 128), (W.INT4_PER_TOKEN_HEAD, 128),
-                                     (W.INT4_PER_TOKEN_HEAD, 64)],
-                         ids=["fp8_per_token_head-128", "int4_per_token_head-128", "int4_per_token_head-64"])
+                                     (W.INT4_PER_TOKEN_HEAD, 64), (W.FP8_PER_TOKEN_HEAD, 64)],
+                         ids=["fp8_per_token_head-128", "int4_per_token_head-128", "int4_per_token_head-64",
+                              "fp8_per_token_head-64"])
 def test_attention_decode_workload_sampled(kvq, orc, mode, hd):
     """Full decode shape: 256 sequences of 8192-8207 cached tokens, 8 KV heads,
-    32 query heads, per-token-head FP8 at head_dim 128 and INT4 at 128 and 64,
-    in the launch configuration the benchmark times; eight sampled sequences
-    against the oracle."""
+    32 query heads, per-token-head FP8 and INT4 at head_dim 128 and 64 (at 64
+    the quad path), in the launch configuration the benchmark times; eight
+    sampled sequences against the oracle."""
     _flush(f"[attention] decode 256 x 8192 {W.MODE_NAMES[mode]} hd {hd} (sampled)")
     g = torch.Generator().manual_seed(11)
     lens = (8192 + torch.randint(0, 16, (256,), generator=g)).tolist()
@@ -298,6 +299,69 @@ def test_attention_decode_workload_sampled(kvq, orc, mode, hd):
         sc.check(out[rows], ref, tol, "decode sampled")
     finally:
         sc.close()
+
+
+QUAD_MODES = [W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD]
+
+
+@pytest.mark.parametrize("hkv,group,bs", [(4, 4, 16), (8, 4, 16), (8, 1, 32), (12, 3, 16), (16, 2, 128), (8, 2, 16)],
+                         ids=["hkv4-g4", "hkv8-g4", "hkv8-g1-bs32", "hkv12-g3", "hkv16-g2-bs128", "hkv8-g2"])
+@pytest.mark.parametrize("mode", QUAD_MODES, ids=[W.MODE_NAMES[m] for m in QUAD_MODES])
+def test_attention_head_quads(kvq, orc, mode, hkv, group, bs):
+    """Head_dim 64 with at most 4 query heads per KV head and 4 or 8 KV heads
+    per workgroup: each wave serves a quad of 4 KV heads (16 columns of 4
+    heads x 4 queries), the quad's 4 waves take every fourth tile and merge
+    through LDS.  Lengths leave some waves of a quad without a tile (1 to 3
+    tiles), end inside and at tile and block boundaries, and run to several
+    splits."""
+    lens = [0, 1, 15, 16, 17, 33, 48, 49, 100, 260, 600]
+    _run(kvq, orc, f"quads mode {W.MODE_NAMES[mode]} hkv {hkv} group {group} bs {bs}", mode=mode, hd=64, hkv=hkv,
+         bs=bs, lens=lens, group=group, seed=200 + hkv * 10 + group + mode)
+
+
+@pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD])
+def test_attention_head_quads_single_split_and_foreign_blocks(kvq, orc, mode):
+    """The quad path with one split (the first kernel writes the output),
+    table entries outside the layer, and clamped lengths."""
+    _flush(f"[attention] quads single split, foreign blocks {W.MODE_NAMES[mode]}")
+    sc = Scenario(kvq, orc, mode=mode, hd=64, hkv=8, bs=16, lens=[70, 120, 40, 3], group=4, seed=230 + mode)
+    try:
+        out = sc.run_gpu()
+        ref, tol = sc.reference()
+        sc.check(out, ref, tol, "quads single split")
+        bt = sc.bt.copy()
+        bt[0, 1] = -1
+        bt[1, 3] = sc.nblocks
+        bt[2, :] = -5
+        out = sc.run_gpu(bt=bt)
+        ref, tol = sc.reference(bt=bt)
+        sc.check(out, ref, tol, "quads foreign blocks")
+        assert not out[2].any() and not ref[2].any()
+        lens = [-3, 10 ** 6, 40, 0]
+        out = sc.run_gpu(lens=lens)
+        ref, tol = sc.reference(lens=lens)
+        sc.check(out, ref, tol, "quads clamped lengths")
+        assert not out[0].any() and not out[3].any()
+    finally:
+        sc.close()
+
+
+def test_attention_head_quads_layer_without_blocks(kvq, orc):
+    """A layer with no blocks gives zeros on the quad path too."""
+    _flush("[attention] quads, layer without blocks")
+    cfg = kvq.CacheConfig(16, 8, 64, [W.INT4_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD], [4, 0])
+    cache = kvq.Cache(cfg, device=DEV)
+    try:
+        for maxb in (2, 64):
+            q = torch.randn((3, 32, 64), generator=torch.Generator().manual_seed(maxb)).to(torch.bfloat16).to(DEV)
+            bt = torch.zeros((3, maxb), dtype=torch.int32, device=DEV)
+            sl = torch.tensor([5, 0, 20], dtype=torch.int32, device=DEV)
+            out = torch.full_like(q, 1.0)
+            cache.decode_attention(1, q, bt, sl, 0.125, out=out)
+            torch.cuda.synchronize()
+            assert not out.any()
+    finally:
+        cache.close()
 
 
 def test_attention_layer_without_blocks_gives_zeros(kvq, orc):
