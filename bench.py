@@ -220,7 +220,8 @@ def measured_traffic(path=PROFILE_TRAFFIC):
 def _kernel_key(name):
     """(kind/head_dim/mode, short name) of a library or ceiling kernel's
     demangled name, or None for other kernels."""
-    m = re.search(r"\b(store_kernel|gather_kernel|attention_kernel|combine_kernel|combine_wide_kernel|calib_kernel|"
+    m = re.search(r"\b(store_kernel|gather_kernel|attention_kernel|attention_quad_kernel|combine_kernel|"
+                  r"combine_wide_kernel|calib_kernel|"
                   r"store_pattern_kernel|gather_pattern_kernel|linear_copy_kernel)(?:<([^>]*)>)?", name)
     if not m:
         return None
@@ -228,7 +229,7 @@ def _kernel_key(name):
     short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
     targs = [t.strip() for t in (m.group(2) or "").split(",") if t.strip()]
     # library kernels by head_dim and mode; the ceiling kernels by all their arguments
-    keep = targs[:2] if kind in ("store", "gather", "attention", "calib") else targs
+    keep = targs[:2] if kind in ("store", "gather", "attention", "attention_quad", "calib") else targs
     return "/".join([kind] + keep), short
 
 
@@ -255,7 +256,7 @@ def _counter_per_kernel(rows, counter):
             acc.setdefault("store", []).append(val)
         elif "gather_kernel" in name:
             acc.setdefault("gather", []).append(val)
-        elif "attention_kernel" in name:
+        elif "attention_kernel" in name or "attention_quad_kernel" in name:
             acc.setdefault("attention", []).append(val)
         elif "combine_kernel" in name:
             acc.setdefault("combine", []).append(val)
@@ -298,7 +299,7 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, la
     # the profiled launches: 4 fused steps (lengths ctx + 1 .. ctx + 4) and 4
     # attention-only passes at ctx + 4, 32 layers each: mean length ctx + 3.25
     algo = attention_bytes(mode, hd, hkv, bs, H, S, int(S * (ctx + 3.25)))
-    flt = "--kernel-include-regex 'attention_kernel|combine_kernel|copyBuffer'"
+    flt = "--kernel-include-regex 'attention_kernel|attention_quad_kernel|combine_kernel|copyBuffer'"
     out = [f"# HBM traffic per launch: decode attention, {mode_name}, head_dim {hd} (256 x ~8195 cached tokens, 8 KV heads)", "",
            "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
            f"    rocprofv3 --pmc FETCH_SIZE {flt} --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(fetch_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
@@ -328,13 +329,15 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, la
     print("\n".join(lines + [""] + out))
 
 
-def summarize_kernels(kt_dir, fetch_dir, write_dir, tag, bytes_json, bench_args):
+def summarize_kernels(kt_dir, fetch_dir, write_dir, tag, bytes_json, bench_args, pmc_filter=""):
     """profiles/kernel_trace_<tag>.md and profiles/traffic_<tag>.md from three
     rocprofv3 runs of `bench.py <bench_args>` (kernel trace with --stats;
     --pmc FETCH_SIZE; --pmc WRITE_SIZE, the counter runs with
-    --calibrate-copy), with each kernel's algorithmic bytes per launch from the
-    JSON the bench wrote with --launch-bytes-out.  Counter KiB are scaled by
-    what the same counters read for a 256 MiB device-to-device copy."""
+    --calibrate-copy and, when pmc_filter is given, that
+    --kernel-include-regex), with each kernel's algorithmic bytes per launch
+    from the JSON the bench wrote with --launch-bytes-out.  Counter KiB are
+    scaled by what the same counters read for a 256 MiB device-to-device
+    copy."""
     import json as _json
     stats = _read_csv(kt_dir, "kernel_stats.csv")
     kt_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(kt_dir))} "
@@ -373,7 +376,8 @@ def summarize_kernels(kt_dir, fetch_dir, write_dir, tag, bytes_json, bench_args)
     write, _, wcopy = per_kernel(_read_csv(write_dir, "counter_collection.csv"), "WRITE_SIZE")
     f_scale, w_scale = COPY_BYTES / (fcopy * 1024.0), COPY_BYTES / (wcopy * 1024.0)
     algo = _json.load(open(bytes_json))
-    cmd = lambda c, d: (f"rocprofv3 --pmc {c} --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(d))} "
+    flt = f"--kernel-include-regex '{pmc_filter}' " if pmc_filter else ""
+    cmd = lambda c, d: (f"rocprofv3 --pmc {c} {flt}--output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(d))} "
                         f"-o run -- python3 $R/bench.py {bench_args} --calibrate-copy")
     out = [f"# HBM traffic per launch: {tag}", "",
            "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
@@ -395,6 +399,55 @@ def summarize_kernels(kt_dir, fetch_dir, write_dir, tag, bytes_json, bench_args)
     with open(os.path.join(ROOT, "profiles", f"traffic_{tag}.md"), "w") as f:
         f.write("\n".join(out + tail) + "\n")
     print("\n".join(lines + [""] + out + tail))
+
+
+SQ_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_WAVE_CYCLES SQ_ACTIVE_INST_VALU "
+               "SQ_BUSY_CYCLES SQ_WAIT_INST_ANY")
+
+
+def summarize_instructions(tag, dirs):
+    """profiles/instructions_<tag>.md: the SQ instruction counters of the
+    decode-attention kernels from rocprofv3 runs of
+    `bench.py --workload attention --mode M --head-dim D --steps 1 --warmup 0 --layers 4`
+    (one directory per run, named pmc_attn_<mode>_<hd>), per dispatch and per
+    head-tile (16 cached tokens of one KV head for its whole query group)."""
+    rows_out = []
+    cmds = []
+    for d in dirs:
+        rows = _read_csv(d, "counter_collection.csv")
+        acc, info = {}, {}
+        for r in rows:
+            acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            info = r
+        mean = {k: sum(v) / len(v) for k, v in acc.items()}
+        dispatches = len(acc["SQ_WAVES"])
+        m = re.search(r"pmc_attn_(\w+)_(\d+)$", os.path.basename(os.path.normpath(d)))
+        mode_name, hd = m.group(1), int(m.group(2))
+        # the profiled step appends one token to 8192 cached ones: 513 tiles per (sequence, KV head)
+        tiles = 256 * 8 * 513
+        kname = info["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
+        rows_out.append(f"| {mode_name} / {hd} | {kname} | {dispatches} | {info['Workgroup_Size']} | "
+                        f"{mean['SQ_WAVES']:.0f} | "
+                        f"{mean['SQ_INSTS_VALU'] / tiles:.1f} | {mean['SQ_INSTS_SALU'] / tiles:.1f} | "
+                        f"{mean['SQ_INSTS_LDS'] / tiles:.2f} | "
+                        f"{100 * mean['SQ_ACTIVE_INST_VALU'] / mean['SQ_WAVE_CYCLES']:.1f}% | "
+                        f"{100 * mean['SQ_WAIT_INST_ANY'] / mean['SQ_WAVE_CYCLES']:.1f}% |")
+        cmds.append(f"    rocprofv3 --pmc {SQ_COUNTERS} --kernel-include-regex 'attention_kernel|attention_quad_kernel' "
+                    f"--output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(d))} -o run -- python3 "
+                    f"$R/bench.py --workload attention --mode {mode_name} --head-dim {hd} --steps 1 --warmup 0 "
+                    f"--layers 4 --no-cpu-baseline")
+    out = ["# Instruction counters: decode attention, 256 sequences x 8193 cached tokens, 8 KV heads, 32 query heads", "",
+           "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", "", *cmds, "",
+           "Means over the dispatches of the attention kernel (4 layers x 3 passes).  A head-tile is 16 cached "
+           "tokens of one KV head for its whole query group: 256 x 8 x 513 = 1.05 M per dispatch.  "
+           "VALU-active and waiting are SQ_ACTIVE_INST_VALU and SQ_WAIT_INST_ANY as shares of SQ_WAVE_CYCLES.", "",
+           "| mode / head_dim | kernel | dispatches | workgroup | waves | VALU per head-tile "
+           "| SALU per head-tile | LDS per head-tile | VALU-active | waiting |",
+           "|---|---|---|---|---|---|---|---|---|---|", *rows_out, "",
+           f"kernel_source_sha256_16: {kernel_source_hash(ATTN_SOURCES)}"]
+    with open(os.path.join(ROOT, "profiles", f"instructions_{tag}.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
 
 
 def write_launch_bytes(path, entries):
@@ -1159,6 +1212,25 @@ def run_other_workload(args, torch, kvq, W):
                                                      Lc.stream)
         counter = {"i": 0}
 
+        # every timed attention launch between its own pair of events, with its
+        # algorithmic bytes: the roofline's average launch (fused steps and
+        # attention-only passes alike, as a kernel trace of this run averages)
+        per_launch = []
+
+        def launch_bytes_at(i):
+            return attention_bytes(mode, hd, hkv, bs, H, S, int(S) * (D["ctx"] + i + 1))
+
+        def attend(a, i, ev):
+            if ev:
+                e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                e[0].record()
+            st_ = attn_fn(*a)
+            if st_ != 0:
+                raise kvq.KVQError(st_, "kvq_decode_attention")
+            if ev:
+                e[1].record()
+                per_launch.append((e, launch_bytes_at(i)))
+
         def step(ev):
             i = counter["i"]
             counter["i"] += 1
@@ -1167,9 +1239,7 @@ def run_other_workload(args, torch, kvq, W):
             if ev: ev[0].record()
             for l in range(L):
                 Lc.store(sa[l])
-                st_ = attn_fn(*aa[l])
-                if st_ != 0:
-                    raise kvq.KVQError(st_, "kvq_decode_attention")
+                attend(aa[l], i, ev)
             if ev: ev[1].record(); ev[2].record()
         sec, evs = _timed(torch, step, args.steps, args.warmup)
         step_s = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps / 1e3
@@ -1179,10 +1249,13 @@ def run_other_workload(args, torch, kvq, W):
         def attn_only(ev):
             if ev: ev[0].record()
             for a in last:
-                attn_fn(*a)
+                attend(a, nsteps - 1, ev)
             if ev: ev[1].record(); ev[2].record()
         _, aevs = _timed(torch, attn_only, args.steps, 1)
         attn_s = sum(e[0].elapsed_time(e[1]) for e in aevs) / (args.steps * L) / 1e3
+        launch_s = sum(e[0].elapsed_time(e[1]) for e, _ in per_launch) / 1e3
+        launch_gbps = sum(b for _, b in per_launch) / launch_s / 1e9
+        launch_us = launch_s / len(per_launch) * 1e6
         if args.calibrate_copy:
             src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
             dst = torch.empty_like(src)
@@ -1194,6 +1267,10 @@ def run_other_workload(args, torch, kvq, W):
         sb, _ = algorithmic_bytes(mode, hd, hkv, bs, S * hkv)
         ab = attention_bytes(mode, hd, hkv, bs, H, S, ntok)
         agbps = ab / attn_s / 1e9
+        # the kernel the library picks: quads of KV heads at head_dim 64 for
+        # the quantized modes with BF16 queries and groups of at most 4
+        attn_kernel = ("attention_quad_kernel" if hd == 64 and mode != kvq.BF16 and not args.q_fp8
+                       and args.q_per_kv <= 4 else "attention_kernel")
         # oracle check: layer L-1 of the last step for 8 sequences, from the
         # oracle's own image of that layer, within the kernel's error bound
         parity, cpu = None, None
@@ -1230,8 +1307,9 @@ def run_other_workload(args, torch, kvq, W):
                "attention_us": round(attn_s * 1e6, 2), "attention_GBps": round(agbps, 1),
                "step_ms_events": round(step_s * 1e3, 4),
                "decode_tokens_per_s": round(S / sec, 1),
-               "roofline": {"bound": "hbm", "kernel": "attention_kernel", "achieved": round(agbps, 1),
-                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(agbps / HBM_PEAK_GBPS, 4),
+               "attention_launch_us": round(launch_us, 2),
+               "roofline": {"bound": "hbm", "kernel": attn_kernel, "achieved": round(launch_gbps, 1),
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(launch_gbps / HBM_PEAK_GBPS, 4),
                             "traffic": None if (args.q_fp8 or args.tp > 1) else measured_attention_traffic(args.mode, hd)},
                "cpu_baseline": cpu,
                "parity_vs_oracle_sampled": parity,
@@ -1271,16 +1349,24 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="gqa32: skip the bandwidth-ceiling kernels")
     ap.add_argument("--launch-bytes-out", default="",
                     help="write the algorithmic bytes per launch of each kernel run (JSON) for --summarize-kernels")
-    ap.add_argument("--summarize-kernels", nargs=6,
-                    metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "TAG", "LAUNCH_BYTES_JSON", "BENCH_ARGS"),
-                    help="write profiles/kernel_trace_TAG.md and traffic_TAG.md from rocprofv3 csv output and exit")
+    ap.add_argument("--summarize-kernels", nargs="+",
+                    metavar="ARG",
+                    help="KERNEL_TRACE_DIR FETCH_DIR WRITE_DIR TAG LAUNCH_BYTES_JSON BENCH_ARGS [PMC_REGEX]: write "
+                         "profiles/kernel_trace_TAG.md and traffic_TAG.md from rocprofv3 csv output and exit")
+    ap.add_argument("--summarize-instructions", nargs="+", metavar="ARG",
+                    help="TAG PMC_DIR...: write profiles/instructions_TAG.md from SQ counter runs and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, copy 256 MiB device-to-device 3 times (reference for counter scaling)")
     ap.add_argument("--summarize-attention-profiles", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the attention profiles/ summaries (for --mode and --head-dim) and exit")
     args = ap.parse_args()
     if args.summarize_kernels:
+        if len(args.summarize_kernels) not in (6, 7):
+            ap.error("--summarize-kernels takes 6 or 7 arguments")
         summarize_kernels(*args.summarize_kernels)
+        return
+    if args.summarize_instructions:
+        summarize_instructions(args.summarize_instructions[0], args.summarize_instructions[1:])
         return
     if args.summarize_attention_profiles:
         summarize_attention_profiles(*args.summarize_attention_profiles, args.mode, args.head_dim, args.layers)
