@@ -73,6 +73,7 @@ def _ceiling_lib():
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P]
     I32 = ctypes.c_int32
     lib.ceil_gather_pattern.argtypes = [P, P, I32, P, I32, P, P, I32, I32, I32, I32, I32, ctypes.c_int64, P]
+    lib.ceil_empty.argtypes = [ctypes.c_int64, P]
     return lib
 
 
@@ -145,6 +146,21 @@ def linear_copy_ceiling(torch, nbytes, buffers, reps):
     del pairs
     torch.cuda.empty_cache()
     return _rate(2 * half, sec)
+
+
+def empty_launch_us(torch, grids, reps=200):
+    """Microseconds per launch of a kernel that does nothing, launched back
+    to back on the current stream, for each grid (workgroups of 256)."""
+    import ctypes
+    lib = _ceiling_lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+    for g in grids:
+        def f(g=g):
+            if lib.ceil_empty(g, stream):
+                raise RuntimeError("ceil_empty failed")
+        out[f"grid_{g}"] = round(_time_launches(torch, [f], reps) * 1e6, 2)
+    return out
 
 
 def store_pattern_ceiling(torch, I, LA, slots, reps, out_buf):
@@ -1460,6 +1476,9 @@ def run_gqa32(args, torch, kvq, W):
         ceilings["gather_pattern_permuted_blocks"] = gather_pattern_ceiling(torch, I, hg, I["bt_d"], reps, out_buf)
         ceilings["gather_pattern_identity_blocks"] = gather_pattern_ceiling(torch, I, hg, ident_bt, reps, out_buf)
         ceilings["linear_nt_copy"] = linear_copy_ceiling(torch, LA["store_bytes"], 16, reps)
+        # the store launches one workgroup per 32 rows: 8192 at this shape
+        store_grid = (I["n"] * I["hkv"] + 31) // 32
+        ceilings["empty_launch_us"] = empty_launch_us(torch, (1, 1024, store_grid))
         for name, g in geos.items():
             if name == args.mode:
                 pc = ceilings["store_pattern_permuted_slots"]
@@ -1491,6 +1510,10 @@ def run_gqa32(args, torch, kvq, W):
         ceilings["gather_vs_pattern_ceiling"] = round(
             gather_gbps / ceilings["gather_pattern_permuted_blocks"]["GBps"], 4)
         ceilings["store_vs_linear_copy"] = round(store_gbps / ceilings["linear_nt_copy"]["GBps"], 4)
+        # the store's rate over its bytes once the fixed cost of an empty
+        # launch of the same grid is taken out of its time
+        empty_s = ceilings["empty_launch_us"][f"grid_{(I['n'] * I['hkv'] + 31) // 32}"] / 1e6
+        ceilings["store_GBps_beyond_empty_launch"] = round(store_bytes / (store_s - empty_s) / 1e9, 1)
 
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")

@@ -22,6 +22,8 @@
 //  ceil_gather_pattern the gather's exact accesses with the dequantization
 //                      left out (block table, sequence offsets, code chunks
 //                      and row scales of the paged blocks, BF16 output rows).
+//  ceil_empty          a kernel that does nothing, for the fixed cost of one
+//                      launch of a given grid (256-thread workgroups).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,6 +31,8 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__global__ __launch_bounds__(256) void empty_kernel() {}
 
 __global__ __launch_bounds__(256) void linear_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                           uint64_t n16) {
@@ -245,6 +249,14 @@ void launch_gather_pattern(const GatherPatternArgs& p, bool half, bool sc, uint3
 }  // namespace
 
 extern "C" {
+
+// Launch `grid` (1 .. 2^31 - 1) workgroups of 256 threads that do nothing.
+// Returns 0 or the hipError_t of the launch; -1 on bad arguments.
+__attribute__((visibility("default"))) int ceil_empty(int64_t grid, void* stream) {
+    if (grid < 1 || grid >= (int64_t{1} << 31)) return -1;
+    hipLaunchKernelGGL(empty_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, static_cast<hipStream_t>(stream));
+    return static_cast<int>(hipGetLastError());
+}
 
 // Copy `bytes` (a multiple of 16, > 0) from src to dst (device, 16-byte
 // aligned).  Returns 0 or the hipError_t of the launch; -1 on bad arguments.
