@@ -990,13 +990,12 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
 // Query groups of at most 4 heads fill at most 4 of the 16 MFMA columns of
 // a KV head's products, so the per-tile softmax would run on 12 idle
 // columns.  Here a wave serves a quad of 4 KV heads at once: column r is
-// query g = r % 4 of KV head h0 + r / 4.  The Q K^T product of a tile
-// accumulates the quad's 4 heads one after another into one accumulator,
-// each with its keys as the A operand and a query operand that holds only
-// that head's columns (the others zero: block diagonal), so every column
-// gets exactly its own head's scores; the P V product likewise takes each
-// head's values with the weights of that head's columns only.  The softmax
-// then runs once per tile for all 16 columns.
+// query g = r % 4 of KV head h0 + r / 4.  The Q K^T product of a tile runs
+// each of the quad's 4 heads' keys (the A operand) against all 16 query
+// columns into an accumulator of its own, and each column then selects its
+// own head's scores (3 selects per score); the P V product takes each
+// head's values with the weights of that head's columns only (the others
+// zero).  The softmax then runs once per tile for all 16 columns.
 //
 // The grid, the plan and the partial results are those of attention_kernel:
 // a workgroup still covers a run of heads_per_wg (4 or 8) KV heads of one
@@ -1005,25 +1004,32 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
 // fourth tile of the split (interleaved, so the workgroup streams adjacent
 // tiles), then merge their (O, m, l) through LDS before the output.
 //
-// Used at head_dim 64 in the FP8 and INT4 modes (tiles of 4 or 8 KiB per
-// quad), with BF16 queries, blocks of at least 16 tokens and query groups
-// of at most 4.
+// Used at head_dim 64 in the FP8 and INT4 modes and at head_dim 128 in the
+// INT4 mode (tiles of 4 or 8 KiB per quad), with BF16 queries, blocks of at
+// least 16 tokens and query groups of at most 4.
 template <int HD, int MODE>
 struct QuadGeo {
     using G = Geo<HD, MODE>;
     static constexpr int QROW = 4 * 2 * G::RB;            // a position's K|V rows of the quad's 4 heads
     static constexpr int NC = 16 * QROW / 1024;            // 16-byte pieces per lane of a tile
+    static constexpr int TPP = 1024 / QROW;                // tokens per 1 KiB piece
+    static_assert(QROW <= 1024 && 1024 % QROW == 0, "whole tokens per 1 KiB piece");
     static constexpr int LDS_ROW = QROW + 16;
     static constexpr int LDS_TILE = 16 * LDS_ROW;
     static constexpr int MERGE = 64 * (2 + 4 * G::J) * 4;  // a wave's (m, l, O) for the merge
     static constexpr int LDS_WAVE = LDS_TILE > MERGE ? LDS_TILE : MERGE;
     static constexpr int D = NC <= 4 ? 3 : 2;              // tiles in flight per wave
+    // Q K^T by per-head accumulators and a select at head_dim 128, where the
+    // block-diagonal query operands (4 x HD / 32 registers of 4) would not
+    // fit beside the tiles; at head_dim 64 the block-diagonal single chain
+    // measured 11% (INT4) and 2% (FP8) faster than the select
+    static constexpr bool SELECT = HD >= 128;
 };
 
 template <int HD, int MODE>
 constexpr bool attention_quads() {
-    // (INT4 at head_dim 128 would fit 8 KiB tiles but spills registers)
-    return MODE != KVQ_BF16 && HD == 64 && QuadGeo<HD, MODE>::NC <= 8;
+    // (FP8 at head_dim 128, 16 KiB quad tiles, is bound by memory already)
+    return MODE != KVQ_BF16 && (HD == 64 || (HD == 128 && MODE == KVQ_INT4_PER_TOKEN_HEAD));
 }
 
 template <int HD, int MODE>
@@ -1033,9 +1039,13 @@ struct QuadRaw {
     uint32_t ok;
 };
 
+// A quad tile's row image is QROW <= 1024 bytes per token, so 1 KiB piece c
+// of the tile starts TPP = 1024 / QROW tokens after piece c - 1: the lane's
+// byte offset of piece c is its offset in piece 0 plus a wave-uniform step.
 struct QuadLaneOff {
-    uint32_t kv[8];                // the lane's 16-byte pieces of the tile's row image
-    uint32_t lds[8];               // ... and where they go in the wave's LDS rows
+    uint32_t kv;                   // the lane's 16 bytes of piece 0 in the block
+    uint32_t lds;                  // ... and where they go in the wave's LDS rows
+    int kv_step;                   // block bytes from one piece to the next (uniform)
     uint32_t s[4];                 // (s_K, s_V) of tokens 4q+i for the lane's column head
 };
 
@@ -1052,7 +1062,7 @@ __device__ __forceinline__ void quad_load(const AttnArgs& a, int blk, int tau, c
         const_cast<uint8_t*>(base), 0, static_cast<int>(a.block_bytes), kBufferDword3);
     const int srow = static_cast<int>(pos0 * static_cast<uint32_t>(a.hkv) * (2 * G::RB));
 #pragma unroll
-    for (int c = 0; c < Q::NC; ++c) buf_load<16, kNonTemporal>(T.kv + 4 * c, rs, lo.kv[c], srow);
+    for (int c = 0; c < Q::NC; ++c) buf_load<16, kNonTemporal>(T.kv + 4 * c, rs, lo.kv, srow + c * lo.kv_step);
     if constexpr (G::DYN) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1073,31 +1083,62 @@ __device__ __forceinline__ void consume(const QuadRaw<HD, MODE>& T) {
         if constexpr (Geo<HD, MODE>::DYN) asm volatile("" ::"v"(T.s[i][0]), "v"(T.s[i][1]));
 }
 
+// Head h's K slice of token r for the lane (hd / 4 dims from q4 * hd / 4)
+// out of the wave's LDS rows.
+template <int HD, int MODE>
+__device__ __forceinline__ void quad_keys(const uint8_t* lds, int r, int q4, int h, uint32_t* k) {
+    using G = Geo<HD, MODE>;
+    using Q = QuadGeo<HD, MODE>;
+    const uint8_t* kp = lds + r * Q::LDS_ROW + h * 2 * G::RB + q4 * G::KB;
+#pragma unroll
+    for (int w = 0; w < G::KW; w += 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(kp + 4 * w);
+        k[w] = v[0];
+        k[w + 1] = v[1];
+    }
+}
+
 // One tile of the quad: scores of all 16 columns, one softmax update, the
 // 4 heads' value products.  MASK = false: every token of the tile lies below
 // len in a block of the layer.
 template <int HD, int MODE, bool MASK>
 __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uint8_t* lds, State<HD, MODE>& st,
-                                           const bf16x8 (*qb)[HD / 32], f32x4 qk_init, int t0, int len, int r,
+                                           const bf16x8* qb, f32x4 qk_init, int t0, int len, int r,
                                            int q4, float k_factor, uint32_t vsh, uint32_t vsel) {
     using G = Geo<HD, MODE>;
     using Q = QuadGeo<HD, MODE>;
     constexpr bool I4 = MODE == KVQ_INT4_PER_TOKEN_HEAD;
-    // Q K^T, head by head into one accumulator
-    f32x4 sacc = qk_init;
+    const int hq = r >> 2;
+    f32x4 sacc;
+    if constexpr (Q::SELECT) {
+        // each head's keys against all 16 columns, into an accumulator of its
+        // own; each column then takes its own head's scores
+        f32x4 acc[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        uint32_t k[G::KW];
-        const uint8_t* kp = lds + r * Q::LDS_ROW + h * 2 * G::RB + q4 * G::KB;
+        for (int h = 0; h < 4; ++h) {
+            uint32_t k[G::KW];
+            quad_keys<HD, MODE>(lds, r, q4, h, k);
+            acc[h] = qk_init;
 #pragma unroll
-        for (int w = 0; w < G::KW; w += 2) {
-            const u32x2 v = *reinterpret_cast<const u32x2*>(kp + 4 * w);
-            k[w] = v[0];
-            k[w + 1] = v[1];
+            for (int j = 0; j < HD / 32; ++j)
+                acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(k, j), qb[j], acc[h], 0, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < HD / 32; ++j)
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(k, j), qb[h][j], sacc, 0, 0, 0);
+        for (int i = 0; i < 4; ++i)
+            sacc[i] = hq == 0 ? acc[0][i] : (hq == 1 ? acc[1][i] : (hq == 2 ? acc[2][i] : acc[3][i]));
+    } else {
+        // head by head into one accumulator, each head's query operand
+        // holding only its own columns (block diagonal: qb[h * HD / 32 + j])
+        sacc = qk_init;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            uint32_t k[G::KW];
+            quad_keys<HD, MODE>(lds, r, q4, h, k);
+#pragma unroll
+            for (int j = 0; j < HD / 32; ++j)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(k, j), qb[h * (HD / 32) + j], sacc,
+                                                               0, 0, 0);
+        }
     }
     bool valid[4];
 #pragma unroll
@@ -1129,7 +1170,6 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
         if constexpr (I4) st.vb *= alpha;
     }
     // P V, head by head: head h's values with the weights of its columns only
-    const int hq = r >> 2;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
         uint32_t v[4][G::VW];
@@ -1211,15 +1251,18 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_quad_kernel(Attn
         int4_query_order<HD>(qo);
         qk_init = int4_key_bias<HD>(qo);
     }
-    // block-diagonal query operands: head h's products see only its columns
-    bf16x8 qb[4][HD / 32];
+    // the query operands: the lane's own (SELECT), or block-diagonal copies
+    // in which head h's products see only its own columns
+    constexpr int NQB = Q::SELECT ? HD / 32 : 4 * (HD / 32);
+    bf16x8 qb[NQB];
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
+    for (int h = 0; h < NQB / (HD / 32); ++h)
 #pragma unroll
         for (int j = 0; j < HD / 32; ++j) {
             const u32x4 w = __builtin_bit_cast(u32x4, qo.b[j]);
-            const u32x4 z = {hq == h ? w[0] : 0u, hq == h ? w[1] : 0u, hq == h ? w[2] : 0u, hq == h ? w[3] : 0u};
-            qb[h][j] = __builtin_bit_cast(bf16x8, z);
+            const bool keep = Q::SELECT || hq == h;
+            const u32x4 z = {keep ? w[0] : 0u, keep ? w[1] : 0u, keep ? w[2] : 0u, keep ? w[3] : 0u};
+            qb[h * (HD / 32) + j] = __builtin_bit_cast(bf16x8, z);
         }
 
     float k_factor = a.c * G::CODE_UNIT;
@@ -1244,13 +1287,11 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_quad_kernel(Attn
     QuadLaneOff lo;
     {
         const uint32_t hkv = static_cast<uint32_t>(a.hkv), uh0 = static_cast<uint32_t>(h0);
-#pragma unroll
-        for (int c = 0; c < Q::NC; ++c) {
-            const uint32_t gb = static_cast<uint32_t>(c) * 1024u + static_cast<uint32_t>(lane) * 16u;
-            const uint32_t tok = gb / Q::QROW, off = gb % Q::QROW;
-            lo.kv[c] = (tok * hkv + uh0) * (2 * G::RB) + off;
-            lo.lds[c] = tok * Q::LDS_ROW + off;
-        }
+        const uint32_t gb = static_cast<uint32_t>(lane) * 16u;
+        const uint32_t tok = gb / Q::QROW, off = gb % Q::QROW;
+        lo.kv = (tok * hkv + uh0) * (2 * G::RB) + off;
+        lo.lds = tok * Q::LDS_ROW + off;
+        lo.kv_step = Q::TPP * a.hkv * 2 * G::RB;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             lo.s[i] = static_cast<uint32_t>(a.code_bytes) +
@@ -1287,7 +1328,7 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_quad_kernel(Attn
 #pragma unroll
                     for (int c = 0; c < Q::NC; ++c) {
                         const u32x4 v = {t[kk].kv[4 * c], t[kk].kv[4 * c + 1], t[kk].kv[4 * c + 2], t[kk].kv[4 * c + 3]};
-                        *reinterpret_cast<u32x4*>(lds + lo.lds[c]) = v;
+                        *reinterpret_cast<u32x4*>(lds + lo.lds + c * Q::TPP * Q::LDS_ROW) = v;
                     }
                     const int t0 = tile_of(k) * kTile;
                     if (t0 + kTile <= lim && t[kk].ok != 0)

@@ -319,12 +319,24 @@ def test_attention_head_quads(kvq, orc, mode, hkv, group, bs):
          bs=bs, lens=lens, group=group, seed=200 + hkv * 10 + group + mode)
 
 
-@pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD])
-def test_attention_head_quads_single_split_and_foreign_blocks(kvq, orc, mode):
+@pytest.mark.parametrize("hkv,group,bs", [(4, 4, 16), (8, 4, 16), (8, 1, 32), (12, 3, 16), (16, 2, 128)],
+                         ids=["hkv4-g4", "hkv8-g4", "hkv8-g1-bs32", "hkv12-g3", "hkv16-g2-bs128"])
+def test_attention_head_quads_int4_hd128(kvq, orc, hkv, group, bs):
+    """INT4 at head_dim 128 takes the quad kernel too (8 KiB quad tiles):
+    the same lengths and shapes as at head_dim 64."""
+    lens = [0, 1, 15, 16, 17, 33, 48, 49, 100, 260, 600]
+    _run(kvq, orc, f"quads int4 hd128 hkv {hkv} group {group} bs {bs}", mode=W.INT4_PER_TOKEN_HEAD, hd=128,
+         hkv=hkv, bs=bs, lens=lens, group=group, seed=260 + hkv * 10 + group)
+
+
+@pytest.mark.parametrize("mode,hd", [(W.FP8_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 64),
+                                     (W.INT4_PER_TOKEN_HEAD, 128)],
+                         ids=["fp8_per_token_head-hd64", "int4_per_token_head-hd64", "int4_per_token_head-hd128"])
+def test_attention_head_quads_single_split_and_foreign_blocks(kvq, orc, mode, hd):
     """The quad path with one split (the first kernel writes the output),
     table entries outside the layer, and clamped lengths."""
-    _flush(f"[attention] quads single split, foreign blocks {W.MODE_NAMES[mode]}")
-    sc = Scenario(kvq, orc, mode=mode, hd=64, hkv=8, bs=16, lens=[70, 120, 40, 3], group=4, seed=230 + mode)
+    _flush(f"[attention] quads single split, foreign blocks {W.MODE_NAMES[mode]} hd {hd}")
+    sc = Scenario(kvq, orc, mode=mode, hd=hd, hkv=8, bs=16, lens=[70, 120, 40, 3], group=4, seed=230 + mode + hd)
     try:
         out = sc.run_gpu()
         ref, tol = sc.reference()
