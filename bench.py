@@ -1283,10 +1283,12 @@ def run_other_workload(args, torch, kvq, W):
         sb, _ = algorithmic_bytes(mode, hd, hkv, bs, S * hkv)
         ab = attention_bytes(mode, hd, hkv, bs, H, S, ntok)
         agbps = ab / attn_s / 1e9
-        # the kernel the library picks: quads of KV heads at head_dim 64 for
-        # the quantized modes with BF16 queries and groups of at most 4
-        attn_kernel = ("attention_quad_kernel" if hd == 64 and mode != kvq.BF16 and not args.q_fp8
-                       and args.q_per_kv <= 4 else "attention_kernel")
+        # the kernel the library picks: quads of KV heads for per-token-head
+        # layers (FP8 at head_dim 64, INT4 at 64 and 128) with groups of at
+        # most 4 and at least 4 KV heads
+        quads = ((mode == kvq.FP8_PER_TOKEN_HEAD and hd == 64) or
+                 (mode == kvq.INT4_PER_TOKEN_HEAD and hd in (64, 128) and not args.q_fp8))
+        attn_kernel = "attention_quad_kernel" if quads and args.q_per_kv <= 4 and hkv % 4 == 0 else "attention_kernel"
         # oracle check: layer L-1 of the last step for 8 sequences, from the
         # oracle's own image of that layer, within the kernel's error bound
         parity, cpu = None, None

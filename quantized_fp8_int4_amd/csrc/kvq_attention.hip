@@ -1004,9 +1004,11 @@ __global__ void __launch_bounds__(kMaxAttnThreads, attention_waves<HD>()) attent
 // fourth tile of the split (interleaved, so the workgroup streams adjacent
 // tiles), then merge their (O, m, l) through LDS before the output.
 //
-// Used at head_dim 64 in the FP8 and INT4 modes and at head_dim 128 in the
-// INT4 mode (tiles of 4 or 8 KiB per quad), with BF16 queries, blocks of at
-// least 16 tokens and query groups of at most 4.
+// Used for per-token-head layers: FP8 at head_dim 64 (BF16 or FP8
+// queries) and INT4 at head_dim 64 and 128 (tiles of 4 or 8 KiB per quad),
+// with blocks of at least 16 tokens and query groups of at most 4.  With FP8 queries the Q K^T product takes the
+// raw K codes and block-diagonal FP8 query codes (FP8 zero in the other
+// heads' columns) through the FP8 MFMA, whose products are exact.
 template <int HD, int MODE>
 struct QuadGeo {
     using G = Geo<HD, MODE>;
@@ -1028,8 +1030,13 @@ struct QuadGeo {
 
 template <int HD, int MODE>
 constexpr bool attention_quads() {
-    // (FP8 at head_dim 128, 16 KiB quad tiles, is bound by memory already)
-    return MODE != KVQ_BF16 && (HD == 64 || (HD == 128 && MODE == KVQ_INT4_PER_TOKEN_HEAD));
+    // The per-token-head layouts only: a static layer's softmax has no
+    // per-token scales to apply, and there the packed rounds of
+    // attention_kernel measured 1.2-1.4% faster at head_dim 64 (BF16 and FP8
+    // queries alike).  FP8 at head_dim 128 (16 KiB quad tiles) is bound by
+    // memory already.
+    return (MODE == KVQ_FP8_PER_TOKEN_HEAD && HD == 64) ||
+           (MODE == KVQ_INT4_PER_TOKEN_HEAD && (HD == 64 || HD == 128));
 }
 
 template <int HD, int MODE>
@@ -1037,6 +1044,19 @@ struct QuadRaw {
     uint32_t kv[4 * QuadGeo<HD, MODE>::NC];
     f32x2 s[4];                    // (s_K, s_V) of tokens 4q+i, KV head h0 + r / 4
     uint32_t ok;
+};
+
+// The query operands of a quad's 16 columns: BF16 (the lane's own, for the
+// per-head select, or 4 block-diagonal copies), or FP8 codes in 4
+// block-diagonal copies.
+template <int HD, int MODE, bool QF8>
+struct QuadQuery {
+    static constexpr int N = QuadGeo<HD, MODE>::SELECT ? HD / 32 : 4 * (HD / 32);
+    bf16x8 b[N];
+};
+template <int HD, int MODE>
+struct QuadQuery<HD, MODE, true> {
+    uint32_t c[4 * (HD / 16)];
 };
 
 // A quad tile's row image is QROW <= 1024 bytes per token, so 1 KiB piece c
@@ -1101,16 +1121,34 @@ __device__ __forceinline__ void quad_keys(const uint8_t* lds, int r, int q4, int
 // One tile of the quad: scores of all 16 columns, one softmax update, the
 // 4 heads' value products.  MASK = false: every token of the tile lies below
 // len in a block of the layer.
-template <int HD, int MODE, bool MASK>
+template <int HD, int MODE, bool MASK, bool QF8>
 __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uint8_t* lds, State<HD, MODE>& st,
-                                           const bf16x8* qb, f32x4 qk_init, int t0, int len, int r,
+                                           const QuadQuery<HD, MODE, QF8>& qq, f32x4 qk_init, int t0, int len, int r,
                                            int q4, float k_factor, uint32_t vsh, uint32_t vsel) {
     using G = Geo<HD, MODE>;
     using Q = QuadGeo<HD, MODE>;
     constexpr bool I4 = MODE == KVQ_INT4_PER_TOKEN_HEAD;
     const int hq = r >> 2;
     f32x4 sacc;
-    if constexpr (Q::SELECT) {
+    if constexpr (QF8) {
+        // FP8 queries: each head's raw K codes against its block-diagonal
+        // query codes (zero codes in the other heads' columns), 2 FP8
+        // products of 32 dims per head, one accumulator
+        static_assert(HD == 64, "FP8-query quads at head_dim 64");
+        sacc = qk_init;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            uint32_t k[G::KW];
+            quad_keys<HD, MODE>(lds, r, q4, h, k);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const long ka = static_cast<long>((static_cast<uint64_t>(k[2 * j + 1]) << 32) | k[2 * j]);
+                const long qa = static_cast<long>((static_cast<uint64_t>(qq.c[h * 4 + 2 * j + 1]) << 32) |
+                                                  qq.c[h * 4 + 2 * j]);
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qa, sacc, 0, 0, 0);
+            }
+        }
+    } else if constexpr (Q::SELECT) {
         // each head's keys against all 16 columns, into an accumulator of its
         // own; each column then takes its own head's scores
         f32x4 acc[4];
@@ -1121,7 +1159,7 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
             acc[h] = qk_init;
 #pragma unroll
             for (int j = 0; j < HD / 32; ++j)
-                acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(k, j), qb[j], acc[h], 0, 0, 0);
+                acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(k, j), qq.b[j], acc[h], 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -1136,8 +1174,8 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
             quad_keys<HD, MODE>(lds, r, q4, h, k);
 #pragma unroll
             for (int j = 0; j < HD / 32; ++j)
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(k, j), qb[h * (HD / 32) + j], sacc,
-                                                               0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(k, j), qq.b[h * (HD / 32) + j],
+                                                               sacc, 0, 0, 0);
         }
     }
     bool valid[4];
@@ -1204,7 +1242,7 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
     if constexpr (I4) st.vb = int4_value_bias(__builtin_bit_cast(s16x4, pb), st.vb);
 }
 
-template <int HD, int MODE>
+template <int HD, int MODE, bool QF8>
 __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_quad_kernel(AttnArgs a) {
     using G = Geo<HD, MODE>;
     using Q = QuadGeo<HD, MODE>;
@@ -1236,36 +1274,57 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_quad_kernel(Attn
 
     const bool qvalid = g < a.group;
     const int qh = hk * a.group + (qvalid ? g : 0);
-    QOperand<HD, false> qo;
+    QOperand<HD, QF8> qo;
+    float q_factor = 1.0f;
     {
         const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.num_q_heads + qh) * HD + q4 * (HD / 4);
+        if constexpr (!QF8) {
 #pragma unroll
-        for (int j = 0; j < HD / 32; ++j) {
-            const uint4 v = qvalid ? ld16<false>(qp + 8 * j) : make_uint4(0, 0, 0, 0);
-            const u32x4 w = {v.x, v.y, v.z, v.w};
-            qo.b[j] = __builtin_bit_cast(bf16x8, w);
+            for (int j = 0; j < HD / 32; ++j) {
+                const uint4 v = qvalid ? ld16<false>(qp + 8 * j) : make_uint4(0, 0, 0, 0);
+                const u32x4 w = {v.x, v.y, v.z, v.w};
+                qo.b[j] = __builtin_bit_cast(bf16x8, w);
+            }
+        } else {
+            // E4M3(RN32(q / s_q)), saturating, exactly as the cache encodes K
+            q_factor = qvalid ? a.q_scales[qh] : 1.0f;
+            const RowQ rq = row_prep(q_factor);
+#pragma unroll
+            for (int j = 0; j < HD / 32; ++j) {
+                const uint4 v = qvalid ? ld16<false>(qp + 8 * j) : make_uint4(0, 0, 0, 0);
+                const uint2 c = encode_fp8<true, true>(v, rq);
+                qo.c[2 * j] = c.x;
+                qo.c[2 * j + 1] = c.y;
+            }
         }
     }
     f32x4 qk_init = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+    if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD && !QF8) {
         int4_query_order<HD>(qo);
         qk_init = int4_key_bias<HD>(qo);
     }
     // the query operands: the lane's own (SELECT), or block-diagonal copies
     // in which head h's products see only its own columns
-    constexpr int NQB = Q::SELECT ? HD / 32 : 4 * (HD / 32);
-    bf16x8 qb[NQB];
+    QuadQuery<HD, MODE, QF8> qq;
+    if constexpr (QF8) {
 #pragma unroll
-    for (int h = 0; h < NQB / (HD / 32); ++h)
+        for (int h = 0; h < 4; ++h)
 #pragma unroll
-        for (int j = 0; j < HD / 32; ++j) {
-            const u32x4 w = __builtin_bit_cast(u32x4, qo.b[j]);
-            const bool keep = Q::SELECT || hq == h;
-            const u32x4 z = {keep ? w[0] : 0u, keep ? w[1] : 0u, keep ? w[2] : 0u, keep ? w[3] : 0u};
-            qb[h * (HD / 32) + j] = __builtin_bit_cast(bf16x8, z);
-        }
+            for (int w = 0; w < HD / 16; ++w) qq.c[h * (HD / 16) + w] = hq == h ? qo.c[w] : 0u;
+    } else {
+        constexpr int NQB = QuadQuery<HD, MODE, false>::N;
+#pragma unroll
+        for (int h = 0; h < NQB / (HD / 32); ++h)
+#pragma unroll
+            for (int j = 0; j < HD / 32; ++j) {
+                const u32x4 w = __builtin_bit_cast(u32x4, qo.b[j]);
+                const bool keep = Q::SELECT || hq == h;
+                const u32x4 z = {keep ? w[0] : 0u, keep ? w[1] : 0u, keep ? w[2] : 0u, keep ? w[3] : 0u};
+                qq.b[h * (HD / 32) + j] = __builtin_bit_cast(bf16x8, z);
+            }
+    }
 
-    float k_factor = a.c * G::CODE_UNIT;
+    float k_factor = a.c * G::CODE_UNIT * q_factor;
     float v_factor = G::CODE_UNIT;
     if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
         k_factor *= a.statics[0];
@@ -1332,9 +1391,11 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_quad_kernel(Attn
                     }
                     const int t0 = tile_of(k) * kTile;
                     if (t0 + kTile <= lim && t[kk].ok != 0)
-                        quad_round<HD, MODE, false>(t[kk], lds, st, qb, qk_init, t0, lim, r, q4, k_factor, vsh, vsel);
+                        quad_round<HD, MODE, false, QF8>(t[kk], lds, st, qq, qk_init, t0, lim, r, q4, k_factor, vsh,
+                                                         vsel);
                     else
-                        quad_round<HD, MODE, true>(t[kk], lds, st, qb, qk_init, t0, lim, r, q4, k_factor, vsh, vsel);
+                        quad_round<HD, MODE, true, QF8>(t[kk], lds, st, qq, qk_init, t0, lim, r, q4, k_factor, vsh,
+                                                        vsel);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1543,10 +1604,11 @@ constexpr bool attention_packs() {
 
 template <int HD, int MODE, bool QF8>
 void launch_attention_q(const AttnArgs& p, int threads, bool small_bs, hipStream_t st) {
-    if constexpr (!QF8 && attention_quads<HD, MODE>()) {
+    // head quads; with FP8 queries at head_dim 64 only
+    if constexpr (attention_quads<HD, MODE>() && (!QF8 || HD == 64)) {
         if (!small_bs && p.group <= 4 && p.heads_per_wg % 4 == 0) {
             const unsigned qlds = static_cast<unsigned>(threads / 64) * QuadGeo<HD, MODE>::LDS_WAVE;
-            hipLaunchKernelGGL((attention_quad_kernel<HD, MODE>), dim3(p.total_wg), dim3(threads), qlds, st, p);
+            hipLaunchKernelGGL((attention_quad_kernel<HD, MODE, QF8>), dim3(p.total_wg), dim3(threads), qlds, st, p);
             return;
         }
     }

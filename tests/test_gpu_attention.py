@@ -301,6 +301,8 @@ def test_attention_decode_workload_sampled(kvq, orc, mode, hd):
         sc.close()
 
 
+# the head-quad kernel serves the per-token-head layers; the static layouts
+# take the packed rounds of the one-head kernel on the same shapes
 QUAD_MODES = [W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD]
 
 
@@ -309,11 +311,12 @@ QUAD_MODES = [W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD, W.INT4_PER
 @pytest.mark.parametrize("mode", QUAD_MODES, ids=[W.MODE_NAMES[m] for m in QUAD_MODES])
 def test_attention_head_quads(kvq, orc, mode, hkv, group, bs):
     """Head_dim 64 with at most 4 query heads per KV head and 4 or 8 KV heads
-    per workgroup: each wave serves a quad of 4 KV heads (16 columns of 4
-    heads x 4 queries), the quad's 4 waves take every fourth tile and merge
-    through LDS.  Lengths leave some waves of a quad without a tile (1 to 3
-    tiles), end inside and at tile and block boundaries, and run to several
-    splits."""
+    per workgroup.  Per-token-head layers take the head-quad kernel: each
+    wave serves a quad of 4 KV heads (16 columns of 4 heads x 4 queries), the
+    quad's 4 waves take every fourth tile and merge through LDS; static
+    layers take the packed rounds on the same shapes.  Lengths leave some
+    waves of a quad without a tile (1 to 3 tiles), end inside and at tile
+    and block boundaries, and run to several splits."""
     lens = [0, 1, 15, 16, 17, 33, 48, 49, 100, 260, 600]
     _run(kvq, orc, f"quads mode {W.MODE_NAMES[mode]} hkv {hkv} group {group} bs {bs}", mode=mode, hd=64, hkv=hkv,
          bs=bs, lens=lens, group=group, seed=200 + hkv * 10 + group + mode)
@@ -421,14 +424,39 @@ def test_fp8_query_attention(kvq, orc, mode, hd, shrink):
         sc.close()
 
 
-def test_fp8_query_decode_workload_sampled(kvq, orc):
+@pytest.mark.parametrize("hkv,group,bs", [(4, 4, 16), (8, 3, 32), (12, 2, 16), (8, 1, 16)],
+                         ids=["hkv4-g4", "hkv8-g3-bs32", "hkv12-g2", "hkv8-g1"])
+@pytest.mark.parametrize("mode", [W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD])
+@pytest.mark.parametrize("shrink", [1.0, 4.0])
+def test_fp8_query_head_quads(kvq, orc, mode, hkv, group, bs, shrink):
+    """FP8 queries at head_dim 64 with groups of at most 4 and 4 or 8 KV heads
+    per workgroup: per-token-head layers take the head-quad kernel
+    (block-diagonal FP8 query codes through the FP8 products), static ones
+    the packed rounds; ragged lengths over several splits."""
+    what = f"fp8 query quads mode {W.MODE_NAMES[mode]} hkv {hkv} group {group} bs {bs} shrink {shrink}"
+    _flush(f"[attention] {what}")
+    lens = [0, 1, 15, 16, 17, 33, 48, 49, 100, 260, 600]
+    sc = Scenario(kvq, orc, mode=mode, hd=64, hkv=hkv, bs=bs, lens=lens, group=group,
+                  seed=300 + hkv * 10 + group + mode)
+    try:
+        qs = _query_scales(sc.q, shrink)
+        out = sc.run_gpu(q_scales=qs)
+        ref, tol = sc.reference(q_scales=qs)
+        sc.check(out, ref, tol, what)
+    finally:
+        sc.close()
+
+
+@pytest.mark.parametrize("hd", [128, 64])
+def test_fp8_query_decode_workload_sampled(kvq, orc, hd):
     """FP8 queries on the full decode shape (256 x 8192-8207 tokens, 32/8 heads,
-    head_dim 128, per-token-head FP8), eight sequences against the oracle."""
-    _flush("[attention] fp8 query decode 256 x 8192 (sampled)")
+    head_dim 128 and 64 (head quads), per-token-head FP8), eight sequences
+    against the oracle."""
+    _flush(f"[attention] fp8 query decode 256 x 8192 hd {hd} (sampled)")
     g = torch.Generator().manual_seed(21)
     lens = (8192 + torch.randint(0, 16, (256,), generator=g)).tolist()
-    k, v = (t.cpu() for t in W.normal_kv(sum(lens), 8, 128, seed=22, device=DEV))
-    sc = Scenario(kvq, orc, mode=W.FP8_PER_TOKEN_HEAD, hd=128, hkv=8, bs=16, lens=lens, group=4, seed=23,
+    k, v = (t.cpu() for t in W.normal_kv(sum(lens), 8, hd, seed=22, device=DEV))
+    sc = Scenario(kvq, orc, mode=W.FP8_PER_TOKEN_HEAD, hd=hd, hkv=8, bs=16, lens=lens, group=4, seed=23,
                   extra_blocks=0, kv=(k, v))
     del k, v
     try:
