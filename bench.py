@@ -293,8 +293,8 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, la
     args_s = f"--workload attention --mode {mode_name} --head-dim {hd}" + (f" --layers {layers}" if layers else "")
     stats = _read_csv(kt_dir, "kernel_stats.csv")
     lines = [f"# Kernel trace: decode attention, 256 x 8192 tokens, 32 query / 8 KV heads, {mode_name}, head_dim {hd}", "",
-             "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
-             f"    rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(kt_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline",
+             "Command (run from /tmp with TMPDIR=/tmp; R = repository root, OUT = an output directory):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/{os.path.basename(os.path.normpath(kt_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline",
              "", "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
     for r in stats:
         name = r.get("Name") or r.get("KernelName") or ""
@@ -317,9 +317,9 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, la
     algo = attention_bytes(mode, hd, hkv, bs, H, S, int(S * (ctx + 3.25)))
     flt = "--kernel-include-regex 'attention_kernel|attention_quad_kernel|combine_kernel|copyBuffer'"
     out = [f"# HBM traffic per launch: decode attention, {mode_name}, head_dim {hd} (256 x ~8195 cached tokens, 8 KV heads)", "",
-           "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
-           f"    rocprofv3 --pmc FETCH_SIZE {flt} --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(fetch_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
-           f"    rocprofv3 --pmc WRITE_SIZE {flt} --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(write_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
+           "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root, OUT = an output directory):", "",
+           f"    rocprofv3 --pmc FETCH_SIZE {flt} --output-format csv -d $OUT/{os.path.basename(os.path.normpath(fetch_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
+           f"    rocprofv3 --pmc WRITE_SIZE {flt} --output-format csv -d $OUT/{os.path.basename(os.path.normpath(write_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
            "",
            f"Calibration: a {COPY_BYTES >> 20} MiB device-to-device copy reads FETCH_SIZE {fetch['copy'][0]:.0f} KiB and "
            f"WRITE_SIZE {write['copy'][0]:.0f} KiB per dispatch; scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
@@ -356,9 +356,9 @@ def summarize_kernels(kt_dir, fetch_dir, write_dir, tag, bytes_json, bench_args,
     copy."""
     import json as _json
     stats = _read_csv(kt_dir, "kernel_stats.csv")
-    kt_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(kt_dir))} "
-              f"-o run -- python3 $R/bench.py {bench_args}")
-    lines = [f"# Kernel trace: {tag}", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+    kt_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/{os.path.basename(os.path.normpath(kt_dir))} "
+              f"-o run -- python3 $R/bench.py {bench_args} --launch-bytes-out $OUT/{os.path.basename(bytes_json)}")
+    lines = [f"# Kernel trace: {tag}", "", "Command (run from /tmp with TMPDIR=/tmp; R = repository root, OUT = an output directory):", "",
              f"    {kt_cmd}", "", "| kernel | calls | average (us) | min (us) | max (us) | share |",
              "|---|---|---|---|---|---|"]
     for r in stats:
@@ -393,10 +393,10 @@ def summarize_kernels(kt_dir, fetch_dir, write_dir, tag, bytes_json, bench_args,
     f_scale, w_scale = COPY_BYTES / (fcopy * 1024.0), COPY_BYTES / (wcopy * 1024.0)
     algo = _json.load(open(bytes_json))
     flt = f"--kernel-include-regex '{pmc_filter}' " if pmc_filter else ""
-    cmd = lambda c, d: (f"rocprofv3 --pmc {c} {flt}--output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(d))} "
+    cmd = lambda c, d: (f"rocprofv3 --pmc {c} {flt}--output-format csv -d $OUT/{os.path.basename(os.path.normpath(d))} "
                         f"-o run -- python3 $R/bench.py {bench_args} --calibrate-copy")
     out = [f"# HBM traffic per launch: {tag}", "",
-           "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+           "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root, OUT = an output directory):", "",
            f"    {cmd('FETCH_SIZE', fetch_dir)}", f"    {cmd('WRITE_SIZE', write_dir)}", "",
            f"Calibration: a {COPY_BYTES >> 20} MiB device-to-device copy reads FETCH_SIZE {fcopy:.0f} KiB and "
            f"WRITE_SIZE {wcopy:.0f} KiB per dispatch; scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write).",
@@ -449,11 +449,11 @@ def summarize_instructions(tag, dirs):
                         f"{100 * mean['SQ_ACTIVE_INST_VALU'] / mean['SQ_WAVE_CYCLES']:.1f}% | "
                         f"{100 * mean['SQ_WAIT_INST_ANY'] / mean['SQ_WAVE_CYCLES']:.1f}% |")
         cmds.append(f"    rocprofv3 --pmc {SQ_COUNTERS} --kernel-include-regex 'attention_kernel|attention_quad_kernel' "
-                    f"--output-format csv -d $R/gpurun_out/{os.path.basename(os.path.normpath(d))} -o run -- python3 "
+                    f"--output-format csv -d $OUT/{os.path.basename(os.path.normpath(d))} -o run -- python3 "
                     f"$R/bench.py --workload attention --mode {mode_name} --head-dim {hd} --steps 1 --warmup 0 "
                     f"--layers 4 --no-cpu-baseline")
     out = ["# Instruction counters: decode attention, 256 sequences x 8193 cached tokens, 8 KV heads, 32 query heads", "",
-           "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", "", *cmds, "",
+           "Commands (run from /tmp with TMPDIR=/tmp; R = repository root, OUT = an output directory):", "", *cmds, "",
            "Means over the dispatches of the attention kernel (4 layers x 3 passes).  A head-tile is 16 cached "
            "tokens of one KV head for its whole query group: 256 x 8 x 513 = 1.05 M per dispatch.  "
            "VALU-active and waiting are SQ_ACTIVE_INST_VALU and SQ_WAIT_INST_ANY as shares of SQ_WAVE_CYCLES.", "",
