@@ -485,3 +485,23 @@ def test_attention_one_long_sequence(kvq, orc, mode, hd):
         sc.check(out, ref, tol, what)
     finally:
         sc.close()
+
+
+@pytest.mark.parametrize("mode,hd", [(W.FP8_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 64),
+                                     (W.INT4_PER_TOKEN_HEAD, 128)],
+                         ids=["fp8_per_token_head-hd64", "int4_per_token_head-hd64", "int4_per_token_head-hd128"])
+def test_attention_head_quads_one_long_sequence(kvq, orc, mode, hd):
+    """Batch 1 on the head-quad kernel: one sequence of 8 KV heads split into
+    dozens of ranges (the workgroup-wide combine merges the quads'
+    partials); one range's blocks are outside the layer."""
+    what = f"quads one long sequence mode {W.MODE_NAMES[mode]} hd {hd}"
+    _flush(f"[attention] {what}")
+    sc = Scenario(kvq, orc, mode=mode, hd=hd, hkv=8, bs=16, lens=[6001], group=4, seed=150 + hd + mode)
+    try:
+        bt = sc.bt.copy()
+        bt[0, 40:48] = -1
+        out = sc.run_gpu(bt=bt)
+        ref, tol = sc.reference(bt=bt)
+        sc.check(out, ref, tol, what)
+    finally:
+        sc.close()
