@@ -96,6 +96,34 @@ def _adversarial_kv(n, hkv, hd, seed):
 MODES = [W.BF16, W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD]
 
 
+@pytest.mark.parametrize("hkv", [31, 32, 33, 40])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_static_per_head_many_kv_heads(kvq, orc, hd, hkv):
+    """Static per-head scales with 31-40 KV heads: up to 32 heads each wave
+    fetches the whole 2 x hkv table once and reads its heads' pairs across
+    lanes; beyond, every lane loads its own pair.  Every head has its own
+    scale pair, so a wrong pair changes the codes."""
+    _flush(f"[parity] per-head many heads hd={hd} hkv={hkv}")
+    bs, nblocks, n = 16, 12, 170
+    pair = Pair(kvq, orc, bs, hkv, hd, [W.FP8_PER_HEAD], [nblocks])
+    rng = np.random.default_rng(7000 + hd + hkv)
+    k, v = _adversarial_kv(n, hkv, hd, seed=int(rng.integers(1 << 30)))
+    slots = rng.permutation(nblocks * bs)[:n].astype(np.int64)
+    slots[3] = -1
+    scales = list((rng.uniform(0.001, 0.05, 2 * hkv) * np.exp2(rng.integers(-4, 5, 2 * hkv))).astype(np.float32))
+    pair.store(0, k, v, torch.from_numpy(slots), scales)
+    pair.assert_buffers_equal()
+    lens = [60, 0, 77, 33]
+    bt = np.full((4, nblocks), -1, dtype=np.int32)
+    order = rng.permutation(nblocks)
+    c = 0
+    for b, ln in enumerate(lens):
+        for j in range((ln + bs - 1) // bs):
+            bt[b, j] = order[c]
+            c += 1
+    pair.gather_and_compare(0, bt, lens)
+
+
 @pytest.mark.parametrize("mode", MODES, ids=[W.MODE_NAMES[m] for m in MODES])
 @pytest.mark.parametrize("hd", [64, 128, 256])
 @pytest.mark.parametrize("hkv", [1, 3, 8])
