@@ -1004,7 +1004,7 @@ def run_other_workload(args, torch, kvq, W):
                     "fp8_skip_sliding": (kvq.FP8_PER_TENSOR, kvq.BF16)}
         ct = __import__("ctypes")
         sm = 1.0 / math.sqrt(hd)
-        slopes, times = {}, {}
+        slopes, times, intercepts = {}, {}, {}
         itl_parity = None
         ocpu_s, ocpu_b = 0.0, 0           # oracle attention: seconds and algorithmic bytes
         for vname, (full_mode, slide_mode) in variants.items():
@@ -1073,6 +1073,7 @@ def run_other_workload(args, torch, kvq, W):
             mx, my = sum(ctxs) / n, sum(ts) / n
             slope = sum((x - mx) * (y - my) for x, y in zip(ctxs, ts)) / sum((x - mx) ** 2 for x in ctxs)
             slopes[vname] = slope
+            intercepts[vname] = my - slope * mx
             times[vname] = [round(t, 5) for t in ts]
             log(f"[bench] itl {vname}: {times[vname]} ms at {ctxs} tokens, slope {slope:.3e} ms/token")
         # one decode step of the FP8 variant with BF16 sliding layers at the
@@ -1103,6 +1104,13 @@ def run_other_workload(args, torch, kvq, W):
                "step_ms": times,
                "pages_h100_full_model_slopes_ms_per_token": {"bf16": 8.94e-06, "fp8": 7.14e-06,
                                                               "fp8_skip_sliding": 6.34e-06},
+               # the context where a variant's fitted line crosses BF16's (None
+               # where it is not slower at short context, or not faster per token)
+               "break_even_vs_bf16_tokens": {
+                   k: (round((intercepts[k] - intercepts["bf16"]) / (slopes["bf16"] - slopes[k]))
+                       if slopes["bf16"] > slopes[k] and intercepts[k] > intercepts["bf16"] else None)
+                   for k in ("fp8", "fp8_skip_sliding")},
+               "pages_h100_break_even_vs_bf16_tokens": {"fp8": 22109, "fp8_skip_sliding": 7659},
                "roofline": roof, "cpu_baseline": cpu, "parity_vs_oracle_sampled": itl_parity}
     elif name == "calib":
         # on-the-fly calibration over the GQA-32 prefill: one amax pass per layer
