@@ -15,7 +15,9 @@
 //   O[g][d] += sum_t P'[t][g] * code_V[t][d]
 // with an online (running-maximum) softmax over 16-token tiles; static
 // scales are applied once, s_K folded into the score factor and s_V into the
-// final output.
+// final output.  INT4 codes enter biased, as (n + 8) / 16 (a nibble XOR 8 is
+// the E4M3 code of (n + 8) 2^-9); the bias leaves through the Q K^T
+// product's initial accumulator and a separate value-bias accumulator.
 //
 // Work split.  A workgroup holds one wave per KV head of a run of heads and
 // walks a range of tiles of one sequence; the waves of a workgroup read
@@ -23,6 +25,9 @@
 // wave serves up to 16 query heads of its KV head (the MFMA N dimension).
 // Long sequences are cut into splits whose partial (O, m, l) a second kernel
 // combines; with one split the first kernel writes the output itself.
+// Per-token-head layers with query groups of at most 4 (FP8 at head_dim 64,
+// INT4 at 64 and 128) take attention_quad_kernel instead, whose waves each
+// serve a quad of 4 KV heads on the same grid, plan and partials.
 //
 // MFMA operand layouts used here (gfx950, lane l, r = l % 16, q = l / 16):
 //   mfma_f32_16x16x32_bf16:     A[m=r][k=8q+i], B[k=8q+i][n=r], D[m=4q+i][n=r]
