@@ -268,10 +268,12 @@ KVQ_API kvq_status kvq_static_scales(const float* amax, int32_t num_kv_heads, kv
                                      float* scales);
 
 /*
- * kvq_decode_attention_workspace -- device workspace bytes that
- * kvq_decode_attention needs for this cache and call shape (0 when the
- * sequences need not be split).  Host arithmetic only; no device call.
- * Arguments as for kvq_decode_attention.
+ * kvq_decode_attention_workspace -- device workspace bytes that are enough
+ * for kvq_decode_attention and kvq_decode_attention_fp8q on any layer of
+ * this cache with this call shape (0 when no call of the shape splits its
+ * sequences); a call on a given layer may use less (kernels that serve
+ * several heads or tiles per wave split less).  Host arithmetic only; no
+ * device call.  Arguments as for kvq_decode_attention.
  *   Errors: KVQ_ERR_INVALID_ARG.
  */
 KVQ_API kvq_status kvq_decode_attention_workspace(const kvq_cache* c, int32_t num_q_heads,

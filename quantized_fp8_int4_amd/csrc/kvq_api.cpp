@@ -241,7 +241,8 @@ kvq_status decode_attention(const kvq_cache* c, int32_t layer, const void* q, co
     if (q_scales && (lmode == KVQ_BF16 || lmode == KVQ_INT4_PER_TOKEN_HEAD)) return KVQ_ERR_UNSUPPORTED;
     if (q_scales && (reinterpret_cast<uintptr_t>(q_scales) & 3u)) return KVQ_ERR_INVALID_ARG;
     const kvq::AttnPlan plan =
-        kvq::attention_plan(L.block_size, L.num_kv_heads, L.head_dim, num_q_heads, max_blocks_per_seq, num_seqs);
+        kvq::attention_plan(L.block_size, L.num_kv_heads, L.head_dim, num_q_heads, max_blocks_per_seq, num_seqs,
+                            lmode, q_scales != nullptr);
     if (plan.grid >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
     if (fixed_scratch) {
         // The allocation-free variant: split partials go to this device's

@@ -117,6 +117,7 @@ struct AttnArgs {
     int32_t max_len;               // max_blocks * block_size, 0 for a layer without blocks
     uint32_t total_wg;
     float c;                       // sm_scale * log2(e)
+    int32_t kind;                  // AttnKind: the kernel the plan sized the grid for
 };
 
 // ------------------------------------------------------------ lane helpers
@@ -1044,6 +1045,22 @@ constexpr bool attention_quads() {
            (MODE == KVQ_INT4_PER_TOKEN_HEAD && (HD == 64 || HD == 128));
 }
 
+// the host's choice of kernel (attention_kind, which sizes the plan) names
+// only kernels this file instantiates
+template <int MODE>
+constexpr bool attention_kind_matches() {
+    return ((attention_kind(MODE, 64, 4, 16, 8, false) == kAttnHeadQuads) == attention_quads<64, MODE>()) &&
+           ((attention_kind(MODE, 128, 4, 16, 8, false) == kAttnHeadQuads) == attention_quads<128, MODE>()) &&
+           ((attention_kind(MODE, 256, 4, 16, 8, false) == kAttnHeadQuads) == attention_quads<256, MODE>()) &&
+           ((attention_kind(MODE, 64, 4, 16, 1, false) == kAttnTileQuads) == attention_quads<64, MODE>()) &&
+           attention_kind(MODE, 128, 4, 16, 1, false) != kAttnTileQuads &&
+           attention_kind(MODE, 128, 4, 16, 8, true) == kAttnOneHead;
+}
+static_assert(attention_kind_matches<KVQ_BF16>() && attention_kind_matches<KVQ_FP8_PER_TENSOR>() &&
+                  attention_kind_matches<KVQ_FP8_PER_HEAD>() && attention_kind_matches<KVQ_FP8_PER_TOKEN_HEAD>() &&
+                  attention_kind_matches<KVQ_INT4_PER_TOKEN_HEAD>(),
+              "attention_kind and attention_quads agree");
+
 template <int HD, int MODE>
 struct QuadRaw {
     uint32_t kv[4 * QuadGeo<HD, MODE>::NC];
@@ -1126,7 +1143,10 @@ __device__ __forceinline__ void quad_keys(const uint8_t* lds, int r, int q4, int
 // One tile of the quad: scores of all 16 columns, one softmax update, the
 // 4 heads' value products.  MASK = false: every token of the tile lies below
 // len in a block of the layer.
-template <int HD, int MODE, bool MASK, bool QF8>
+// TILES: the 4 column groups are 4 consecutive tiles of one KV head (tile
+// t0 / 16 + r / 4, its block's bit r / 4 of R.ok) instead of 4 heads of one
+// tile (every bit of R.ok the same).
+template <int HD, int MODE, bool MASK, bool QF8, bool TILES = false>
 __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uint8_t* lds, State<HD, MODE>& st,
                                            const QuadQuery<HD, MODE, QF8>& qq, f32x4 qk_init, int t0, int len, int r,
                                            int q4, float k_factor, uint32_t vsh, uint32_t vsel) {
@@ -1134,6 +1154,10 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
     using Q = QuadGeo<HD, MODE>;
     constexpr bool I4 = MODE == KVQ_INT4_PER_TOKEN_HEAD;
     const int hq = r >> 2;
+    // token tok of tile h of a TILES round lies in the range, in a block of the layer
+    auto tile_token_ok = [&](int h, int tok) {
+        return !MASK || ((t0 + kTile * h + tok < len) && ((R.ok >> h) & 1u));
+    };
     f32x4 sacc;
     if constexpr (QF8) {
         // FP8 queries: each head's raw K codes against its block-diagonal
@@ -1145,6 +1169,13 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
         for (int h = 0; h < 4; ++h) {
             uint32_t k[G::KW];
             quad_keys<HD, MODE>(lds, r, q4, h, k);
+            if constexpr (TILES && MASK && !I4) {
+                // a stale FP8 key of tile h (NaN codes included) would reach
+                // the other groups' columns through their zero queries
+                if (!tile_token_ok(h, r))
+#pragma unroll
+                    for (int w = 0; w < G::KW; ++w) k[w] = 0u;
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const long ka = static_cast<long>((static_cast<uint64_t>(k[2 * j + 1]) << 32) | k[2 * j]);
@@ -1161,6 +1192,13 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
         for (int h = 0; h < 4; ++h) {
             uint32_t k[G::KW];
             quad_keys<HD, MODE>(lds, r, q4, h, k);
+            if constexpr (TILES && MASK && !I4) {
+                // a stale FP8 key of tile h (NaN codes included) would reach
+                // the other groups' columns through their zero queries
+                if (!tile_token_ok(h, r))
+#pragma unroll
+                    for (int w = 0; w < G::KW; ++w) k[w] = 0u;
+            }
             acc[h] = qk_init;
 #pragma unroll
             for (int j = 0; j < HD / 32; ++j)
@@ -1177,6 +1215,13 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
         for (int h = 0; h < 4; ++h) {
             uint32_t k[G::KW];
             quad_keys<HD, MODE>(lds, r, q4, h, k);
+            if constexpr (TILES && MASK && !I4) {
+                // a stale FP8 key of tile h (NaN codes included) would reach
+                // the other groups' columns through their zero queries
+                if (!tile_token_ok(h, r))
+#pragma unroll
+                    for (int w = 0; w < G::KW; ++w) k[w] = 0u;
+            }
 #pragma unroll
             for (int j = 0; j < HD / 32; ++j)
                 sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(k, j), qq.b[h * (HD / 32) + j],
@@ -1185,7 +1230,12 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
     }
     bool valid[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) valid[i] = !MASK || ((t0 + 4 * q4 + i < len) && ((R.ok >> i) & 1u));
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (TILES)
+            valid[i] = tile_token_ok(hq, 4 * q4 + i);
+        else
+            valid[i] = !MASK || ((t0 + 4 * q4 + i < len) && ((R.ok >> i) & 1u));
+    }
     float s[4];
     float tmax = -INFINITY;
 #pragma unroll
@@ -1224,7 +1274,7 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
                 const uint32_t x = reinterpret_cast<const uint32_t*>(vp)[w];
                 // masked tokens may hold any bytes (NaN codes included): zero
                 // them, except INT4, whose biased codes are all finite
-                v[i][w] = (I4 || valid[i]) ? x : 0u;
+                v[i][w] = (I4 || (TILES ? tile_token_ok(h, 4 * q4 + i) : valid[i])) ? x : 0u;
             }
         }
         s16x4 av[G::J];
@@ -1486,6 +1536,326 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_quad_kernel(Attn
     }
 }
 
+// ------------------------------------------------ tile quads (few KV heads)
+//
+// A workgroup of fewer than 4 KV heads (one or two: a tensor-parallel shard,
+// a multi-query model) has no quad of heads.  Here the 4 column groups of a
+// wave are instead 4 consecutive tiles of one KV head: column r is query
+// r % 4 against tile base + r / 4.  The products and the softmax are those
+// of the head quads (quad_round with TILES): head h's role is taken by tile
+// h of the round, each column group keeps its own running (m, l, O), and a
+// round covers 64 tokens.  A workgroup holds 4 waves per KV head, which take
+// every fourth round of the split; at the end each head's 16 partial states
+// per query (4 waves x 4 column groups) merge through LDS.
+//
+// A round's row image is the 4 tiles' 16 K|V rows of the head side by side
+// (row p: tiles 0..3 at position p), the same LDS layout as a head quad's
+// tile, loaded as 1 KiB pieces of one tile each.  The per-token scales of a
+// lane's tile come from that tile's block, so they are read by address
+// rather than through a block's buffer descriptor.
+template <int HD, int MODE>
+struct TquadGeo {
+    using G = Geo<HD, MODE>;
+    static constexpr int TR = 2 * G::RB;                   // one token's K|V rows of the head
+    static constexpr int PPT = kTile * TR / 1024;           // 1 KiB pieces per tile
+    static constexpr int TPC = 1024 / TR;                  // tokens per piece
+    static_assert(PPT >= 1 && PPT * 4 == QuadGeo<HD, MODE>::NC, "a round is 4 tiles of whole pieces");
+};
+
+struct TquadLaneOff {
+    uint32_t kv;                   // the lane's 16 bytes of a tile's first piece
+    uint32_t lds;                  // ... and where they go in the wave's LDS rows
+    int kv_step;                   // block bytes from one piece of a tile to the next (uniform)
+    uint32_t s;                    // (s_K, s_V) of token 4 q4 of the lane's tile, from its block
+};
+
+template <int HD, int MODE>
+__device__ __forceinline__ void tquad_load(const AttnArgs& a, const int (&blk)[4], const int (&tau)[4], int hq,
+                                           const TquadLaneOff& lo, QuadRaw<HD, MODE>& T) {
+    using G = Geo<HD, MODE>;
+    using Q = QuadGeo<HD, MODE>;
+    using TQ = TquadGeo<HD, MODE>;
+    const uint32_t pmask = (1u << a.bs_log2) - 1u;
+    uint32_t ok = 0u;
+    uint64_t lane_base = 0;
+    uint32_t lane_pos0 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool okj = static_cast<uint32_t>(blk[j]) < static_cast<uint32_t>(a.num_blocks);
+        ok |= okj ? (1u << j) : 0u;
+        const uint32_t ublk = okj ? static_cast<uint32_t>(blk[j]) : 0u;
+        const uint32_t pos0 = static_cast<uint32_t>(tau[j] * kTile) & pmask;
+        const uint64_t boff = static_cast<uint64_t>(ublk) * static_cast<uint64_t>(a.block_bytes);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(a.layer + boff), 0, static_cast<int>(a.block_bytes), kBufferDword3);
+        const int srow = static_cast<int>(pos0 * static_cast<uint32_t>(a.hkv) * TQ::TR);
+#pragma unroll
+        for (int pc = 0; pc < TQ::PPT; ++pc)
+            buf_load<16, kNonTemporal>(T.kv + 4 * (j * TQ::PPT + pc), rs, lo.kv, srow + pc * lo.kv_step);
+        lane_base = hq == j ? boff : lane_base;
+        lane_pos0 = hq == j ? pos0 : lane_pos0;
+    }
+    if constexpr (G::DYN) {
+        const uint8_t* sp = a.layer + lane_base + static_cast<uint64_t>(a.code_bytes) +
+                            static_cast<uint64_t>(lane_pos0 * static_cast<uint32_t>(a.hkv) * 8u + lo.s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            T.s[i] = *reinterpret_cast<const f32x2*>(sp + static_cast<uint64_t>(i) * static_cast<uint32_t>(a.hkv) * 8u);
+    }
+    T.ok = ok;
+}
+
+template <int HD, int MODE, bool QF8>
+__global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(AttnArgs a) {
+    using G = Geo<HD, MODE>;
+    using Q = QuadGeo<HD, MODE>;
+    using TQ = TquadGeo<HD, MODE>;
+    // work item: as attention_kernel (qgroups is 1: groups of at most 4)
+    const uint32_t p = blockIdx.x;
+    const uint32_t xcd = p % 8u, slot = p / 8u;
+    const uint32_t per = a.total_wg / 8u, rem = a.total_wg % 8u;
+    uint32_t item = xcd * per + min(xcd, rem) + slot;
+    const int chunk = static_cast<int>(item % static_cast<uint32_t>(a.head_chunks));
+    item /= static_cast<uint32_t>(a.head_chunks);
+    const int split = static_cast<int>(item % static_cast<uint32_t>(a.splits));
+    const int b = static_cast<int>(item / static_cast<uint32_t>(a.splits));
+
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int sr = wave & 3;                                   // the wave's share of the rounds
+    const int hh = chunk * a.heads_per_wg + (wave >> 2);       // the wave's KV head
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, q4 = lane >> 4;
+    const int hq = r >> 2, g = r & 3;                          // column group (tile of the round), query
+
+    const int len = max(0, min(a.seq_lens[b], a.max_len));
+    const int ntiles = (len + kTile - 1) / kTile;
+    const int tbeg = split * a.tiles_per_split;
+    const int tend = min(ntiles, tbeg + a.tiles_per_split);
+    if (a.splits > 1 && tbeg >= tend) return;      // (the whole workgroup) the combine reads only non-empty splits
+
+    const bool qvalid = g < a.group;
+    const int qh = hh * a.group + (qvalid ? g : 0);
+    QOperand<HD, QF8> qo;
+    float q_factor = 1.0f;
+    {
+        const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.num_q_heads + qh) * HD + q4 * (HD / 4);
+        if constexpr (!QF8) {
+#pragma unroll
+            for (int j = 0; j < HD / 32; ++j) {
+                const uint4 v = qvalid ? ld16<false>(qp + 8 * j) : make_uint4(0, 0, 0, 0);
+                const u32x4 w = {v.x, v.y, v.z, v.w};
+                qo.b[j] = __builtin_bit_cast(bf16x8, w);
+            }
+        } else {
+            // E4M3(RN32(q / s_q)), saturating, exactly as the cache encodes K
+            q_factor = qvalid ? a.q_scales[qh] : 1.0f;
+            const RowQ rq = row_prep(q_factor);
+#pragma unroll
+            for (int j = 0; j < HD / 32; ++j) {
+                const uint4 v = qvalid ? ld16<false>(qp + 8 * j) : make_uint4(0, 0, 0, 0);
+                const uint2 c = encode_fp8<true, true>(v, rq);
+                qo.c[2 * j] = c.x;
+                qo.c[2 * j + 1] = c.y;
+            }
+        }
+    }
+    f32x4 qk_init = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD && !QF8) {
+        int4_query_order<HD>(qo);
+        qk_init = int4_key_bias<HD>(qo);
+    }
+    // query operands: tile h's products see only the columns of group h
+    QuadQuery<HD, MODE, QF8> qq;
+    if constexpr (QF8) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int w = 0; w < HD / 16; ++w) qq.c[h * (HD / 16) + w] = hq == h ? qo.c[w] : 0u;
+    } else {
+        constexpr int NQB = QuadQuery<HD, MODE, false>::N;
+#pragma unroll
+        for (int h = 0; h < NQB / (HD / 32); ++h)
+#pragma unroll
+            for (int j = 0; j < HD / 32; ++j) {
+                const u32x4 w = __builtin_bit_cast(u32x4, qo.b[j]);
+                const bool keep = Q::SELECT || hq == h;
+                const u32x4 z = {keep ? w[0] : 0u, keep ? w[1] : 0u, keep ? w[2] : 0u, keep ? w[3] : 0u};
+                qq.b[h * (HD / 32) + j] = __builtin_bit_cast(bf16x8, z);
+            }
+    }
+
+    float k_factor = a.c * G::CODE_UNIT * q_factor;
+    float v_factor = G::CODE_UNIT;
+    if constexpr (MODE == KVQ_FP8_PER_TENSOR) {
+        k_factor *= a.statics[0];
+        v_factor = a.statics[1];
+    } else if constexpr (MODE == KVQ_FP8_PER_HEAD) {
+        k_factor *= a.statics[hh];
+        v_factor = a.statics[a.hkv + hh];
+    }
+
+    State<HD, MODE> st;
+#pragma unroll
+    for (int j = 0; j < G::J; ++j) st.o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    st.vb = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    st.m = -INFINITY;
+    st.l = 0.0f;
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    uint8_t* const lds = lds_dyn + wave * Q::LDS_WAVE;
+    TquadLaneOff lo;
+    {
+        const uint32_t hkv = static_cast<uint32_t>(a.hkv);
+        const uint32_t bl = static_cast<uint32_t>(lane) * 16u;
+        const uint32_t tok = bl / TQ::TR, off = bl % TQ::TR;
+        lo.kv = (tok * hkv + static_cast<uint32_t>(hh)) * TQ::TR + off;
+        lo.lds = tok * Q::LDS_ROW + off;
+        lo.kv_step = TQ::TPC * a.hkv * TQ::TR;
+        lo.s = (static_cast<uint32_t>(4 * q4) * hkv + static_cast<uint32_t>(hh)) * 8u;
+    }
+    const uint32_t vsh = G::VB == 2 ? 16u * static_cast<uint32_t>(r & 1) : 0u;
+    const uint32_t vsel = (r & 1) ? 0x07030602u : 0x05010400u;
+
+    const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+    const int nr = (tend - tbeg + 3) / 4;                          // rounds of 4 tiles in the split
+    const int nt = sr < nr ? (nr - sr + 3) / 4 : 0;                // this wave's rounds: sr, sr + 4, ...
+    if (nt > 0) {
+        constexpr int D = Q::D;
+        const int lim = min(len, tend * kTile);
+        // rounds past the wave's last re-read the last; tiles past the
+        // split's end read its last tile (masked: their tokens lie at or past lim)
+        auto base_of = [&](int k) { return tbeg + 4 * (sr + 4 * min(k, nt - 1)); };
+        auto tiles_of = [&](int k, int (&tau)[4], int (&blk)[4]) {
+            const int t = base_of(k);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                tau[j] = min(t + j, tend - 1);
+                blk[j] = bt_row[(tau[j] * kTile) >> a.bs_log2];
+            }
+        };
+        QuadRaw<HD, MODE> t[D];
+#pragma unroll
+        for (int k = 0; k < D - 1; ++k) {
+            int tau[4], blk[4];
+            tiles_of(k, tau, blk);
+            tquad_load<HD, MODE>(a, blk, tau, hq, lo, t[k]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int k0 = 0; k0 < nt; k0 += D) {
+#pragma unroll
+            for (int kk = 0; kk < D; ++kk) {
+                const int k = k0 + kk;
+                {
+                    int tau[4], blk[4];
+                    tiles_of(k + D - 1, tau, blk);
+                    tquad_load<HD, MODE>(a, blk, tau, hq, lo, t[(kk + D - 1) % D]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (k < nt) {
+                    // the round's 4 tiles into the wave's LDS rows, side by side
+#pragma unroll
+                    for (int c = 0; c < Q::NC; ++c) {
+                        const int j = c / TQ::PPT, pc = c % TQ::PPT;
+                        const u32x4 v = {t[kk].kv[4 * c], t[kk].kv[4 * c + 1], t[kk].kv[4 * c + 2], t[kk].kv[4 * c + 3]};
+                        *reinterpret_cast<u32x4*>(lds + lo.lds + pc * TQ::TPC * Q::LDS_ROW + j * TQ::TR) = v;
+                    }
+                    const int t0 = base_of(k) * kTile;
+                    if (t0 + 4 * kTile <= lim && t[kk].ok == 0xFu)
+                        quad_round<HD, MODE, false, QF8, true>(t[kk], lds, st, qq, qk_init, t0, lim, r, q4, k_factor,
+                                                               vsh, vsel);
+                    else
+                        quad_round<HD, MODE, true, QF8, true>(t[kk], lds, st, qq, qk_init, t0, lim, r, q4, k_factor,
+                                                              vsh, vsel);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < D - 1; ++k) consume(t[k]);
+    }
+
+    float l = sum_q4(st.l);
+    if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+#pragma unroll
+        for (int j = 0; j < G::J; ++j) st.o[j] -= st.vb;
+    }
+    // merge the head's 16 partial states of each query (its 4 waves x 4
+    // column groups): each wave writes (m, l, O) to its LDS, and the first
+    // wave's group-0 lanes combine them
+    __syncthreads();
+    float* const mine = reinterpret_cast<float*>(lds_dyn + wave * Q::LDS_WAVE);
+    mine[lane] = st.m;
+    mine[64 + lane] = l;
+#pragma unroll
+    for (int j = 0; j < G::J; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[(2 + 4 * j + i) * 64 + lane] = st.o[j][i];
+    __syncthreads();
+    if (sr != 0 || hq != 0) return;
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            m = fmaxf(m, reinterpret_cast<const float*>(lds_dyn + (wave + w) * Q::LDS_WAVE)[lane + 4 * c]);
+    const float mref = m == -INFINITY ? 0.0f : m;
+    l = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G::J; ++j) st.o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float* other = reinterpret_cast<const float*>(lds_dyn + (wave + w) * Q::LDS_WAVE);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int ln = lane + 4 * c;                       // column group c of the same query, same q4
+            const float f = __builtin_amdgcn_exp2f(other[ln] - mref);
+            l += f * other[64 + ln];
+#pragma unroll
+            for (int j = 0; j < G::J; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st.o[j][i] += f * other[(2 + 4 * j + i) * 64 + ln];
+        }
+    }
+    st.m = m;
+    // lane holds dims J*(4*q4 + i) + j of query head qh, as attention_kernel
+    const int64_t row = static_cast<int64_t>(b) * a.num_q_heads + qh;
+    if (!qvalid) return;
+    if (a.splits == 1) {
+        const float inv = l > 0.0f ? v_factor / l : 0.0f;
+        uint16_t* op = a.out + row * HD + q4 * (HD / 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t w[G::J / 2];
+#pragma unroll
+            for (int j = 0; j < G::J; j += 2) w[j / 2] = pack_bf16(st.o[j][i] * inv, st.o[j + 1][i] * inv);
+            uint16_t* dst = op + i * G::J;
+            if constexpr (G::J >= 8) {
+#pragma unroll
+                for (int k = 0; k < G::J / 8; ++k) st16<false>(dst + 8 * k, make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]));
+            } else {
+                st8<false>(dst, make_uint2(w[0], w[1]));
+            }
+        }
+    } else {
+        const int64_t prow = row * a.splits + split;
+        float* op = a.part_o + prow * HD + q4 * (HD / 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < G::J; j += 4) {
+                const uint4 w = make_uint4(__float_as_uint(st.o[j][i] * v_factor), __float_as_uint(st.o[j + 1][i] * v_factor),
+                                           __float_as_uint(st.o[j + 2][i] * v_factor),
+                                           __float_as_uint(st.o[j + 3][i] * v_factor));
+                st16<false>(op + i * G::J + j, w);
+            }
+        }
+        if (q4 == 0) {
+            const u32x2 ml = {__float_as_uint(st.m), __float_as_uint(l)};
+            *reinterpret_cast<u32x2*>(a.part_ml + prow * 2) = ml;
+        }
+    }
+}
+
 // Combine of the splits' partial results: one wave per (sequence, query head).
 struct CombineArgs {
     const float* part_o;
@@ -1609,12 +1979,22 @@ constexpr bool attention_packs() {
 
 template <int HD, int MODE, bool QF8>
 void launch_attention_q(const AttnArgs& p, int threads, bool small_bs, hipStream_t st) {
-    // head quads; with FP8 queries at head_dim 64 only
+    // the plan's kind (attention_kind): head quads, with FP8 queries at
+    // head_dim 64 only; tile quads at head_dim 64, 4 waves per KV head
     if constexpr (attention_quads<HD, MODE>() && (!QF8 || HD == 64)) {
-        if (!small_bs && p.group <= 4 && p.heads_per_wg % 4 == 0) {
+        if (p.kind == kAttnHeadQuads) {
             const unsigned qlds = static_cast<unsigned>(threads / 64) * QuadGeo<HD, MODE>::LDS_WAVE;
             hipLaunchKernelGGL((attention_quad_kernel<HD, MODE, QF8>), dim3(p.total_wg), dim3(threads), qlds, st, p);
             return;
+        }
+        if constexpr (HD == 64) {
+            if (p.kind == kAttnTileQuads) {
+                const int tthreads = 4 * threads;
+                const unsigned qlds = static_cast<unsigned>(tthreads / 64) * QuadGeo<HD, MODE>::LDS_WAVE;
+                hipLaunchKernelGGL((attention_tquad_kernel<HD, MODE, QF8>), dim3(p.total_wg), dim3(tthreads), qlds,
+                                   st, p);
+                return;
+            }
         }
     }
     // staged tiles: one LDS tile image per wave of the workgroup
@@ -1713,6 +2093,7 @@ int launch_attention(const AttnLaunch& a, const AttnPlan& pl, void* stream) {
     p.max_len = a.num_blocks > 0 ? a.max_blocks << a.bs_log2 : 0;
     p.total_wg = static_cast<uint32_t>(pl.grid);
     p.c = a.sm_scale * kLog2e;
+    p.kind = pl.kind;
     const int threads = 64 * pl.heads_per_wg;
     const bool small_bs = a.bs_log2 < 4;
     switch (a.head_dim) {

@@ -126,16 +126,35 @@ constexpr int kAttnMaxHeadsPerWg = 8;  // waves (KV heads) per attention workgro
 // Splits per sequence never exceed the plan's target wave count, so the wide
 // combine's LDS weight table holds them all.
 constexpr int kAttnMaxSplits = 4096;
+// The decode-attention kernel that serves a call.  Head quads: per-token-head
+// FP8 at head_dim 64 (BF16 or FP8 queries) and INT4 at head_dim 64 and 128
+// (BF16 queries), with blocks of at least 16 tokens, query groups of at most
+// 4 and 4 or 8 KV heads per workgroup.  Tile quads: the same layers at
+// head_dim 64 with 1 or 2 KV heads per workgroup (4 waves per head).  Any
+// other call takes the one-head kernel.
+enum AttnKind : int32_t { kAttnOneHead = 0, kAttnHeadQuads = 1, kAttnTileQuads = 2 };
+constexpr int32_t attention_kind(int32_t mode, int32_t head_dim, int32_t group, int32_t block_size,
+                                 int32_t heads_per_wg, bool fp8_queries) {
+    const bool quad_layer = (mode == KVQ_FP8_PER_TOKEN_HEAD && head_dim == 64) ||
+                            (mode == KVQ_INT4_PER_TOKEN_HEAD && !fp8_queries && (head_dim == 64 || head_dim == 128));
+    if (!quad_layer || block_size < 16 || group > 4) return kAttnOneHead;
+    if (heads_per_wg % 4 == 0) return kAttnHeadQuads;
+    return head_dim == 64 ? kAttnTileQuads : kAttnOneHead;
+}
+
 struct AttnPlan {
     int32_t splits;                // tile ranges per sequence
     int32_t tiles_per_split;       // 16-token tiles per range
-    int32_t heads_per_wg;          // KV heads (waves) per workgroup
+    int32_t heads_per_wg;          // KV heads per workgroup
     int32_t qgroups;               // 16-query-head groups per KV head
+    int32_t kind;                  // AttnKind of the kernel
     int64_t grid;                  // workgroups of the attention kernel
     uint64_t workspace_bytes;      // partial results (0 with one split)
 };
+// mode < 0 plans for the one-head kernel, whose partials are never fewer
+// than those of the quads (the workspace a cache's calls need at most).
 AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t num_q_heads,
-                        int32_t max_blocks, int32_t num_seqs);
+                        int32_t max_blocks, int32_t num_seqs, int32_t mode = -1, bool fp8_queries = false);
 
 struct AttnLaunch {
     const uint8_t* layer;

@@ -23,23 +23,28 @@ int64_t gather_grid(const GatherLaunch& a) {
 // workgroup, up to 16 query heads per wave, tile ranges of one sequence per
 // workgroup.
 AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t num_q_heads,
-                        int32_t max_blocks, int32_t num_seqs) {
+                        int32_t max_blocks, int32_t num_seqs, int32_t mode, bool fp8_queries) {
     AttnPlan pl{};
     int hpw = 1;
     while (hpw < kAttnMaxHeadsPerWg && num_kv_heads % (2 * hpw) == 0) hpw *= 2;
     pl.heads_per_wg = hpw;
     const int group = num_q_heads / num_kv_heads;
     pl.qgroups = (group + 15) / 16;
+    pl.kind = mode < 0 ? kAttnOneHead : attention_kind(mode, head_dim, group, block_size, hpw, fp8_queries);
+    // waves per workgroup: one per KV head, four per KV head on the tile quads
+    const int64_t wpw = static_cast<int64_t>(hpw) * (pl.kind == kAttnTileQuads ? 4 : 1);
     const int64_t units = static_cast<int64_t>(num_seqs) * (num_kv_heads / hpw) * pl.qgroups;
     const int64_t max_tiles = (static_cast<int64_t>(max_blocks) * block_size + kAttnTile - 1) / kAttnTile;
     // About 1024 waves in all (measured best against 4096 and 2048: a wave
     // streams best over a long tile range, and fewer splits write fewer
     // partials); a split keeps at least 8 tiles.  A long single sequence gets
-    // up to 1024 / heads_per_wg splits; a large batch gets one split, and the
-    // kernel then writes the output itself.
+    // up to 1024 / (waves per workgroup) splits; a large batch gets one split,
+    // and the kernel then writes the output itself.  (Tile quads counted one
+    // wave per head, as the other kernels, measured 4-20% slower at head_dim
+    // 64 on one or two KV heads.)
     constexpr int64_t kTargetWaves = 1024, kMinTilesPerSplit = 8;
     static_assert(kTargetWaves <= kAttnMaxSplits, "the wide combine holds every split's weight");
-    const int64_t want = (kTargetWaves / hpw + units - 1) / units;
+    const int64_t want = (kTargetWaves / wpw + units - 1) / units;
     const int64_t cap = (max_tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
     int64_t splits = want < cap ? want : cap;
     if (splits < 1) splits = 1;

@@ -28,6 +28,7 @@
 #include <vector>
 
 #include "kvq.h"
+#include "kvq_internal.h"
 
 extern "C" {
 void orc_cache_bytes(int, int64_t, int64_t, int64_t, const int32_t*, const int64_t*, int64_t*);
@@ -199,10 +200,19 @@ void drive_abi(Rng& r) {
                     const int ws_st = kvq_decode_attention_workspace(c, H, maxb, ns, &need);
                     CHECK(status_ok(ws_st), "workspace status");
                     const uint64_t have = r.p(0.5) ? need : (need ? need - 1 : 0);
+                    void* const ws = r.p(0.8) ? reinterpret_cast<void*>(kFake) : nullptr;
                     st = kvq_decode_attention(c, layer, fake_ptr(r), H, static_cast<const int32_t*>(fake_ptr(r)), maxb,
-                                              static_cast<const int32_t*>(fake_ptr(r)), ns, sm, fake_ptr(r),
-                                              r.p(0.8) ? reinterpret_cast<void*>(kFake) : nullptr, have, nullptr);
-                    if (st == KVQ_OK && ns > 0) CHECK(ws_st == KVQ_OK && have >= need, "workspace honoured");
+                                              static_cast<const int32_t*>(fake_ptr(r)), ns, sm, fake_ptr(r), ws, have,
+                                              nullptr);
+                    // the query covers every layer of the cache; a layer whose
+                    // kernel splits less (the tile quads) needs no more
+                    if (st == KVQ_OK && ns > 0) {
+                        const kvq::AttnPlan pl =
+                            kvq::attention_plan(bs, hkv, hd, H, maxb, ns, modes[layer], false);
+                        CHECK(ws_st == KVQ_OK && have >= pl.workspace_bytes && pl.workspace_bytes <= need,
+                              "workspace honoured");
+                    }
+                    CHECK(!(ws_st == KVQ_OK && ws && have >= need && st == KVQ_ERR_BUFFER_TOO_SMALL), "query sufficient");
                 } else {
                     st = kvq_decode_attention_noalloc(c, layer, fake_ptr(r), H, static_cast<const int32_t*>(fake_ptr(r)),
                                                       maxb, static_cast<const int32_t*>(fake_ptr(r)), ns, sm,

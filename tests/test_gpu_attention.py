@@ -424,6 +424,80 @@ def test_fp8_query_attention(kvq, orc, mode, hd, shrink):
         sc.close()
 
 
+TQUAD_CASES = [(W.FP8_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 128)]
+TQUAD_IDS = ["fp8_per_token_head-hd64", "int4_per_token_head-hd64", "int4_per_token_head-hd128"]
+
+
+@pytest.mark.parametrize("hkv,group,bs", [(1, 4, 16), (2, 4, 16), (3, 3, 32), (6, 2, 16), (1, 1, 128), (2, 2, 64)],
+                         ids=["hkv1-g4", "hkv2-g4", "hkv3-g3-bs32", "hkv6-g2", "hkv1-g1-bs128", "hkv2-g2-bs64"])
+@pytest.mark.parametrize("mode,hd", TQUAD_CASES, ids=TQUAD_IDS)
+def test_attention_tile_quads(kvq, orc, mode, hd, hkv, group, bs):
+    """Workgroups of one or two KV heads (a tensor-parallel shard, few-head
+    models): 4 consecutive tiles of one head share a wave's 16 columns, 4
+    waves per head take every fourth round and merge 16 partial states per
+    query.  Lengths end inside a round, at tile and block boundaries, leave
+    waves without a round, and run to several splits."""
+    lens = [0, 1, 15, 16, 17, 33, 48, 49, 64, 65, 100, 130, 260, 600]
+    _run(kvq, orc, f"tile quads mode {W.MODE_NAMES[mode]} hd {hd} hkv {hkv} group {group} bs {bs}", mode=mode,
+         hd=hd, hkv=hkv, bs=bs, lens=lens, group=group, seed=400 + hkv * 10 + group + mode + hd)
+
+
+@pytest.mark.parametrize("mode,hd", TQUAD_CASES, ids=TQUAD_IDS)
+def test_attention_tile_quads_single_split_foreign_blocks_and_long(kvq, orc, mode, hd):
+    """Tile quads with one split (the first kernel writes the output), table
+    entries outside the layer inside a round, clamped lengths, and one long
+    sequence over dozens of split ranges (the wide combine)."""
+    _flush(f"[attention] tile quads single split, foreign blocks {W.MODE_NAMES[mode]} hd {hd}")
+    sc = Scenario(kvq, orc, mode=mode, hd=hd, hkv=1, bs=16, lens=[70, 120, 40, 3], group=4, seed=450 + mode + hd)
+    try:
+        out = sc.run_gpu()
+        ref, tol = sc.reference()
+        sc.check(out, ref, tol, "tile quads single split")
+        bt = sc.bt.copy()
+        bt[0, 1] = -1
+        bt[1, 3] = sc.nblocks
+        bt[1, 5] = -2
+        bt[2, :] = -5
+        out = sc.run_gpu(bt=bt)
+        ref, tol = sc.reference(bt=bt)
+        sc.check(out, ref, tol, "tile quads foreign blocks")
+        assert not out[2].any() and not ref[2].any()
+        lens = [-3, 10 ** 6, 40, 0]
+        out = sc.run_gpu(lens=lens)
+        ref, tol = sc.reference(lens=lens)
+        sc.check(out, ref, tol, "tile quads clamped lengths")
+        assert not out[0].any() and not out[3].any()
+    finally:
+        sc.close()
+    sc = Scenario(kvq, orc, mode=mode, hd=hd, hkv=2, bs=16, lens=[6001], group=4, seed=460 + mode + hd)
+    try:
+        bt = sc.bt.copy()
+        bt[0, 40:48] = -1
+        out = sc.run_gpu(bt=bt)
+        ref, tol = sc.reference(bt=bt)
+        sc.check(out, ref, tol, "tile quads one long sequence")
+    finally:
+        sc.close()
+
+
+@pytest.mark.parametrize("shrink", [1.0, 4.0])
+@pytest.mark.parametrize("hkv,group", [(1, 4), (2, 3)], ids=["hkv1-g4", "hkv2-g3"])
+def test_fp8_query_tile_quads(kvq, orc, hkv, group, shrink):
+    """FP8 queries on the tile quads (per-token-head FP8, head_dim 64)."""
+    what = f"fp8 query tile quads hkv {hkv} group {group} shrink {shrink}"
+    _flush(f"[attention] {what}")
+    lens = [0, 1, 17, 49, 65, 130, 600]
+    sc = Scenario(kvq, orc, mode=W.FP8_PER_TOKEN_HEAD, hd=64, hkv=hkv, bs=16, lens=lens, group=group,
+                  seed=470 + hkv * 10 + group)
+    try:
+        qs = _query_scales(sc.q, shrink)
+        out = sc.run_gpu(q_scales=qs)
+        ref, tol = sc.reference(q_scales=qs)
+        sc.check(out, ref, tol, what)
+    finally:
+        sc.close()
+
+
 @pytest.mark.parametrize("hkv,group,bs", [(4, 4, 16), (8, 3, 32), (12, 2, 16), (8, 1, 16)],
                          ids=["hkv4-g4", "hkv8-g3-bs32", "hkv12-g2", "hkv8-g1"])
 @pytest.mark.parametrize("mode", [W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD])
