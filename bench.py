@@ -236,7 +236,8 @@ def measured_traffic(path=PROFILE_TRAFFIC):
 def _kernel_key(name):
     """(kind/head_dim/mode, short name) of a library or ceiling kernel's
     demangled name, or None for other kernels."""
-    m = re.search(r"\b(store_kernel|gather_kernel|attention_kernel|attention_quad_kernel|combine_kernel|"
+    m = re.search(r"\b(store_kernel|gather_kernel|attention_kernel|attention_quad_kernel|attention_tquad_kernel|"
+                  r"combine_kernel|"
                   r"combine_wide_kernel|calib_kernel|"
                   r"store_pattern_kernel|gather_pattern_kernel|linear_copy_kernel)(?:<([^>]*)>)?", name)
     if not m:
@@ -245,7 +246,7 @@ def _kernel_key(name):
     short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
     targs = [t.strip() for t in (m.group(2) or "").split(",") if t.strip()]
     # library kernels by head_dim and mode; the ceiling kernels by all their arguments
-    keep = targs[:2] if kind in ("store", "gather", "attention", "attention_quad", "calib") else targs
+    keep = targs[:2] if kind in ("store", "gather", "attention", "attention_quad", "attention_tquad", "calib") else targs
     return "/".join([kind] + keep), short
 
 
@@ -272,7 +273,7 @@ def _counter_per_kernel(rows, counter):
             acc.setdefault("store", []).append(val)
         elif "gather_kernel" in name:
             acc.setdefault("gather", []).append(val)
-        elif "attention_kernel" in name or "attention_quad_kernel" in name:
+        elif "attention_kernel" in name or "attention_quad_kernel" in name or "attention_tquad_kernel" in name:
             acc.setdefault("attention", []).append(val)
         elif "combine_kernel" in name:
             acc.setdefault("combine", []).append(val)
@@ -281,6 +282,24 @@ def _counter_per_kernel(rows, counter):
     top = max(copies)
     acc["copy"] = [v for v in copies if v >= 0.5 * top]
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def attention_kernel_name(mode, hd, group, block_size, hkv, q_fp8):
+    """The decode-attention kernel the library picks for a call (a label for
+    the JSON line): quads of KV heads for per-token-head layers (FP8 at
+    head_dim 64, INT4 at 64 and 128 with BF16 queries), groups of at most 4
+    and blocks of at least 16 tokens, when a workgroup holds 4 or 8 KV heads;
+    quads of tiles on the same layers when it holds 1 or 2; else the one-head
+    kernel."""
+    import quantized_fp8_int4_amd as kvq
+    quad_layer = ((mode == kvq.FP8_PER_TOKEN_HEAD and hd == 64) or
+                  (mode == kvq.INT4_PER_TOKEN_HEAD and hd in (64, 128) and not q_fp8))
+    if not quad_layer or block_size < 16 or group > 4:
+        return "attention_kernel"
+    hpw = 1
+    while hpw < 8 and hkv % (2 * hpw) == 0:
+        hpw *= 2
+    return "attention_quad_kernel" if hpw % 4 == 0 else "attention_tquad_kernel"
 
 
 def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, layers=0):
@@ -315,7 +334,7 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, la
     # the profiled launches: 4 fused steps (lengths ctx + 1 .. ctx + 4) and 4
     # attention-only passes at ctx + 4, 32 layers each: mean length ctx + 3.25
     algo = attention_bytes(mode, hd, hkv, bs, H, S, int(S * (ctx + 3.25)))
-    flt = "--kernel-include-regex 'attention_kernel|attention_quad_kernel|combine_kernel|copyBuffer'"
+    flt = "--kernel-include-regex 'attention_kernel|attention_quad_kernel|attention_tquad_kernel|combine_kernel|copyBuffer'"
     out = [f"# HBM traffic per launch: decode attention, {mode_name}, head_dim {hd} (256 x ~8195 cached tokens, 8 KV heads)", "",
            "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root, OUT = an output directory):", "",
            f"    rocprofv3 --pmc FETCH_SIZE {flt} --output-format csv -d $OUT/{os.path.basename(os.path.normpath(fetch_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
@@ -448,7 +467,7 @@ def summarize_instructions(tag, dirs):
                         f"{mean['SQ_INSTS_LDS'] / tiles:.2f} | "
                         f"{100 * mean['SQ_ACTIVE_INST_VALU'] / mean['SQ_WAVE_CYCLES']:.1f}% | "
                         f"{100 * mean['SQ_WAIT_INST_ANY'] / mean['SQ_WAVE_CYCLES']:.1f}% |")
-        cmds.append(f"    rocprofv3 --pmc {SQ_COUNTERS} --kernel-include-regex 'attention_kernel|attention_quad_kernel' "
+        cmds.append(f"    rocprofv3 --pmc {SQ_COUNTERS} --kernel-include-regex 'attention_kernel|attention_quad_kernel|attention_tquad_kernel' "
                     f"--output-format csv -d $OUT/{os.path.basename(os.path.normpath(d))} -o run -- python3 "
                     f"$R/bench.py --workload attention --mode {mode_name} --head-dim {hd} --steps 1 --warmup 0 "
                     f"--layers 4 --no-cpu-baseline")
@@ -1291,12 +1310,7 @@ def run_other_workload(args, torch, kvq, W):
         sb, _ = algorithmic_bytes(mode, hd, hkv, bs, S * hkv)
         ab = attention_bytes(mode, hd, hkv, bs, H, S, ntok)
         agbps = ab / attn_s / 1e9
-        # the kernel the library picks: quads of KV heads for per-token-head
-        # layers (FP8 at head_dim 64, INT4 at 64 and 128) with groups of at
-        # most 4 and at least 4 KV heads
-        quads = ((mode == kvq.FP8_PER_TOKEN_HEAD and hd == 64) or
-                 (mode == kvq.INT4_PER_TOKEN_HEAD and hd in (64, 128) and not args.q_fp8))
-        attn_kernel = "attention_quad_kernel" if quads and args.q_per_kv <= 4 and hkv % 4 == 0 else "attention_kernel"
+        attn_kernel = attention_kernel_name(mode, hd, args.q_per_kv, bs, hkv, args.q_fp8)
         # oracle check: layer L-1 of the last step for 8 sequences, from the
         # oracle's own image of that layer, within the kernel's error bound
         parity, cpu = None, None

@@ -29,8 +29,8 @@
 // INT4 at 64 and 128) take attention_quad_kernel instead, whose waves each
 // serve a quad of 4 KV heads on the same grid, plan and partials.  Where a
 // workgroup holds only one or two KV heads (a tensor-parallel shard), those
-// layers at head_dim 64 take attention_tquad_kernel, whose waves each spread
-// 4 consecutive tiles of one head over the 16 MFMA columns.
+// layers take attention_tquad_kernel, whose waves each spread 4 consecutive
+// tiles of one head over the 16 MFMA columns.
 //
 // MFMA operand layouts used here (gfx950, lane l, r = l % 16, q = l / 16):
 //   mfma_f32_16x16x32_bf16:     A[m=r][k=8q+i], B[k=8q+i][n=r], D[m=4q+i][n=r]
@@ -1056,7 +1056,7 @@ constexpr bool attention_kind_matches() {
            ((attention_kind(MODE, 128, 4, 16, 8, false) == kAttnHeadQuads) == attention_quads<128, MODE>()) &&
            ((attention_kind(MODE, 256, 4, 16, 8, false) == kAttnHeadQuads) == attention_quads<256, MODE>()) &&
            ((attention_kind(MODE, 64, 4, 16, 1, false) == kAttnTileQuads) == attention_quads<64, MODE>()) &&
-           attention_kind(MODE, 128, 4, 16, 1, false) != kAttnTileQuads &&
+           ((attention_kind(MODE, 128, 4, 16, 2, false) == kAttnTileQuads) == attention_quads<128, MODE>()) &&
            attention_kind(MODE, 128, 4, 16, 8, true) == kAttnOneHead;
 }
 static_assert(attention_kind_matches<KVQ_BF16>() && attention_kind_matches<KVQ_FP8_PER_TENSOR>() &&
@@ -1983,21 +1983,19 @@ constexpr bool attention_packs() {
 template <int HD, int MODE, bool QF8>
 void launch_attention_q(const AttnArgs& p, int threads, bool small_bs, hipStream_t st) {
     // the plan's kind (attention_kind): head quads, with FP8 queries at
-    // head_dim 64 only; tile quads at head_dim 64, 4 waves per KV head
+    // head_dim 64 only; tile quads with 4 waves per KV head
     if constexpr (attention_quads<HD, MODE>() && (!QF8 || HD == 64)) {
         if (p.kind == kAttnHeadQuads) {
             const unsigned qlds = static_cast<unsigned>(threads / 64) * QuadGeo<HD, MODE>::LDS_WAVE;
             hipLaunchKernelGGL((attention_quad_kernel<HD, MODE, QF8>), dim3(p.total_wg), dim3(threads), qlds, st, p);
             return;
         }
-        if constexpr (HD == 64) {
-            if (p.kind == kAttnTileQuads) {
-                const int tthreads = 4 * threads;
-                const unsigned qlds = static_cast<unsigned>(tthreads / 64) * QuadGeo<HD, MODE>::LDS_WAVE;
-                hipLaunchKernelGGL((attention_tquad_kernel<HD, MODE, QF8>), dim3(p.total_wg), dim3(tthreads), qlds,
-                                   st, p);
-                return;
-            }
+        if (p.kind == kAttnTileQuads) {
+            const int tthreads = 4 * threads;
+            const unsigned qlds = static_cast<unsigned>(tthreads / 64) * QuadGeo<HD, MODE>::LDS_WAVE;
+            hipLaunchKernelGGL((attention_tquad_kernel<HD, MODE, QF8>), dim3(p.total_wg), dim3(tthreads), qlds, st,
+                               p);
+            return;
         }
     }
     // staged tiles: one LDS tile image per wave of the workgroup

@@ -129,9 +129,9 @@ constexpr int kAttnMaxSplits = 4096;
 // The decode-attention kernel that serves a call.  Head quads: per-token-head
 // FP8 at head_dim 64 (BF16 or FP8 queries) and INT4 at head_dim 64 and 128
 // (BF16 queries), with blocks of at least 16 tokens, query groups of at most
-// 4 and 4 or 8 KV heads per workgroup.  Tile quads: the same layers at
-// head_dim 64 with 1 or 2 KV heads per workgroup (4 waves per head).  Any
-// other call takes the one-head kernel.
+// 4 and 4 or 8 KV heads per workgroup.  Tile quads: the same layers with 1
+// or 2 KV heads per workgroup (4 waves per head).  Any other call takes the
+// one-head kernel.
 enum AttnKind : int32_t { kAttnOneHead = 0, kAttnHeadQuads = 1, kAttnTileQuads = 2 };
 constexpr int32_t attention_kind(int32_t mode, int32_t head_dim, int32_t group, int32_t block_size,
                                  int32_t heads_per_wg, bool fp8_queries) {
@@ -139,7 +139,7 @@ constexpr int32_t attention_kind(int32_t mode, int32_t head_dim, int32_t group, 
                             (mode == KVQ_INT4_PER_TOKEN_HEAD && !fp8_queries && (head_dim == 64 || head_dim == 128));
     if (!quad_layer || block_size < 16 || group > 4) return kAttnOneHead;
     if (heads_per_wg % 4 == 0) return kAttnHeadQuads;
-    return head_dim == 64 ? kAttnTileQuads : kAttnOneHead;
+    return kAttnTileQuads;
 }
 
 struct AttnPlan {

@@ -31,8 +31,12 @@ AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_d
     const int group = num_q_heads / num_kv_heads;
     pl.qgroups = (group + 15) / 16;
     pl.kind = mode < 0 ? kAttnOneHead : attention_kind(mode, head_dim, group, block_size, hpw, fp8_queries);
-    // waves per workgroup: one per KV head, four per KV head on the tile quads
-    const int64_t wpw = static_cast<int64_t>(hpw) * (pl.kind == kAttnTileQuads ? 4 : 1);
+    // waves per workgroup: one per KV head, four per KV head on the tile
+    // quads.  The count that sizes the splits takes the tile quads' four
+    // waves for FP8 but two for INT4, whose VALU-heavier rounds gain from
+    // twice the splits (measured on one and two KV heads per workgroup).
+    const int64_t wpw = static_cast<int64_t>(hpw) *
+                        (pl.kind == kAttnTileQuads ? (mode == KVQ_INT4_PER_TOKEN_HEAD ? 2 : 4) : 1);
     const int64_t units = static_cast<int64_t>(num_seqs) * (num_kv_heads / hpw) * pl.qgroups;
     const int64_t max_tiles = (static_cast<int64_t>(max_blocks) * block_size + kAttnTile - 1) / kAttnTile;
     // About 1024 waves in all (measured best against 4096 and 2048: a wave
@@ -40,8 +44,8 @@ AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_d
     // partials); a split keeps at least 8 tiles.  A long single sequence gets
     // up to 1024 / (waves per workgroup) splits; a large batch gets one split,
     // and the kernel then writes the output itself.  (Tile quads counted one
-    // wave per head, as the other kernels, measured 4-20% slower at head_dim
-    // 64 on one or two KV heads.)
+    // wave per head, as the other kernels, measured 4-20% slower on one or two
+    // KV heads; FP8 tile quads counted two per head, 5% slower.)
     constexpr int64_t kTargetWaves = 1024, kMinTilesPerSplit = 8;
     static_assert(kTargetWaves <= kAttnMaxSplits, "the wide combine holds every split's weight");
     const int64_t want = (kTargetWaves / wpw + units - 1) / units;

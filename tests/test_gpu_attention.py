@@ -301,6 +301,35 @@ def test_attention_decode_workload_sampled(kvq, orc, mode, hd):
         sc.close()
 
 
+# the tile-quad kernel's layers (workgroups of one or two KV heads)
+TQUAD_CASES = [(W.FP8_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 128)]
+TQUAD_IDS = ["fp8_per_token_head-hd64", "int4_per_token_head-hd64", "int4_per_token_head-hd128"]
+
+
+@pytest.mark.parametrize("hkv", [1, 2], ids=["tp8-hkv1", "tp4-hkv2"])
+@pytest.mark.parametrize("mode,hd", TQUAD_CASES, ids=TQUAD_IDS)
+def test_attention_tensor_parallel_shard_sampled(kvq, orc, mode, hd, hkv):
+    """The decode shape at one tensor-parallel shard's share of the heads (1
+    or 2 of the 8 KV heads, their 4 or 8 query heads; 256 sequences of
+    8192-8207 cached tokens), the tile-quad kernel in the launch configuration
+    the benchmark's --tp 8 and --tp 4 lines time; eight sampled sequences
+    against the oracle."""
+    _flush(f"[attention] shard decode 256 x 8192 {W.MODE_NAMES[mode]} hd {hd} hkv {hkv} (sampled)")
+    g = torch.Generator().manual_seed(31)
+    lens = (8192 + torch.randint(0, 16, (256,), generator=g)).tolist()
+    k, v = (t.cpu() for t in W.normal_kv(sum(lens), hkv, hd, seed=32 + hkv, device=DEV))
+    sc = Scenario(kvq, orc, mode=mode, hd=hd, hkv=hkv, bs=16, lens=lens, group=4, seed=33 + hkv,
+                  extra_blocks=0, kv=(k, v))
+    del k, v
+    try:
+        out = sc.run_gpu()
+        rows = [0, 3, 64, 127, 128, 190, 254, 255]
+        ref, tol = sc.reference(rows=rows)
+        sc.check(out[rows], ref, tol, "shard decode sampled")
+    finally:
+        sc.close()
+
+
 # the head-quad kernel serves the per-token-head layers; the static layouts
 # take the packed rounds of the one-head kernel on the same shapes
 QUAD_MODES = [W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD]
@@ -422,10 +451,6 @@ def test_fp8_query_attention(kvq, orc, mode, hd, shrink):
         assert np.abs(ref - plain).max() > 0
     finally:
         sc.close()
-
-
-TQUAD_CASES = [(W.FP8_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 128)]
-TQUAD_IDS = ["fp8_per_token_head-hd64", "int4_per_token_head-hd64", "int4_per_token_head-hd128"]
 
 
 @pytest.mark.parametrize("hkv,group,bs", [(1, 4, 16), (2, 4, 16), (3, 3, 32), (6, 2, 16), (1, 1, 128), (2, 2, 64)],
