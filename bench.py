@@ -1024,10 +1024,12 @@ def run_other_workload(args, torch, kvq, W):
         ct = __import__("ctypes")
         sm = 1.0 / math.sqrt(hd)
         slopes, times, intercepts = {}, {}, {}
+        times_eager, slopes_eager = {}, {}
+        graph_ok = True                   # every graph replay equal to the eager step, bit for bit
         itl_parity = None
         ocpu_s, ocpu_b = 0.0, 0           # oracle attention: seconds and algorithmic bytes
         for vname, (full_mode, slide_mode) in variants.items():
-            ts = []
+            ts, ts_eager = [], []
             for T in ctxs:
                 sliding = [W.gptoss_layer_is_sliding(l) for l in range(L)]
                 modes = [slide_mode if sl_ else full_mode for sl_ in sliding]
@@ -1044,32 +1046,69 @@ def run_other_workload(args, torch, kvq, W):
                 sl_full = torch.tensor([T], dtype=torch.int32, device=dev)
                 sl_ring = torch.tensor([Wn], dtype=torch.int32, device=dev)
                 q = W.normal_kv(1, H, hd, seed=9999, device=dev)[0]
-                out = torch.empty_like(q)
+                outs = torch.zeros((L,) + tuple(q.shape), dtype=q.dtype, device=dev)   # one output per layer
                 ws_n = max(kvq.kvq_decode_attention_workspace(cache.handle, H, T // bs, 1), 16)
                 ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
-                stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
-                aa = []
-                for l in range(L):
-                    bt, sl_ = (bt_ring, sl_ring) if sliding[l] else (bt_full, sl_full)
-                    aa.append((cache.handle, l, ct.c_void_p(q.data_ptr()), H, ct.c_void_p(bt.data_ptr()),
-                               int(bt.shape[1]), ct.c_void_p(sl_.data_ptr()), 1, ct.c_float(sm),
-                               ct.c_void_p(out.data_ptr()), ct.c_void_p(ws.data_ptr()), ws_n, stream))
 
-                def step(ev):
-                    if ev: ev[0].record()
+                def calls(stream_handle):
+                    stream = ct.c_void_p(stream_handle)
+                    aa = []
+                    for l in range(L):
+                        bt, sl_ = (bt_ring, sl_ring) if sliding[l] else (bt_full, sl_full)
+                        aa.append((cache.handle, l, ct.c_void_p(q.data_ptr()), H, ct.c_void_p(bt.data_ptr()),
+                                   int(bt.shape[1]), ct.c_void_p(sl_.data_ptr()), 1, ct.c_float(sm),
+                                   ct.c_void_p(outs[l].data_ptr()), ct.c_void_p(ws.data_ptr()), ws_n, stream))
+                    return aa
+
+                def launch_all(aa):
                     for a in aa:
                         st_ = kvq._lib.kvq_decode_attention(*a)
                         if st_ != 0:
                             raise kvq.KVQError(st_, "kvq_decode_attention")
+
+                aa = calls(torch.cuda.current_stream().cuda_stream)
+
+                def step(ev):
+                    if ev: ev[0].record()
+                    launch_all(aa)
                     if ev: ev[1].record(); ev[2].record()
                 _, evs = _timed(torch, step, args.steps, args.warmup)
-                ts.append(sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps)     # ms per decode step
+                ts_eager.append(sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps)   # ms per decode step
+                eager_outs = outs.clone()
+                # the same 24 launches captured once in a HIP graph and replayed,
+                # as a serving engine replays its decode step
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    launch_all(calls(side.cuda_stream))
+                torch.cuda.current_stream().wait_stream(side)
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    launch_all(calls(torch.cuda.current_stream().cuda_stream))
+                torch.cuda.synchronize()
+                for _ in range(3):
+                    # each checked replay follows eager work and a synchronization
+                    outs.zero_()
+                    torch.cuda.synchronize()
+                    graph.replay()
+                    torch.cuda.synchronize()
+                    graph_ok = graph_ok and bool(torch.equal(outs, eager_outs))
+
+                def gstep(ev):
+                    if ev: ev[0].record()
+                    graph.replay()
+                    if ev: ev[1].record(); ev[2].record()
+                _, gevs = _timed(torch, gstep, args.steps, args.warmup)
+                ts.append(sum(e[0].elapsed_time(e[1]) for e in gevs) / args.steps)
+                graph_ok = graph_ok and bool(torch.equal(outs, eager_outs))
+                del graph
                 if T == ctxs[0] and not args.no_cpu_baseline:
                     # oracle check of the first sliding and the first full layer
                     ok_layers = []
                     for l in (0, 1):
                         bt, sl_ = (bt_ring, sl_ring) if sliding[l] else (bt_full, sl_full)
-                        o_l = cache.decode_attention(l, q, bt, sl_, sm)
+                        o_l = eager_outs[l]
                         g1 = oracle.Geometry(bs, hkv, hd, [modes[l]], [nbs[l]])
                         img = oracle.new_cache(g1)
                         k, v = W.normal_kv(T, hkv, hd, seed=9000 + l, device=dev)
@@ -1089,12 +1128,18 @@ def run_other_workload(args, torch, kvq, W):
                 del cache
                 torch.cuda.empty_cache()
             n = len(ctxs)
-            mx, my = sum(ctxs) / n, sum(ts) / n
-            slope = sum((x - mx) * (y - my) for x, y in zip(ctxs, ts)) / sum((x - mx) ** 2 for x in ctxs)
-            slopes[vname] = slope
-            intercepts[vname] = my - slope * mx
+            mx = sum(ctxs) / n
+
+            def fit(ys):
+                my = sum(ys) / n
+                sl = sum((x - mx) * (y - my) for x, y in zip(ctxs, ys)) / sum((x - mx) ** 2 for x in ctxs)
+                return sl, my - sl * mx
+            slopes[vname], intercepts[vname] = fit(ts)
+            slopes_eager[vname] = fit(ts_eager)[0]
             times[vname] = [round(t, 5) for t in ts]
-            log(f"[bench] itl {vname}: {times[vname]} ms at {ctxs} tokens, slope {slope:.3e} ms/token")
+            times_eager[vname] = [round(t, 5) for t in ts_eager]
+            log(f"[bench] itl {vname}: graph {times[vname]} ms, eager {times_eager[vname]} ms at {ctxs} tokens, "
+                f"slope {slopes[vname]:.3e} ms/token (eager {slopes_eager[vname]:.3e})")
         # one decode step of the FP8 variant with BF16 sliding layers at the
         # longest context: 12 full layers of T tokens, 12 rings of W tokens
         T = ctxs[-1]
@@ -1121,6 +1166,10 @@ def run_other_workload(args, torch, kvq, W):
                           "contexts": ctxs, "variants": list(variants)},
                "slopes_ms_per_token": {k: float(f"{v:.4g}") for k, v in slopes.items()},
                "step_ms": times,
+               "timing": "HIP graph replay of the step's 24 launches (eager launches in step_ms_eager)",
+               "graph_replays_equal_eager": graph_ok,
+               "slopes_ms_per_token_eager": {k: float(f"{v:.4g}") for k, v in slopes_eager.items()},
+               "step_ms_eager": times_eager,
                "pages_h100_full_model_slopes_ms_per_token": {"bf16": 8.94e-06, "fp8": 7.14e-06,
                                                               "fp8_skip_sliding": 6.34e-06},
                # the context where a variant's fitted line crosses BF16's (None

@@ -1576,7 +1576,6 @@ template <int HD, int MODE>
 __device__ __forceinline__ void tquad_load(const AttnArgs& a, const int (&blk)[4], const int (&tau)[4], int hq,
                                            const TquadLaneOff& lo, QuadRaw<HD, MODE>& T) {
     using G = Geo<HD, MODE>;
-    using Q = QuadGeo<HD, MODE>;
     using TQ = TquadGeo<HD, MODE>;
     const uint32_t pmask = (1u << a.bs_log2) - 1u;
     uint32_t ok = 0u;
@@ -1872,30 +1871,70 @@ struct CombineArgs {
     int32_t max_len;               // as in AttnArgs
 };
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int k = 32; k > 0; k >>= 1) v = fmaxf(v, __shfl_xor(v, k, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int k = 32; k > 0; k >>= 1) v += __shfl_xor(v, k, 64);
+    return v;
+}
+
+// A row's split count is small here (below kWideCombineSplits), so every
+// load of the row is issued at once, together with the sequence length:
+// lane s takes split s's (m, l), and each lane loads its dims of every
+// planned split's O before the weights are known.  The merge is then one
+// memory latency, not one per split.  Splits past the sequence's last hold
+// stale workspace bytes: they are loaded (in bounds) but never used.  The
+// loads take clamped indices rather than branches, so none waits on another.
 template <int HD>
 __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     constexpr int DPL = HD / 64;   // dims per lane
+    constexpr int NS = kWideCombineSplits - 1;
+    static_assert(NS <= 64, "one split per lane");
     const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (row >= a.rows) return;
     const int lane = threadIdx.x & 63;
+    const int sp = min(a.splits, NS);                 // at least 2: a combine follows a split launch
+    const f32x2 mlr = *reinterpret_cast<const f32x2*>(a.part_ml + (row * a.splits + min(lane, sp - 1)) * 2);
+    const float* po = a.part_o + row * a.splits * HD + lane * DPL;
+    float o[NS][DPL];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int sc = min(s, sp - 1);
+        if constexpr (DPL == 1) {
+            o[s][0] = po[sc * HD];
+        } else if constexpr (DPL == 2) {
+            const f32x2 v = *reinterpret_cast<const f32x2*>(po + sc * HD);
+            o[s][0] = v[0];
+            o[s][1] = v[1];
+        } else {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(po + sc * HD);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) o[s][d] = v[d];
+        }
+    }
     const int b = static_cast<int>(row / a.num_q_heads);
     const int len = max(0, min(a.seq_lens[b], a.max_len));
     const int ntiles = (len + kTile - 1) / kTile;
-    const int nsp = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
-    const float* ml = a.part_ml + row * a.splits * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < nsp; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.0f;
+    const int nsp = min((ntiles + a.tiles_per_split - 1) / a.tiles_per_split, sp);
+    const f32x2 ml = lane < nsp ? mlr : f32x2{-INFINITY, 0.0f};
+    const float M = wave_max(ml[0]);
+    // lane s's weight; lanes past the last split weigh exp2(-inf) = 0
+    const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - M);
+    const float L = wave_sum(w * ml[1]);
     float acc[DPL];
 #pragma unroll
     for (int d = 0; d < DPL; ++d) acc[d] = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < nsp; ++s) {
-            const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-            L += w * ml[2 * s + 1];
-            const float* o = a.part_o + (row * a.splits + s) * HD + lane * DPL;
 #pragma unroll
-            for (int d = 0; d < DPL; ++d) acc[d] += w * o[d];
+    for (int s = 0; s < NS; ++s) {
+        const float ws = __shfl(w, s, 64);
+        if (s < nsp) {
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) acc[d] += ws * o[s][d];
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -1903,70 +1942,102 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     if constexpr (DPL == 1) {
         dst[0] = static_cast<uint16_t>(pack_bf16(acc[0] * inv, 0.0f) & 0xFFFFu);
     } else {
-        uint32_t w[DPL / 2];
+        uint32_t wd[DPL / 2];
 #pragma unroll
-        for (int d = 0; d < DPL; d += 2) w[d / 2] = pack_bf16(acc[d] * inv, acc[d + 1] * inv);
-        if constexpr (DPL == 2) st4<false>(dst, w[0]);
-        else st8<false>(dst, make_uint2(w[0], w[1]));
+        for (int d = 0; d < DPL; d += 2) wd[d / 2] = pack_bf16(acc[d] * inv, acc[d + 1] * inv);
+        if constexpr (DPL == 2) st4<false>(dst, wd[0]);
+        else st8<false>(dst, make_uint2(wd[0], wd[1]));
     }
 }
 
 // The same combine with the splits spread over a workgroup, one workgroup
 // per (sequence, query head): for long single sequences, whose few rows
-// each carry hundreds of splits, a serial walk over the splits would leave
-// the combine latency-bound.  The weights go through LDS; each thread sums a
-// strided share of the splits for one dim, and the shares are added in LDS.
+// each carry hundreds of splits.  Thread t sums 4 dims (quad t % (HD/4)) of
+// every (T / (HD/4))-th split; the loads of U such splits are in flight
+// together, the first U (and the first T splits' (m, l)) issued with the
+// sequence length's load, before anything is known of the row, so a row of
+// up to U * T / (HD/4) splits costs one memory latency.  Splits past the
+// sequence's last hold stale workspace bytes: loaded (in bounds, clamped
+// indices), never used.  The weights go through LDS, the quads' sums too.
 constexpr int kWideCombineThreads = 256;
 
 template <int HD>
 __global__ void __launch_bounds__(kWideCombineThreads) combine_wide_kernel(CombineArgs a) {
     constexpr int T = kWideCombineThreads;
-    constexpr int G = T / HD;          // split groups per dim
+    constexpr int NW = T / 64;
+    constexpr int Q4 = HD / 4;         // 4-dim quads of a split's O
+    constexpr int SPP = T / Q4;        // splits one pass of the workgroup covers
+    constexpr int U = 8;               // passes whose loads are in flight together
     __shared__ float wts[kMaxSplits];
-    __shared__ float red[T];
+    __shared__ float red[2 * NW];
+    __shared__ f32x4 part[T];
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int sp = a.splits;
+    const float* ml = a.part_ml + row * sp * 2;
+    const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o + row * sp * HD);
+    const int q = tid % Q4, s0 = tid / Q4;
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    const f32x2 mlr = *reinterpret_cast<const f32x2*>(ml + 2 * min(tid, sp - 1));
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = po[min(s0 + SPP * u, sp - 1) * Q4 + q];
     const int b = static_cast<int>(row / a.num_q_heads);
     const int len = max(0, min(a.seq_lens[b], a.max_len));
     const int ntiles = (len + kTile - 1) / kTile;
-    const int nsp = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
-    const float* ml = a.part_ml + row * a.splits * 2;
-
-    float mx = -INFINITY;
-    for (int s = tid; s < nsp; s += T) mx = fmaxf(mx, ml[2 * s]);
-    red[tid] = mx;
+    const int nsp = min((ntiles + a.tiles_per_split - 1) / a.tiles_per_split, sp);
+    const f32x2 ml0 = tid < nsp ? mlr : f32x2{-INFINITY, 0.0f};
+    float mx = ml0[0];
+    for (int s = tid + T; s < nsp; s += T) mx = fmaxf(mx, ml[2 * s]);
+    mx = wave_max(mx);
+    if (lane == 0) red[wv] = mx;
     __syncthreads();
-    for (int k = T / 2; k > 0; k >>= 1) {
-        if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
-        __syncthreads();
-    }
-    const float M = red[0];
-    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
     float lsum = 0.0f;
-    for (int s = tid; s < nsp; s += T) {
+    if (tid < nsp) {
+        const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml0[0] - M);
+        wts[tid] = w;
+        lsum = w * ml0[1];
+    }
+    for (int s = tid + T; s < nsp; s += T) {
         const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[2 * s] - M);
         wts[s] = w;
         lsum += w * ml[2 * s + 1];
     }
-    red[tid] = lsum;
+    lsum = wave_sum(lsum);
+    if (lane == 0) red[NW + wv] = lsum;
     __syncthreads();
-    for (int k = T / 2; k > 0; k >>= 1) {
-        if (tid < k) red[tid] += red[tid + k];
-        __syncthreads();
-    }
-    const float L = red[0];
-    __syncthreads();
-    const int d = tid % HD, grp = tid / HD;
-    float acc = 0.0f;
-    for (int s = grp; s < nsp; s += G) acc += wts[s] * a.part_o[(row * a.splits + s) * HD + d];
-    red[tid] = acc;
-    __syncthreads();
-    if (grp == 0) {
-        float sum = 0.0f;
+    float L = 0.0f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) sum += red[g * HD + d];
+    for (int w = 0; w < NW; ++w) L += red[NW + w];
+
+    f32x4 acc = zero;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int s = s0 + SPP * u;
+        if (s < nsp) acc += wts[s] * v[u];
+    }
+    for (int k0 = s0 + SPP * U; k0 < nsp; k0 += SPP * U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = po[min(k0 + SPP * u, nsp - 1) * Q4 + q];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = k0 + SPP * u;
+            if (s < nsp) acc += wts[s] * v[u];
+        }
+    }
+    part[tid] = acc;
+    __syncthreads();
+    if (tid < Q4) {
+        f32x4 sum = part[tid];
+#pragma unroll
+        for (int g = 1; g < SPP; ++g) sum += part[g * Q4 + tid];
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        a.out[row * HD + d] = static_cast<uint16_t>(pack_bf16(sum * inv, 0.0f) & 0xFFFFu);
+        st8<false>(a.out + row * HD + 4 * tid,
+                   make_uint2(pack_bf16(sum[0] * inv, sum[1] * inv), pack_bf16(sum[2] * inv, sum[3] * inv)));
     }
 }
 
