@@ -200,15 +200,15 @@ ATTN_SOURCES = [os.path.join(ROOT, "quantized_fp8_int4_amd", "csrc", f)
                 for f in ("kvq_attention.hip", "kvq_device.h", "kvq_exact.h")]
 
 
-def attention_profile_paths(mode_name, hd):
-    base = f"attention_decode_{mode_name}_hd{hd}.md"
+def attention_profile_paths(mode_name, hd, tp=1):
+    base = f"attention_decode_{mode_name}_hd{hd}.md" if tp == 1 else f"attention_decode_tp{tp}_{mode_name}_hd{hd}.md"
     return (os.path.join(ROOT, "profiles", "kernel_trace_" + base), os.path.join(ROOT, "profiles", "traffic_" + base))
 
 
-def measured_attention_traffic(mode_name, hd):
+def measured_attention_traffic(mode_name, hd, tp=1):
     """Per-launch HBM bytes of the attention kernel from the committed counter
     summary, if it was taken on the current kernel source."""
-    path = attention_profile_paths(mode_name, hd)[1]
+    path = attention_profile_paths(mode_name, hd, tp)[1]
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -260,15 +260,24 @@ def _read_csv(directory, suffix):
         return list(csv.DictReader(f))
 
 
-def _counter_per_kernel(rows, counter):
+def _counter_per_kernel(rows, counter, names=None):
     """Mean counter value (KiB) per dispatch of the store kernel, the gather
-    kernel and the calibration copy (the largest device-to-device copies)."""
+    kernel, the attention and combine kernels and the calibration copy (the
+    largest device-to-device copies); names, if given, receives each kind's
+    kernel name."""
     acc = {}
     copies = []
     for r in rows:
         if r.get("Counter_Name") != counter:
             continue
         name, val = r["Kernel_Name"], float(r["Counter_Value"])
+        if names is not None and "kvq" in name:
+            short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
+            for kind in ("store", "gather", "combine"):
+                if kind + "_kernel" in name:
+                    names.setdefault(kind, short)
+            if "attention" in name:
+                names.setdefault("attention", short)
         if "store_kernel" in name:
             acc.setdefault("store", []).append(val)
         elif "gather_kernel" in name:
@@ -302,16 +311,19 @@ def attention_kernel_name(mode, hd, group, block_size, hkv, q_fp8):
     return "attention_quad_kernel" if hpw % 4 == 0 else "attention_tquad_kernel"
 
 
-def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, layers=0):
+def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, layers=0, tp=1):
     """profiles/ summaries of the decode-attention workload from three
     rocprofv3 runs of bench.py --workload attention (kernel trace with
     --stats; --pmc FETCH_SIZE; --pmc WRITE_SIZE, the latter two with
     --calibrate-copy); layers > 0 when the runs took --layers (a cache of
-    32 layers that would not fit in HBM)."""
-    kt_path, tr_path = attention_profile_paths(mode_name, hd)
-    args_s = f"--workload attention --mode {mode_name} --head-dim {hd}" + (f" --layers {layers}" if layers else "")
+    32 layers that would not fit in HBM); tp > 1 for a tensor-parallel
+    shard's share of the heads (8/tp KV and 32/tp query heads)."""
+    kt_path, tr_path = attention_profile_paths(mode_name, hd, tp)
+    args_s = (f"--workload attention --mode {mode_name} --head-dim {hd}" + (f" --layers {layers}" if layers else "") +
+              (f" --tp {tp}" if tp > 1 else ""))
+    hkv, H = 8 // tp, 32 // tp
     stats = _read_csv(kt_dir, "kernel_stats.csv")
-    lines = [f"# Kernel trace: decode attention, 256 x 8192 tokens, 32 query / 8 KV heads, {mode_name}, head_dim {hd}", "",
+    lines = [f"# Kernel trace: decode attention, 256 x 8192 tokens, {H} query / {hkv} KV heads, {mode_name}, head_dim {hd}", "",
              "Command (run from /tmp with TMPDIR=/tmp; R = repository root, OUT = an output directory):", "",
              f"    rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/{os.path.basename(os.path.normpath(kt_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline",
              "", "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
@@ -324,18 +336,19 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, la
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
     with open(kt_path, "w") as f:
         f.write("\n".join(lines) + "\n")
-    fetch = _counter_per_kernel(_read_csv(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    knames = {}
+    fetch = _counter_per_kernel(_read_csv(fetch_dir, "counter_collection.csv"), "FETCH_SIZE", knames)
     write = _counter_per_kernel(_read_csv(write_dir, "counter_collection.csv"), "WRITE_SIZE")
     f_scale = COPY_BYTES / (fetch["copy"][0] * 1024.0)
     w_scale = COPY_BYTES / (write["copy"][0] * 1024.0)
     mode = {"bf16": 0, "fp8_per_tensor": 1, "fp8_per_head": 2, "fp8_per_token_head": 3,
             "int4_per_token_head": 4}[mode_name]
-    S, ctx, hkv, H, bs = 256, 8192, 8, 32, 16
+    S, ctx, bs = 256, 8192, 16
     # the profiled launches: 4 fused steps (lengths ctx + 1 .. ctx + 4) and 4
     # attention-only passes at ctx + 4, 32 layers each: mean length ctx + 3.25
     algo = attention_bytes(mode, hd, hkv, bs, H, S, int(S * (ctx + 3.25)))
     flt = "--kernel-include-regex 'attention_kernel|attention_quad_kernel|attention_tquad_kernel|combine_kernel|copyBuffer'"
-    out = [f"# HBM traffic per launch: decode attention, {mode_name}, head_dim {hd} (256 x ~8195 cached tokens, 8 KV heads)", "",
+    out = [f"# HBM traffic per launch: decode attention, {mode_name}, head_dim {hd} (256 x ~8195 cached tokens, {hkv} KV heads)", "",
            "Two counter runs of the same bench command (run from /tmp with TMPDIR=/tmp; R = repository root, OUT = an output directory):", "",
            f"    rocprofv3 --pmc FETCH_SIZE {flt} --output-format csv -d $OUT/{os.path.basename(os.path.normpath(fetch_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
            f"    rocprofv3 --pmc WRITE_SIZE {flt} --output-format csv -d $OUT/{os.path.basename(os.path.normpath(write_dir))} -o run -- python3 $R/bench.py {args_s} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy",
@@ -355,7 +368,7 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, la
         tot += fb + wb
         a_s = f"{algo:.4g}" if k == "attention" else "-"
         r_s = f"{(fb + wb) / algo:.3f}" if k == "attention" else "-"
-        out.append(f"| {k}_kernel | {fetch[k][1]} | {fetch[k][0]:.0f} | {write[k][0]:.0f} | {fb:.4g} | {wb:.4g} | "
+        out.append(f"| {knames.get(k, k + '_kernel')} | {fetch[k][1]} | {fetch[k][0]:.0f} | {write[k][0]:.0f} | {fb:.4g} | {wb:.4g} | "
                    f"{fb + wb:.4g} | {a_s} | {r_s} |")
     out += ["", f"kernel_source_sha256_16: {kernel_source_hash(ATTN_SOURCES)}",
             f"traffic_bytes_per_launch[attention]: {tot:.6g}"]
@@ -443,9 +456,10 @@ SQ_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_WAVE_CYCLES
 def summarize_instructions(tag, dirs):
     """profiles/instructions_<tag>.md: the SQ instruction counters of the
     decode-attention kernels from rocprofv3 runs of
-    `bench.py --workload attention --mode M --head-dim D --steps 1 --warmup 0 --layers 4`
-    (one directory per run, named pmc_attn_<mode>_<hd>), per dispatch and per
-    head-tile (16 cached tokens of one KV head for its whole query group)."""
+    `bench.py --workload attention --mode M --head-dim D --steps 1 --warmup 0 --layers 4 [--tp T]`
+    (one directory per run, named pmc_attn_<mode>_<hd>[_tp<T>]), per dispatch
+    and per head-tile (16 cached tokens of one KV head for its whole query
+    group)."""
     rows_out = []
     cmds = []
     for d in dirs:
@@ -456,12 +470,13 @@ def summarize_instructions(tag, dirs):
             info = r
         mean = {k: sum(v) / len(v) for k, v in acc.items()}
         dispatches = len(acc["SQ_WAVES"])
-        m = re.search(r"pmc_attn_(\w+)_(\d+)$", os.path.basename(os.path.normpath(d)))
-        mode_name, hd = m.group(1), int(m.group(2))
+        m = re.search(r"pmc_attn_([a-z0-9_]+?)_(\d+)(?:_tp(\d+))?$", os.path.basename(os.path.normpath(d)))
+        mode_name, hd, tp = m.group(1), int(m.group(2)), int(m.group(3) or 1)
         # the profiled step appends one token to 8192 cached ones: 513 tiles per (sequence, KV head)
-        tiles = 256 * 8 * 513
+        tiles = 256 * (8 // tp) * 513
         kname = info["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
-        rows_out.append(f"| {mode_name} / {hd} | {kname} | {dispatches} | {info['Workgroup_Size']} | "
+        shape = f"{mode_name} / {hd}" + (f" (TP {tp}: {8 // tp} KV heads)" if tp > 1 else "")
+        rows_out.append(f"| {shape} | {kname} | {dispatches} | {info['Workgroup_Size']} | "
                         f"{mean['SQ_WAVES']:.0f} | "
                         f"{mean['SQ_INSTS_VALU'] / tiles:.1f} | {mean['SQ_INSTS_SALU'] / tiles:.1f} | "
                         f"{mean['SQ_INSTS_LDS'] / tiles:.2f} | "
@@ -470,11 +485,13 @@ def summarize_instructions(tag, dirs):
         cmds.append(f"    rocprofv3 --pmc {SQ_COUNTERS} --kernel-include-regex 'attention_kernel|attention_quad_kernel|attention_tquad_kernel' "
                     f"--output-format csv -d $OUT/{os.path.basename(os.path.normpath(d))} -o run -- python3 "
                     f"$R/bench.py --workload attention --mode {mode_name} --head-dim {hd} --steps 1 --warmup 0 "
-                    f"--layers 4 --no-cpu-baseline")
-    out = ["# Instruction counters: decode attention, 256 sequences x 8193 cached tokens, 8 KV heads, 32 query heads", "",
+                    f"--layers 4 --no-cpu-baseline" + (f" --tp {tp}" if tp > 1 else ""))
+    out = ["# Instruction counters: decode attention, 256 sequences x 8193 cached tokens, 8 KV heads, 32 query heads "
+           "(a TP-T shard: 8/T and 32/T)", "",
            "Commands (run from /tmp with TMPDIR=/tmp; R = repository root, OUT = an output directory):", "", *cmds, "",
            "Means over the dispatches of the attention kernel (4 layers x 3 passes).  A head-tile is 16 cached "
-           "tokens of one KV head for its whole query group: 256 x 8 x 513 = 1.05 M per dispatch.  "
+           "tokens of one KV head for its whole query group: 256 x 8 x 513 = 1.05 M per dispatch (divided by T "
+           "on a TP-T shard).  "
            "VALU-active and waiting are SQ_ACTIVE_INST_VALU and SQ_WAIT_INST_ANY as shares of SQ_WAVE_CYCLES.", "",
            "| mode / head_dim | kernel | dispatches | workgroup | waves | VALU per head-tile "
            "| SALU per head-tile | LDS per head-tile | VALU-active | waiting |",
@@ -1399,7 +1416,7 @@ def run_other_workload(args, torch, kvq, W):
                "attention_launch_us": round(launch_us, 2),
                "roofline": {"bound": "hbm", "kernel": attn_kernel, "achieved": round(launch_gbps, 1),
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(launch_gbps / HBM_PEAK_GBPS, 4),
-                            "traffic": None if (args.q_fp8 or args.tp > 1) else measured_attention_traffic(args.mode, hd)},
+                            "traffic": None if args.q_fp8 else measured_attention_traffic(args.mode, hd, args.tp)},
                "cpu_baseline": cpu,
                "parity_vs_oracle_sampled": parity,
                "workspace_bytes": wsb, "cache_GiB": round(D["cache"].bytes["total"] / 2**30, 3)}
@@ -1458,7 +1475,7 @@ def main():
         summarize_instructions(args.summarize_instructions[0], args.summarize_instructions[1:])
         return
     if args.summarize_attention_profiles:
-        summarize_attention_profiles(*args.summarize_attention_profiles, args.mode, args.head_dim, args.layers)
+        summarize_attention_profiles(*args.summarize_attention_profiles, args.mode, args.head_dim, args.layers, args.tp)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
