@@ -1607,7 +1607,7 @@ __device__ __forceinline__ void tquad_load(const AttnArgs& a, const int (&blk)[4
     T.ok = ok;
 }
 
-template <int HD, int MODE, bool QF8>
+template <int HD, int MODE, bool QF8, int WPH>
 __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(AttnArgs a) {
     using G = Geo<HD, MODE>;
     using Q = QuadGeo<HD, MODE>;
@@ -1623,8 +1623,8 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
     const int b = static_cast<int>(item / static_cast<uint32_t>(a.splits));
 
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int sr = wave & 3;                                   // the wave's share of the rounds
-    const int hh = chunk * a.heads_per_wg + (wave >> 2);       // the wave's KV head
+    const int sr = wave % WPH;                                 // the wave's share of the rounds
+    const int hh = chunk * a.heads_per_wg + wave / WPH;        // the wave's KV head
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, q4 = lane >> 4;
     const int hq = r >> 2, g = r & 3;                          // column group (tile of the round), query
@@ -1720,13 +1720,13 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
 
     const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
     const int nr = (tend - tbeg + 3) / 4;                          // rounds of 4 tiles in the split
-    const int nt = sr < nr ? (nr - sr + 3) / 4 : 0;                // this wave's rounds: sr, sr + 4, ...
+    const int nt = sr < nr ? (nr - sr + WPH - 1) / WPH : 0;        // this wave's rounds: sr, sr + WPH, ...
     if (nt > 0) {
         constexpr int D = Q::D;
         const int lim = min(len, tend * kTile);
         // rounds past the wave's last re-read the last; tiles past the
         // split's end read its last tile (masked: their tokens lie at or past lim)
-        auto base_of = [&](int k) { return tbeg + 4 * (sr + 4 * min(k, nt - 1)); };
+        auto base_of = [&](int k) { return tbeg + 4 * (sr + WPH * min(k, nt - 1)); };
         auto tiles_of = [&](int k, int (&tau)[4], int (&blk)[4]) {
             const int t = base_of(k);
 #pragma unroll
@@ -1781,9 +1781,9 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
 #pragma unroll
         for (int j = 0; j < G::J; ++j) st.o[j] -= st.vb;
     }
-    // merge the head's 16 partial states of each query (its 4 waves x 4
-    // column groups): each wave writes (m, l, O) to its LDS, and the first
-    // wave's group-0 lanes combine them
+    // merge the head's 4 * WPH partial states of each query (its WPH waves x
+    // 4 column groups): each wave writes (m, l, O) to its LDS, then every
+    // thread of the head's waves merges PER adjacent output dims of one query
     __syncthreads();
     float* const mine = reinterpret_cast<float*>(lds_dyn + wave * Q::LDS_WAVE);
     mine[lane] = st.m;
@@ -1793,66 +1793,58 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
 #pragma unroll
         for (int i = 0; i < 4; ++i) mine[(2 + 4 * j + i) * 64 + lane] = st.o[j][i];
     __syncthreads();
-    if (sr != 0 || hq != 0) return;
+    constexpr int HT = 64 * WPH;                               // threads of a head
+    constexpr int PER = 4 * HD > HT ? 4 * HD / HT : 1;         // output dims per thread
+    static_assert(PER <= G::J && G::J % PER == 0, "a thread's dims share one source lane");
+    const int t = sr * 64 + lane;
+    if (t * PER >= 4 * HD) return;
+    const int gq = t * PER / HD, d0 = t * PER % HD;            // query of the group, first dim
+    if (gq >= a.group) return;
+    const int dq = d0 / G::J, jj = d0 % G::J;                  // source slots: i = dq % 4, j = jj + e
+    const int src = (dq / 4) * 16 + gq;                        // lane of column group 0 holding them
+    const float* const hw = reinterpret_cast<const float*>(lds_dyn + (wave - sr) * Q::LDS_WAVE);
     float m = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < WPH; ++w)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            m = fmaxf(m, reinterpret_cast<const float*>(lds_dyn + (wave + w) * Q::LDS_WAVE)[lane + 4 * c]);
+        for (int c = 0; c < 4; ++c) m = fmaxf(m, hw[w * (Q::LDS_WAVE / 4) + src + 4 * c]);
     const float mref = m == -INFINITY ? 0.0f : m;
-    l = 0.0f;
+    float lsum = 0.0f;
+    float o[PER];
 #pragma unroll
-    for (int j = 0; j < G::J; ++j) st.o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int e = 0; e < PER; ++e) o[e] = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const float* other = reinterpret_cast<const float*>(lds_dyn + (wave + w) * Q::LDS_WAVE);
+    for (int w = 0; w < WPH; ++w) {
+        const float* const other = hw + w * (Q::LDS_WAVE / 4);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const int ln = lane + 4 * c;                       // column group c of the same query, same q4
+            const int ln = src + 4 * c;                        // column group c of the same query
             const float f = __builtin_amdgcn_exp2f(other[ln] - mref);
-            l += f * other[64 + ln];
+            lsum += f * other[64 + ln];
 #pragma unroll
-            for (int j = 0; j < G::J; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) st.o[j][i] += f * other[(2 + 4 * j + i) * 64 + ln];
+            for (int e = 0; e < PER; ++e) o[e] += f * other[(2 + 4 * (jj + e) + dq % 4) * 64 + ln];
         }
     }
-    st.m = m;
-    // lane holds dims J*(4*q4 + i) + j of query head qh, as attention_kernel
-    const int64_t row = static_cast<int64_t>(b) * a.num_q_heads + qh;
-    if (!qvalid) return;
+    const int64_t row = static_cast<int64_t>(b) * a.num_q_heads + hh * a.group + gq;
     if (a.splits == 1) {
-        const float inv = l > 0.0f ? v_factor / l : 0.0f;
-        uint16_t* op = a.out + row * HD + q4 * (HD / 4);
+        const float inv = lsum > 0.0f ? v_factor / lsum : 0.0f;
+        uint16_t* op = a.out + row * HD + d0;
+        if constexpr (PER == 1) {
+            *op = static_cast<uint16_t>(pack_bf16(o[0] * inv, 0.0f) & 0xFFFFu);
+        } else {
+            uint32_t w[PER / 2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t w[G::J / 2];
-#pragma unroll
-            for (int j = 0; j < G::J; j += 2) w[j / 2] = pack_bf16(st.o[j][i] * inv, st.o[j + 1][i] * inv);
-            uint16_t* dst = op + i * G::J;
-            if constexpr (G::J >= 8) {
-#pragma unroll
-                for (int k = 0; k < G::J / 8; ++k) st16<false>(dst + 8 * k, make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]));
-            } else {
-                st8<false>(dst, make_uint2(w[0], w[1]));
-            }
+            for (int e = 0; e < PER; e += 2) w[e / 2] = pack_bf16(o[e] * inv, o[e + 1] * inv);
+            if constexpr (PER == 2) st4<false>(op, w[0]);
+            else st8<false>(op, make_uint2(w[0], w[1]));
         }
     } else {
         const int64_t prow = row * a.splits + split;
-        float* op = a.part_o + prow * HD + q4 * (HD / 4);
+        float* op = a.part_o + prow * HD + d0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int j = 0; j < G::J; j += 4) {
-                const uint4 w = make_uint4(__float_as_uint(st.o[j][i] * v_factor), __float_as_uint(st.o[j + 1][i] * v_factor),
-                                           __float_as_uint(st.o[j + 2][i] * v_factor),
-                                           __float_as_uint(st.o[j + 3][i] * v_factor));
-                st16<false>(op + i * G::J + j, w);
-            }
-        }
-        if (q4 == 0) {
-            const u32x2 ml = {__float_as_uint(st.m), __float_as_uint(l)};
+        for (int e = 0; e < PER; ++e) op[e] = o[e] * v_factor;
+        if (d0 == 0) {
+            const u32x2 ml = {__float_as_uint(m), __float_as_uint(lsum)};
             *reinterpret_cast<u32x2*>(a.part_ml + prow * 2) = ml;
         }
     }
@@ -2062,9 +2054,17 @@ void launch_attention_q(const AttnArgs& p, int threads, bool small_bs, hipStream
             return;
         }
         if (p.kind == kAttnTileQuads) {
-            const int tthreads = 4 * threads;
+            const int wph = tquad_waves_per_head(MODE, p.heads_per_wg);
+            const int tthreads = wph * threads;
             const unsigned qlds = static_cast<unsigned>(tthreads / 64) * QuadGeo<HD, MODE>::LDS_WAVE;
-            hipLaunchKernelGGL((attention_tquad_kernel<HD, MODE, QF8>), dim3(p.total_wg), dim3(tthreads), qlds, st,
+            if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
+                if (wph == 8) {
+                    hipLaunchKernelGGL((attention_tquad_kernel<HD, MODE, QF8, 8>), dim3(p.total_wg), dim3(tthreads),
+                                       qlds, st, p);
+                    return;
+                }
+            }
+            hipLaunchKernelGGL((attention_tquad_kernel<HD, MODE, QF8, 4>), dim3(p.total_wg), dim3(tthreads), qlds, st,
                                p);
             return;
         }

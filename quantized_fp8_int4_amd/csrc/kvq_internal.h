@@ -142,6 +142,14 @@ constexpr int32_t attention_kind(int32_t mode, int32_t head_dim, int32_t group, 
     return kAttnTileQuads;
 }
 
+// Waves per KV head of the tile-quad kernel: 4, or 8 for INT4 on one KV head
+// per workgroup (the VALU-heavier rounds gain from the extra waves, which
+// the planner counts, so such calls split less).  At most 8 waves per
+// workgroup either way.
+constexpr int32_t tquad_waves_per_head(int32_t mode, int32_t heads_per_wg) {
+    return mode == KVQ_INT4_PER_TOKEN_HEAD && heads_per_wg == 1 ? 8 : 4;
+}
+
 struct AttnPlan {
     int32_t splits;                // tile ranges per sequence
     int32_t tiles_per_split;       // 16-token tiles per range

@@ -31,12 +31,9 @@ AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_d
     const int group = num_q_heads / num_kv_heads;
     pl.qgroups = (group + 15) / 16;
     pl.kind = mode < 0 ? kAttnOneHead : attention_kind(mode, head_dim, group, block_size, hpw, fp8_queries);
-    // waves per workgroup: one per KV head, four per KV head on the tile
-    // quads.  The count that sizes the splits takes the tile quads' four
-    // waves for FP8 but two for INT4, whose VALU-heavier rounds gain from
-    // twice the splits (measured on one and two KV heads per workgroup).
-    const int64_t wpw = static_cast<int64_t>(hpw) *
-                        (pl.kind == kAttnTileQuads ? (mode == KVQ_INT4_PER_TOKEN_HEAD ? 2 : 4) : 1);
+    // waves per workgroup: one per KV head, 4 or 8 per KV head on the tile
+    // quads
+    const int64_t wpw = static_cast<int64_t>(hpw) * (pl.kind == kAttnTileQuads ? tquad_waves_per_head(mode, hpw) : 1);
     const int64_t units = static_cast<int64_t>(num_seqs) * (num_kv_heads / hpw) * pl.qgroups;
     const int64_t max_tiles = (static_cast<int64_t>(max_blocks) * block_size + kAttnTile - 1) / kAttnTile;
     // About 1024 waves in all (measured best against 4096 and 2048: a wave
