@@ -568,6 +568,28 @@ def test_fp8_query_decode_workload_sampled(kvq, orc, hd):
         sc.close()
 
 
+@pytest.mark.parametrize("mode,hd,group", [(W.BF16, 64, 8), (W.FP8_PER_TOKEN_HEAD, 128, 8),
+                                           (W.INT4_PER_TOKEN_HEAD, 64, 4), (W.INT4_PER_TOKEN_HEAD, 128, 4)],
+                         ids=["bf16-hd64-g8", "fp8-hd128-g8", "int4-hd64-g4-tquads", "int4-hd128-g4-tquads"])
+def test_attention_hundreds_of_splits(kvq, orc, mode, hd, group):
+    """One sequence of 40000 tokens on one KV head: the one-head kernel (groups
+    of 8) takes 313 split ranges of 8 tiles, more than the wide merge's 256
+    threads hold in one pass of (m, l) pairs and several passes of its O
+    loads; the 8-wave INT4 tile quads (groups of 4) take 125 ranges of 20
+    tiles.  Every query head against the oracle."""
+    what = f"hundreds of splits mode {W.MODE_NAMES[mode]} hd {hd} group {group}"
+    _flush(f"[attention] {what}")
+    sc = Scenario(kvq, orc, mode=mode, hd=hd, hkv=1, bs=16, lens=[40000], group=group, seed=170 + hd + mode)
+    try:
+        bt = sc.bt.copy()
+        bt[0, 1000:1003] = -1                # three blocks of one range take no part
+        out = sc.run_gpu(bt=bt)
+        ref, tol = sc.reference(bt=bt)
+        sc.check(out, ref, tol, what)
+    finally:
+        sc.close()
+
+
 @pytest.mark.parametrize("hd", [64, 128, 256])
 @pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.BF16, W.INT4_PER_TOKEN_HEAD])
 def test_attention_one_long_sequence(kvq, orc, mode, hd):
