@@ -1547,9 +1547,10 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_quad_kernel(Attn
 // r % 4 against tile base + r / 4.  The products and the softmax are those
 // of the head quads (quad_round with TILES): head h's role is taken by tile
 // h of the round, each column group keeps its own running (m, l, O), and a
-// round covers 64 tokens.  A workgroup holds 4 waves per KV head, which take
-// every fourth round of the split; at the end each head's 16 partial states
-// per query (4 waves x 4 column groups) merge through LDS.
+// round covers 64 tokens.  A workgroup holds WPH waves per KV head (4, or 8
+// for INT4 on one KV head), which take every WPH-th round of the split; at
+// the end each head's 4 * WPH partial states per query (waves x column
+// groups) merge through LDS, every thread of the head merging its own dims.
 //
 // A round's row image is the 4 tiles' 16 K|V rows of the head side by side
 // (row p: tiles 0..3 at position p), the same LDS layout as a head quad's

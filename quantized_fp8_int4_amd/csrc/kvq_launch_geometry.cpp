@@ -20,8 +20,8 @@ int64_t gather_grid(const GatherLaunch& a) {
 }
 
 // One wave per KV head of a run of up to kAttnMaxHeadsPerWg heads in a
-// workgroup, up to 16 query heads per wave, tile ranges of one sequence per
-// workgroup.
+// workgroup (4 or 8 per head on the tile quads), up to 16 query heads per
+// wave, tile ranges of one sequence per workgroup.
 AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t num_q_heads,
                         int32_t max_blocks, int32_t num_seqs, int32_t mode, bool fp8_queries) {
     AttnPlan pl{};
@@ -42,7 +42,7 @@ AttnPlan attention_plan(int32_t block_size, int32_t num_kv_heads, int32_t head_d
     // up to 1024 / (waves per workgroup) splits; a large batch gets one split,
     // and the kernel then writes the output itself.  (Tile quads counted one
     // wave per head, as the other kernels, measured 4-20% slower on one or two
-    // KV heads; FP8 tile quads counted two per head, 5% slower.)
+    // KV heads.)
     constexpr int64_t kTargetWaves = 1024, kMinTilesPerSplit = 8;
     static_assert(kTargetWaves <= kAttnMaxSplits, "the wide combine holds every split's weight");
     const int64_t want = (kTargetWaves / wpw + units - 1) / units;
