@@ -1146,10 +1146,10 @@ __device__ __forceinline__ void quad_keys(const uint8_t* lds, int r, int q4, int
 // One tile of the quad: scores of all 16 columns, one softmax update, the
 // 4 heads' value products.  MASK = false: every token of the tile lies below
 // len in a block of the layer.
-// TILES: the 4 column groups are 4 consecutive tiles of one KV head (tile
-// t0 / 16 + r / 4, its block's bit r / 4 of R.ok) instead of 4 heads of one
-// tile (every bit of R.ok the same).
-template <int HD, int MODE, bool MASK, bool QF8, bool TILES = false>
+// TILES: the 4 column groups are 4 / HPR consecutive tiles of HPR adjacent
+// KV heads (group h: tile t0 / 16 + h / HPR, its block's bit h / HPR of R.ok,
+// head h % HPR) instead of 4 heads of one tile (every bit of R.ok the same).
+template <int HD, int MODE, bool MASK, bool QF8, bool TILES = false, int HPR = 1>
 __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uint8_t* lds, State<HD, MODE>& st,
                                            const QuadQuery<HD, MODE, QF8>& qq, f32x4 qk_init, int t0, int len, int r,
                                            int q4, float k_factor, uint32_t vsh, uint32_t vsel) {
@@ -1157,9 +1157,10 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
     using Q = QuadGeo<HD, MODE>;
     constexpr bool I4 = MODE == KVQ_INT4_PER_TOKEN_HEAD;
     const int hq = r >> 2;
-    // token tok of tile h of a TILES round lies in the range, in a block of the layer
+    // token tok of column group h's tile in a TILES round lies in the range,
+    // in a block of the layer
     auto tile_token_ok = [&](int h, int tok) {
-        return !MASK || ((t0 + kTile * h + tok < len) && ((R.ok >> h) & 1u));
+        return !MASK || ((t0 + kTile * (h / HPR) + tok < len) && ((R.ok >> (h / HPR)) & 1u));
     };
     f32x4 sacc;
     if constexpr (QF8) {
@@ -1551,19 +1552,26 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_quad_kernel(Attn
 // for INT4 on one KV head), which take every WPH-th round of the split; at
 // the end each head's 4 * WPH partial states per query (waves x column
 // groups) merge through LDS, every thread of the head merging its own dims.
+// A workgroup of two KV heads runs them as a pair (HPR = 2): the column
+// groups are 2 tiles x the 2 heads, a round covers 32 tokens of both, and
+// the pair's 8 waves take every eighth round; both heads' K|V rows of a
+// position are adjacent in the block, so a round's loads are whole runs.
 //
 // A round's row image is the 4 tiles' 16 K|V rows of the head side by side
 // (row p: tiles 0..3 at position p), the same LDS layout as a head quad's
 // tile, loaded as 1 KiB pieces of one tile each.  The per-token scales of a
 // lane's tile come from that tile's block, so they are read by address
 // rather than through a block's buffer descriptor.
-template <int HD, int MODE>
+template <int HD, int MODE, int HPR = 1>
 struct TquadGeo {
     using G = Geo<HD, MODE>;
-    static constexpr int TR = 2 * G::RB;                   // one token's K|V rows of the head
-    static constexpr int PPT = kTile * TR / 1024;           // 1 KiB pieces per tile
-    static constexpr int TPC = 1024 / TR;                  // tokens per piece
-    static_assert(PPT >= 1 && PPT * 4 == QuadGeo<HD, MODE>::NC, "a round is 4 tiles of whole pieces");
+    static constexpr int TR = 2 * G::RB;                   // one token's K|V rows of one head
+    static constexpr int UR = HPR * TR;                    // ... of the round's HPR adjacent heads
+    static constexpr int TPR = 4 / HPR;                    // tiles per round
+    static constexpr int PPT = kTile * UR / 1024;          // 1 KiB pieces per tile
+    static constexpr int TPC = 1024 / UR;                  // tokens per piece
+    static_assert(HPR == 1 || HPR == 2, "one head of 4 tiles or two heads of 2 tiles per round");
+    static_assert(PPT >= 1 && PPT * TPR == QuadGeo<HD, MODE>::NC, "a round is TPR tiles of whole pieces");
 };
 
 struct TquadLaneOff {
@@ -1573,17 +1581,17 @@ struct TquadLaneOff {
     uint32_t s;                    // (s_K, s_V) of token 4 q4 of the lane's tile, from its block
 };
 
-template <int HD, int MODE>
-__device__ __forceinline__ void tquad_load(const AttnArgs& a, const int (&blk)[4], const int (&tau)[4], int hq,
+template <int HD, int MODE, int HPR>
+__device__ __forceinline__ void tquad_load(const AttnArgs& a, const int (&blk)[4], const int (&tau)[4], int jt,
                                            const TquadLaneOff& lo, QuadRaw<HD, MODE>& T) {
     using G = Geo<HD, MODE>;
-    using TQ = TquadGeo<HD, MODE>;
+    using TQ = TquadGeo<HD, MODE, HPR>;
     const uint32_t pmask = (1u << a.bs_log2) - 1u;
     uint32_t ok = 0u;
     uint64_t lane_base = 0;
     uint32_t lane_pos0 = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < TQ::TPR; ++j) {
         const bool okj = static_cast<uint32_t>(blk[j]) < static_cast<uint32_t>(a.num_blocks);
         ok |= okj ? (1u << j) : 0u;
         const uint32_t ublk = okj ? static_cast<uint32_t>(blk[j]) : 0u;
@@ -1595,8 +1603,8 @@ __device__ __forceinline__ void tquad_load(const AttnArgs& a, const int (&blk)[4
 #pragma unroll
         for (int pc = 0; pc < TQ::PPT; ++pc)
             buf_load<16, kNonTemporal>(T.kv + 4 * (j * TQ::PPT + pc), rs, lo.kv, srow + pc * lo.kv_step);
-        lane_base = hq == j ? boff : lane_base;
-        lane_pos0 = hq == j ? pos0 : lane_pos0;
+        lane_base = jt == j ? boff : lane_base;
+        lane_pos0 = jt == j ? pos0 : lane_pos0;
     }
     if constexpr (G::DYN) {
         const uint8_t* sp = a.layer + lane_base + static_cast<uint64_t>(a.code_bytes) +
@@ -1608,11 +1616,11 @@ __device__ __forceinline__ void tquad_load(const AttnArgs& a, const int (&blk)[4
     T.ok = ok;
 }
 
-template <int HD, int MODE, bool QF8, int WPH>
+template <int HD, int MODE, bool QF8, int WPH, int HPR>
 __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(AttnArgs a) {
     using G = Geo<HD, MODE>;
     using Q = QuadGeo<HD, MODE>;
-    using TQ = TquadGeo<HD, MODE>;
+    using TQ = TquadGeo<HD, MODE, HPR>;
     // work item: as attention_kernel (qgroups is 1: groups of at most 4)
     const uint32_t p = blockIdx.x;
     const uint32_t xcd = p % 8u, slot = p / 8u;
@@ -1625,10 +1633,12 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
 
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int sr = wave % WPH;                                 // the wave's share of the rounds
-    const int hh = chunk * a.heads_per_wg + wave / WPH;        // the wave's KV head
+    const int hh0 = chunk * a.heads_per_wg + (wave / WPH) * HPR;   // the wave's first KV head
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, q4 = lane >> 4;
-    const int hq = r >> 2, g = r & 3;                          // column group (tile of the round), query
+    const int hq = r >> 2, g = r & 3;                          // column group, query
+    const int jt = hq / HPR;                                   // the group's tile of the round
+    const int hh = hh0 + hq % HPR;                             // ... and KV head
 
     const int len = max(0, min(a.seq_lens[b], a.max_len));
     const int ntiles = (len + kTile - 1) / kTile;
@@ -1710,8 +1720,8 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
     {
         const uint32_t hkv = static_cast<uint32_t>(a.hkv);
         const uint32_t bl = static_cast<uint32_t>(lane) * 16u;
-        const uint32_t tok = bl / TQ::TR, off = bl % TQ::TR;
-        lo.kv = (tok * hkv + static_cast<uint32_t>(hh)) * TQ::TR + off;
+        const uint32_t tok = bl / TQ::UR, off = bl % TQ::UR;
+        lo.kv = (tok * hkv + static_cast<uint32_t>(hh0)) * TQ::TR + off;
         lo.lds = tok * Q::LDS_ROW + off;
         lo.kv_step = TQ::TPC * a.hkv * TQ::TR;
         lo.s = (static_cast<uint32_t>(4 * q4) * hkv + static_cast<uint32_t>(hh)) * 8u;
@@ -1720,18 +1730,18 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
     const uint32_t vsel = (r & 1) ? 0x07030602u : 0x05010400u;
 
     const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
-    const int nr = (tend - tbeg + 3) / 4;                          // rounds of 4 tiles in the split
+    const int nr = (tend - tbeg + TQ::TPR - 1) / TQ::TPR;          // rounds of TPR tiles in the split
     const int nt = sr < nr ? (nr - sr + WPH - 1) / WPH : 0;        // this wave's rounds: sr, sr + WPH, ...
     if (nt > 0) {
         constexpr int D = Q::D;
         const int lim = min(len, tend * kTile);
         // rounds past the wave's last re-read the last; tiles past the
         // split's end read its last tile (masked: their tokens lie at or past lim)
-        auto base_of = [&](int k) { return tbeg + 4 * (sr + WPH * min(k, nt - 1)); };
+        auto base_of = [&](int k) { return tbeg + TQ::TPR * (sr + WPH * min(k, nt - 1)); };
         auto tiles_of = [&](int k, int (&tau)[4], int (&blk)[4]) {
             const int t = base_of(k);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < TQ::TPR; ++j) {
                 tau[j] = min(t + j, tend - 1);
                 blk[j] = bt_row[(tau[j] * kTile) >> a.bs_log2];
             }
@@ -1741,7 +1751,7 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
         for (int k = 0; k < D - 1; ++k) {
             int tau[4], blk[4];
             tiles_of(k, tau, blk);
-            tquad_load<HD, MODE>(a, blk, tau, hq, lo, t[k]);
+            tquad_load<HD, MODE, HPR>(a, blk, tau, jt, lo, t[k]);
             __builtin_amdgcn_sched_barrier(0);
         }
         for (int k0 = 0; k0 < nt; k0 += D) {
@@ -1751,24 +1761,24 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
                 {
                     int tau[4], blk[4];
                     tiles_of(k + D - 1, tau, blk);
-                    tquad_load<HD, MODE>(a, blk, tau, hq, lo, t[(kk + D - 1) % D]);
+                    tquad_load<HD, MODE, HPR>(a, blk, tau, jt, lo, t[(kk + D - 1) % D]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (k < nt) {
-                    // the round's 4 tiles into the wave's LDS rows, side by side
+                    // the round's tiles into the wave's LDS rows, side by side
 #pragma unroll
                     for (int c = 0; c < Q::NC; ++c) {
                         const int j = c / TQ::PPT, pc = c % TQ::PPT;
                         const u32x4 v = {t[kk].kv[4 * c], t[kk].kv[4 * c + 1], t[kk].kv[4 * c + 2], t[kk].kv[4 * c + 3]};
-                        *reinterpret_cast<u32x4*>(lds + lo.lds + pc * TQ::TPC * Q::LDS_ROW + j * TQ::TR) = v;
+                        *reinterpret_cast<u32x4*>(lds + lo.lds + pc * TQ::TPC * Q::LDS_ROW + j * TQ::UR) = v;
                     }
                     const int t0 = base_of(k) * kTile;
-                    if (t0 + 4 * kTile <= lim && t[kk].ok == 0xFu)
-                        quad_round<HD, MODE, false, QF8, true>(t[kk], lds, st, qq, qk_init, t0, lim, r, q4, k_factor,
-                                                               vsh, vsel);
+                    if (t0 + TQ::TPR * kTile <= lim && t[kk].ok == (1u << TQ::TPR) - 1u)
+                        quad_round<HD, MODE, false, QF8, true, HPR>(t[kk], lds, st, qq, qk_init, t0, lim, r, q4,
+                                                                    k_factor, vsh, vsel);
                     else
-                        quad_round<HD, MODE, true, QF8, true>(t[kk], lds, st, qq, qk_init, t0, lim, r, q4, k_factor,
-                                                              vsh, vsel);
+                        quad_round<HD, MODE, true, QF8, true, HPR>(t[kk], lds, st, qq, qk_init, t0, lim, r, q4,
+                                                                   k_factor, vsh, vsel);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1782,9 +1792,10 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
 #pragma unroll
         for (int j = 0; j < G::J; ++j) st.o[j] -= st.vb;
     }
-    // merge the head's 4 * WPH partial states of each query (its WPH waves x
-    // 4 column groups): each wave writes (m, l, O) to its LDS, then every
-    // thread of the head's waves merges PER adjacent output dims of one query
+    // merge each head's 4 / HPR * WPH partial states of each query (the
+    // round's WPH waves x its column groups of the head): each wave writes
+    // (m, l, O) to its LDS, then every thread of the waves merges PER adjacent
+    // output dims of one query of one head
     __syncthreads();
     float* const mine = reinterpret_cast<float*>(lds_dyn + wave * Q::LDS_WAVE);
     mine[lane] = st.m;
@@ -1794,21 +1805,23 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
 #pragma unroll
         for (int i = 0; i < 4; ++i) mine[(2 + 4 * j + i) * 64 + lane] = st.o[j][i];
     __syncthreads();
-    constexpr int HT = 64 * WPH;                               // threads of a head
-    constexpr int PER = 4 * HD > HT ? 4 * HD / HT : 1;         // output dims per thread
+    constexpr int HT = 64 * WPH;                               // threads of the round's waves
+    constexpr int OUTS = HPR * 4 * HD;                         // their outputs: heads x queries x dims
+    constexpr int PER = OUTS > HT ? OUTS / HT : 1;             // output dims per thread
     static_assert(PER <= G::J && G::J % PER == 0, "a thread's dims share one source lane");
     const int t = sr * 64 + lane;
-    if (t * PER >= 4 * HD) return;
-    const int gq = t * PER / HD, d0 = t * PER % HD;            // query of the group, first dim
+    if (t * PER >= OUTS) return;
+    const int eh = t * PER / (4 * HD);                         // head of the round
+    const int gq = t * PER % (4 * HD) / HD, d0 = t * PER % HD; // query of the group, first dim
     if (gq >= a.group) return;
     const int dq = d0 / G::J, jj = d0 % G::J;                  // source slots: i = dq % 4, j = jj + e
-    const int src = (dq / 4) * 16 + gq;                        // lane of column group 0 holding them
+    const int src = (dq / 4) * 16 + 4 * eh + gq;               // lane of the head's first column group
     const float* const hw = reinterpret_cast<const float*>(lds_dyn + (wave - sr) * Q::LDS_WAVE);
     float m = -INFINITY;
 #pragma unroll
     for (int w = 0; w < WPH; ++w)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) m = fmaxf(m, hw[w * (Q::LDS_WAVE / 4) + src + 4 * c]);
+        for (int c = 0; c < TQ::TPR; ++c) m = fmaxf(m, hw[w * (Q::LDS_WAVE / 4) + src + 4 * HPR * c]);
     const float mref = m == -INFINITY ? 0.0f : m;
     float lsum = 0.0f;
     float o[PER];
@@ -1818,15 +1831,15 @@ __global__ void __launch_bounds__(kMaxAttnThreads, 2) attention_tquad_kernel(Att
     for (int w = 0; w < WPH; ++w) {
         const float* const other = hw + w * (Q::LDS_WAVE / 4);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int ln = src + 4 * c;                        // column group c of the same query
+        for (int c = 0; c < TQ::TPR; ++c) {
+            const int ln = src + 4 * HPR * c;                  // the head's column group of tile c
             const float f = __builtin_amdgcn_exp2f(other[ln] - mref);
             lsum += f * other[64 + ln];
 #pragma unroll
             for (int e = 0; e < PER; ++e) o[e] += f * other[(2 + 4 * (jj + e) + dq % 4) * 64 + ln];
         }
     }
-    const int64_t row = static_cast<int64_t>(b) * a.num_q_heads + hh * a.group + gq;
+    const int64_t row = static_cast<int64_t>(b) * a.num_q_heads + (hh0 + eh) * a.group + gq;
     if (a.splits == 1) {
         const float inv = lsum > 0.0f ? v_factor / lsum : 0.0f;
         uint16_t* op = a.out + row * HD + d0;
@@ -2058,15 +2071,21 @@ void launch_attention_q(const AttnArgs& p, int threads, bool small_bs, hipStream
             const int wph = tquad_waves_per_head(MODE, p.heads_per_wg);
             const int tthreads = wph * threads;
             const unsigned qlds = static_cast<unsigned>(tthreads / 64) * QuadGeo<HD, MODE>::LDS_WAVE;
+            if (tquad_head_pairs(p.heads_per_wg)) {
+                // two KV heads of two tiles per round, the pair's 8 waves
+                hipLaunchKernelGGL((attention_tquad_kernel<HD, MODE, QF8, 8, 2>), dim3(p.total_wg), dim3(tthreads),
+                                   qlds, st, p);
+                return;
+            }
             if constexpr (MODE == KVQ_INT4_PER_TOKEN_HEAD) {
                 if (wph == 8) {
-                    hipLaunchKernelGGL((attention_tquad_kernel<HD, MODE, QF8, 8>), dim3(p.total_wg), dim3(tthreads),
-                                       qlds, st, p);
+                    hipLaunchKernelGGL((attention_tquad_kernel<HD, MODE, QF8, 8, 1>), dim3(p.total_wg),
+                                       dim3(tthreads), qlds, st, p);
                     return;
                 }
             }
-            hipLaunchKernelGGL((attention_tquad_kernel<HD, MODE, QF8, 4>), dim3(p.total_wg), dim3(tthreads), qlds, st,
-                               p);
+            hipLaunchKernelGGL((attention_tquad_kernel<HD, MODE, QF8, 4, 1>), dim3(p.total_wg), dim3(tthreads), qlds,
+                               st, p);
             return;
         }
     }

@@ -150,6 +150,13 @@ constexpr int32_t tquad_waves_per_head(int32_t mode, int32_t heads_per_wg) {
     return mode == KVQ_INT4_PER_TOKEN_HEAD && heads_per_wg == 1 ? 8 : 4;
 }
 
+// Tile quads on two KV heads per workgroup run as head pairs: each round
+// takes two tiles of both heads, whose K|V rows are adjacent in a block, so
+// a wave reads both heads' rows as one contiguous run (whole lines where one
+// head's rows are half a 128-byte line, INT4 at head_dim 64).  The pair's 8
+// waves are the heads' 4 + 4.
+constexpr bool tquad_head_pairs(int32_t heads_per_wg) { return heads_per_wg == 2; }
+
 struct AttnPlan {
     int32_t splits;                // tile ranges per sequence
     int32_t tiles_per_split;       // 16-token tiles per range
