@@ -458,10 +458,11 @@ def test_fp8_query_attention(kvq, orc, mode, hd, shrink):
 @pytest.mark.parametrize("mode,hd", TQUAD_CASES, ids=TQUAD_IDS)
 def test_attention_tile_quads(kvq, orc, mode, hd, hkv, group, bs):
     """Workgroups of one or two KV heads (a tensor-parallel shard, few-head
-    models): 4 consecutive tiles of one head share a wave's 16 columns, 4
-    waves per head take every fourth round and merge 16 partial states per
-    query.  Lengths end inside a round, at tile and block boundaries, leave
-    waves without a round, and run to several splits."""
+    models): 4 consecutive tiles of one head share a wave's 16 columns (4
+    waves per head, 8 for INT4), or 2 tiles of a pair of heads (the pair's 8
+    waves); the waves take every fourth or eighth round and merge their
+    partial states per query.  Lengths end inside a round, at tile and block
+    boundaries, leave waves without a round, and run to several splits."""
     lens = [0, 1, 15, 16, 17, 33, 48, 49, 64, 65, 100, 130, 260, 600]
     _run(kvq, orc, f"tile quads mode {W.MODE_NAMES[mode]} hd {hd} hkv {hkv} group {group} bs {bs}", mode=mode,
          hd=hd, hkv=hkv, bs=bs, lens=lens, group=group, seed=400 + hkv * 10 + group + mode + hd)
@@ -508,7 +509,8 @@ def test_attention_tile_quads_single_split_foreign_blocks_and_long(kvq, orc, mod
 @pytest.mark.parametrize("shrink", [1.0, 4.0])
 @pytest.mark.parametrize("hkv,group", [(1, 4), (2, 3)], ids=["hkv1-g4", "hkv2-g3"])
 def test_fp8_query_tile_quads(kvq, orc, hkv, group, shrink):
-    """FP8 queries on the tile quads (per-token-head FP8, head_dim 64)."""
+    """FP8 queries on the tile quads (per-token-head FP8, head_dim 64): one KV
+    head, and two as a head pair."""
     what = f"fp8 query tile quads hkv {hkv} group {group} shrink {shrink}"
     _flush(f"[attention] {what}")
     lens = [0, 1, 17, 49, 65, 130, 600]
