@@ -521,6 +521,9 @@ def gqa32_inputs(args, torch, W):
     L, hkv, hd, bs = spec["num_layers"], spec["hkv"], spec["hd"], spec["block_size"]
     # a tensor-parallel shard stores only its own KV heads for the same tokens
     hkv //= getattr(args, "tp", 1)
+    # --block-size: the same block-level permutation with larger blocks (the
+    # sensitivity of the random block order to the block size)
+    bs = getattr(args, "block_size", 0) or bs
     nseq, slen = spec["num_seqs"], spec["seq_len"]
     n = nseq * slen
     nblocks = n // bs
@@ -1444,6 +1447,8 @@ def main():
                     help="gqa32, decode and attention workloads: one tensor-parallel shard's share, "
                          "8/TP KV heads per GPU")
     ap.add_argument("--layers", type=int, default=0, help="attention workload: layers (default: the workload's 32)")
+    ap.add_argument("--block-size", type=int, default=0, choices=[0, 16, 32, 64, 128, 256],
+                    help="gqa32: block size of the permuted cache (default: the workload's 16)")
     ap.add_argument("--q-per-kv", type=int, default=4, help="attention workload: query heads per KV head")
     ap.add_argument("--q-fp8", action="store_true", help="attention workload: FP8 queries (kvq_decode_attention_fp8q)")
     ap.add_argument("--mode", default="fp8_per_token_head",
@@ -1614,7 +1619,7 @@ def run_gqa32(args, torch, kvq, W):
 
     write_launch_bytes(args.launch_bytes_out, launch_bytes)
     # the committed counters were taken on the default shape only
-    traffic = measured_traffic() if args.tp == 1 else None
+    traffic = measured_traffic() if args.tp == 1 and I["bs"] == 16 else None
     dom_key = f"{dominant}/{I['hd']}/{LA['mode']}"
     result = {
         "metric": METRIC,
@@ -1631,7 +1636,7 @@ def run_gqa32(args, torch, kvq, W):
         "data": "synthetic",
         "config": {"workload": (f"gqa32 tensor-parallel shard (TP {args.tp}): 32 layers, {I['hkv']} of 8 KV heads per GPU, "
                                 if args.tp > 1 else "gqa32: 32 layers, 8 KV heads, ")
-                               + "head_dim 128, block 16, prefill of 8 x 4096 "
+                               + f"head_dim 128, block {I['bs']}, prefill of 8 x 4096 "
                                f"tokens per layer call, store + gather_dequant of every layer, {args.mode}",
                    "mode": args.mode, "layers": L, "tokens_per_layer_call": I["n"], "num_kv_heads": I["hkv"],
                    "head_dim": I["hd"], "block_size": I["bs"], "tp": args.tp},
