@@ -334,6 +334,7 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, la
         short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    lines += ["", f"kernel_source_sha256_16: {kernel_source_hash(ATTN_SOURCES)}"]
     with open(kt_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     knames = {}
@@ -399,6 +400,7 @@ def summarize_kernels(kt_dir, fetch_dir, write_dir, tag, bytes_json, bench_args,
             continue
         lines.append(f"| {_kernel_key(name)[1]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    lines += ["", f"kernel_source_sha256_16: {kernel_source_hash()}"]
     with open(os.path.join(ROOT, "profiles", f"kernel_trace_{tag}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
