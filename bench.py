@@ -378,6 +378,45 @@ def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, la
     print("\n".join(lines + [""] + out))
 
 
+def summarize_itl_trace(kt_dir):
+    """profiles/kernel_trace_itl_gptoss_batch1.md from a rocprofv3 kernel
+    trace of `bench.py --workload itl`: every attention and merge dispatch
+    grouped by kernel and grid (the grid names the layer type and the
+    context: one workgroup for a sliding layer, one per split range for a
+    full layer), with the median and minimum duration."""
+    import csv
+    import glob
+    import statistics
+    files = sorted(glob.glob(os.path.join(kt_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *kernel_trace.csv under {kt_dir}")
+    groups = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            key = _kernel_key(r["Kernel_Name"])
+            if key is None or not (key[0].startswith("attention") or key[0].startswith("combine")):
+                continue
+            grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+            wg = int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or 1)
+            groups.setdefault((key[1], grid // max(wg, 1)), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# Kernel trace: batch-1 decode attention, gpt-oss-20b shape (24 layers, 64 query / 8 KV heads, "
+             "head_dim 64, one sequence of 8K / 16K / 32K tokens)", "",
+             "Command (run from /tmp with TMPDIR=/tmp; R = repository root, OUT = an output directory):", "",
+             f"    rocprofv3 --kernel-trace --output-format csv -d $OUT/{os.path.basename(os.path.normpath(kt_dir))} "
+             "-o run -- python3 $R/bench.py --workload itl --steps 20 --warmup 5 --no-cpu-baseline", "",
+             "Every dispatch of the three cache variants (eager and graph-replayed steps alike), grouped by kernel "
+             "and workgroup count: one workgroup is a sliding layer (128 cached tokens, one split), more are the "
+             "split ranges of a full layer, whose merge (combine) runs one workgroup per query head.", "",
+             "| kernel | workgroups | dispatches | median (us) | min (us) |", "|---|---|---|---|---|"]
+    for (name, wgs), ds in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        lines.append(f"| {name} | {wgs} | {len(ds)} | {statistics.median(ds):.2f} | {min(ds):.2f} |")
+    lines += ["", f"kernel_source_sha256_16: {kernel_source_hash(ATTN_SOURCES)}"]
+    with open(os.path.join(ROOT, "profiles", "kernel_trace_itl_gptoss_batch1.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_kernels(kt_dir, fetch_dir, write_dir, tag, bytes_json, bench_args, pmc_filter=""):
     """profiles/kernel_trace_<tag>.md and profiles/traffic_<tag>.md from three
     rocprofv3 runs of `bench.py <bench_args>` (kernel trace with --stats;
@@ -1468,6 +1507,8 @@ def main():
                          "profiles/kernel_trace_TAG.md and traffic_TAG.md from rocprofv3 csv output and exit")
     ap.add_argument("--summarize-instructions", nargs="+", metavar="ARG",
                     help="TAG PMC_DIR...: write profiles/instructions_TAG.md from SQ counter runs and exit")
+    ap.add_argument("--summarize-itl-trace", metavar="KERNEL_TRACE_DIR",
+                    help="write profiles/kernel_trace_itl_gptoss_batch1.md from a kernel trace of --workload itl and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, copy 256 MiB device-to-device 3 times (reference for counter scaling)")
     ap.add_argument("--summarize-attention-profiles", nargs=3, metavar=("KERNEL_TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -1480,6 +1521,9 @@ def main():
         return
     if args.summarize_instructions:
         summarize_instructions(args.summarize_instructions[0], args.summarize_instructions[1:])
+        return
+    if args.summarize_itl_trace:
+        summarize_itl_trace(args.summarize_itl_trace)
         return
     if args.summarize_attention_profiles:
         summarize_attention_profiles(*args.summarize_attention_profiles, args.mode, args.head_dim, args.layers, args.tp)
