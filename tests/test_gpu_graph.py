@@ -1,11 +1,16 @@
-"""The library's launches under HIP graph capture.  A store, a dequantizing
+"""The library's launches under HIP graph capture and on concurrent streams.
+
+Graphs: a store, a dequantizing
 gather and a split decode attention with its merge (through a caller
 workspace and through the allocation-free entry point) are captured once in
 a torch CUDA graph and replayed.  Each replay follows eager work on the same
 stream (its outputs cleared by fill kernels, unrelated arithmetic) and a
 synchronization, and must reproduce the eager calls' outputs bit for bit:
 the calls allocate nothing, clear nothing with a memset, and launch on the
-stream they are given, so the captured launches are the eager ones."""
+stream they are given, so the captured launches are the eager ones.
+
+Streams: two caches stored and gathered at once from two streams give what
+each gives alone."""
 import ctypes
 
 import pytest
@@ -99,3 +104,57 @@ def test_graph_replays_equal_eager(kvq, mode, hd):
     finally:
         del graph
         cache.close()
+
+
+def test_two_streams_two_caches(kvq):
+    """Distinct caches used at once from two streams: each stream stores a
+    layer and gathers it back while the other does the same; the results
+    equal one stream's calls made alone, bit for bit."""
+    hkv, hd, bs = 8, 128, 16
+    lens = [1500, 900, 41]
+    need = [-(-n // bs) for n in lens]
+    maxb, nblocks = max(need) + 1, sum(need) + 2
+    st = W.DecodeState(len(lens), bs, nblocks, maxb, seed=81)
+    slots = []
+    for b, n in enumerate(lens):
+        slots += st.append(b, n)
+    n = len(slots)
+    slots = torch.tensor(slots, dtype=torch.int64, device=DEV)
+    bt = st.block_table.to(DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    modes = (W.FP8_PER_TOKEN_HEAD, W.INT4_PER_TOKEN_HEAD)
+    inputs = [W.gqa_kv(n, hkv, hd, seed=82 + i, device=DEV) for i in range(2)]
+
+    def run(cache, kv, out):
+        cache.store(0, kv[0], kv[1], slots)
+        cache.gather_dequant(0, bt, sl, total_tokens=n, out=out)
+
+    def outs():
+        return (torch.empty((n, hkv, hd), dtype=torch.bfloat16, device=DEV),
+                torch.empty((n, hkv, hd), dtype=torch.bfloat16, device=DEV))
+
+    caches = [kvq.Cache(kvq.CacheConfig(bs, hkv, hd, [m], [nblocks]), device=DEV) for m in modes]
+    try:
+        alone = []
+        for c, kv in zip(caches, inputs):
+            o = outs()
+            run(c, kv, o)
+            torch.cuda.synchronize()
+            alone.append(o)
+        together = [outs(), outs()]
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        for rep in range(3):
+            for c, kv, o, s in zip(caches, inputs, together, streams):
+                with torch.cuda.stream(s):
+                    o[0].zero_()
+                    o[1].zero_()
+                    run(c, kv, o)
+            torch.cuda.synchronize()
+            for i in range(2):
+                assert torch.equal(together[i][0], alone[i][0]) and torch.equal(together[i][1], alone[i][1]), \
+                    f"rep {rep}: cache {i} differs when run beside the other"
+    finally:
+        for c in caches:
+            c.close()
