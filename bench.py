@@ -298,17 +298,20 @@ def attention_kernel_name(mode, hd, group, block_size, hkv, q_fp8):
     the JSON line): quads of KV heads for per-token-head layers (FP8 at
     head_dim 64, INT4 at 64 and 128 with BF16 queries), groups of at most 4
     and blocks of at least 16 tokens, when a workgroup holds 4 or 8 KV heads;
-    quads of tiles on the same layers when it holds 1 or 2; else the one-head
-    kernel."""
+    quads of tiles on the same layers when it holds 1 or 2, and on FP8 at
+    head_dim 128 when it holds 2; else the one-head kernel."""
     import quantized_fp8_int4_amd as kvq
     quad_layer = ((mode == kvq.FP8_PER_TOKEN_HEAD and hd == 64) or
                   (mode == kvq.INT4_PER_TOKEN_HEAD and hd in (64, 128) and not q_fp8))
-    if not quad_layer or block_size < 16 or group > 4:
+    tile_layer = quad_layer or (mode == kvq.FP8_PER_TOKEN_HEAD and hd == 128 and not q_fp8)
+    if not tile_layer or block_size < 16 or group > 4:
         return "attention_kernel"
     hpw = 1
     while hpw < 8 and hkv % (2 * hpw) == 0:
         hpw *= 2
-    return "attention_quad_kernel" if hpw % 4 == 0 else "attention_tquad_kernel"
+    if hpw % 4 == 0:
+        return "attention_quad_kernel" if quad_layer else "attention_kernel"
+    return "attention_tquad_kernel" if quad_layer or hpw == 2 else "attention_kernel"
 
 
 def summarize_attention_profiles(kt_dir, fetch_dir, write_dir, mode_name, hd, layers=0, tp=1):

@@ -1048,6 +1048,14 @@ constexpr bool attention_quads() {
            (MODE == KVQ_INT4_PER_TOKEN_HEAD && (HD == 64 || HD == 128));
 }
 
+// The layers the tile quads serve (workgroups of one or two KV heads): the
+// head quads' layers, and FP8 per-token-head at head_dim 128 (two heads,
+// as a pair).
+template <int HD, int MODE>
+constexpr bool attention_tquads() {
+    return attention_quads<HD, MODE>() || (MODE == KVQ_FP8_PER_TOKEN_HEAD && HD == 128);
+}
+
 // the host's choice of kernel (attention_kind, which sizes the plan) names
 // only kernels this file instantiates
 template <int MODE>
@@ -1055,8 +1063,9 @@ constexpr bool attention_kind_matches() {
     return ((attention_kind(MODE, 64, 4, 16, 8, false) == kAttnHeadQuads) == attention_quads<64, MODE>()) &&
            ((attention_kind(MODE, 128, 4, 16, 8, false) == kAttnHeadQuads) == attention_quads<128, MODE>()) &&
            ((attention_kind(MODE, 256, 4, 16, 8, false) == kAttnHeadQuads) == attention_quads<256, MODE>()) &&
-           ((attention_kind(MODE, 64, 4, 16, 1, false) == kAttnTileQuads) == attention_quads<64, MODE>()) &&
-           ((attention_kind(MODE, 128, 4, 16, 2, false) == kAttnTileQuads) == attention_quads<128, MODE>()) &&
+           ((attention_kind(MODE, 64, 4, 16, 2, false) == kAttnTileQuads) == attention_tquads<64, MODE>()) &&
+           ((attention_kind(MODE, 128, 4, 16, 2, false) == kAttnTileQuads) == attention_tquads<128, MODE>()) &&
+           ((attention_kind(MODE, 256, 4, 16, 1, false) == kAttnTileQuads) == attention_tquads<256, MODE>()) &&
            attention_kind(MODE, 128, 4, 16, 8, true) == kAttnOneHead;
 }
 static_assert(attention_kind_matches<KVQ_BF16>() && attention_kind_matches<KVQ_FP8_PER_TENSOR>() &&
@@ -2067,6 +2076,8 @@ void launch_attention_q(const AttnArgs& p, int threads, bool small_bs, hipStream
             hipLaunchKernelGGL((attention_quad_kernel<HD, MODE, QF8>), dim3(p.total_wg), dim3(threads), qlds, st, p);
             return;
         }
+    }
+    if constexpr (attention_tquads<HD, MODE>() && (!QF8 || HD == 64)) {
         if (p.kind == kAttnTileQuads) {
             const int wph = tquad_waves_per_head(MODE, p.heads_per_wg);
             const int tthreads = wph * threads;

@@ -130,15 +130,21 @@ constexpr int kAttnMaxSplits = 4096;
 // FP8 at head_dim 64 (BF16 or FP8 queries) and INT4 at head_dim 64 and 128
 // (BF16 queries), with blocks of at least 16 tokens, query groups of at most
 // 4 and 4 or 8 KV heads per workgroup.  Tile quads: the same layers with 1
-// or 2 KV heads per workgroup (4 waves per head).  Any other call takes the
-// one-head kernel.
+// or 2 KV heads per workgroup, and FP8 at head_dim 128 (BF16 queries) with
+// 2.  Any other call takes the one-head kernel.
 enum AttnKind : int32_t { kAttnOneHead = 0, kAttnHeadQuads = 1, kAttnTileQuads = 2 };
 constexpr int32_t attention_kind(int32_t mode, int32_t head_dim, int32_t group, int32_t block_size,
                                  int32_t heads_per_wg, bool fp8_queries) {
     const bool quad_layer = (mode == KVQ_FP8_PER_TOKEN_HEAD && head_dim == 64) ||
                             (mode == KVQ_INT4_PER_TOKEN_HEAD && !fp8_queries && (head_dim == 64 || head_dim == 128));
-    if (!quad_layer || block_size < 16 || group > 4) return kAttnOneHead;
-    if (heads_per_wg % 4 == 0) return kAttnHeadQuads;
+    // FP8 at head_dim 128 takes the tile quads as head pairs only: its
+    // 16 KiB head-quad tiles are not built (the one-head kernel is bound by
+    // memory there), and on one KV head the one-head kernel measured 3-5%
+    // faster than the tile quads, on two 5% slower than the pairs
+    const bool tile_layer = quad_layer || (mode == KVQ_FP8_PER_TOKEN_HEAD && !fp8_queries && head_dim == 128);
+    if (!tile_layer || block_size < 16 || group > 4) return kAttnOneHead;
+    if (heads_per_wg % 4 == 0) return quad_layer ? kAttnHeadQuads : kAttnOneHead;
+    if (!quad_layer && heads_per_wg != 2) return kAttnOneHead;
     return kAttnTileQuads;
 }
 

@@ -302,8 +302,10 @@ def test_attention_decode_workload_sampled(kvq, orc, mode, hd):
 
 
 # the tile-quad kernel's layers (workgroups of one or two KV heads)
-TQUAD_CASES = [(W.FP8_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 128)]
-TQUAD_IDS = ["fp8_per_token_head-hd64", "int4_per_token_head-hd64", "int4_per_token_head-hd128"]
+TQUAD_CASES = [(W.FP8_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 64), (W.INT4_PER_TOKEN_HEAD, 128),
+               (W.FP8_PER_TOKEN_HEAD, 128)]
+TQUAD_IDS = ["fp8_per_token_head-hd64", "int4_per_token_head-hd64", "int4_per_token_head-hd128",
+             "fp8_per_token_head-hd128"]
 
 
 @pytest.mark.parametrize("hkv", [1, 2], ids=["tp8-hkv1", "tp4-hkv2"])
