@@ -1210,7 +1210,7 @@ def run_other_workload(args, torch, kvq, W):
         step_b = 12 * attention_bytes(kvq.FP8_PER_TENSOR, hd, hkv, bs, H, 1, T) + \
             12 * attention_bytes(kvq.BF16, hd, hkv, bs, H, 1, Wn)
         ach = step_b / (times["fp8_skip_sliding"][-1] / 1e3) / 1e9
-        roof = {"bound": "hbm", "kernel": f"attention_kernel + combine_kernel, a step of {L} layers at {T} tokens "
+        roof = {"bound": "hbm", "kernel": f"attention_kernel + combine_wide_kernel, a step of {L} layers at {T} tokens "
                                           "(fp8_skip_sliding)",
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
