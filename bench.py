@@ -1264,6 +1264,20 @@ def run_other_workload(args, torch, kvq, W):
             if ev: ev[1].record(); ev[2].record()
         sec, evs = _timed(torch, step, args.steps, args.warmup)
         cal_s = sum(e[0].elapsed_time(e[1]) for e in evs) / (args.steps * L) / 1e3
+        # the later batches of a warmup loop accumulate into the running
+        # maxima: the call is then calib_kernel alone, without the fill
+        # kernel that clears amax for a first batch
+        args_acc = [a[:6] + (1,) + a[7:] for a in args_c]
+
+        def step_acc(ev):
+            if ev: ev[0].record()
+            for a in args_acc:
+                st_ = kvq._lib.kvq_calibrate_amax(*a)
+                if st_ != 0:
+                    raise kvq.KVQError(st_, "kvq_calibrate_amax")
+            if ev: ev[1].record(); ev[2].record()
+        _, evs_acc = _timed(torch, step_acc, args.steps, args.warmup)
+        acc_s = sum(e[0].elapsed_time(e[1]) for e in evs_acc) / (args.steps * L) / 1e3
         cal_b = n * hkv * 4 * hd
         t0 = time.perf_counter()
         ref = oracle.calibrate_amax(_bits(torch, ins[0][0]), _bits(torch, ins[0][1]), hkv, hd)
@@ -1277,8 +1291,11 @@ def run_other_workload(args, torch, kvq, W):
                "config": {"workload": "calibration amax of each GQA-32 layer's prefill K/V (32768 tokens x 8 KV heads x 128)",
                           "layers": L},
                "calib_us": round(cal_s * 1e6, 2),
-               "roofline": {"bound": "hbm", "kernel": "calib_kernel", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+               "calib_accumulate_us": round(acc_s * 1e6, 2),
+               "calib_accumulate_GBps": round(cal_b / acc_s / 1e9, 1),
+               "roofline": {"bound": "hbm", "kernel": "calib_kernel (accumulating calls: the kernel alone)",
+                            "achieved": round(cal_b / acc_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(cal_b / acc_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None},
                "cpu_baseline": {"value": round(cal_b / csec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                                 "sample": f"one layer's amax (single-threaded loop), {csec:.2f} s wall"},
                "parity_vs_oracle_sampled": parity}
