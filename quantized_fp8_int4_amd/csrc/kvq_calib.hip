@@ -111,10 +111,10 @@ int launch_calibrate(const CalibLaunch& a, void* stream) {
     p.hkv_shift = dm.shift;
     // 8 rows per lane per iteration (32 KiB of loads in flight per wave) on
     // at most 256 workgroups that loop: measured on the GQA-32 prefill, 23.8
-    // us per call against 24.9 for 4 rows on 512 workgroups.  A small grid
-    // also keeps the final global atomics (2 * Hkv per workgroup, all on the
-    // same few addresses) few: 2048 workgroups of one iteration each took
-    // 34 us.
+    // us per call against 24.9 for 4 rows on 512 workgroups, and 2048
+    // workgroups of one iteration each took 34 us.  (The final global
+    // atomics, 2 * Hkv per workgroup, cost under half a microsecond per call
+    // at 256 workgroups.)
     constexpr int kCalibRpl = 8;
     constexpr int64_t kCalibMaxGrid = 256;
     const int64_t supers = (a.num_rows + 32 * kCalibRpl - 1) / (32 * kCalibRpl);
