@@ -288,10 +288,10 @@ __device__ __forceinline__ void v_operands_int4(const uint32_t (*v)[Geo<HD, KVQ_
     for (int p = 0; p < G::J / 4; ++p) {
         const int w = G::VB == 2 ? 0 : p / 2;
         const uint32_t sel = G::VB == 2 ? vsel : ((p & 1) ? 0x07030602u : 0x05010400u);
-        const uint32_t x01 = __builtin_amdgcn_perm(v[1][w], v[0][w], sel) ^ 0x88888888u;
-        const uint32_t x23 = __builtin_amdgcn_perm(v[3][w], v[2][w], sel) ^ 0x88888888u;
-        const uint32_t lo01 = x01 & 0x0F0F0F0Fu, hi01 = (x01 >> 4) & 0x0F0F0F0Fu;
-        const uint32_t lo23 = x23 & 0x0F0F0F0Fu, hi23 = (x23 >> 4) & 0x0F0F0F0Fu;
+        const uint32_t x01 = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
+        const uint32_t x23 = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
+        const uint32_t lo01 = (x01 & 0x0F0F0F0Fu) ^ 0x08080808u, hi01 = ((x01 >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+        const uint32_t lo23 = (x23 & 0x0F0F0F0Fu) ^ 0x08080808u, hi23 = ((x23 >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
         const u32x2 d0 = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo01, 32.0f, false)),
                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo23, 32.0f, false))};
         const u32x2 d1 = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi01, 32.0f, false)),
@@ -646,16 +646,18 @@ __device__ __forceinline__ void int4_query_order(QOperand<HD, false>& q) {
 }
 
 // Minus the bias of the biased INT4 keys, (8 / 16) sum(q) for each query
-// column, through the same products with every key element 1/2: the initial
-// accumulator of each tile's Q K^T product.
+// column, through the same products with every key element -1/2 (negated
+// products sum to the exact negation, and the loop then reuses the
+// accumulator as it stands): the initial accumulator of each tile's Q K^T
+// product.
 template <int HD>
 __device__ __forceinline__ f32x4 int4_key_bias(const QOperand<HD, false>& q) {
-    const u32x4 halves = {0x3F003F00u, 0x3F003F00u, 0x3F003F00u, 0x3F003F00u};   // BF16 0.5
+    const u32x4 halves = {0xBF00BF00u, 0xBF00BF00u, 0xBF00BF00u, 0xBF00BF00u};   // BF16 -0.5
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < HD / 32; ++j)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, halves), q.b[j], acc, 0, 0, 0);
-    return -acc;
+    return acc;
 }
 
 // One round of the online softmax over NT consecutive tiles (16 NT tokens):
@@ -1217,9 +1219,16 @@ __device__ __forceinline__ void quad_round(const QuadRaw<HD, MODE>& R, const uin
             for (int j = 0; j < HD / 32; ++j)
                 acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<HD, MODE>(k, j), qq.b[j], acc[h], 0, 0, 0);
         }
+        // two levels of per-lane selects on the bits of hq (a chain of
+        // comparisons with hq compiled to divergent branches with copies:
+        // 1.5-5% slower at head_dim 128)
+        const bool odd = (hq & 1) != 0, upper = (hq & 2) != 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            sacc[i] = hq == 0 ? acc[0][i] : (hq == 1 ? acc[1][i] : (hq == 2 ? acc[2][i] : acc[3][i]));
+        for (int i = 0; i < 4; ++i) {
+            const float lo = odd ? acc[1][i] : acc[0][i];
+            const float hi = odd ? acc[3][i] : acc[2][i];
+            sacc[i] = upper ? hi : lo;
+        }
     } else {
         // head by head into one accumulator, each head's query operand
         // holding only its own columns (block diagonal: qb[h * HD / 32 + j])
