@@ -29,8 +29,9 @@
 // INT4 at 64 and 128) take attention_quad_kernel instead, whose waves each
 // serve a quad of 4 KV heads on the same grid, plan and partials.  Where a
 // workgroup holds only one or two KV heads (a tensor-parallel shard), those
-// layers take attention_tquad_kernel, whose waves each spread 4 consecutive
-// tiles of one head over the 16 MFMA columns.
+// layers, and FP8 at head_dim 128 on two heads, take attention_tquad_kernel,
+// whose waves each spread 4 consecutive tiles of one head (or 2 tiles of
+// each head of a pair) over the 16 MFMA columns.
 //
 // MFMA operand layouts used here (gfx950, lane l, r = l % 16, q = l / 16):
 //   mfma_f32_16x16x32_bf16:     A[m=r][k=8q+i], B[k=8q+i][n=r], D[m=4q+i][n=r]
