@@ -69,7 +69,7 @@ def _ceiling_lib():
     lib = ctypes.CDLL(CEILING_LIB)
     P = ctypes.c_void_p
     lib.ceil_linear_copy.argtypes = [P, P, ctypes.c_uint64, P]
-    lib.ceil_store_pattern.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+    lib.ceil_store_pattern.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P]
     I32 = ctypes.c_int32
     lib.ceil_gather_pattern.argtypes = [P, P, I32, P, I32, P, P, I32, I32, I32, I32, I32, ctypes.c_int64, P]
@@ -163,10 +163,11 @@ def empty_launch_us(torch, grids, reps=200):
     return out
 
 
-def store_pattern_ceiling(torch, I, LA, slots, reps, out_buf):
+def store_pattern_ceiling(torch, I, LA, slots, reps, out_buf, order=None):
     """The store's exact loads and stores (every layer's own K/V, the given
     slots, the layer's code rows and scale trailer) with no arithmetic,
-    written to a scratch buffer laid out like the layout's cache."""
+    written to a scratch buffer laid out like the layout's cache; with an
+    order (int32 permutation on the device), the tokens taken in it."""
     import ctypes
     lib = _ceiling_lib()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -179,7 +180,9 @@ def store_pattern_ceiling(torch, I, LA, slots, reps, out_buf):
 
         def f():
             if lib.ceil_store_pattern(ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-                                      ctypes.c_void_p(slots.data_ptr()), ctypes.c_void_p(base), I["n"], I["hkv"],
+                                      ctypes.c_void_p(slots.data_ptr()),
+                                      ctypes.c_void_p(order.data_ptr() if order is not None else 0),
+                                      ctypes.c_void_p(base), I["n"], I["hkv"],
                                       I["hd"], rb, sc, I["bs"], I["nblocks"], stream):
                 raise RuntimeError("ceil_store_pattern failed")
         return f
@@ -247,6 +250,9 @@ def _kernel_key(name):
     targs = [t.strip() for t in (m.group(2) or "").split(",") if t.strip()]
     # library kernels by head_dim and mode; the ceiling kernels by all their arguments
     keep = targs[:2] if kind in ("store", "gather", "attention", "attention_quad", "attention_tquad", "calib") else targs
+    # the store that follows a token order (its last template argument) apart
+    if kind == "store" and len(targs) >= 10 and targs[9] == "true":
+        keep = keep + ["ordered"]
     return "/".join([kind] + keep), short
 
 
@@ -573,7 +579,12 @@ def gqa32_inputs(args, torch, W):
     nblocks = n // bs
     dev = torch.device("cuda", 0)
     bt = W.permuted_block_table(nseq, slen // bs, nblocks, seed=1000)
-    slots = W.slots_from_block_table(bt, [slen] * nseq, bs).to(dev)
+    slots_h = W.slots_from_block_table(bt, [slen] * nseq, bs)
+    slots = slots_h.to(dev)
+    # the tokens in slot order: made on the host with the slot mapping, as a
+    # serving step's scheduler makes both, and shared by every layer's store
+    import numpy as np
+    slot_order = torch.from_numpy(np.argsort(slots_h.numpy(), kind="stable").astype(np.int32)).to(dev)
     keys, values, outs = [], [], []
     for layer in range(L):
         k, v = W.gqa_kv(n, hkv, hd, seed=1000 + layer, device=dev)
@@ -582,7 +593,7 @@ def gqa32_inputs(args, torch, W):
         outs.append((torch.empty_like(k), torch.empty_like(v)))
     torch.cuda.synchronize()
     return dict(L=L, hkv=hkv, hd=hd, bs=bs, n=n, nseq=nseq, slen=slen, nblocks=nblocks, bt=bt, bt_d=bt.to(dev),
-                slots=slots, identity_slots=torch.arange(n, dtype=torch.int64, device=dev),
+                slots=slots, slot_order=slot_order, identity_slots=torch.arange(n, dtype=torch.int64, device=dev),
                 seq_lens=torch.full((nseq,), slen, dtype=torch.int32, device=dev), keys=keys, values=values, outs=outs)
 
 
@@ -609,16 +620,19 @@ def gqa32_layout(torch, kvq, W, I, mode_name):
             scales.append(None)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     P = ctypes.c_void_p
-    sa, ga = [], []
+    sa, sa_tok, ga = [], [], []
     for layer in range(L):
         sc = scales[layer]
         csc = None if sc is None else (ctypes.c_float * len(sc))(*[float(x) for x in sc])
+        sa_tok.append((cache.handle, layer, P(I["keys"][layer].data_ptr()), P(I["values"][layer].data_ptr()),
+                       P(I["slots"].data_ptr()), I["n"], mode, csc, stream))
         sa.append((cache.handle, layer, P(I["keys"][layer].data_ptr()), P(I["values"][layer].data_ptr()),
-                   P(I["slots"].data_ptr()), I["n"], mode, csc, stream))
+                   P(I["slots"].data_ptr()), P(I["slot_order"].data_ptr()), I["n"], mode, csc, stream))
         ga.append((cache.handle, layer, P(I["bt_d"].data_ptr()), I["bt_d"].shape[1], P(I["seq_lens"].data_ptr()),
                    I["nseq"], P(I["outs"][layer][0].data_ptr()), P(I["outs"][layer][1].data_ptr()),
                    int(I["outs"][layer][0].shape[0]), stream))
-    return dict(layout_geometry(kvq, W, I, mode_name), cache=cache, scales=scales, store_args=sa, gather_args=ga)
+    return dict(layout_geometry(kvq, W, I, mode_name), cache=cache, scales=scales, ordered_store_args=sa,
+                token_store_args=sa_tok, gather_args=ga)
 
 
 def layout_geometry(kvq, W, I, mode_name):
@@ -634,19 +648,30 @@ def layout_geometry(kvq, W, I, mode_name):
                 layers_bytes=L * layer_bytes, store_bytes=store_b, gather_bytes=gather_b)
 
 
-def time_layout(torch, kvq, LA, steps, warmup):
+def store_follows_order(mode, hd):
+    """Whether kvq_store_ordered follows the token order for a layer (asked of
+    the library); other layers take the tokens in their own order."""
+    import quantized_fp8_int4_amd as kvq
+    return bool(kvq._lib.kvq_store_follows_order(int(mode), int(hd)))
+
+
+def time_layout(torch, kvq, LA, steps, warmup, ordered=True):
     """W untimed warmup steps, then exactly K timed steps of every layer's
     store followed by every layer's gather; HIP events on the launch stream
-    bracket each step's stores and gathers.  Returns seconds per store launch,
-    per gather launch and per step (wall clock, synchronized on both sides)."""
+    bracket each step's stores and gathers.  The stores take the tokens in
+    slot order (kvq_store_ordered), or in token order (kvq_store).  Returns
+    seconds per store launch, per gather launch and per step (wall clock,
+    synchronized on both sides)."""
     lib = kvq._lib
-    sa, ga = LA["store_args"], LA["gather_args"]
+    ga = LA["gather_args"]
+    sa, store = ((LA["ordered_store_args"], lib.kvq_store_ordered) if ordered
+                 else (LA["token_store_args"], lib.kvq_store))
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
         for a in sa:
-            st = lib.kvq_store(*a)
+            st = store(*a)
             if st != 0:
                 raise kvq.KVQError(st, "kvq_store")
         if ev is not None:
@@ -1519,6 +1544,9 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="gqa32: time only the --mode layout (default: also the other three layouts of the target)")
     ap.add_argument("--no-ceiling", action="store_true", help="gqa32: skip the bandwidth-ceiling kernels")
+    ap.add_argument("--token-order", action="store_true",
+                    help="gqa32: store the tokens in their own order (kvq_store) instead of slot order "
+                         "(kvq_store_ordered with the slot mapping's argsort)")
     ap.add_argument("--launch-bytes-out", default="",
                     help="write the algorithmic bytes per launch of each kernel run (JSON) for --summarize-kernels")
     ap.add_argument("--summarize-kernels", nargs="+",
@@ -1581,7 +1609,7 @@ def run_gqa32(args, torch, kvq, W):
     launch_bytes = {}
     for name in order:
         LA = gqa32_layout(torch, kvq, W, I, name)
-        store_s, gather_s, wall = time_layout(torch, kvq, LA, args.steps, args.warmup)
+        store_s, gather_s, wall = time_layout(torch, kvq, LA, args.steps, args.warmup, ordered=not args.token_order)
         sg, gg = LA["store_bytes"] / store_s / 1e9, LA["gather_bytes"] / gather_s / 1e9
         log(f"[bench] {name}: {wall * 1e3:.3f} ms/step; store {store_s * 1e6:.2f} us ({sg:.0f} GB/s), "
             f"gather {gather_s * 1e6:.2f} us ({gg:.0f} GB/s)")
@@ -1589,6 +1617,14 @@ def run_gqa32(args, torch, kvq, W):
                "store_frac_of_peak": round(sg / HBM_PEAK_GBPS, 4), "gather_us": round(gather_s * 1e6, 2),
                "gather_GBps": round(gg, 1), "gather_frac_of_peak": round(gg / HBM_PEAK_GBPS, 4),
                "store_bytes_per_launch": int(LA["store_bytes"]), "gather_bytes_per_launch": int(LA["gather_bytes"])}
+        rec["store_order"] = "slot" if not args.token_order and store_follows_order(LA["mode"], I["hd"]) else "token"
+        if rec["store_order"] == "slot":
+            # the same stores in token order, for comparison (same cache contents)
+            tok_s, _, _ = time_layout(torch, kvq, LA, args.steps, args.warmup, ordered=False)
+            tg = LA["store_bytes"] / tok_s / 1e9
+            rec.update({"store_us_token_order": round(tok_s * 1e6, 2), "store_GBps_token_order": round(tg, 1),
+                        "store_frac_of_peak_token_order": round(tg / HBM_PEAK_GBPS, 4)})
+            log(f"[bench] {name}: store in token order {tok_s * 1e6:.2f} us ({tg:.0f} GB/s)")
         if name == args.mode:
             head = dict(LA=LA, store_s=store_s, gather_s=gather_s, wall=wall)
         # the oracle's check of this layout, while the outputs hold its gather
@@ -1614,6 +1650,7 @@ def run_gqa32(args, torch, kvq, W):
             rec["parity_layers"] = len(sample)
         layouts[name] = rec
         launch_bytes[f"store/{I['hd']}/{LA['mode']}"] = LA["store_bytes"]
+        launch_bytes[f"store/{I['hd']}/{LA['mode']}/ordered"] = LA["store_bytes"]
         launch_bytes[f"gather/{I['hd']}/{LA['mode']}"] = LA["gather_bytes"]
         if name != args.mode:
             LA["cache"].close()
@@ -1632,6 +1669,8 @@ def run_gqa32(args, torch, kvq, W):
         ident_bt = torch.arange(I["nblocks"], dtype=torch.int32, device=dev).view(I["nseq"], -1)
         hg = geos[args.mode]
         ceilings["store_pattern_permuted_slots"] = store_pattern_ceiling(torch, I, hg, I["slots"], reps, out_buf)
+        ceilings["store_pattern_permuted_slots_slot_order"] = store_pattern_ceiling(
+            torch, I, hg, I["slots"], reps, out_buf, order=I["slot_order"])
         ceilings["store_pattern_identity_slots"] = store_pattern_ceiling(torch, I, hg, I["identity_slots"], reps,
                                                                          out_buf)
         ceilings["gather_pattern_permuted_blocks"] = gather_pattern_ceiling(torch, I, hg, I["bt_d"], reps, out_buf)
@@ -1641,11 +1680,14 @@ def run_gqa32(args, torch, kvq, W):
         store_grid = (I["n"] * I["hkv"] + 31) // 32
         ceilings["empty_launch_us"] = empty_launch_us(torch, (1, 1024, store_grid))
         for name, g in geos.items():
+            # each store against the pattern of the order it takes the tokens in
+            ordered = not args.token_order and store_follows_order(g["mode"], I["hd"])
             if name == args.mode:
-                pc = ceilings["store_pattern_permuted_slots"]
+                pc = ceilings["store_pattern_permuted_slots_slot_order" if ordered else "store_pattern_permuted_slots"]
                 gc = ceilings["gather_pattern_permuted_blocks"]
             else:
-                pc = store_pattern_ceiling(torch, I, g, I["slots"], reps, out_buf)
+                pc = store_pattern_ceiling(torch, I, g, I["slots"], reps, out_buf,
+                                           order=I["slot_order"] if ordered else None)
                 gc = gather_pattern_ceiling(torch, I, g, I["bt_d"], reps, out_buf)
             layouts[name]["store_pattern_ceiling_GBps"] = pc["GBps"]
             layouts[name]["store_vs_pattern_ceiling"] = round(layouts[name]["store_GBps"] / pc["GBps"], 4)
@@ -1653,9 +1695,11 @@ def run_gqa32(args, torch, kvq, W):
             layouts[name]["gather_vs_pattern_ceiling"] = round(layouts[name]["gather_GBps"] / gc["GBps"], 4)
         del out_buf
         torch.cuda.empty_cache()
-        log("[bench] ceilings: store pattern {:.0f} GB/s (permuted slots), {:.0f} (identity); gather pattern "
-            "{:.0f} (permuted blocks), {:.0f} (identity); linear copy {:.0f}".format(
-                *(ceilings[k]["GBps"] for k in ("store_pattern_permuted_slots", "store_pattern_identity_slots",
+        log("[bench] ceilings: store pattern {:.0f} GB/s (permuted slots), {:.0f} (the same in slot order), "
+            "{:.0f} (identity); gather pattern {:.0f} (permuted blocks), {:.0f} (identity); linear copy {:.0f}".format(
+                *(ceilings[k]["GBps"] for k in ("store_pattern_permuted_slots",
+                                                "store_pattern_permuted_slots_slot_order",
+                                                "store_pattern_identity_slots",
                                                 "gather_pattern_permuted_blocks", "gather_pattern_identity_blocks",
                                                 "linear_nt_copy"))))
 
@@ -1667,7 +1711,7 @@ def run_gqa32(args, torch, kvq, W):
     dominant = "store" if store_s >= gather_s else "gather"
     dom_gbps = store_gbps if dominant == "store" else gather_gbps
     if ceilings:
-        ceilings["store_vs_pattern_ceiling"] = round(store_gbps / ceilings["store_pattern_permuted_slots"]["GBps"], 4)
+        ceilings["store_vs_pattern_ceiling"] = layouts[args.mode]["store_vs_pattern_ceiling"]
         ceilings["gather_vs_pattern_ceiling"] = round(
             gather_gbps / ceilings["gather_pattern_permuted_blocks"]["GBps"], 4)
         ceilings["store_vs_linear_copy"] = round(store_gbps / ceilings["linear_nt_copy"]["GBps"], 4)
@@ -1687,6 +1731,8 @@ def run_gqa32(args, torch, kvq, W):
     # the committed counters were taken on the default shape only
     traffic = measured_traffic() if args.tp == 1 and I["bs"] == 16 else None
     dom_key = f"{dominant}/{I['hd']}/{LA['mode']}"
+    if dominant == "store" and layouts[args.mode].get("store_order") == "slot":
+        dom_key += "/ordered"
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -1705,7 +1751,11 @@ def run_gqa32(args, torch, kvq, W):
                                + f"head_dim 128, block {I['bs']}, prefill of 8 x 4096 "
                                f"tokens per layer call, store + gather_dequant of every layer, {args.mode}",
                    "mode": args.mode, "layers": L, "tokens_per_layer_call": I["n"], "num_kv_heads": I["hkv"],
-                   "head_dim": I["hd"], "block_size": I["bs"], "tp": args.tp},
+                   "head_dim": I["hd"], "block_size": I["bs"], "tp": args.tp,
+                   "store_order": ("token order (kvq_store)" if args.token_order else
+                                   "slot order: kvq_store_ordered with the argsort of the slot mapping, made on the "
+                                   "host with the slot mapping and shared by the 32 layers (followed by FP8 layers "
+                                   "at head_dim >= 128; INT4 takes the tokens in their own order)")},
         "store_GBps": round(store_gbps, 1),
         "gather_GBps": round(gather_gbps, 1),
         "store_frac_of_peak": round(store_gbps / HBM_PEAK_GBPS, 4),

@@ -63,6 +63,7 @@ struct PatternArgs {
     uint32_t hkv_magic;
     uint32_t hkv_shift;
     uint32_t bs_log2;
+    const int32_t* order;          // token order (nullptr: the tokens' own order)
 };
 
 // HD elements per row, HALF: INT4-sized code rows (HD / 2 bytes), SC: an
@@ -83,7 +84,12 @@ __global__ __launch_bounds__(256) void store_pattern_kernel(PatternArgs p) {
     const uint32_t sub = lane & 7u;
     const int64_t row = static_cast<int64_t>(blockIdx.x) * 32 + (threadIdx.x >> 6) * 8 + (lane >> 3);
     const bool valid = row < p.num_rows;
-    const uint32_t rowc = valid ? static_cast<uint32_t>(row) : 0u;
+    uint32_t rowc = valid ? static_cast<uint32_t>(row) : 0u;
+    if (p.order != nullptr) {
+        // the same token order as the store's: row i * Hkv + h is token order[i]'s head h
+        const uint32_t i = static_cast<uint32_t>((static_cast<uint64_t>(rowc) * p.hkv_magic) >> p.hkv_shift);
+        rowc = static_cast<uint32_t>(p.order[i]) * p.hkv + (rowc - i * p.hkv);
+    }
     uint32_t in[8 * CPL];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
@@ -274,11 +280,14 @@ __attribute__((visibility("default"))) int ceil_linear_copy(const void* src, voi
 // The store's access pattern for num_tokens rows of num_kv_heads heads:
 // keys/values BF16 [num_tokens][num_kv_heads][head_dim] (device, 16-byte
 // aligned), slots int64 [num_tokens], layer = the layer's first block (device),
-// num_blocks blocks of block_size tokens.  row_bytes = head_dim or head_dim / 2;
-// scale_bytes = 8 (per-token-head trailer) or 0.  Returns 0, the launch's
-// hipError_t, or -1 on bad arguments.
+// num_blocks blocks of block_size tokens; order NULL (the tokens in their own
+// order) or a permutation of 0 .. num_tokens-1 (device int32: the tokens in
+// that order, as kvq_store_ordered takes them).  row_bytes = head_dim or
+// head_dim / 2; scale_bytes = 8 (per-token-head trailer) or 0.  Returns 0,
+// the launch's hipError_t, or -1 on bad arguments.
 __attribute__((visibility("default"))) int ceil_store_pattern(const void* keys, const void* values,
-                                                              const int64_t* slots, void* layer, int64_t num_tokens,
+                                                              const int64_t* slots, const int32_t* order,
+                                                              void* layer, int64_t num_tokens,
                                                               int32_t num_kv_heads, int32_t head_dim,
                                                               int32_t row_bytes, int32_t scale_bytes,
                                                               int32_t block_size, int64_t num_blocks, void* stream) {
@@ -293,6 +302,7 @@ __attribute__((visibility("default"))) int ceil_store_pattern(const void* keys, 
     p.keys = static_cast<const u32x4*>(keys);
     p.values = static_cast<const u32x4*>(values);
     p.slots = slots;
+    p.order = order;
     p.layer = static_cast<uint8_t*>(layer);
     p.num_rows = rows;
     p.num_slots = num_blocks * block_size;

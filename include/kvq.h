@@ -193,6 +193,42 @@ KVQ_API kvq_status kvq_store(kvq_cache* c, int32_t layer, const void* keys, cons
                      kvq_mode mode, const float* scales, void* stream);
 
 /*
+ * kvq_store_ordered -- kvq_store with the tokens taken in a caller's order.
+ * The cache contents are those of kvq_store: every token still lands in its
+ * own slot with the same codes and scales; only the order in which the
+ * kernel walks the tokens changes.  Blocks are handed out from a free list
+ * ("Per-token-head KV cache scale overhead", "Convert bytes into block
+ * capacity"), so consecutive tokens land in scattered blocks; walking the
+ * tokens in slot order instead makes the writes run through the layer in
+ * address order (the reads of the new K/V rows are then the scattered
+ * side).  All layers of a model step share one slot mapping, so one order
+ * serves every layer's call.
+ *   token_order    device, int32 [num_tokens]: a permutation of
+ *                  0 .. num_tokens-1, token_order[i] being the token taken
+ *                  i-th; the slot order is argsort(slot_mapping).  4-byte
+ *                  aligned; NULL only when num_tokens is 0.  Nothing checks
+ *                  that it is a permutation.  A layer that follows the order
+ *                  skips entries outside [0, num_tokens), so no access
+ *                  leaves the arguments, and stores exactly the tokens the
+ *                  order names (a repeated token is stored twice alike, an
+ *                  omitted one not at all); a layer that does not follow it
+ *                  stores every token.
+ *   Every other argument, the errors and the no-op cases are kvq_store's.
+ *   The order is followed for FP8 and BF16 layers at head_dim 128 and 256,
+ *   where slot order measured faster; other layers (INT4, head_dim 64) take
+ *   the tokens in their own order, which for a permutation gives the same
+ *   contents.
+ */
+KVQ_API kvq_status kvq_store_ordered(kvq_cache* c, int32_t layer, const void* keys, const void* values,
+                             const int64_t* slot_mapping, const int32_t* token_order, int64_t num_tokens,
+                             kvq_mode mode, const float* scales, void* stream);
+
+/* kvq_store_follows_order -- 1 if kvq_store_ordered follows the token order
+ * on layers of this mode and head_dim, 0 if it takes the tokens in their own
+ * order (also for an unknown mode or head_dim).  Host only. */
+KVQ_API int32_t kvq_store_follows_order(kvq_mode mode, int32_t head_dim);
+
+/*
  * kvq_gather_dequant -- read one layer's cached tokens of num_seqs sequences
  * through their block tables and write them back as BF16.  The scales are
  * read back when the cache is consumed ("Per-tensor vs per-head FP8 KV cache

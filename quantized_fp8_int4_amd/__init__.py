@@ -39,7 +39,8 @@ MODE_NAMES = {BF16: "bf16", FP8_PER_TENSOR: "fp8_per_tensor", FP8_PER_HEAD: "fp8
 OK, ERR_INVALID_ARG, ERR_MODE_MISMATCH, ERR_BUFFER_TOO_SMALL, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_SPACE = \
     0, -1, -2, -3, -4, -5, -6
 
-EXPORTED_SYMBOLS = ("kvq_cache_bytes", "kvq_create_cache", "kvq_destroy_cache", "kvq_store",
+EXPORTED_SYMBOLS = ("kvq_cache_bytes", "kvq_create_cache", "kvq_destroy_cache", "kvq_store", "kvq_store_ordered",
+                    "kvq_store_follows_order",
                     "kvq_gather_dequant", "kvq_calibrate_amax", "kvq_static_scales",
                     "kvq_decode_attention_workspace", "kvq_decode_attention", "kvq_decode_attention_fp8q",
                     "kvq_decode_attention_noalloc",
@@ -80,6 +81,9 @@ def _load_library():
     lib.kvq_create_cache.argtypes = [ctypes.POINTER(_Config), P, ctypes.c_uint64, ctypes.POINTER(P)]
     lib.kvq_destroy_cache.argtypes = [P]
     lib.kvq_store.argtypes = [P, I32, P, P, P, I64, ctypes.c_int, P, P]
+    lib.kvq_store_ordered.argtypes = [P, I32, P, P, P, P, I64, ctypes.c_int, P, P]
+    lib.kvq_store_follows_order.argtypes = [ctypes.c_int, I32]
+    lib.kvq_store_follows_order.restype = I32
     lib.kvq_gather_dequant.argtypes = [P, I32, P, I32, P, I32, P, P, I64, P]
     lib.kvq_calibrate_amax.argtypes = [P, P, I64, I32, I32, P, I32, P]
     lib.kvq_static_scales.argtypes = [P, I32, ctypes.c_int, P]
@@ -173,23 +177,35 @@ def _dev(t: torch.Tensor, dtype, name: str) -> int:
 
 
 def kvq_store(handle, layer: int, keys: torch.Tensor, values: torch.Tensor, slot_mapping: torch.Tensor,
-              mode: int, scales=None, stream=None) -> None:
+              mode: int, scales=None, stream=None, order=None) -> None:
     """keys/values: bf16 [N, Hkv, hd] on the device; slot_mapping: int64 [N] on
-    the device; scales: host float32 values for static layers, else None."""
+    the device; scales: host float32 values for static layers, else None;
+    order: None, or int32 [N] on the device, a permutation of the tokens
+    (kvq_store_ordered: the tokens taken in that order, the same result)."""
     n = int(slot_mapping.numel())
     kp = _dev(keys, torch.bfloat16, "keys") if n else 0
     vp = _dev(values, torch.bfloat16, "values") if n else 0
     sp = _dev(slot_mapping, torch.int64, "slot_mapping") if n else 0
     if n and (keys.shape != values.shape or keys.shape[0] != n):
         raise ValueError("keys, values and slot_mapping disagree in token count")
+    op = 0
+    if order is not None:
+        if order.dim() != 1 or int(order.numel()) != n:
+            raise ValueError("order must be int32 [num_tokens]")
+        op = _dev(order, torch.int32, "order") if n else 0
     sc = None
     if scales is not None:
         if isinstance(scales, torch.Tensor):
             scales = scales.detach().cpu().to(torch.float32).reshape(-1).tolist()
         vals = [float(x) for x in scales]
         sc = (ctypes.c_float * len(vals))(*vals)
-    _check(_lib.kvq_store(handle, int(layer), ctypes.c_void_p(kp), ctypes.c_void_p(vp), ctypes.c_void_p(sp),
-                          n, int(mode), sc, _stream_ptr(stream, keys.device if n else None)), "kvq_store")
+    if order is None:
+        _check(_lib.kvq_store(handle, int(layer), ctypes.c_void_p(kp), ctypes.c_void_p(vp), ctypes.c_void_p(sp),
+                              n, int(mode), sc, _stream_ptr(stream, keys.device if n else None)), "kvq_store")
+    else:
+        _check(_lib.kvq_store_ordered(handle, int(layer), ctypes.c_void_p(kp), ctypes.c_void_p(vp),
+                                      ctypes.c_void_p(sp), ctypes.c_void_p(op), n, int(mode), sc,
+                                      _stream_ptr(stream, keys.device if n else None)), "kvq_store_ordered")
 
 
 def kvq_gather_dequant(handle, layer: int, block_table: torch.Tensor, seq_lens: torch.Tensor,
@@ -438,11 +454,16 @@ class Cache:
             lead = "N" if first is None else str(first)
             raise ValueError(f"{name} must be [{lead}, {want[0]}, {want[1]}], got {tuple(t.shape)}")
 
-    def store(self, layer, keys, values, slot_mapping, scales=None, stream=None):
+    def store(self, layer, keys, values, slot_mapping, scales=None, stream=None, order=None):
+        """order: None, or a permutation of the tokens (int32 on the device)
+        in which to take them; the slot order (argsort of slot_mapping),
+        shared by every layer of a step, makes the writes sequential.  The
+        cache contents are the same either way."""
         n = int(slot_mapping.numel())
         self._rows("keys", keys, n)
         self._rows("values", values, n)
-        kvq_store(self.handle, layer, keys, values, slot_mapping, self.cfg.layer_modes[layer], scales, stream)
+        kvq_store(self.handle, layer, keys, values, slot_mapping, self.cfg.layer_modes[layer], scales, stream,
+                  order)
 
     def check_slots(self, layer, slot_mapping) -> int:
         """Debug check of a store's slot_mapping, off the store path: raises

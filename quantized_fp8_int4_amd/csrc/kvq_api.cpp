@@ -92,9 +92,11 @@ kvq_status kvq_destroy_cache(kvq_cache* c) {
     return KVQ_OK;
 }
 
-kvq_status kvq_store(kvq_cache* c, int32_t layer, const void* keys, const void* values,
-                     const int64_t* slot_mapping, int64_t num_tokens, kvq_mode mode,
-                     const float* scales, void* stream) {
+namespace {
+
+kvq_status store_impl(kvq_cache* c, int32_t layer, const void* keys, const void* values,
+                      const int64_t* slot_mapping, const int32_t* token_order, int64_t num_tokens, kvq_mode mode,
+                      const float* scales, void* stream) {
     if (!c || layer < 0 || layer >= c->layout.num_layers || num_tokens < 0) return KVQ_ERR_INVALID_ARG;
     const kvq::Layout& L = c->layout;
     const int32_t lmode = L.mode[layer];
@@ -119,6 +121,7 @@ kvq_status kvq_store(kvq_cache* c, int32_t layer, const void* keys, const void* 
         if (!keys || !values || !slot_mapping) return KVQ_ERR_INVALID_ARG;
         if (!aligned16(keys) || !aligned16(values) || (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
             return KVQ_ERR_INVALID_ARG;
+        if (token_order && (reinterpret_cast<uintptr_t>(token_order) & 3u)) return KVQ_ERR_INVALID_ARG;
         if (num_tokens * static_cast<int64_t>(L.num_kv_heads) >= (int64_t{1} << 31)) return KVQ_ERR_UNSUPPORTED;
     }
     if (L.block_bytes[layer] % 16 != 0) return KVQ_ERR_UNSUPPORTED;
@@ -145,11 +148,33 @@ kvq_status kvq_store(kvq_cache* c, int32_t layer, const void* keys, const void* 
     a.bs_log2 = L.bs_log2;
     a.head_dim = L.head_dim;
     a.mode = lmode;
+    a.order = token_order;
     if (log_enabled())
-        std::fprintf(stderr, "[kvq] store layer=%d mode=%s hd=%d tokens=%lld rows=%lld\n", layer,
+        std::fprintf(stderr, "[kvq] store layer=%d mode=%s hd=%d tokens=%lld rows=%lld%s\n", layer,
                      mode_name(lmode), L.head_dim, static_cast<long long>(num_tokens),
-                     static_cast<long long>(a.num_rows));
+                     static_cast<long long>(a.num_rows), token_order ? " ordered" : "");
     return kvq::launch_store(a, stream) == 0 ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace
+
+kvq_status kvq_store(kvq_cache* c, int32_t layer, const void* keys, const void* values,
+                     const int64_t* slot_mapping, int64_t num_tokens, kvq_mode mode,
+                     const float* scales, void* stream) {
+    return store_impl(c, layer, keys, values, slot_mapping, nullptr, num_tokens, mode, scales, stream);
+}
+
+kvq_status kvq_store_ordered(kvq_cache* c, int32_t layer, const void* keys, const void* values,
+                             const int64_t* slot_mapping, const int32_t* token_order, int64_t num_tokens,
+                             kvq_mode mode, const float* scales, void* stream) {
+    if (num_tokens > 0 && !token_order) return KVQ_ERR_INVALID_ARG;
+    return store_impl(c, layer, keys, values, slot_mapping, token_order, num_tokens, mode, scales, stream);
+}
+
+int32_t kvq_store_follows_order(kvq_mode mode, int32_t head_dim) {
+    const bool known = (head_dim == 64 || head_dim == 128 || head_dim == 256) && mode >= KVQ_BF16 &&
+                       mode <= KVQ_INT4_PER_TOKEN_HEAD;
+    return known && kvq::store_follows_order(head_dim, static_cast<int32_t>(mode)) ? 1 : 0;
 }
 
 kvq_status kvq_gather_dequant(const kvq_cache* c, int32_t layer, const int32_t* block_table,

@@ -53,6 +53,8 @@ struct StoreArgs {
     uint32_t hkv_magic;
     uint32_t hkv_shift;
     uint32_t bs_log2;
+    const int32_t* __restrict__ order;   // ORD: token order[i] is processed i-th
+    uint32_t num_tokens;
 };
 
 // Tuning knobs of the store kernel: EPL elements of a row per lane (LPR =
@@ -213,8 +215,11 @@ __device__ __forceinline__ void store_row(const StoreArgs& p, uint32_t rowc, boo
 // adjacent lanes.  Chunk k of a lane is elements [(k * LPR + sub) * 8, +8),
 // so each load instruction reads LPR * 16 contiguous bytes of every row.  A
 // wave owns RPL groups of 64 / LPR consecutive rows and loads all of them
-// before quantizing any.
-template <int HD, int MODE, int EPL, int RPL, bool NTL, bool NTS, bool CONTIG, int TPB, bool WT>
+// before quantizing any.  ORD: the rows are taken in the caller's token
+// order (row i * Hkv + h is token order[i]'s head h), which, sorted by slot,
+// makes the writes run through the layer in address order and the reads
+// scattered instead; an entry outside [0, num_tokens) stores nothing.
+template <int HD, int MODE, int EPL, int RPL, bool NTL, bool NTS, bool CONTIG, int TPB, bool WT, bool ORD>
 __global__ __launch_bounds__(TPB) void store_kernel(StoreArgs p) {
     constexpr int LPR = HD / EPL;
     constexpr int CPL = EPL / 8;
@@ -228,11 +233,22 @@ __global__ __launch_bounds__(TPB) void store_kernel(StoreArgs p) {
     const int64_t row0 = static_cast<int64_t>(blockIdx.x) * RPB + wave * (RPW * RPL) + lane / LPR;
 
     uint4 kx[RPL][CPL], vx[RPL][CPL];
+    uint32_t src[RPL];             // the source row of each group (the row itself without ORD)
+    bool ok[RPL];
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
         const int64_t row = row0 + j * RPW;
-        const bool valid = row < p.num_rows;
-        const uint64_t rowc = valid ? static_cast<uint64_t>(row) : 0u;
+        bool valid = row < p.num_rows;
+        uint64_t rowc = valid ? static_cast<uint64_t>(row) : 0u;
+        if constexpr (ORD) {
+            const uint32_t r32 = static_cast<uint32_t>(rowc);
+            const uint32_t i = static_cast<uint32_t>((static_cast<uint64_t>(r32) * p.hkv_magic) >> p.hkv_shift);
+            const uint32_t tok = static_cast<uint32_t>(p.order[i]);
+            valid = valid && tok < p.num_tokens;
+            rowc = valid ? static_cast<uint64_t>(tok) * p.hkv + (r32 - i * p.hkv) : 0u;
+        }
+        src[j] = static_cast<uint32_t>(rowc);
+        ok[j] = valid;
         const uint4* kp = p.keys + rowc * (HD / 8) + sub;
         const uint4* vp = p.values + rowc * (HD / 8) + sub;
         // Unconditional loads (rows past the end read row 0 and never write):
@@ -246,12 +262,10 @@ __global__ __launch_bounds__(TPB) void store_kernel(StoreArgs p) {
     }
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
-        const int64_t row = row0 + j * RPW;
-        const bool valid = row < p.num_rows;
-        // the wave's first row of this group
+        // the wave's first row of this group (the same KV heads, row for row,
+        // as its source rows: an order moves whole tokens)
         const uint64_t wrow = static_cast<uint64_t>(blockIdx.x) * RPB + wave * (RPW * RPL) + j * RPW;
-        store_row<HD, MODE, LPR, CPL, CONTIG, NTS, WT>(p, valid ? static_cast<uint32_t>(row) : 0u, valid, sub, kx[j],
-                                                       vx[j], wrow);
+        store_row<HD, MODE, LPR, CPL, CONTIG, NTS, WT>(p, src[j], ok[j], sub, kx[j], vx[j], wrow);
     }
 }
 
@@ -538,6 +552,8 @@ StoreArgs make_store_args(const StoreLaunch& a) {
     p.hkv_magic = dm.magic;
     p.hkv_shift = dm.shift;
     p.bs_log2 = static_cast<uint32_t>(a.bs_log2);
+    p.order = a.order;
+    p.num_tokens = static_cast<uint32_t>(a.num_rows / a.num_kv_heads);
     return p;
 }
 
@@ -564,22 +580,32 @@ GatherArgs make_gather_args(const GatherLaunch& a) {
     return p;
 }
 
-template <int HD, int MODE, int EPL, int RPL, bool NTL, bool NTS, bool CONTIG = false, int TPB = 256>
-int launch_store_v(const StoreLaunch& a, void* stream) {
+template <int HD, int MODE, int EPL, int RPL, bool NTL, bool NTS, bool CONTIG, int TPB, bool ORD>
+int launch_store_o(const StoreArgs& p, int64_t num_rows, int32_t num_kv_heads, void* stream) {
     constexpr int RPB = (64 / (HD / EPL)) * RPL * (TPB / 64);
-    const StoreArgs p = make_store_args(a);
-    const uint32_t grid = static_cast<uint32_t>((a.num_rows + RPB - 1) / RPB);
+    const uint32_t grid = static_cast<uint32_t>((num_rows + RPB - 1) / RPB);
     // static per-head tables of at most 32 KV heads are fetched whole by each wave
     if constexpr (MODE == KVQ_FP8_PER_HEAD) {
-        if (a.num_kv_heads <= 32) {
-            hipLaunchKernelGGL((store_kernel<HD, MODE, EPL, RPL, NTL, NTS, CONTIG, TPB, true>), dim3(grid), dim3(TPB),
-                               0, static_cast<hipStream_t>(stream), p);
+        if (num_kv_heads <= 32) {
+            hipLaunchKernelGGL((store_kernel<HD, MODE, EPL, RPL, NTL, NTS, CONTIG, TPB, true, ORD>), dim3(grid),
+                               dim3(TPB), 0, static_cast<hipStream_t>(stream), p);
             return static_cast<int>(hipGetLastError());
         }
     }
-    hipLaunchKernelGGL((store_kernel<HD, MODE, EPL, RPL, NTL, NTS, CONTIG, TPB, false>), dim3(grid), dim3(TPB), 0,
-                       static_cast<hipStream_t>(stream), p);
+    hipLaunchKernelGGL((store_kernel<HD, MODE, EPL, RPL, NTL, NTS, CONTIG, TPB, false, ORD>), dim3(grid), dim3(TPB),
+                       0, static_cast<hipStream_t>(stream), p);
     return static_cast<int>(hipGetLastError());
+}
+
+template <int HD, int MODE, int EPL, int RPL, bool NTL, bool NTS, bool CONTIG = false, int TPB = 256>
+int launch_store_v(const StoreLaunch& a, void* stream) {
+    const StoreArgs p = make_store_args(a);
+    if constexpr (store_follows_order(HD, MODE)) {
+        if (a.order != nullptr)
+            return launch_store_o<HD, MODE, EPL, RPL, NTL, NTS, CONTIG, TPB, true>(p, a.num_rows, a.num_kv_heads,
+                                                                                  stream);
+    }
+    return launch_store_o<HD, MODE, EPL, RPL, NTL, NTS, CONTIG, TPB, false>(p, a.num_rows, a.num_kv_heads, stream);
 }
 
 template <int HD, int MODE, int CB, int U, bool NTS, bool LDSS, int TPB = 256>

@@ -77,6 +77,9 @@ int main(void) {
           "buffer too small");
     CHECK(kvq_store(NULL, 0, NULL, NULL, NULL, 1, KVQ_FP8_PER_TOKEN_HEAD, NULL, NULL) == KVQ_ERR_INVALID_ARG,
           "store without a cache");
+    CHECK(kvq_store_ordered(NULL, 0, NULL, NULL, NULL, NULL, 1, KVQ_FP8_PER_TOKEN_HEAD, NULL, NULL) ==
+              KVQ_ERR_INVALID_ARG,
+          "ordered store without a cache");
     CHECK(kvq_status_string(KVQ_ERR_HIP) != NULL && strlen(kvq_status_string(KVQ_ERR_HIP)) > 0, "status string");
 
     /* static scales: RN32(amax / 448); a zero maximum gives the smallest

@@ -182,8 +182,16 @@ void drive_abi(Rng& r) {
                 const bool with = r.p(0.5);
                 // mostly the layer's own mode, so that the launch path is reached often
                 const int mode = (layer >= 0 && layer < nl && r.p(0.8)) ? modes[layer] : static_cast<int>(r.in(0, 5));
-                st = kvq_store(c, layer, fake_ptr(r), fake_ptr(r), static_cast<const int64_t*>(fake_ptr(r)), n,
-                               static_cast<kvq_mode>(mode), with ? sc : nullptr, nullptr);
+                if (r.p(0.5)) {
+                    st = kvq_store(c, layer, fake_ptr(r), fake_ptr(r), static_cast<const int64_t*>(fake_ptr(r)), n,
+                                   static_cast<kvq_mode>(mode), with ? sc : nullptr, nullptr);
+                } else {
+                    const int32_t* order = static_cast<const int32_t*>(fake_ptr(r));
+                    st = kvq_store_ordered(c, layer, fake_ptr(r), fake_ptr(r),
+                                           static_cast<const int64_t*>(fake_ptr(r)), order, n,
+                                           static_cast<kvq_mode>(mode), with ? sc : nullptr, nullptr);
+                    CHECK(!(n > 0 && order == nullptr && st == KVQ_OK), "ordered store without an order refused");
+                }
             } else if (op == 1) {
                 st = kvq_gather_dequant(c, layer, static_cast<const int32_t*>(fake_ptr(r)),
                                         static_cast<int32_t>(r.in(-1, 70)), static_cast<const int32_t*>(fake_ptr(r)),

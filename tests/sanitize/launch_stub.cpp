@@ -39,6 +39,7 @@ int launch_store(const StoreLaunch& a, void*) {
     require(a.num_rows > 0 && a.num_rows < (int64_t{1} << 31), "store rows");
     require(a.num_rows % a.num_kv_heads == 0, "store rows are whole tokens");
     require(a.keys && a.values && a.slots, "store inputs");
+    require((reinterpret_cast<uintptr_t>(a.order) & 3u) == 0, "store order aligned");
     require(a.block_bytes % 16 == 0 && a.code_bytes <= a.block_bytes, "store block bytes");
     require(a.num_slots % (int64_t{1} << a.bs_log2) == 0, "store slots are whole blocks");
     inside_cache(a.layer, (a.num_slots >> a.bs_log2) * a.block_bytes, "store layer inside the cache");

@@ -48,6 +48,25 @@ class Pair:
         sc = None if orc_scales is None else np.asarray(orc_scales, np.float32)
         self.orc.store(self.g, self.host, layer, _bits(k), _bits(v), slots.cpu().numpy(), sc)
 
+    def store_ordered(self, layer, k, v, slots, order, scales=None, orc_scales=None, followed=True):
+        """The device side takes the tokens in `order` (kvq_store_ordered);
+        the oracle stores, in token order, the tokens the order names (an
+        entry outside [0, n) names none) where the layer follows the order,
+        else every token: the same cache bytes."""
+        n = int(slots.numel())
+        self.cache.store(layer, k.to(DEV), v.to(DEV), slots.to(DEV), scales,
+                         order=torch.as_tensor(order, dtype=torch.int32).to(DEV))
+        o = np.asarray(order, np.int64)
+        named = np.zeros(n, bool)
+        named[o[(o >= 0) & (o < n)]] = True
+        if not followed:
+            named[:] = True
+        kept = np.where(named, slots.cpu().numpy(), -1).astype(np.int64)
+        if orc_scales is None:
+            orc_scales = scales
+        sc = None if orc_scales is None else np.asarray(orc_scales, np.float32)
+        self.orc.store(self.g, self.host, layer, _bits(k), _bits(v), kept, sc)
+
     def assert_buffers_equal(self):
         torch.cuda.synchronize()
         dev = self.cache.buffer.cpu().numpy()
@@ -157,6 +176,42 @@ def test_store_gather_parity_small(kvq, orc, mode, hd, hkv):
     pair.gather_and_compare(1, bt, seq_lens)
     pair.gather_and_compare(1, bt, [3, -4, 12 * bs])
     pair.cache.close()
+
+
+@pytest.mark.parametrize("mode", MODES, ids=[W.MODE_NAMES[m] for m in MODES])
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("hkv", [1, 8])
+def test_store_ordered_parity(kvq, orc, mode, hd, hkv):
+    """kvq_store_ordered: the tokens taken in slot order, in a random order,
+    and in an order with entries outside [0, n) and a repeated token; every
+    cache byte against the oracle.  Layers that follow the order (FP8 and
+    BF16 at head_dim >= 128) store exactly the tokens it names; the others
+    take every token in its own order."""
+    _flush(f"[ordered] mode={W.MODE_NAMES[mode]} hd={hd} hkv={hkv}")
+    bs, nblocks, n = 16, 40, 437
+    rng = np.random.default_rng(77 + hd * 10 + hkv + 1000 * mode)
+    slots = rng.permutation(nblocks * bs)[:n].astype(np.int64)
+    slots[3] = -1
+    slots[n - 2] = nblocks * bs + 5
+    scales = None
+    if mode == W.FP8_PER_TENSOR:
+        scales = [0.017, 0.011]
+    elif mode == W.FP8_PER_HEAD:
+        scales = list(rng.uniform(0.001, 0.05, 2 * hkv).astype(np.float32))
+    broken = rng.permutation(n).astype(np.int64)
+    broken[10] = -3                          # names no token
+    broken[11] = n + 9                       # names no token
+    broken[12] = broken[13]                  # one token twice, another never
+    orders = {"slot": np.argsort(slots, kind="stable"), "random": rng.permutation(n), "broken": broken}
+    for name, order in orders.items():
+        pair = Pair(kvq, orc, bs, hkv, hd, [mode], [nblocks])
+        try:
+            k, v = _adversarial_kv(n, hkv, hd, seed=int(rng.integers(1 << 30)))
+            pair.store_ordered(0, k, v, torch.from_numpy(slots), order.astype(np.int32), scales,
+                               followed=bool(kvq._lib.kvq_store_follows_order(mode, hd)))
+            pair.assert_buffers_equal()
+        finally:
+            pair.cache.close()
 
 
 def _random_geometry(seed):
@@ -333,6 +388,36 @@ def test_gqa32_layer_full_size(kvq, orc, mode):
     pair.assert_buffers_equal()
     pair.gather_and_compare(0, bt.numpy(), [cfgw["seq_len"]] * cfgw["num_seqs"])
     pair.cache.close()
+
+
+@pytest.mark.parametrize("mode", [W.FP8_PER_TOKEN_HEAD, W.FP8_PER_TENSOR, W.FP8_PER_HEAD, W.INT4_PER_TOKEN_HEAD],
+                         ids=["fp8_per_token_head", "fp8_per_tensor", "fp8_per_head", "int4_per_token_head"])
+def test_gqa32_layer_full_size_slot_order(kvq, orc, mode):
+    """The GQA-32 layer call as the benchmark times it: 8 sequences x 4096
+    tokens under the permuted block table, stored in slot order
+    (kvq_store_ordered with argsort of the slots); every cache byte compared."""
+    cfgw = W.WORKLOADS["gqa32"]
+    layer = 9
+    _flush(f"[gqa32 slot order] mode={W.MODE_NAMES[mode]} layer={layer}")
+    n = cfgw["num_seqs"] * cfgw["seq_len"]
+    nblocks = n // 16
+    k, v = W.gqa_kv(n, 8, 128, seed=1000 + layer, device=DEV)
+    bt = W.permuted_block_table(cfgw["num_seqs"], cfgw["seq_len"] // 16, nblocks, seed=1000)
+    slots = W.slots_from_block_table(bt, [cfgw["seq_len"]] * cfgw["num_seqs"], 16)
+    order = np.argsort(slots.numpy(), kind="stable").astype(np.int32)
+    scales = orc_scales = None
+    if mode == W.FP8_PER_TENSOR:
+        scales = [1.0, 1.0]
+    elif mode == W.FP8_PER_HEAD:
+        kc, vc = W.gqa_kv(4096, 8, 128, seed=2000 + layer, device=DEV)
+        scales = C.hip_static_scales(kvq, kc, vc, mode)
+        orc_scales = C.oracle_static_scales(orc, kc, vc, mode)
+    pair = Pair(kvq, orc, 16, 8, 128, [mode], [nblocks])
+    try:
+        pair.store_ordered(0, k.cpu(), v.cpu(), slots, order, scales, orc_scales)
+        pair.assert_buffers_equal()
+    finally:
+        pair.cache.close()
 
 
 @pytest.mark.parametrize("tp,mode", [(8, W.FP8_PER_TOKEN_HEAD), (8, W.INT4_PER_TOKEN_HEAD), (2, W.FP8_PER_TOKEN_HEAD)],

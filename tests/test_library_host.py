@@ -143,6 +143,38 @@ def test_store_argument_checks(kvq):
         kvq.kvq_destroy_cache(h)
 
 
+def test_ordered_store_argument_checks(kvq):
+    """kvq_store_ordered: kvq_store's checks, plus a 4-byte aligned order that
+    may be NULL only for an empty call; and the host query of which layers
+    follow the order."""
+    lib = kvq._lib
+    cfg = _cfg(kvq, [kvq.FP8_PER_TOKEN_HEAD, kvq.FP8_PER_TENSOR, kvq.FP8_PER_HEAD, kvq.BF16])
+    h = _handle(kvq, cfg)
+    P = ctypes.c_void_p
+
+    def st(layer, n, mode, order=FAKE_DEV + 4096):
+        return lib.kvq_store_ordered(h, layer, P(FAKE_DEV), P(FAKE_DEV + 1024), P(FAKE_DEV + 2048), P(order), n,
+                                     mode, None, None)
+    try:
+        assert st(0, 1, kvq.FP8_PER_TOKEN_HEAD, order=0) == kvq.ERR_INVALID_ARG        # no order
+        assert st(0, 1, kvq.FP8_PER_TOKEN_HEAD, order=FAKE_DEV + 2) == kvq.ERR_INVALID_ARG
+        assert st(0, 0, kvq.FP8_PER_TOKEN_HEAD, order=0) == kvq.OK                    # empty: no order needed
+        assert st(4, 1, kvq.BF16) == kvq.ERR_INVALID_ARG
+        assert st(0, 1, kvq.INT4_PER_TOKEN_HEAD) == kvq.ERR_MODE_MISMATCH
+        assert st(0, -1, kvq.FP8_PER_TOKEN_HEAD) == kvq.ERR_INVALID_ARG
+        assert st(0, 1 << 30, kvq.FP8_PER_TOKEN_HEAD) == kvq.ERR_UNSUPPORTED
+    finally:
+        kvq.kvq_destroy_cache(h)
+    follows = lib.kvq_store_follows_order
+    for hd in (128, 256):
+        for m in (kvq.BF16, kvq.FP8_PER_TENSOR, kvq.FP8_PER_HEAD, kvq.FP8_PER_TOKEN_HEAD):
+            assert follows(m, hd) == 1, (m, hd)
+    for m in (kvq.BF16, kvq.FP8_PER_TENSOR, kvq.FP8_PER_HEAD, kvq.FP8_PER_TOKEN_HEAD, kvq.INT4_PER_TOKEN_HEAD):
+        assert follows(m, 64) == 0
+    assert follows(kvq.INT4_PER_TOKEN_HEAD, 128) == 0 and follows(kvq.INT4_PER_TOKEN_HEAD, 256) == 0
+    assert follows(kvq.FP8_PER_TOKEN_HEAD, 96) == 0 and follows(7, 128) == 0 and follows(-1, 128) == 0
+
+
 def test_odd_block_with_scales_is_unsupported(kvq):
     """An odd block_size * num_kv_heads makes per-token-head blocks 8 mod 16
     bytes long; the kernels' 16-byte accesses need 16-byte blocks."""
