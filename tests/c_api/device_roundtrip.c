@@ -79,10 +79,11 @@ int main(void) {
     const int32_t table[NBLK] = {5, 2, 7, 0, 3, 6, 1, 4};
     const int32_t len = NTOK;
     int64_t slots[NTOK];
+    int32_t order[NTOK];
     kvq_cache_config cfg;
     kvq_bytes bytes;
     kvq_cache* cache = NULL;
-    void *dcache, *dk, *dv, *dok, *dov, *dslots, *dtable, *dlen;
+    void *dcache, *dk, *dv, *dok, *dov, *dslots, *dorder, *dtable, *dlen;
     int layer, t, bad = 0;
 
     cfg.num_layers = 2;
@@ -101,6 +102,11 @@ int main(void) {
     HIP_OK(hipMalloc(&dok, sizeof ok));
     HIP_OK(hipMalloc(&dov, sizeof ov));
     HIP_OK(hipMalloc(&dslots, sizeof slots));
+    HIP_OK(hipMalloc(&dorder, sizeof order));
+    /* layer 1 goes through kvq_store_ordered (last token first; head_dim 64 keeps
+     * token order, with the same contents) */
+    for (t = 0; t < NTOK; ++t) order[t] = NTOK - 1 - t;
+    HIP_OK(hipMemcpy(dorder, order, sizeof order, hipMemcpyHostToDevice));
     HIP_OK(hipMalloc(&dtable, sizeof table));
     HIP_OK(hipMalloc(&dlen, sizeof len));
     HIP_OK(hipMemcpy(dslots, slots, sizeof slots, hipMemcpyHostToDevice));
@@ -113,7 +119,12 @@ int main(void) {
         make_rows(layer == 1, hk, hv);
         HIP_OK(hipMemcpy(dk, hk, sizeof hk, hipMemcpyHostToDevice));
         HIP_OK(hipMemcpy(dv, hv, sizeof hv, hipMemcpyHostToDevice));
-        if (kvq_store(cache, layer, dk, dv, (const int64_t*)dslots, NTOK, (kvq_mode)modes[layer], NULL, NULL) != KVQ_OK ||
+        const kvq_status sst =
+            layer == 0 ? kvq_store(cache, layer, dk, dv, (const int64_t*)dslots, NTOK, (kvq_mode)modes[layer], NULL,
+                                   NULL)
+                       : kvq_store_ordered(cache, layer, dk, dv, (const int64_t*)dslots, (const int32_t*)dorder, NTOK,
+                                           (kvq_mode)modes[layer], NULL, NULL);
+        if (sst != KVQ_OK ||
             kvq_gather_dequant(cache, layer, (const int32_t*)dtable, NBLK, (const int32_t*)dlen, 1, dok, dov,
                                NTOK, NULL) != KVQ_OK) {
             fprintf(stderr, "store/gather of layer %d\n", layer);
@@ -137,6 +148,7 @@ int main(void) {
     HIP_OK(hipFree(dok));
     HIP_OK(hipFree(dov));
     HIP_OK(hipFree(dslots));
+    HIP_OK(hipFree(dorder));
     HIP_OK(hipFree(dtable));
     HIP_OK(hipFree(dlen));
     if (bad) {
