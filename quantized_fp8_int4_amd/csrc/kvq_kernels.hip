@@ -186,13 +186,14 @@ __device__ __forceinline__ void store_row(const StoreArgs& p, uint32_t rowc, boo
 #pragma unroll
                 for (int k = 0; k < CPL; ++k) { ck[k] = encode_fp8<false, CLAMP>(kx[k], qk); cv[k] = encode_fp8<false, CLAMP>(vx[k], qv); }
             }
-            if constexpr (!CONTIG && HB == 128 && LPR == 8) {
+            if constexpr (!CONTIG && LPR == 8 && (2 * HB) % 128 == 0) {
                 // staged through the wave's LDS so that each store
                 // instruction writes whole 128-byte lines: lane sub of a row
-                // writes code bytes [16 sub, 16 sub + 16) of its K and V rows
-                // (two 64-byte half lines per instruction before; measured on
-                // the GQA-32 prefill: +3% in slot order, 0 to +2% in token
-                // order)
+                // writes bytes [128 l + 16 sub, +16) of the row's K|V codes
+                // (2 HB contiguous bytes), where each direct store had
+                // written 64-byte half lines.  Measured on 32768-token
+                // prefills: head_dim 128 +3% in slot order and 0 to +2% in
+                // token order, head_dim 64 +3%, head_dim 256 +2 to +3%.
                 __shared__ __attribute__((aligned(16))) uint8_t stage[4][8][2 * HB];
                 const uint32_t wv = (threadIdx.x >> 6) & 3u, rl = (threadIdx.x & 63u) / LPR;
                 uint8_t* const sr = &stage[wv][rl][0];
@@ -204,13 +205,16 @@ __device__ __forceinline__ void store_row(const StoreArgs& p, uint32_t rowc, boo
                 }
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                 __builtin_amdgcn_wave_barrier();
-                const uint4 kl = *reinterpret_cast<const uint4*>(sr + 16 * sub);
-                const uint4 vl = *reinterpret_cast<const uint4*>(sr + HB + 16 * sub);
+                // the row's K|V codes are 2 HB contiguous bytes: NL whole lines
+                constexpr int NL = 2 * HB / 128;
+                uint4 ln[NL];
+#pragma unroll
+                for (int l = 0; l < NL; ++l) ln[l] = *reinterpret_cast<const uint4*>(sr + 128 * l + 16 * sub);
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 if (write) {
-                    st16<NTS>(krow + 16 * sub, kl);
-                    st16<NTS>(vrow + 16 * sub, vl);
+#pragma unroll
+                    for (int l = 0; l < NL; ++l) st16<NTS>(krow + 128 * l + 16 * sub, ln[l]);
                 }
             } else if (write) {
                 if constexpr (CONTIG && CPL % 2 == 0) {
