@@ -160,7 +160,34 @@ __device__ __forceinline__ void store_row(const StoreArgs& p, uint32_t rowc, boo
 #pragma unroll
                 for (int k = 0; k < CPL; ++k) { ck[k] = encode_int4<false>(kx[k], qk); cv[k] = encode_int4<false>(vx[k], qv); }
             }
-            if (write) {
+            if constexpr (!CONTIG && LPR == 8 && (2 * HB) % 128 == 0) {
+                // whole-line stores through the wave's LDS, as for FP8 (a
+                // direct store wrote 4 bytes per lane, a quarter line per
+                // row): measured +2.8% at head_dim 128 and +6.8% at 256; at
+                // 64 a row's K|V codes are half a line and keep the direct
+                // stores
+                __shared__ __attribute__((aligned(16))) uint8_t stage4[4][8][2 * HB];
+                const uint32_t wv = (threadIdx.x >> 6) & 3u, rl = (threadIdx.x & 63u) / LPR;
+                uint8_t* const sr = &stage4[wv][rl][0];
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) {
+                    const uint32_t c = chunk_index<LPR, CPL, CONTIG>(k, sub);
+                    *reinterpret_cast<uint32_t*>(sr + c * 4) = ck[k];
+                    *reinterpret_cast<uint32_t*>(sr + HB + c * 4) = cv[k];
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                constexpr int NL = 2 * HB / 128;
+                uint4 ln[NL];
+#pragma unroll
+                for (int l = 0; l < NL; ++l) ln[l] = *reinterpret_cast<const uint4*>(sr + 128 * l + 16 * sub);
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                if (write) {
+#pragma unroll
+                    for (int l = 0; l < NL; ++l) st16<NTS>(krow + 128 * l + 16 * sub, ln[l]);
+                }
+            } else if (write) {
                 if constexpr (CONTIG && CPL % 2 == 0) {
 #pragma unroll
                     for (int k = 0; k < CPL; k += 2) {
